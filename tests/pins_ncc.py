@@ -1,0 +1,233 @@
+"""Pins for the u8 normalized-correlation oracle.
+
+Each ``pin_*`` function checks the oracle (or, with ``lib=``, another build
+of ``oracle.c``) against something other than itself: the hand-worked
+fixture, closed forms, invariants, brute force through numpy primitives and
+``numpy.corrcoef``.  They raise ``AssertionError`` on a mismatch.
+
+Definition followed: "The CUDA Handbook", section 15.5 "Instruction-Level
+Parallelism and DP4A" -- per window the unsigned sums SumI, SumISq, SumIT over
+8-bit pixels (the two-column accumulator fragment and the three DP4A lines);
+the template width is a multiple of four and the unsigned byte product is
+required (pixels above 127 must not turn negative); only SumIT pairs image and
+template lanes, so a byte-order slip shows in SumIT alone.  The coefficient is
+read as Pearson's r from the five sums, with 0 where a variance is zero.
+"""
+from __future__ import annotations
+
+import numpy as np
+from numpy.lib.stride_tricks import sliding_window_view
+
+import oracle
+from cross_correlation_amd.inputs import ncc_case, pitch_for, u8_uniform
+
+import _golden
+
+
+def _pad(img: np.ndarray, extra: int = 16) -> np.ndarray:
+    h, w = img.shape
+    out = np.zeros((h, pitch_for(w) + extra), dtype=np.uint8)
+    out[:, :w] = img
+    return out
+
+
+def _run(img: np.ndarray, tmpl: np.ndarray, lib=None) -> dict:
+    h, w = img.shape
+    return oracle.ncc_u8(_pad(img), w, h, tmpl, lib=lib)
+
+
+def _numpy_sums(img: np.ndarray, tmpl: np.ndarray):
+    """Brute force through numpy: every window as a strided view, int64 sums."""
+    win = sliding_window_view(img.astype(np.int64), tmpl.shape)
+    t = tmpl.astype(np.int64)
+    si = win.sum(axis=(2, 3))
+    sq = (win * win).sum(axis=(2, 3))
+    st = np.einsum("yxji,ji->yx", win, t)
+    return si, sq, st
+
+
+def pin_hand_worked(lib=None):
+    g = _golden.load("ncc_hand_2x6_t1x4.txt")
+    img = g["image"].astype(np.uint8)
+    tmpl = g["template"].astype(np.uint8)
+    r = _run(img, tmpl, lib)
+    for k in ("sum_i", "sum_isq", "sum_it"):
+        assert np.array_equal(r[k].astype(np.int64), g[k]), k
+    vt = float(g["v_t"][0, 0])
+    expect = g["num"].astype(np.float64) / np.sqrt(g["v_i"].astype(np.float64) * vt)
+    assert np.array_equal(r["coef"], expect.astype(np.float32))
+    assert np.allclose(r["coef64"], expect, rtol=0, atol=1e-15)
+
+
+def pin_sums_bruteforce(lib=None):
+    rng = np.random.default_rng(101)
+    for _ in range(12):
+        th = int(rng.integers(1, 7))
+        tw = 4 * int(rng.integers(1, 4))
+        h = th + int(rng.integers(0, 9))
+        w = tw + int(rng.integers(0, 13))
+        img = u8_uniform(rng, (h, w))
+        tmpl = u8_uniform(rng, (th, tw))
+        r = _run(img, tmpl, lib)
+        si, sq, st = _numpy_sums(img, tmpl)
+        assert np.array_equal(r["sum_i"].astype(np.int64), si)
+        assert np.array_equal(r["sum_isq"].astype(np.int64), sq)
+        assert np.array_equal(r["sum_it"].astype(np.int64), st)
+
+
+def pin_coef_corrcoef(lib=None):
+    """Textbook Pearson routine on random windows."""
+    rng = np.random.default_rng(102)
+    for th, tw, h, w in ((3, 4, 9, 13), (5, 8, 12, 20), (16, 16, 40, 40)):
+        img = u8_uniform(rng, (h, w))
+        tmpl = u8_uniform(rng, (th, tw))
+        r = _run(img, tmpl, lib)
+        for y in range(0, h - th + 1, 3):
+            for x in range(0, w - tw + 1, 5):
+                win = img[y:y + th, x:x + tw].astype(np.float64).ravel()
+                ref = np.corrcoef(win, tmpl.astype(np.float64).ravel())[0, 1]
+                assert abs(r["coef64"][y, x] - ref) <= 1e-12, (y, x)
+                assert r["coef"][y, x] == np.float32(r["coef64"][y, x])
+
+
+def pin_cut_template(lib=None):
+    """Cut from the image at (oy, ox): SumI = SumT, SumISq = SumIT = SumTSq, coef = 1."""
+    rng = np.random.default_rng(103)
+    img = u8_uniform(rng, (40, 61))
+    for ox in (8, 9, 10, 11, 20, 37):  # covers ox mod 4 = 0, 1, 2, 3
+        oy = int(rng.integers(0, 40 - 12))
+        tmpl = np.ascontiguousarray(img[oy:oy + 12, ox:ox + 16])
+        r = _run(img, tmpl, lib)
+        t = tmpl.astype(np.int64)
+        assert int(r["sum_i"][oy, ox]) == int(t.sum())
+        assert int(r["sum_isq"][oy, ox]) == int((t * t).sum())
+        assert int(r["sum_it"][oy, ox]) == int((t * t).sum())
+        assert r["coef"][oy, ox] == np.float32(1.0)
+
+
+def pin_delta_template(lib=None):
+    """T = t * e(ty, tx): SumIT(y, x) = t * I[y+ty][x+tx] -- the lane-order test."""
+    rng = np.random.default_rng(104)
+    img = u8_uniform(rng, (20, 37))
+    th, tw = 3, 12
+    for tx in range(tw):  # every byte lane of every template word
+        ty = tx % th
+        tmpl = np.zeros((th, tw), dtype=np.uint8)
+        tmpl[ty, tx] = 7
+        r = _run(img, tmpl, lib)
+        oh, ow = r["sum_it"].shape
+        expect = 7 * img[ty:ty + oh, tx:tx + ow].astype(np.int64)
+        assert np.array_equal(r["sum_it"].astype(np.int64), expect), tx
+
+
+def pin_asymmetric_lane_order(lib=None):
+    """A template whose four byte lanes all differ; reversing the bytes inside each
+    4-byte word must change SumIT while SumI and SumISq stay put."""
+    rng = np.random.default_rng(105)
+    img = u8_uniform(rng, (24, 50))
+    j, i = np.mgrid[0:8, 0:16]
+    tmpl = (1 + (i % 4) * 50 + j).astype(np.uint8)
+    swapped = tmpl.reshape(8, 4, 4)[:, :, ::-1].reshape(8, 16).copy()
+    a = _run(img, tmpl, lib)
+    b = _run(img, swapped, lib)
+    si, sq, st = _numpy_sums(img, tmpl)
+    assert np.array_equal(a["sum_it"].astype(np.int64), st)
+    assert np.array_equal(a["sum_i"], b["sum_i"]) and np.array_equal(a["sum_isq"], b["sum_isq"])
+    assert np.count_nonzero(a["sum_it"] != b["sum_it"]) > 0.9 * a["sum_it"].size
+
+
+def pin_all_255(lib=None):
+    """A saturated window: SumISq = 65025 N, which a signed byte product breaks."""
+    img = np.full((10, 24), 255, dtype=np.uint8)
+    rng = np.random.default_rng(106)
+    tmpl = u8_uniform(rng, (4, 8))
+    r = _run(img, tmpl, lib)
+    n = tmpl.size
+    assert np.all(r["sum_i"] == 255 * n)
+    assert np.all(r["sum_isq"] == 65025 * n)
+    assert np.all(r["sum_it"] == 255 * int(tmpl.astype(np.int64).sum()))
+    assert np.all(r["coef"] == 0.0)  # constant window -> zero variance -> 0
+
+
+def pin_complement(lib=None):
+    """I' = 255 - I: closed forms for the sums, and coef(I') = -coef(I)."""
+    rng = np.random.default_rng(107)
+    img = u8_uniform(rng, (30, 45))
+    tmpl = u8_uniform(rng, (6, 12))
+    a = _run(img, tmpl, lib)
+    b = _run((255 - img).astype(np.uint8), tmpl, lib)
+    n = tmpl.size
+    st = int(tmpl.astype(np.int64).sum())
+    si = a["sum_i"].astype(np.int64)
+    assert np.array_equal(b["sum_i"].astype(np.int64), 255 * n - si)
+    assert np.array_equal(b["sum_isq"].astype(np.int64), 65025 * n - 510 * si + a["sum_isq"].astype(np.int64))
+    assert np.array_equal(b["sum_it"].astype(np.int64), 255 * st - a["sum_it"].astype(np.int64))
+    assert np.max(np.abs(b["coef64"] + a["coef64"])) <= 1e-12
+
+
+def pin_affine(lib=None):
+    """Pearson's r ignores a positive affine map: coef(2I + 1) = coef(I) for I <= 127."""
+    rng = np.random.default_rng(108)
+    img = rng.integers(0, 128, size=(28, 40)).astype(np.uint8)
+    tmpl = u8_uniform(rng, (5, 8))
+    a = _run(img, tmpl, lib)
+    b = _run((2 * img + 1).astype(np.uint8), tmpl, lib)
+    assert np.max(np.abs(a["coef64"] - b["coef64"])) <= 1e-12
+
+
+def pin_constant(lib=None):
+    """Constant image or constant template: zero variance, coefficient 0; sums N c, N c^2."""
+    rng = np.random.default_rng(109)
+    tmpl = u8_uniform(rng, (4, 8))
+    r = _run(np.full((9, 17), 77, dtype=np.uint8), tmpl, lib)
+    n = tmpl.size
+    assert np.all(r["sum_i"] == 77 * n) and np.all(r["sum_isq"] == 77 * 77 * n)
+    assert np.all(r["coef"] == 0.0)
+    img = u8_uniform(rng, (9, 17))
+    r = _run(img, np.full((4, 8), 200, dtype=np.uint8), lib)
+    si, sq, st = _numpy_sums(img, np.full((4, 8), 200, dtype=np.uint8))
+    assert np.array_equal(r["sum_it"].astype(np.int64), st)
+    assert np.all(r["coef"] == 0.0)
+
+
+def pin_bounded(lib=None):
+    """Cauchy-Schwarz: |coef| <= 1 after rounding to fp32."""
+    rng = np.random.default_rng(110)
+    case = ncc_case("t", 111, 64, 80, 8, 16, image_kind="gradient", cut=True)
+    r = oracle.ncc_u8(case.image, case.width, case.height, case.tmpl, lib=lib)
+    assert np.all(np.abs(r["coef"]) <= 1.0)
+    img = rng.integers(0, 2, size=(20, 30)).astype(np.uint8) * 255
+    r = _run(img, img[3:7, 5:13].copy(), lib)
+    assert np.all(np.abs(r["coef"]) <= 1.0)
+
+
+def pin_points_and_rows(lib=None):
+    """Selected windows and row ranges agree with the full run."""
+    case = ncc_case("t", 112, 33, 50, 7, 8, cut=False)
+    full = oracle.ncc_u8(case.image, case.width, case.height, case.tmpl, lib=lib)
+    part = oracle.ncc_u8(case.image, case.width, case.height, case.tmpl, y_begin=5, y_end=19, lib=lib)
+    for k in ("sum_i", "sum_isq", "sum_it", "coef"):
+        assert np.array_equal(part[k], full[k][5:19])
+    rng = np.random.default_rng(113)
+    oh, ow = case.out_shape
+    ys = rng.integers(0, oh, 40)
+    xs = rng.integers(0, ow, 40)
+    pts = oracle.ncc_u8_points(case.image, case.width, case.height, case.tmpl, ys, xs, lib=lib)
+    for k in ("sum_i", "sum_isq", "sum_it", "coef"):
+        assert np.array_equal(pts[k], full[k][ys, xs])
+
+
+ALL_PINS = [
+    pin_hand_worked,
+    pin_sums_bruteforce,
+    pin_coef_corrcoef,
+    pin_cut_template,
+    pin_delta_template,
+    pin_asymmetric_lane_order,
+    pin_all_255,
+    pin_complement,
+    pin_affine,
+    pin_constant,
+    pin_bounded,
+    pin_points_and_rows,
+]
