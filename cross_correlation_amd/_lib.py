@@ -1,0 +1,97 @@
+"""ctypes binding of the C ABI declared in ``include/xcorr.h``.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libxcorr_hip.so``.  Loading fails loudly when the library has not
+been built; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libxcorr_hip.so")
+
+# Status codes (include/xcorr.h)
+XC_OK = 0
+XC_ERR_NULL = -1
+XC_ERR_SHAPE = -2
+XC_ERR_TEMPLATE_WIDTH = -3
+XC_ERR_OVERFLOW = -4
+XC_ERR_ALIGN = -5
+XC_ERR_HIP = -6
+XC_ERR_VARIANT = -7
+
+XC_NCC_AUTO = 0
+XC_NCC_DOT4_ILP = 1
+XC_NCC_DOT4_C1 = 2
+XC_NCC_SCALAR_C1 = 3
+
+XC_XCORR_AUTO = 0
+XC_XCORR_OVERLAP = 1
+XC_XCORR_BLOCKDIAG = 2
+
+XC_NCC_MAX_TEMPLATE_PIXELS = 66051
+
+# Every symbol the public header declares.
+EXPORTED = ("ncc_u8_run", "ncc_u8_run_variant", "xcorr_f32_run", "xcorr_f32_run_algo", "xc_status_str")
+
+
+class XcError(RuntimeError):
+    """A non-zero status returned by the library."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_str(status)} (status {status})")
+
+
+_lib = None
+
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+
+
+def load(path: str = LIB_PATH):
+    """Load ``libxcorr_hip.so`` (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(
+            f"{path} not found: build the HIP library first "
+            "(python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(path)
+    lib.ncc_u8_run.restype = _i
+    lib.ncc_u8_run.argtypes = [_vp, _i, _i, _i, _vp, _i, _i, _vp, _vp, _vp, _vp, _vp]
+    lib.ncc_u8_run_variant.restype = _i
+    lib.ncc_u8_run_variant.argtypes = [_vp, _i, _i, _i, _vp, _i, _i, _vp, _vp, _vp, _vp, _i, _vp]
+    lib.xcorr_f32_run.restype = _i
+    lib.xcorr_f32_run.argtypes = [_vp, _i, _vp, _i, _i, _i, _vp, _vp]
+    lib.xcorr_f32_run_algo.restype = _i
+    lib.xcorr_f32_run_algo.argtypes = [_vp, _i, _vp, _i, _i, _i, _vp, _i, _vp]
+    lib.xc_status_str.restype = ctypes.c_char_p
+    lib.xc_status_str.argtypes = [_i]
+    _lib = lib
+    return lib
+
+
+def status_str(status: int) -> str:
+    return load().xc_status_str(status).decode()
+
+
+def check(status: int, where: str) -> None:
+    if status != XC_OK:
+        raise XcError(status, where)
+
+
+def ncc_u8_run(image, width, height, pitch, tmpl, t_width, t_height, sum_i, sum_isq, sum_it, coef,
+               stream=None, variant=XC_NCC_AUTO) -> int:
+    """Raw call with integer device addresses (0 for NULL); returns the status."""
+    return load().ncc_u8_run_variant(image, width, height, pitch, tmpl, t_width, t_height,
+                                     sum_i or None, sum_isq or None, sum_it or None, coef or None,
+                                     variant, stream or None)
+
+
+def xcorr_f32_run(left, n_left, right, n_right, rows, cols, out, stream=None, algo=XC_XCORR_AUTO) -> int:
+    """Raw call with integer device addresses; returns the status."""
+    return load().xcorr_f32_run_algo(left, n_left, right, n_right, rows, cols, out, algo, stream or None)

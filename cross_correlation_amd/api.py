@@ -1,0 +1,79 @@
+"""Torch-facing wrappers: device memory and streams from PyTorch, every
+computation in the HIP library (``_lib``).  The u32 sums come back in int32
+tensors holding the 32-bit patterns (``.view(torch.uint32)`` or
+``numpy().view(np.uint32)`` recovers the unsigned values).
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+
+
+def _stream_handle(stream) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+def _device_u8(t: torch.Tensor, name: str) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or t.dtype != torch.uint8:
+        raise TypeError(f"{name} must be a uint8 CUDA tensor")
+    return t
+
+
+def ncc_u8(image: torch.Tensor, tmpl: torch.Tensor, *, width: int | None = None,
+           outputs=("sum_i", "sum_isq", "sum_it", "coef"), variant: int = _lib.XC_NCC_AUTO,
+           out: dict | None = None, stream=None) -> dict:
+    """Valid-mode u8 normalized correlation.
+
+    ``image`` is a [height, pitch] uint8 CUDA tensor (rows contiguous, pitch a
+    multiple of 16 bytes, only the first ``width`` columns are pixels);
+    ``tmpl`` a dense [t_height, t_width] uint8 CUDA tensor.  Returns a dict of
+    the requested outputs, each [out_h, out_w]; pass ``out`` to reuse buffers.
+    """
+    _device_u8(image, "image")
+    _device_u8(tmpl, "tmpl")
+    if image.dim() != 2 or image.stride(1) != 1 or tmpl.dim() != 2 or not tmpl.is_contiguous():
+        raise ValueError("image must be 2D with unit column stride; tmpl must be 2D contiguous")
+    height, pitch = image.shape[0], image.stride(0)
+    width = image.shape[1] if width is None else width
+    th, tw = tmpl.shape
+    oh, ow = height - th + 1, width - tw + 1
+    if out is None:
+        out = {}
+        for k in outputs:
+            dt = torch.float32 if k == "coef" else torch.int32
+            out[k] = torch.empty((max(oh, 0), max(ow, 0)), dtype=dt, device=image.device)
+    ptr = {k: (out[k].data_ptr() if k in out else 0) for k in ("sum_i", "sum_isq", "sum_it", "coef")}
+    st = _lib.ncc_u8_run(image.data_ptr(), width, height, pitch, tmpl.data_ptr(), tw, th,
+                         ptr["sum_i"], ptr["sum_isq"], ptr["sum_it"], ptr["coef"],
+                         _stream_handle(stream), variant)
+    _lib.check(st, "ncc_u8_run")
+    return out
+
+
+def xcorr_f32(left: torch.Tensor, right: torch.Tensor, *, algo: int = _lib.XC_XCORR_AUTO,
+              out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Full cross-correlation of every (left, right) pair.
+
+    ``left`` [n_left, rows, cols] and ``right`` [n_right, rows, cols] are
+    contiguous float32 CUDA tensors (2D inputs are taken as one matrix).
+    Returns [n_left, n_right, 2*rows-1, 2*cols-1] float32.
+    """
+    if left.dim() == 2:
+        left = left.unsqueeze(0)
+    if right.dim() == 2:
+        right = right.unsqueeze(0)
+    for t, n in ((left, "left"), (right, "right")):
+        if t.device.type != "cuda" or t.dtype != torch.float32 or not t.is_contiguous():
+            raise TypeError(f"{n} must be a contiguous float32 CUDA tensor")
+    nl, rows, cols = left.shape
+    nr = right.shape[0]
+    if tuple(right.shape[1:]) != (rows, cols):
+        raise ValueError("left and right matrices must share (rows, cols)")
+    if out is None:
+        out = torch.empty((nl, nr, 2 * rows - 1, 2 * cols - 1), dtype=torch.float32, device=left.device)
+    st = _lib.xcorr_f32_run(left.data_ptr(), nl, right.data_ptr(), nr, rows, cols, out.data_ptr(),
+                            _stream_handle(stream), algo)
+    _lib.check(st, "xcorr_f32_run")
+    return out

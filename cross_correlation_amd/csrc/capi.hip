@@ -1,0 +1,161 @@
+// capi.hip -- the library's C ABI (declared in include/xcorr.h): argument
+// validation on the host, kernel selection, launch on the caller's stream and
+// mapping of HIP errors to status codes.  No exception crosses this boundary.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.h"
+#include "xcorr.h"
+
+namespace {
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? XC_OK : XC_ERR_HIP; }
+
+// Host-side validation shared by both NCC entry points; fills `a` on success.
+int ncc_validate(const uint8_t *image, int width, int height, int pitch_bytes, const uint8_t *tmpl,
+                 int t_width, int t_height, uint32_t *sum_i, uint32_t *sum_isq, uint32_t *sum_it,
+                 float *coef, xc::NccArgs &a)
+{
+    if (!image || !tmpl)
+        return XC_ERR_NULL;
+    if (!sum_i && !sum_isq && !sum_it && !coef)
+        return XC_ERR_NULL;
+    if (width <= 0 || height <= 0 || t_width <= 0 || t_height <= 0 || pitch_bytes <= 0)
+        return XC_ERR_SHAPE;
+    if (t_width > width || t_height > height || pitch_bytes < width)
+        return XC_ERR_SHAPE;
+    if (t_width % 4 != 0)
+        return XC_ERR_TEMPLATE_WIDTH;
+    if ((int64_t)t_width * t_height > XC_NCC_MAX_TEMPLATE_PIXELS)
+        return XC_ERR_OVERFLOW;
+    const int64_t out_w = width - t_width + 1, out_h = height - t_height + 1;
+    if (out_w * out_h > INT32_MAX || (int64_t)height * pitch_bytes > ((int64_t)1 << 40))
+        return XC_ERR_OVERFLOW;
+    if (!aligned(image, 16) || pitch_bytes % 16 != 0 || !aligned(tmpl, 4))
+        return XC_ERR_ALIGN;
+    if ((sum_i && !aligned(sum_i, 4)) || (sum_isq && !aligned(sum_isq, 4)) || (sum_it && !aligned(sum_it, 4)) ||
+        (coef && !aligned(coef, 4)))
+        return XC_ERR_ALIGN;
+    a.image = image;
+    a.width = width;
+    a.height = height;
+    a.pitch = pitch_bytes;
+    a.tmpl = tmpl;
+    a.t_width = t_width;
+    a.t_height = t_height;
+    a.sum_i = sum_i;
+    a.sum_isq = sum_isq;
+    a.sum_it = sum_it;
+    a.coef = coef;
+    a.out_w = (int)out_w;
+    a.out_h = (int)out_h;
+    a.hc = a.cw = a.lds_stride = 0;
+    return XC_OK;
+}
+
+int xcorr_validate(const float *left, int n_left, const float *right, int n_right, int rows, int cols,
+                   float *out, xc::XcorrArgs &a)
+{
+    if (!left || !right || !out)
+        return XC_ERR_NULL;
+    if (n_left <= 0 || n_right <= 0 || rows <= 0 || cols <= 0)
+        return XC_ERR_SHAPE;
+    const int64_t per_pair = (int64_t)(2 * (int64_t)rows - 1) * (2 * (int64_t)cols - 1);
+    if (per_pair > INT32_MAX || (int64_t)rows * cols > INT32_MAX)
+        return XC_ERR_OVERFLOW;
+    if ((int64_t)n_left * n_right > ((int64_t)1 << 40) / per_pair)
+        return XC_ERR_OVERFLOW;
+    if (!aligned(left, 16) || !aligned(right, 16) || !aligned(out, 4))
+        return XC_ERR_ALIGN;
+    a.left = left;
+    a.right = right;
+    a.out = out;
+    a.n_left = n_left;
+    a.n_right = n_right;
+    a.rows = rows;
+    a.cols = cols;
+    return XC_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+int ncc_u8_run_variant(const uint8_t *image, int width, int height, int pitch_bytes, const uint8_t *tmpl,
+                       int t_width, int t_height, uint32_t *sum_i, uint32_t *sum_isq, uint32_t *sum_it,
+                       float *coef, int variant, void *stream)
+{
+    xc::NccArgs a;
+    const int st = ncc_validate(image, width, height, pitch_bytes, tmpl, t_width, t_height, sum_i, sum_isq,
+                                sum_it, coef, a);
+    if (st != XC_OK)
+        return st;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    switch (variant) {
+    case XC_NCC_AUTO:
+    case XC_NCC_DOT4_ILP:
+        return hip_status(xc::ncc_launch_ilp(a, s));
+    case XC_NCC_DOT4_C1:
+        return hip_status(xc::ncc_launch_c1(a, true, s));
+    case XC_NCC_SCALAR_C1:
+        return hip_status(xc::ncc_launch_c1(a, false, s));
+    default:
+        return XC_ERR_VARIANT;
+    }
+}
+
+int ncc_u8_run(const uint8_t *image, int width, int height, int pitch_bytes, const uint8_t *tmpl, int t_width,
+               int t_height, uint32_t *sum_i, uint32_t *sum_isq, uint32_t *sum_it, float *coef, void *stream)
+{
+    return ncc_u8_run_variant(image, width, height, pitch_bytes, tmpl, t_width, t_height, sum_i, sum_isq, sum_it,
+                              coef, XC_NCC_AUTO, stream);
+}
+
+int xcorr_f32_run_algo(const float *left, int n_left, const float *right, int n_right, int rows, int cols,
+                       float *out, int algo, void *stream)
+{
+    xc::XcorrArgs a;
+    const int st = xcorr_validate(left, n_left, right, n_right, rows, cols, out, a);
+    if (st != XC_OK)
+        return st;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    switch (algo) {
+    case XC_XCORR_AUTO:
+        if (xc::xcorr_blockdiag_supported(a))
+            return hip_status(xc::xcorr_launch_blockdiag(a, s));
+        return hip_status(xc::xcorr_launch_overlap(a, s));
+    case XC_XCORR_OVERLAP:
+        return hip_status(xc::xcorr_launch_overlap(a, s));
+    case XC_XCORR_BLOCKDIAG:
+        if (!xc::xcorr_blockdiag_supported(a))
+            return XC_ERR_SHAPE;
+        return hip_status(xc::xcorr_launch_blockdiag(a, s));
+    default:
+        return XC_ERR_VARIANT;
+    }
+}
+
+int xcorr_f32_run(const float *left, int n_left, const float *right, int n_right, int rows, int cols, float *out,
+                  void *stream)
+{
+    return xcorr_f32_run_algo(left, n_left, right, n_right, rows, cols, out, XC_XCORR_AUTO, stream);
+}
+
+const char *xc_status_str(int status)
+{
+    switch (status) {
+    case XC_OK: return "success";
+    case XC_ERR_NULL: return "a required pointer is NULL, or no output was requested";
+    case XC_ERR_SHAPE: return "a size is not positive, the template is larger than the image, or the shape is not supported by the chosen algorithm";
+    case XC_ERR_TEMPLATE_WIDTH: return "template width is not a multiple of 4";
+    case XC_ERR_OVERFLOW: return "template area over 66,051 pixels (32-bit sums could wrap) or an index range exceeded";
+    case XC_ERR_ALIGN: return "a base pointer or the row pitch is not suitably aligned (16 bytes for images and matrices)";
+    case XC_ERR_HIP: return "HIP launch or runtime error (or no device)";
+    case XC_ERR_VARIANT: return "unknown variant or algorithm selector";
+    default: return "unknown status";
+    }
+}
+
+} // extern "C"

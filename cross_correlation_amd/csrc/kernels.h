@@ -1,0 +1,42 @@
+// kernels.h -- internal interface between the C ABI (capi.hip) and the gfx950
+// kernels of this library.  Not installed; the public interface is
+// include/xcorr.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace xc {
+
+// Arguments of every u8 normalized-correlation kernel (validated on the host).
+struct NccArgs {
+    const uint8_t *image;
+    int width, height, pitch;
+    const uint8_t *tmpl;
+    int t_width, t_height;
+    uint32_t *sum_i, *sum_isq, *sum_it;
+    float *coef;
+    int out_w, out_h;
+    // chunking of the template, chosen by the launcher
+    int hc;          // template rows per chunk
+    int cw;          // template words (4 bytes) per chunk
+    int lds_stride;  // LDS words per staged image row
+};
+
+hipError_t ncc_launch_ilp(NccArgs a, hipStream_t s);
+hipError_t ncc_launch_c1(NccArgs a, bool dot4, hipStream_t s);
+
+// Arguments of the fp32 cross-correlation kernels (validated on the host).
+struct XcorrArgs {
+    const float *left;
+    const float *right;
+    float *out;
+    int n_left, n_right;
+    int rows, cols;
+};
+
+hipError_t xcorr_launch_overlap(const XcorrArgs &a, hipStream_t s);
+hipError_t xcorr_launch_blockdiag(const XcorrArgs &a, hipStream_t s);
+bool xcorr_blockdiag_supported(const XcorrArgs &a);
+
+} // namespace xc

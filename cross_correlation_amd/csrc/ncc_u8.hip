@@ -1,0 +1,348 @@
+// ncc_u8.hip -- gfx950 kernels for valid-mode 8-bit normalized correlation.
+//
+// What is computed ("The CUDA Handbook", ch. 15 "Image Processing: Normalized
+// Correlation", section 15.5 "Instruction-Level Parallelism and DP4A"): for
+// every window the unsigned sums SumI, SumISq and SumIT over the window's
+// bytes, then Pearson's coefficient from them and the template sums.
+//
+// How it maps to CDNA4 (prior art on the page: DP4A over packed bytes, two
+// independent output columns per thread, a funnel shift to line the image
+// bytes up with the template bytes; kept, and re-shaped for wave64):
+//   * v_dot4_u32_u8 (__builtin_amdgcn_udot4) replaces DP4A: one instruction
+//     multiplies four unsigned byte lanes pairwise and adds them to a u32.
+//     Three per packed word and output: against 0x01010101 (SumI), against
+//     itself (SumISq) and against the template word (SumIT).
+//   * v_alignbyte_b32 replaces the funnel shift: output column x reads bytes
+//     x+4i .. x+4i+3, taken from the two aligned LDS words straddling them.
+//     Lane b of a packed word is pixel offset b (little-endian) in both the
+//     image word and the template word, so SumIT pairs matching pixels.
+//   * Each lane owns 4 adjacent columns (one aligned word group: shift 0 is
+//     free, shifts 1..3 cost one alignbyte each) and Q output rows.  The loop
+//     walks image rows: every image word loaded from LDS and its three shifts
+//     serve all Q rows the lane owns (template row j = image row - output
+//     row), so the shifts are amortised over 12*Q dot4 per word.  The 3*4*Q
+//     accumulator chains are independent, which supplies the ILP the page
+//     found essential.
+//   * The template row for each (image row, output row) pair is wave-uniform,
+//     so it is read with scalar loads and fed to v_dot4 straight from SGPRs.
+//   * Image tiles are staged into LDS with 16-byte loads (the page's uint4
+//     versus int finding: wide coalesced copies into on-chip memory).
+//   * The epilogue forms num, vI, vT exactly in 64-bit integers and divides in
+//     fp64, so the coefficient is the correctly rounded fp32 of the fp64 value.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.h"
+
+namespace xc {
+
+__device__ __forceinline__ uint32_t dot4u(uint32_t a, uint32_t b, uint32_t c)
+{
+    return __builtin_amdgcn_udot4(a, b, c, false);
+}
+
+__device__ __forceinline__ uint32_t shift_bytes(uint32_t hi, uint32_t lo, uint32_t s)
+{
+    // ({hi, lo} >> 8*s)[31:0]: bytes s..s+3 of the little-endian pair lo, hi.
+    return __builtin_amdgcn_alignbyte(hi, lo, s);
+}
+
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v)
+{
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1)
+        v += (uint32_t)__shfl_xor((int)v, m, 64);
+    return v;
+}
+
+// Copy image rows [gy0, gy0 + nrows) x 16-byte chunks [gx0, gx0 + 16*nchunks)
+// into LDS (row stride `stride` words).  Rows at or past `height` and chunks
+// at or past `pitch` are zero-filled, so no load leaves the image allocation.
+__device__ __forceinline__ void stage_tile(const uint8_t *__restrict__ image, int height, int pitch,
+                                           int gy0, int gx0, int nrows, int nchunks,
+                                           uint32_t *lds, int stride)
+{
+    const int total = nrows * nchunks;
+    for (int t = threadIdx.x; t < total; t += blockDim.x) {
+        const int r = t / nchunks;
+        const int b = t - r * nchunks;
+        const int gy = gy0 + r;
+        const int gx = gx0 + 16 * b;
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (gy < height && gx < pitch)
+            v = *reinterpret_cast<const uint4 *>(image + (size_t)gy * pitch + gx);
+        *reinterpret_cast<uint4 *>(lds + r * stride + 4 * b) = v;
+    }
+}
+
+// SumT and SumTSq over the whole template (every wave computes them; cheap).
+__device__ __forceinline__ void template_sums(const uint32_t *__restrict__ tw, int nwords,
+                                              uint32_t &sum_t, uint32_t &sum_tsq)
+{
+    const int lane = threadIdx.x & 63;
+    uint32_t a = 0, b = 0;
+    for (int k = lane; k < nwords; k += 64) {
+        const uint32_t w = tw[k];
+        a = dot4u(w, 0x01010101u, a);
+        b = dot4u(w, w, b);
+    }
+    sum_t = wave_sum_u32(a);
+    sum_tsq = wave_sum_u32(b);
+}
+
+// Exact epilogue for one window; writes whichever outputs are requested.
+__device__ __forceinline__ void ncc_store(const NccArgs &a, size_t o, uint32_t si, uint32_t sq, uint32_t st,
+                                          int64_t n, int64_t sum_t, int64_t vt)
+{
+    if (a.sum_i) a.sum_i[o] = si;
+    if (a.sum_isq) a.sum_isq[o] = sq;
+    if (a.sum_it) a.sum_it[o] = st;
+    if (a.coef) {
+        const int64_t num = n * (int64_t)st - (int64_t)si * sum_t;
+        const int64_t vi = n * (int64_t)sq - (int64_t)si * (int64_t)si;
+        double c = 0.0;
+        if (vi != 0 && vt != 0)
+            c = (double)num / sqrt((double)vi * (double)vt);
+        a.coef[o] = (float)c;
+    }
+}
+
+// One image row of one template chunk: for each template word k of the chunk
+// load the next aligned image word, form the three shifted words, and for each
+// output row q the row serves, accumulate 3 x 4 dot4 with template row (rl - q).
+template <int Q, int WC, bool FULL>
+__device__ __forceinline__ void ncc_row(const uint32_t *rp, const uint32_t *__restrict__ t0, int nw, int cw,
+                                        int qlo, int qhi, uint32_t (&ai)[Q][4], uint32_t (&aq)[Q][4],
+                                        uint32_t (&at)[Q][4])
+{
+    uint32_t w0 = rp[0];
+    for (int kb = 0; kb < cw; kb += WC) {
+#pragma unroll
+        for (int kk = 0; kk < WC; ++kk) {
+            const int k = kb + kk;
+            const uint32_t w1 = rp[k + 1];
+            uint32_t s[4];
+            s[0] = w0;
+            s[1] = shift_bytes(w1, w0, 1);
+            s[2] = shift_bytes(w1, w0, 2);
+            s[3] = shift_bytes(w1, w0, 3);
+#pragma unroll
+            for (int q = 0; q < Q; ++q) {
+                if (FULL || (q >= qlo && q <= qhi)) {
+                    const uint32_t t = t0[k - q * nw];
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        ai[q][c] = dot4u(s[c], 0x01010101u, ai[q][c]);
+                        aq[q][c] = dot4u(s[c], s[c], aq[q][c]);
+                        at[q][c] = dot4u(s[c], t, at[q][c]);
+                    }
+                }
+            }
+            w0 = w1;
+        }
+    }
+}
+
+// Main kernel: a workgroup of WV waves covers 256 output columns x WV*Q rows;
+// wave w owns rows [w*Q, w*Q + Q) of the tile, lane l owns columns 4l..4l+3.
+template <int Q, int WV, int WC>
+__global__ __launch_bounds__(64 * WV) void ncc_u8_ilp_kernel(NccArgs a)
+{
+    extern __shared__ uint32_t lds[];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int x0 = blockIdx.x * 256;
+    const int y0 = blockIdx.y * (WV * Q);
+    const int nw = a.t_width >> 2;
+    const uint32_t *__restrict__ tw = reinterpret_cast<const uint32_t *>(a.tmpl);
+
+    uint32_t sum_t, sum_tsq;
+    template_sums(tw, nw * a.t_height, sum_t, sum_tsq);
+
+    uint32_t ai[Q][4], aq[Q][4], at[Q][4];
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            ai[q][c] = aq[q][c] = at[q][c] = 0u;
+
+    const int stride = a.lds_stride;
+    for (int jc = 0; jc < a.t_height; jc += a.hc) {
+        const int hc = min(a.hc, a.t_height - jc);
+        for (int ic = 0; ic < nw; ic += a.cw) {
+            const int cw = min(a.cw, nw - ic);
+            __syncthreads();
+            // lane l reads words l + k and l + k + 1, k < cw: 64 + cw words per row
+            stage_tile(a.image, a.height, a.pitch, y0 + jc, x0 + 4 * ic, WV * Q + hc - 1,
+                       (64 + cw + 3) / 4, lds, stride);
+            __syncthreads();
+            const uint32_t *wrow = lds + (wave * Q) * stride + lane;
+            for (int rl = 0; rl < Q + hc - 1; ++rl) {
+                const int qlo = max(0, rl - hc + 1);
+                const int qhi = min(Q - 1, rl);
+                const uint32_t *t0 = tw + (size_t)(jc + rl) * nw + ic;
+                if (qlo == 0 && qhi == Q - 1)
+                    ncc_row<Q, WC, true>(wrow + rl * stride, t0, nw, cw, qlo, qhi, ai, aq, at);
+                else
+                    ncc_row<Q, WC, false>(wrow + rl * stride, t0, nw, cw, qlo, qhi, ai, aq, at);
+            }
+        }
+    }
+
+    const int64_t n = (int64_t)a.t_width * a.t_height;
+    const int64_t st64 = sum_t;
+    const int64_t vt = n * (int64_t)sum_tsq - st64 * st64;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        const int y = y0 + wave * Q + q;
+        if (y >= a.out_h)
+            break;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int x = x0 + 4 * lane + c;
+            if (x < a.out_w)
+                ncc_store(a, (size_t)y * a.out_w + x, ai[q][c], aq[q][c], at[q][c], n, st64, vt);
+        }
+    }
+}
+
+// Ablation kernels: one output per thread, a 64 x 4 tile per workgroup, the
+// image tile in LDS.  DOT4 selects packed-byte dot products; otherwise the
+// bytes are multiplied and added one at a time.  Each thread runs one
+// dependent chain per sum, as the page's baseline kernels do.
+template <bool DOT4>
+__global__ __launch_bounds__(256) void ncc_u8_c1_kernel(NccArgs a)
+{
+    extern __shared__ uint32_t lds[];
+    const int tx = threadIdx.x & 63;
+    const int ty = threadIdx.x >> 6;
+    const int x0 = blockIdx.x * 64;
+    const int y0 = blockIdx.y * 4;
+    const int nw = a.t_width >> 2;
+    const uint32_t *__restrict__ tw = reinterpret_cast<const uint32_t *>(a.tmpl);
+
+    uint32_t sum_t, sum_tsq;
+    template_sums(tw, nw * a.t_height, sum_t, sum_tsq);
+
+    uint32_t si = 0, sq = 0, st = 0;
+    const int stride = a.lds_stride;
+    const uint32_t sh = (uint32_t)(tx & 3);
+    for (int jc = 0; jc < a.t_height; jc += a.hc) {
+        const int hc = min(a.hc, a.t_height - jc);
+        for (int ic = 0; ic < nw; ic += a.cw) {
+            const int cw = min(a.cw, nw - ic);
+            __syncthreads();
+            // thread tx reads words tx/4 + k and tx/4 + k + 1, k < cw: 16 + cw words per row
+            stage_tile(a.image, a.height, a.pitch, y0 + jc, x0 + 4 * ic, 4 + hc - 1, (16 + cw + 3) / 4,
+                       lds, stride);
+            __syncthreads();
+            for (int j = 0; j < hc; ++j) {
+                const uint32_t *rp = lds + (ty + j) * stride + (tx >> 2);
+                const uint32_t *tr = tw + (size_t)(jc + j) * nw + ic;
+                for (int k = 0; k < cw; ++k) {
+                    const uint32_t i4 = shift_bytes(rp[k + 1], rp[k], sh);
+                    const uint32_t t4 = tr[k];
+                    if (DOT4) {
+                        si = dot4u(i4, 0x01010101u, si);
+                        sq = dot4u(i4, i4, sq);
+                        st = dot4u(i4, t4, st);
+                    } else {
+#pragma unroll
+                        for (int b = 0; b < 4; ++b) {
+                            const uint32_t p = (i4 >> (8 * b)) & 0xFFu;
+                            const uint32_t t = (t4 >> (8 * b)) & 0xFFu;
+                            si += p;
+                            sq += p * p;
+                            st += p * t;
+                        }
+                    }
+                }
+            }
+        }
+    }
+    const int y = y0 + ty;
+    const int x = x0 + tx;
+    if (y < a.out_h && x < a.out_w) {
+        const int64_t n = (int64_t)a.t_width * a.t_height;
+        const int64_t st64 = sum_t;
+        ncc_store(a, (size_t)y * a.out_w + x, si, sq, st, n, st64, n * (int64_t)sum_tsq - st64 * st64);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Host-side launch helpers (called by the C ABI after validation).
+
+template <int Q, int WV, int WC>
+static hipError_t launch_ilp(const NccArgs &a, hipStream_t s)
+{
+    dim3 grid((a.out_w + 255) / 256, (a.out_h + WV * Q - 1) / (WV * Q));
+    const size_t lds = (size_t)(WV * Q + a.hc - 1) * a.lds_stride * 4;
+    hipLaunchKernelGGL((ncc_u8_ilp_kernel<Q, WV, WC>), grid, dim3(64 * WV), lds, s, a);
+    return hipGetLastError();
+}
+
+template <int Q, int WV>
+static hipError_t dispatch_wc(const NccArgs &a, int wc, hipStream_t s)
+{
+    switch (wc) {
+    case 4: return launch_ilp<Q, WV, 4>(a, s);
+    case 2: return launch_ilp<Q, WV, 2>(a, s);
+    default: return launch_ilp<Q, WV, 1>(a, s);
+    }
+}
+
+// Chooses the tile (Q rows per lane, WV waves), the unroll WC and the chunking
+// so that the LDS tile stays within `lds_budget` bytes.
+hipError_t ncc_launch_ilp(NccArgs a, hipStream_t s)
+{
+    const int nw = a.t_width / 4;
+    // Unroll of the template-word loop: the largest power of two <= 4 dividing
+    // the words per row (a deeper unroll makes the compiler hold more template
+    // words in SGPRs than fit).
+    int wc = 4;
+    while (nw % wc) wc >>= 1;
+    // Tile shape: the big tile when the image yields enough work to fill
+    // 256 CUs, smaller ones for small images.
+    int q = 4, wv = 4;
+    const long col_tiles = (a.out_w + 255) / 256;
+    if (col_tiles * ((a.out_h + 15) / 16) < 256) { q = 2; wv = 2; }
+    if (col_tiles * ((a.out_h + 3) / 4) < 256) { q = 1; wv = 1; }
+    const int lds_budget = 64 * 1024;
+    // chunk of template words: a multiple of lcm(wc, 4) words
+    const int unit = wc < 4 ? 4 : wc;
+    int cw = nw;
+    const int max_cw = 1024 - 64;
+    if (cw > max_cw) cw = max_cw / unit * unit;
+    a.cw = cw;
+    a.lds_stride = (64 + cw + 3) / 4 * 4;
+    const int th = wv * q;
+    int hc = lds_budget / (a.lds_stride * 4) - th + 1;
+    if (hc < 1) hc = 1;
+    if (hc > a.t_height) hc = a.t_height;
+    a.hc = hc;
+    if (q == 4) return dispatch_wc<4, 4>(a, wc, s);
+    if (q == 2) return dispatch_wc<2, 2>(a, wc, s);
+    return dispatch_wc<1, 1>(a, wc, s);
+}
+
+hipError_t ncc_launch_c1(NccArgs a, bool dot4, hipStream_t s)
+{
+    const int nw = a.t_width / 4;
+    int cw = nw;
+    if (cw > 512) cw = 512;
+    a.cw = cw;
+    a.lds_stride = (16 + cw + 3) / 4 * 4;
+    int hc = (48 * 1024) / (a.lds_stride * 4) - 3;
+    if (hc < 1) hc = 1;
+    if (hc > a.t_height) hc = a.t_height;
+    a.hc = hc;
+    dim3 grid((a.out_w + 63) / 64, (a.out_h + 3) / 4);
+    const size_t lds = (size_t)(4 + hc - 1) * a.lds_stride * 4;
+    if (dot4)
+        hipLaunchKernelGGL((ncc_u8_c1_kernel<true>), grid, dim3(256), lds, s, a);
+    else
+        hipLaunchKernelGGL((ncc_u8_c1_kernel<false>), grid, dim3(256), lds, s, a);
+    return hipGetLastError();
+}
+
+} // namespace xc

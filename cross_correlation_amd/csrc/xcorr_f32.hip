@@ -1,0 +1,392 @@
+// xcorr_f32.hip -- gfx950 kernels for fp32 full 2D cross-correlation.
+//
+// What is computed (JPDC 2023 artifact README "Efficient GPU-accelerated
+// Parallel Cross-correlation"): for every (left, right) pair and every shift
+// (dy, dx) at which the matrices overlap, the sum of products over the
+// overlap:  out[y][x] = sum_{i,j} L[i+dy][j+dx] * R[i][j],
+// dy = y - (rows-1), dx = x - (cols-1).
+//
+// Two kernels:
+//
+// * xcorr_overlap_kernel -- the overlap-wise baseline the page compares
+//   against: one thread per output shift, no data reuse.
+//
+// * xcorr_bd_kernel -- the register-blocked kernel.  The page's kernels give
+//   each thread one or several neighbouring overlaps and cache the left rows
+//   in warp-wide register buffers moved by shuffles; a thread-per-overlap
+//   mapping leaves SIMT lanes idle wherever neighbouring overlaps have
+//   different extents.  Here every lane of a wave runs the *same* number of
+//   steps, with no idle work except a P-column border:
+//     - Rows are grouped into blocks of 4.  Lane (slot s, block b) owns right
+//       rows [4b, 4b+4) of pair s and pairs them with left row blocks
+//       kb1 = (b + delta) mod nb and kb2 = kb1 + 1 (mod nb), where delta is
+//       the wave's block diagonal.  Row pair (k, i) adds to dy = k - i, so
+//       block kb1 with in-block offsets a >= e gives dy = 4*delta + (a-e) and
+//       block kb2 with a < e gives dy = 4*delta + 4 + (a-e): the wave owns
+//       output rows 4*delta .. 4*delta+3 completely, and lanes whose block
+//       index wrapped past nb own the rows 4*delta - 4*nb .. +3 instead.  The
+//       16 (a, e) row pairs cover every row pair exactly once over all
+//       diagonals, so no lane ever multiplies outside the overlap in y.
+//     - Columns: a lane owns P shift classes c0 .. c0+P-1; class c yields
+//       dx = c (summed over j < w - c) and dx = c - w (j >= w - c).  Both are
+//       one walk over j with a P-wide sliding window of left columns kept in
+//       registers (the register buffer of the page, per lane instead of per
+//       warp); zero-filled LDS columns make the border exact.
+//     - Each step: one float4 of each of the two left blocks and one of the
+//       right block from LDS, 16 x P fp32 FMAs.
+//     - The per-lane partial sums of the same output are reduced across the
+//       wave through LDS in a fixed order (deterministic, no atomics): the
+//       split of one overlap over several lanes is the page's split-row idea.
+//   Left and right columns are staged into LDS chunk by chunk (double
+//   buffered, transposed to [block][column][4 rows] so one 16-byte read gives
+//   a lane its 4 rows of a column).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.h"
+
+namespace xc {
+
+// ---------------------------------------------------------------------------
+// Overlap-wise baseline: one thread per output shift.
+
+__global__ __launch_bounds__(256) void xcorr_overlap_kernel(XcorrArgs a)
+{
+    const int rows = a.rows, cols = a.cols;
+    const int ow = 2 * cols - 1;
+    const int per_pair = (2 * rows - 1) * ow;
+    const int idx = blockIdx.x * 256 + threadIdx.x;
+    if (idx >= per_pair)
+        return;
+    const int y = idx / ow;
+    const int x = idx - y * ow;
+    const int dy = y - (rows - 1);
+    const int dx = x - (cols - 1);
+    const int i0 = max(0, -dy), i1 = min(rows, rows - dy);
+    const int j0 = max(0, -dx), j1 = min(cols, cols - dx);
+    const int64_t npairs = (int64_t)a.n_left * a.n_right;
+    const size_t mat = (size_t)rows * cols;
+    for (int64_t p = blockIdx.y; p < npairs; p += gridDim.y) {
+        const int l = (int)(p / a.n_right);
+        const int r = (int)(p - (int64_t)l * a.n_right);
+        const float *L = a.left + (size_t)l * mat;
+        const float *R = a.right + (size_t)r * mat;
+        float acc = 0.0f;
+        for (int i = i0; i < i1; ++i) {
+            const float *lr = L + (size_t)(i + dy) * cols + dx;
+            const float *rr = R + (size_t)i * cols;
+            for (int j = j0; j < j1; ++j)
+                acc = fmaf(lr[j], rr[j], acc);
+        }
+        a.out[(size_t)p * per_pair + idx] = acc;
+    }
+}
+
+hipError_t xcorr_launch_overlap(const XcorrArgs &a, hipStream_t s)
+{
+    const int per_pair = (2 * a.rows - 1) * (2 * a.cols - 1);
+    const int64_t npairs = (int64_t)a.n_left * a.n_right;
+    dim3 grid((per_pair + 255) / 256, (unsigned)(npairs < 65535 ? npairs : 65535));
+    hipLaunchKernelGGL(xcorr_overlap_kernel, grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Block-diagonal register-blocked kernel.
+
+constexpr int BD_P = 4;  // shift classes (columns) per lane
+
+struct BdArgs {
+    XcorrArgs x;
+    int nb;          // row blocks of 4 (rows padded with zero rows to 4*nb)
+    int wp;          // columns padded with zero columns to a multiple of BD_P
+    int S;           // pairs per wave (slots); S * nb <= 64
+    int n_groups;    // pair groups of S pairs
+    int n_xtiles;    // wp / BD_P
+    int n_dgroups;   // ceil(nb / waves per workgroup)
+};
+
+// LDS geometry of one staging buffer for J walk steps.
+template <int J>
+struct BdLds {
+    static constexpr int NCL = (J + BD_P - 1) | 1;  // left columns per block (odd: spreads banks)
+    static constexpr int NCR = J | 1;               // right columns per block
+    static constexpr int NLR = J + BD_P - 1;        // left columns actually used
+};
+
+// One walk step range of a chunk: accumulate `nsteps` steps (multiple of P).
+template <int J>
+__device__ __forceinline__ void bd_compute(const float4 *Lb1, const float4 *Lb2, const float4 *Rb, int nsteps,
+                                           float (&acc1)[4][BD_P], float (&acc2)[3][BD_P])
+{
+    constexpr int P = BD_P;
+    float4 w1[P], w2[P];
+#pragma unroll
+    for (int p = 0; p < P - 1; ++p) {
+        w1[p] = Lb1[p];
+        w2[p] = Lb2[p];
+    }
+    for (int m0 = 0; m0 < nsteps; m0 += P) {
+#pragma unroll
+        for (int sp = 0; sp < P; ++sp) {
+            const int m = m0 + sp;
+            w1[(sp + P - 1) % P] = Lb1[m + P - 1];
+            w2[(sp + P - 1) % P] = Lb2[m + P - 1];
+            const float4 rv = Rb[m];
+            const float re[4] = {rv.x, rv.y, rv.z, rv.w};
+#pragma unroll
+            for (int p = 0; p < P; ++p) {
+                const float4 l1 = w1[(sp + p) % P];
+                const float4 l2 = w2[(sp + p) % P];
+                const float la[4] = {l1.x, l1.y, l1.z, l1.w};
+                const float lb[3] = {l2.x, l2.y, l2.z};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+#pragma unroll
+                    for (int ar = 0; ar < 4; ++ar) {
+                        if (ar >= e)
+                            acc1[ar - e][p] = fmaf(la[ar], re[e], acc1[ar - e][p]);
+                        else
+                            acc2[ar - e + 3][p] = fmaf(lb[ar], re[e], acc2[ar - e + 3][p]);
+                    }
+                }
+            }
+        }
+    }
+}
+
+template <int NW, int J>
+__global__ __launch_bounds__(64 * NW) void xcorr_bd_kernel(BdArgs a)
+{
+    constexpr int P = BD_P;
+    using G = BdLds<J>;
+    extern __shared__ float4 smem[];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    int bid = blockIdx.x;
+    const int dgrp = bid % a.n_dgroups;
+    bid /= a.n_dgroups;
+    const int xt = bid % a.n_xtiles;
+    const int grp = bid / a.n_xtiles;
+    const int c0 = xt * P;
+    const int nb = a.nb, S = a.S, wp = a.wp;
+    const int rows = a.x.rows, cols = a.x.cols;
+    const int h4 = 4 * nb;
+    const int64_t npairs = (int64_t)a.x.n_left * a.x.n_right;
+    const int delta = dgrp * NW + wave;  // this wave's block diagonal
+    const bool wave_on = delta < nb;
+
+    int s = lane / nb;
+    const int b = lane - s * nb;
+    if (s >= S) s = S - 1;  // spare lanes shadow the last slot; never stored
+    const int dl = wave_on ? delta : 0;
+    const int kb1 = (b + dl) % nb;
+    const int kb2 = (b + dl + 1) % nb;
+
+    // LDS: two staging buffers, each L [S][nb][NCL] then R [S][nb][NCR] (a
+    // float4 holds the 4 rows of a row block at one column), then the
+    // reduction area.
+    const int l_elems = S * nb * G::NCL;
+    const int buf_elems = l_elems + S * nb * G::NCR;
+    constexpr int NV = 4 * P;  // per-lane partial sums per side: (r, p)
+    float *const red = reinterpret_cast<float *>(smem + 2 * buf_elems);
+    float *const wred = red + wave * (NV * 64 + S * 3 * P);
+    float *const wextra = wred + NV * 64;
+
+    // Staging: thread t owns row block sb = t / NW (slot * nb + block, all
+    // S*nb <= 64 blocks) and the columns congruent to t mod NW.  One item is
+    // the 4 rows of that block at one column, stored as one float4; the NW
+    // threads of a block read consecutive columns (coalesced per row).
+    constexpr int LPT = (G::NLR + NW - 1) / NW;  // left items per thread
+    constexpr int RPT = J / NW;                   // right items per thread
+    static_assert(J % NW == 0, "J must be a multiple of the waves per workgroup");
+    const int tid = threadIdx.x;
+    const int sb = tid / NW;
+    const int cres = tid - sb * NW;
+    const int st_slot = sb / nb;
+    const int st_row0 = 4 * (sb - st_slot * nb);
+    const int64_t st_pair = (int64_t)grp * S + st_slot;
+    const bool st_on = sb < S * nb && st_pair < npairs;
+    const float *st_l = a.x.left;
+    const float *st_r = a.x.right;
+    if (st_on) {
+        const int l = (int)(st_pair / a.x.n_right);
+        const int r = (int)(st_pair - (int64_t)l * a.x.n_right);
+        st_l += ((size_t)l * rows + st_row0) * cols;
+        st_r += ((size_t)r * rows + st_row0) * cols;
+    }
+    const int nrow_ok = min(4, rows - st_row0);  // rows of the block inside the matrix
+    const int bstar = nb - dl - 1;  // the lane whose block 1 is unwrapped and block 2 wrapped
+    const int oh = 2 * rows - 1, ow = 2 * cols - 1;
+
+    for (int side = 0; side < 2; ++side) {
+        // Walk of this side: positive dx classes c (j from 0) or negative dx = c - wp.
+        const int j_first = side ? wp - c0 - P : 0;
+        const int j_end = side ? wp : wp - c0;
+        const int nch = (j_end - j_first + J - 1) / J;
+        const int lshift = side ? c0 - wp : c0;  // left column = j + lshift + window position
+
+        auto load4 = [&](const float *src, int gc) {
+            float4 val = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            if (st_on && nrow_ok > 0 && gc >= 0 && gc < cols) {
+                val.x = src[gc];
+                if (nrow_ok > 1) val.y = src[(size_t)cols + gc];
+                if (nrow_ok > 2) val.z = src[(size_t)2 * cols + gc];
+                if (nrow_ok > 3) val.w = src[(size_t)3 * cols + gc];
+            }
+            return val;
+        };
+        auto load_chunk = [&](int t, float4 (&vl)[LPT], float4 (&vr)[RPT]) {
+            const int ja = j_first + t * J;
+#pragma unroll
+            for (int k = 0; k < LPT; ++k)
+                vl[k] = load4(st_l, ja + lshift + cres + k * NW);
+#pragma unroll
+            for (int k = 0; k < RPT; ++k)
+                vr[k] = load4(st_r, ja + cres + k * NW);
+        };
+        auto store_chunk = [&](float4 *buf, const float4 (&vl)[LPT], const float4 (&vr)[RPT]) {
+            if (sb < S * nb) {
+#pragma unroll
+                for (int k = 0; k < LPT; ++k)
+                    if (cres + k * NW < G::NLR) buf[sb * G::NCL + cres + k * NW] = vl[k];
+#pragma unroll
+                for (int k = 0; k < RPT; ++k)
+                    buf[l_elems + sb * G::NCR + cres + k * NW] = vr[k];
+            }
+        };
+
+        float acc1[4][P], acc2[3][P];
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc1[r][p] = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 3; ++r) acc2[r][p] = 0.0f;
+        }
+
+        {
+            float4 vl[LPT], vr[RPT];
+            load_chunk(0, vl, vr);
+            store_chunk(smem, vl, vr);
+        }
+        __syncthreads();
+        for (int t = 0; t < nch; ++t) {
+            float4 vl[LPT], vr[RPT];
+            const bool more = t + 1 < nch;
+            if (more) load_chunk(t + 1, vl, vr);
+            if (wave_on) {
+                const int ns = min(J, j_end - (j_first + t * J));
+                const float4 *buf = smem + (t & 1) * buf_elems;
+                bd_compute<J>(buf + (s * nb + kb1) * G::NCL, buf + (s * nb + kb2) * G::NCL,
+                              buf + l_elems + (s * nb + b) * G::NCR, ns, acc1, acc2);
+            }
+            if (more) store_chunk(smem + ((t + 1) & 1) * buf_elems, vl, vr);
+            __syncthreads();
+        }
+
+        // ---- cross-lane reduction in a fixed order, then store ----
+        // comb: block-1 sums plus block-2 sums when both blocks share the wrap
+        // status (every lane but bstar); bstar keeps its block-2 sums apart.
+        if (wave_on) {
+#pragma unroll
+            for (int p = 0; p < P; ++p)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float c = acc1[r][p];
+                    if (r >= 1 && b != bstar) c += acc2[r - 1][p];
+                    wred[(r * P + p) * 64 + lane] = c;
+                }
+            if (b == bstar && lane < S * nb) {
+#pragma unroll
+                for (int p = 0; p < P; ++p)
+#pragma unroll
+                    for (int r = 0; r < 3; ++r)
+                        wextra[(s * 3 + r) * P + p] = acc2[r][p];
+            }
+        }
+        __syncthreads();
+        if (wave_on) {
+            const int per_slot = NV * 2;  // (r, p, wrapped)
+            for (int o = lane; o < S * per_slot; o += 64) {
+                const int sl = o / per_slot;
+                const int q = o - sl * per_slot;
+                const int wr = q & 1;
+                const int p = (q >> 1) % P;
+                const int r = (q >> 1) / P;
+                const int64_t pair = (int64_t)grp * S + sl;
+                const int dy = 4 * delta + r - (wr ? h4 : 0);
+                const int c = c0 + p;
+                const int dx = side ? c - wp : c;
+                if (pair >= npairs || dy <= -rows || dy >= rows || dx <= -cols || dx >= cols)
+                    continue;
+                const int blo = wr ? nb - delta : 0;
+                const int bhi = wr ? nb : nb - delta;
+                const float *col = wred + (r * P + p) * 64 + sl * nb;
+                float sum = 0.0f;
+                for (int bb = blo; bb < bhi; ++bb)
+                    sum += col[bb];
+                if (wr && r >= 1)
+                    sum += wextra[(sl * 3 + (r - 1)) * P + p];
+                a.x.out[((size_t)pair * oh + (dy + rows - 1)) * ow + (dx + cols - 1)] = sum;
+            }
+        }
+        // The next side's first barrier orders these reads before the
+        // reduction area is written again.
+    }
+}
+
+bool xcorr_blockdiag_supported(const XcorrArgs &a)
+{
+    const int nb = (a.rows + 3) / 4;
+    return nb >= 4 && nb <= 64;
+}
+
+template <int NW, int J>
+static hipError_t launch_bd(const BdArgs &b, hipStream_t s)
+{
+    using G = BdLds<J>;
+    const size_t buf = (size_t)b.S * b.nb * (G::NCL + G::NCR);
+    const size_t stage_bytes = 2 * buf * sizeof(float4);
+    const size_t red_bytes = (size_t)NW * (4 * BD_P * 64 + b.S * 3 * BD_P) * sizeof(float);
+    const size_t lds = stage_bytes + red_bytes;
+    const unsigned blocks = (unsigned)((int64_t)b.n_groups * b.n_xtiles * b.n_dgroups);
+    // Dynamic LDS above 64 KiB must be allowed explicitly (gfx950 has 160 KiB).
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&xcorr_bd_kernel<NW, J>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        if (e != hipSuccess)
+            return e;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL((xcorr_bd_kernel<NW, J>), dim3(blocks), dim3(64 * NW), lds, s, b);
+    return hipGetLastError();
+}
+
+hipError_t xcorr_launch_blockdiag(const XcorrArgs &a, hipStream_t s)
+{
+    BdArgs b;
+    b.x = a;
+    b.nb = (a.rows + 3) / 4;
+    b.wp = (a.cols + BD_P - 1) / BD_P * BD_P;
+    b.S = 64 / b.nb;
+    const int64_t npairs = (int64_t)a.n_left * a.n_right;
+    b.n_groups = (int)((npairs + b.S - 1) / b.S);
+    b.n_xtiles = b.wp / BD_P;
+    // Largest workgroup (more waves share one staged chunk) that still gives
+    // at least 256 workgroups.
+    int nw = 4;
+    const int64_t base = (int64_t)b.n_groups * b.n_xtiles;
+    if (b.nb >= 16 && base * ((b.nb + 15) / 16) >= 256)
+        nw = 16;
+    else if (b.nb >= 8 && base * ((b.nb + 7) / 8) >= 256)
+        nw = 8;
+    b.n_dgroups = (b.nb + nw - 1) / nw;
+    if (nw == 16) return launch_bd<16, 16>(b, s);
+    if (nw == 8) return launch_bd<8, 8>(b, s);
+    return launch_bd<4, 8>(b, s);
+}
+
+} // namespace xc

@@ -1,0 +1,143 @@
+/*
+ * xcorr.h -- C ABI of the gfx950 (MI355X) library for direct sliding-window
+ * 2D correlation.  Two forms:
+ *
+ *   ncc_u8_run     8-bit normalized correlation (template matching).
+ *                  Defined by "The CUDA Handbook", chapter 15 "Image
+ *                  Processing: Normalized Correlation", section 15.5
+ *                  "Instruction-Level Parallelism and DP4A": per window the
+ *                  unsigned 32-bit sums SumI (pixels), SumISq (squared pixels)
+ *                  and SumIT (pixel times template pixel) over unsigned bytes,
+ *                  the template width a multiple of four, then a correlation
+ *                  coefficient from those sums and the template sums.
+ *
+ *   xcorr_f32_run  fp32 full 2D cross-correlation over every shift at which
+ *                  two matrices overlap, for one-to-one, one-to-many and
+ *                  n-to-m groupings.  Defined by the JPDC 2023 artifact README
+ *                  "Efficient GPU-accelerated Parallel Cross-correlation"
+ *                  (overview of ccn_shuffle / warp_shuffle_impl, split-row,
+ *                  grouped-overlap and the multi-matrix variants).
+ *
+ * Conventions shared by every entry point
+ *   - Every data pointer is a DEVICE pointer (hipMalloc'd or equivalent) on
+ *     the current HIP device.  `stream` is a hipStream_t passed as void*;
+ *     NULL means the default stream.
+ *   - The caller allocates and owns every buffer; the library allocates
+ *     nothing and keeps no state between calls.  Inputs and outputs must not
+ *     alias.  Calls are thread-safe.
+ *   - Calls are asynchronous: work is enqueued on `stream` and the function
+ *     returns.  The caller synchronizes before reading results.
+ *   - Every output element is written (no pre-zeroing needed).
+ *   - Results are deterministic: the same inputs give bit-identical outputs.
+ *   - Arguments are validated on the host before any HIP call; on error
+ *     nothing is enqueued and a negative status is returned.
+ */
+#ifndef XCORR_MI355X_H
+#define XCORR_MI355X_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define XC_OK 0
+#define XC_ERR_NULL (-1)           /* a required pointer is NULL, or no output requested        */
+#define XC_ERR_SHAPE (-2)          /* a size is <= 0, or the template is larger than the image */
+#define XC_ERR_TEMPLATE_WIDTH (-3) /* t_width is not a multiple of 4                           */
+#define XC_ERR_OVERFLOW (-4)       /* sums could wrap 32 bits, or an index range is exceeded    */
+#define XC_ERR_ALIGN (-5)          /* a base pointer or the pitch is not 16-byte aligned        */
+#define XC_ERR_HIP (-6)            /* HIP launch or runtime error (including: no device)        */
+#define XC_ERR_VARIANT (-7)        /* unknown variant / algorithm selector                      */
+
+/* Largest template area for which the u32 sums cannot wrap: N * 255^2 < 2^32. */
+#define XC_NCC_MAX_TEMPLATE_PIXELS 66051
+
+/*
+ * ncc_u8_run -- valid-mode 8-bit normalized correlation.
+ *
+ * image   [height][pitch_bytes] u8, row-major; pixel (y, x) at image[y*pitch + x]
+ *         for x < width.  Base and pitch_bytes must be multiples of 16.
+ * tmpl    [t_height][t_width] u8, dense row-major; 4-byte aligned.
+ *         Requires 0 < t_width <= width, 0 < t_height <= height,
+ *         t_width % 4 == 0 and t_width * t_height <= 66,051.
+ * Outputs dense row-major [out_h][out_w], out_h = height - t_height + 1,
+ *         out_w = width - t_width + 1; entry (y, x) is the window whose
+ *         top-left pixel is image (y, x):
+ *   sum_i   u32  SumI   = sum of the window's pixels             (may be NULL)
+ *   sum_isq u32  SumISq = sum of their squares                   (may be NULL)
+ *   sum_it  u32  SumIT  = sum of pixel * template pixel          (may be NULL)
+ *   coef    f32  Pearson correlation of the N = t_width*t_height (pixel,
+ *                template) pairs: with SumT, SumTSq the template sums,
+ *                num = N*SumIT - SumI*SumT, vI = N*SumISq - SumI^2,
+ *                vT = N*SumTSq - SumT^2 (exact 64-bit integers),
+ *                coef = 0 if vI == 0 or vT == 0, else
+ *                (float) round-to-nearest( (double)num / sqrt((double)vI*(double)vT) )
+ *                                                            (may be NULL)
+ *         At least one output must be non-NULL; each must be 4-byte aligned.
+ * The template sums SumT and SumTSq are computed by the library on every call.
+ */
+int ncc_u8_run(const uint8_t *image, int width, int height, int pitch_bytes,
+               const uint8_t *tmpl, int t_width, int t_height,
+               uint32_t *sum_i, uint32_t *sum_isq, uint32_t *sum_it, float *coef,
+               void *stream);
+
+/*
+ * ncc_u8_run_variant -- the same computation through a chosen kernel variant,
+ * for ablation studies.  Every variant returns identical outputs.
+ *   XC_NCC_AUTO          the library's choice (what ncc_u8_run uses)
+ *   XC_NCC_DOT4_ILP      packed-byte dot products, 4 columns x several rows per lane
+ *   XC_NCC_DOT4_C1       packed-byte dot products, one output per lane
+ *   XC_NCC_SCALAR_C1     byte-at-a-time multiply-adds, one output per lane
+ */
+#define XC_NCC_AUTO 0
+#define XC_NCC_DOT4_ILP 1
+#define XC_NCC_DOT4_C1 2
+#define XC_NCC_SCALAR_C1 3
+int ncc_u8_run_variant(const uint8_t *image, int width, int height, int pitch_bytes,
+                       const uint8_t *tmpl, int t_width, int t_height,
+                       uint32_t *sum_i, uint32_t *sum_isq, uint32_t *sum_it, float *coef,
+                       int variant, void *stream);
+
+/*
+ * xcorr_f32_run -- fp32 full 2D cross-correlation of every (left, right) pair.
+ *
+ * left   [n_left][rows][cols]  f32, contiguous, 16-byte aligned base.
+ * right  [n_right][rows][cols] f32, contiguous, 16-byte aligned base.
+ * out    [n_left][n_right][2*rows-1][2*cols-1] f32, contiguous, 4-byte aligned;
+ *        pair (l, r) is slice l*n_right + r (left-major), and
+ *        out[l][r][y][x] = sum over the overlap of left[l][i+dy][j+dx] * right[r][i][j]
+ *        with dy = y - (rows-1), dx = x - (cols-1) (the convention of
+ *        scipy.signal.correlate2d(L, R, 'full')).
+ * One-to-one is n_left = n_right = 1; one-to-many is n_left = 1.
+ * Requires rows, cols, n_left, n_right > 0 and each pair's output
+ * (2*rows-1)*(2*cols-1) below 2^31 elements.
+ * Accuracy: each output is within 1e-5 * sum|l*r| of the exact value (fp32
+ * accumulation in a fixed, input-independent order).
+ */
+int xcorr_f32_run(const float *left, int n_left, const float *right, int n_right,
+                  int rows, int cols, float *out, void *stream);
+
+/*
+ * xcorr_f32_run_algo -- the same result through a chosen algorithm.
+ *   XC_XCORR_AUTO        the library's choice (what xcorr_f32_run uses)
+ *   XC_XCORR_OVERLAP     one thread per output shift, no data reuse (the
+ *                        overlap-wise baseline)
+ *   XC_XCORR_BLOCKDIAG   register-blocked kernel: 4x4 row blocks along block
+ *                        diagonals, a sliding column window per lane
+ */
+#define XC_XCORR_AUTO 0
+#define XC_XCORR_OVERLAP 1
+#define XC_XCORR_BLOCKDIAG 2
+int xcorr_f32_run_algo(const float *left, int n_left, const float *right, int n_right,
+                       int rows, int cols, float *out, int algo, void *stream);
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char *xc_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* XCORR_MI355X_H */

@@ -1,0 +1,80 @@
+"""The C ABI library on the CPU: it loads, exports every symbol the header
+declares, and rejects invalid arguments before any HIP call.  No compute call
+is made here (there is no GPU in this container)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from cross_correlation_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "xcorr.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char \*)\s*(\w+)\s*\(", text, re.M)))
+
+
+def test_header_symbols_exported():
+    lib = _lib.load()
+    names = _declared()
+    assert set(names) == set(_lib.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for code in range(0, -8, -1):
+        assert _lib.status_str(code) and _lib.status_str(code) != "unknown status"
+    assert _lib.status_str(-99) == "unknown status"
+
+
+FAKE = 1 << 20  # a 16-byte aligned non-null address; never dereferenced (validation fails first)
+
+
+@pytest.mark.parametrize("args,expect", [
+    (dict(image=0), _lib.XC_ERR_NULL),
+    (dict(tmpl=0), _lib.XC_ERR_NULL),
+    (dict(sum_i=0, sum_isq=0, sum_it=0, coef=0), _lib.XC_ERR_NULL),
+    (dict(width=0), _lib.XC_ERR_SHAPE),
+    (dict(t_height=0), _lib.XC_ERR_SHAPE),
+    (dict(t_width=80), _lib.XC_ERR_SHAPE),
+    (dict(t_height=70), _lib.XC_ERR_SHAPE),
+    (dict(pitch=32), _lib.XC_ERR_SHAPE),
+    (dict(t_width=6), _lib.XC_ERR_TEMPLATE_WIDTH),
+    (dict(width=70000, pitch=70016, height=2, t_width=33028, t_height=2), _lib.XC_ERR_OVERFLOW),
+    (dict(image=FAKE + 4), _lib.XC_ERR_ALIGN),
+    (dict(pitch=72), _lib.XC_ERR_ALIGN),
+    (dict(tmpl=FAKE + 2), _lib.XC_ERR_ALIGN),
+    (dict(coef=FAKE + 2), _lib.XC_ERR_ALIGN),
+    (dict(variant=42), _lib.XC_ERR_VARIANT),
+])
+def test_ncc_validation(args, expect):
+    a = dict(image=FAKE, width=64, height=64, pitch=64, tmpl=FAKE, t_width=8, t_height=8,
+             sum_i=FAKE, sum_isq=0, sum_it=0, coef=FAKE, variant=0)
+    a.update(args)
+    st = _lib.ncc_u8_run(a["image"], a["width"], a["height"], a["pitch"], a["tmpl"], a["t_width"], a["t_height"],
+                         a["sum_i"], a["sum_isq"], a["sum_it"], a["coef"], None, a["variant"])
+    assert st == expect, _lib.status_str(st)
+
+
+@pytest.mark.parametrize("args,expect", [
+    (dict(left=0), _lib.XC_ERR_NULL),
+    (dict(out=0), _lib.XC_ERR_NULL),
+    (dict(n_left=0), _lib.XC_ERR_SHAPE),
+    (dict(rows=-1), _lib.XC_ERR_SHAPE),
+    (dict(rows=40000, cols=40000), _lib.XC_ERR_OVERFLOW),
+    (dict(left=FAKE + 8), _lib.XC_ERR_ALIGN),
+    (dict(out=FAKE + 2), _lib.XC_ERR_ALIGN),
+    (dict(algo=9), _lib.XC_ERR_VARIANT),
+    (dict(rows=8, algo=_lib.XC_XCORR_BLOCKDIAG), _lib.XC_ERR_SHAPE),
+])
+def test_xcorr_validation(args, expect):
+    a = dict(left=FAKE, n_left=1, right=FAKE, n_right=1, rows=32, cols=32, out=FAKE, algo=0)
+    a.update(args)
+    st = _lib.xcorr_f32_run(a["left"], a["n_left"], a["right"], a["n_right"], a["rows"], a["cols"], a["out"],
+                            None, a["algo"])
+    assert st == expect, _lib.status_str(st)

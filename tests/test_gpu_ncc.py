@@ -1,0 +1,184 @@
+"""GPU parity of the u8 normalized correlation against the CPU oracle.
+
+Integer sums must match bit for bit; the coefficient within 1e-5.  Each test
+prints the case it runs before touching the GPU.
+"""
+import numpy as np
+import pytest
+
+from cross_correlation_amd import _lib
+from cross_correlation_amd.inputs import ncc_case, u8_uniform, workload, pitch_for
+
+import _gpu
+
+pytestmark = pytest.mark.gpu
+
+VARIANTS = [_lib.XC_NCC_AUTO, _lib.XC_NCC_DOT4_C1, _lib.XC_NCC_SCALAR_C1]
+
+
+def _case_from(img, tmpl, name="t", pitch=None):
+    from cross_correlation_amd.inputs import NccCase
+    h, w = img.shape
+    p = pitch_for(w) if pitch is None else pitch
+    buf = np.zeros((h, p), np.uint8)
+    buf[:, :w] = img
+    return NccCase(name, buf, w, h, np.ascontiguousarray(tmpl), None)
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_ncc_256_t16_cut(variant):
+    case = workload("ncc_256x256_t16")
+    _gpu.log(f"ncc 256x256 t16 variant={variant}")
+    res = _gpu.run_ncc(case, variant)
+    _gpu.check_ncc(case, res)
+    oy, ox = case.cut
+    assert res["coef"][oy, ox] == np.float32(1.0)
+
+
+def test_ncc_1080p_t64_full():
+    case = workload("ncc_1920x1080_t64")
+    _gpu.log("ncc 1920x1080 t64 (auto)")
+    res = _gpu.run_ncc(case)
+    _gpu.check_ncc(case, res)
+    oy, ox = case.cut
+    assert res["coef"][oy, ox] == np.float32(1.0)
+
+
+@pytest.mark.parametrize("variant", [_lib.XC_NCC_DOT4_C1, _lib.XC_NCC_SCALAR_C1])
+def test_ncc_1080p_variants_sampled(variant):
+    """Ablation variants at full size: compare against the auto path bit for bit."""
+    case = workload("ncc_1920x1080_t64")
+    _gpu.log(f"ncc 1920x1080 t64 variant={variant} vs auto")
+    a = _gpu.run_ncc(case)
+    b = _gpu.run_ncc(case, variant)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("ox_mod", [0, 1, 2, 3])
+def test_ncc_cut_template_every_byte_phase(ox_mod):
+    rng = np.random.default_rng(300 + ox_mod)
+    img = u8_uniform(rng, (70, 300))
+    oy, ox = 21, 40 + ox_mod
+    tmpl = img[oy:oy + 20, ox:ox + 32]
+    case = _case_from(img, tmpl)
+    _gpu.log(f"ncc cut template ox%4={ox_mod}")
+    res = _gpu.run_ncc(case)
+    _gpu.check_ncc(case, res)
+    t = tmpl.astype(np.int64)
+    assert res["coef"][oy, ox] == np.float32(1.0)
+    assert int(res["sum_i"][oy, ox]) == int(t.sum())
+    assert int(res["sum_it"][oy, ox]) == int((t * t).sum())
+
+
+def test_ncc_delta_templates_lane_order():
+    """SumIT of a one-hot template is the shifted image: every byte lane of a word."""
+    rng = np.random.default_rng(310)
+    img = u8_uniform(rng, (40, 270))
+    for tx in range(8):
+        tmpl = np.zeros((3, 8), np.uint8)
+        tmpl[tx % 3, tx] = 9
+        case = _case_from(img, tmpl)
+        _gpu.log(f"ncc delta template tx={tx}")
+        res = _gpu.run_ncc(case, outputs=("sum_it",))
+        oh, ow = case.out_shape
+        expect = 9 * img[tx % 3:tx % 3 + oh, tx:tx + ow].astype(np.uint32)
+        assert np.array_equal(res["sum_it"], expect), tx
+
+
+def test_ncc_asymmetric_template():
+    rng = np.random.default_rng(311)
+    img = u8_uniform(rng, (50, 333))
+    j, i = np.mgrid[0:9, 0:24]
+    tmpl = (1 + (i % 4) * 50 + j).astype(np.uint8)
+    case = _case_from(img, tmpl)
+    _gpu.log("ncc asymmetric lane template")
+    _gpu.check_ncc(case, _gpu.run_ncc(case))
+
+
+def test_ncc_saturated_and_constant():
+    rng = np.random.default_rng(312)
+    tmpl = u8_uniform(rng, (5, 12))
+    for val in (255, 0, 77):
+        img = np.full((30, 290), val, np.uint8)
+        case = _case_from(img, tmpl)
+        _gpu.log(f"ncc constant image {val}")
+        res = _gpu.run_ncc(case)
+        _gpu.check_ncc(case, res)
+        assert np.all(res["coef"] == 0.0)
+        assert np.all(res["sum_isq"] == np.uint32(val * val * tmpl.size))
+    img = u8_uniform(rng, (30, 290))
+    case = _case_from(img, np.full((5, 12), 200, np.uint8))
+    _gpu.log("ncc constant template")
+    res = _gpu.run_ncc(case)
+    _gpu.check_ncc(case, res)
+    assert np.all(res["coef"] == 0.0)
+
+
+def test_ncc_complement():
+    rng = np.random.default_rng(313)
+    img = u8_uniform(rng, (64, 300))
+    tmpl = u8_uniform(rng, (8, 16))
+    a = _gpu.run_ncc(_case_from(img, tmpl))
+    b = _gpu.run_ncc(_case_from((255 - img).astype(np.uint8), tmpl))
+    _gpu.log("ncc complement image")
+    n = tmpl.size
+    st = int(tmpl.astype(np.int64).sum())
+    assert np.array_equal(b["sum_i"].astype(np.int64), 255 * n - a["sum_i"].astype(np.int64))
+    assert np.array_equal(b["sum_it"].astype(np.int64), 255 * st - a["sum_it"].astype(np.int64))
+    assert np.max(np.abs(b["coef"] + a["coef"])) <= 2e-7
+
+
+@pytest.mark.parametrize("shape", [
+    # (height, width, t_height, t_width, pitch_extra)
+    (16, 16, 16, 16, 0),      # template = image -> 1x1 output
+    (17, 33, 1, 4, 0),        # one-row template, odd sizes
+    (33, 257, 7, 12, 32),     # ragged column tile, pitch > width
+    (100, 513, 3, 4, 0),      # 2 column tiles + ragged tail
+    (5, 1000, 5, 20, 0),      # one output row; 5-word template rows (unroll 1)
+    (230, 300, 200, 300, 0),  # tall template: several row chunks
+    (40, 4200, 16, 4096, 0),  # 1024-word template rows: several column chunks
+    (1, 64, 1, 64, 0),        # single pixel row
+])
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_ncc_edge_shapes(shape, variant):
+    h, w, th, tw, extra = shape
+    rng = np.random.default_rng(h * 7919 + w)
+    img = u8_uniform(rng, (h, w))
+    tmpl = u8_uniform(rng, (th, tw))
+    case = _case_from(img, tmpl, pitch=pitch_for(w) + extra)
+    _gpu.log(f"ncc edge shape {shape} variant={variant}")
+    _gpu.check_ncc(case, _gpu.run_ncc(case, variant))
+
+
+def test_ncc_output_subsets():
+    case = ncc_case("t", 320, 90, 280, 9, 16, cut=True)
+    ref = None
+    for outs in (("coef",), ("sum_it",), ("sum_i", "coef"), ("sum_isq",)):
+        _gpu.log(f"ncc outputs {outs}")
+        ref = _gpu.check_ncc(case, _gpu.run_ncc(case, outputs=outs), ref)
+
+
+def test_ncc_deterministic():
+    case = workload("ncc_256x256_t16")
+    _gpu.log("ncc repeat determinism")
+    a = _gpu.run_ncc(case)
+    b = _gpu.run_ncc(case)
+    for k in a:
+        assert np.array_equal(a[k].view(np.uint32), b[k].view(np.uint32))
+
+
+def test_ncc_invalid_arguments_rejected_before_launch():
+    import torch
+    from cross_correlation_amd import api
+    img = torch.zeros((32, 64), dtype=torch.uint8, device="cuda")
+    with pytest.raises(_lib.XcError) as e:
+        api.ncc_u8(img, torch.zeros((4, 6), dtype=torch.uint8, device="cuda"))
+    assert e.value.status == _lib.XC_ERR_TEMPLATE_WIDTH
+    out = torch.zeros(64, dtype=torch.int32, device="cuda")
+    tall = torch.zeros((40, 8), dtype=torch.uint8, device="cuda")
+    st = _lib.ncc_u8_run(img.data_ptr(), 64, 32, 64, tall.data_ptr(), 8, 40, out.data_ptr(), 0, 0, 0)
+    assert st == _lib.XC_ERR_SHAPE
+    with pytest.raises(_lib.XcError) as e:
+        api.ncc_u8(img[:, 1:], torch.zeros((4, 8), dtype=torch.uint8, device="cuda"))
+    assert e.value.status == _lib.XC_ERR_ALIGN

@@ -1,0 +1,141 @@
+"""GPU parity of the fp32 full cross-correlation against the fp64 oracle.
+
+Bar: |gpu - oracle| <= 1e-5 * sum|l*r| per output; small-integer inputs,
+deltas and all-ones must match exactly.  Each test prints its case first.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from cross_correlation_amd import _lib
+from cross_correlation_amd.inputs import f32_uniform, workload
+
+import _gpu
+
+pytestmark = pytest.mark.gpu
+
+ALGOS = [_lib.XC_XCORR_AUTO, _lib.XC_XCORR_OVERLAP, _lib.XC_XCORR_BLOCKDIAG]
+
+
+@pytest.mark.parametrize("name", ["xcorr_1to1_256", "xcorr_1to64_64", "xcorr_8to16_32"])
+@pytest.mark.parametrize("algo", ALGOS)
+def test_xcorr_workloads_full(name, algo):
+    case = workload(name)
+    _gpu.log(f"xcorr {name} algo={algo}")
+    ref, ab = oracle.xcorr_f32(case.left, case.right)
+    got = _gpu.run_xcorr(case.left, case.right, algo)
+    _gpu.check_xcorr(got, ref, ab)
+
+
+@pytest.mark.parametrize("shape", [
+    # (n_left, n_right, rows, cols)
+    (1, 1, 13, 17),
+    (1, 1, 16, 16),
+    (2, 3, 37, 5),
+    (3, 2, 21, 64),
+    (1, 5, 64, 63),
+    (5, 1, 100, 7),
+    (1, 1, 255, 3),
+    (1, 1, 256, 1),
+    (2, 2, 24, 40),
+    (3, 7, 32, 33),
+    (1, 1, 1, 9),
+    (1, 2, 3, 2),
+    (1, 1, 257, 19),
+])
+@pytest.mark.parametrize("algo", [_lib.XC_XCORR_AUTO, _lib.XC_XCORR_OVERLAP])
+def test_xcorr_edge_shapes(shape, algo):
+    nl, nr, rows, cols = shape
+    rng = np.random.default_rng(rows * 131 + cols * 7 + nl + 17 * nr)
+    L = f32_uniform(rng, (nl, rows, cols))
+    R = f32_uniform(rng, (nr, rows, cols))
+    _gpu.log(f"xcorr edge {shape} algo={algo}")
+    ref, ab = oracle.xcorr_f32(L, R)
+    _gpu.check_xcorr(_gpu.run_xcorr(L, R, algo), ref, ab)
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 16, 16), (2, 3, 37, 5), (1, 5, 64, 63), (3, 7, 32, 33),
+                                   (1, 1, 255, 3), (1, 1, 256, 1), (2, 2, 24, 40), (4, 3, 200, 12)])
+def test_xcorr_blockdiag_edge_shapes(shape):
+    nl, nr, rows, cols = shape
+    rng = np.random.default_rng(rows * 31 + cols)
+    L = f32_uniform(rng, (nl, rows, cols))
+    R = f32_uniform(rng, (nr, rows, cols))
+    _gpu.log(f"xcorr blockdiag edge {shape}")
+    ref, ab = oracle.xcorr_f32(L, R)
+    _gpu.check_xcorr(_gpu.run_xcorr(L, R, _lib.XC_XCORR_BLOCKDIAG), ref, ab)
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+def test_xcorr_small_integers_exact(algo):
+    """Every partial sum is an integer below 2^24: any summation order is exact."""
+    rng = np.random.default_rng(400)
+    L = rng.integers(-2, 3, size=(3, 40, 28)).astype(np.float32)
+    R = rng.integers(-2, 3, size=(4, 40, 28)).astype(np.float32)
+    _gpu.log(f"xcorr small-integer exact algo={algo}")
+    ref, _ = oracle.xcorr_f32(L, R)
+    got = _gpu.run_xcorr(L, R, algo)
+    assert np.array_equal(got.astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+def test_xcorr_delta_orientation(algo):
+    rows, cols = 20, 28
+    for (a, b, c, d) in ((0, 0, 19, 27), (19, 27, 0, 0), (3, 11, 17, 2), (5, 5, 5, 5)):
+        L = np.zeros((1, rows, cols), np.float32)
+        R = np.zeros((1, rows, cols), np.float32)
+        L[0, a, b] = 1.0
+        R[0, c, d] = 1.0
+        _gpu.log(f"xcorr delta ({a},{b}) ({c},{d}) algo={algo}")
+        got = _gpu.run_xcorr(L, R, algo)
+        expect = np.zeros((2 * rows - 1, 2 * cols - 1), np.float32)
+        expect[a - c + rows - 1, b - d + cols - 1] = 1.0
+        assert np.array_equal(got[0, 0], expect)
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+def test_xcorr_all_ones(algo):
+    rows, cols = 48, 36
+    _gpu.log(f"xcorr all ones algo={algo}")
+    got = _gpu.run_xcorr(np.ones((1, rows, cols), np.float32), np.ones((2, rows, cols), np.float32), algo)
+    dy = np.arange(2 * rows - 1) - (rows - 1)
+    dx = np.arange(2 * cols - 1) - (cols - 1)
+    expect = np.outer(rows - np.abs(dy), cols - np.abs(dx)).astype(np.float32)
+    assert np.array_equal(got[0, 0], expect) and np.array_equal(got[0, 1], expect)
+
+
+def test_xcorr_grouping_consistency():
+    """Slice [l][r] of an n-to-m run equals the one-to-one run of (L_l, R_r)."""
+    rng = np.random.default_rng(401)
+    L = f32_uniform(rng, (3, 32, 32))
+    R = f32_uniform(rng, (5, 32, 32))
+    _gpu.log("xcorr grouping consistency")
+    many = _gpu.run_xcorr(L, R)
+    ref, ab = oracle.xcorr_f32(L, R)
+    for l in range(3):
+        for r in range(5):
+            one = _gpu.run_xcorr(L[l:l + 1], R[r:r + 1])
+            _gpu.check_xcorr(one[0, 0], ref[l, r], ab[l, r])
+            _gpu.check_xcorr(many[l, r], ref[l, r], ab[l, r])
+
+
+def test_xcorr_deterministic():
+    case = workload("xcorr_8to16_32")
+    _gpu.log("xcorr repeat determinism")
+    a = _gpu.run_xcorr(case.left, case.right)
+    b = _gpu.run_xcorr(case.left, case.right)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_xcorr_invalid_arguments_rejected_before_launch():
+    import torch
+    from cross_correlation_amd import api
+    L = torch.zeros((1, 8, 8), device="cuda")
+    with pytest.raises(_lib.XcError) as e:
+        api.xcorr_f32(L, L, algo=7)
+    assert e.value.status == _lib.XC_ERR_VARIANT
+    with pytest.raises(_lib.XcError) as e:
+        api.xcorr_f32(L, L, algo=_lib.XC_XCORR_BLOCKDIAG)  # 8 rows: too few for block diagonals
+    assert e.value.status == _lib.XC_ERR_SHAPE
+    st = _lib.xcorr_f32_run(L.data_ptr() + 4, 1, L.data_ptr(), 1, 8, 8, L.data_ptr())
+    assert st == _lib.XC_ERR_ALIGN
