@@ -32,9 +32,34 @@ METRIC = "u8 NCC Gdot4/s & fp32 xcorr GFLOP/s, % of gfx950 peak, 1 GPU"
 
 # MI355X figures (spec sheet): 256 CUs at 2.4 GHz, 64 lanes per CU per clock.
 CUS, CLOCK_HZ, LANES = 256, 2.4e9, 64
-DOT4_PEAK = CUS * LANES * CLOCK_HZ          # one v_dot4_u32_u8 per lane per clock
-FP32_PEAK = 157.3e12                        # spec vector peak (packed FMA)
-FP32_NONPACKED = CUS * LANES * 2 * CLOCK_HZ  # v_fma_f32: 78.6 TFLOP/s
+DOT4_PEAK = CUS * LANES * CLOCK_HZ  # one v_dot4_u32_u8 per lane per clock: 39.32 T/s
+FP32_PEAK = 157.3e12                # spec FP32 vector peak (2 FMA per lane per clock)
+
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "cross_correlation_amd", "csrc")
+
+
+def source_digest(name: str) -> str:
+    import hashlib
+    with open(os.path.join(CSRC, name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def profiled_traffic(profile: str, source: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or None
+    when the kernel source changed since the counters were taken."""
+    path = os.path.join(PROFILES, profile)
+    if not os.path.exists(path):
+        return None
+    fig = {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("figure "):
+                k, v = line[len("figure "):].split("=", 1)
+                fig[k.strip()] = v.strip()
+    if fig.get("source_sha256_16") != source_digest(source):
+        return None
+    return int(fig["hbm_bytes_per_launch"])
 
 
 def parse():
@@ -46,7 +71,24 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the CPU sample")
     ap.add_argument("--only", choices=["ncc", "xcorr", "all"], default="all")
     ap.add_argument("--json-out", default=None)
+    ap.add_argument("--no-peak-probe", action="store_true", help="skip the measured issue-rate ceilings")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB (a known-size kernel that "
+                         "calibrates the FETCH_SIZE / WRITE_SIZE counters), then exit")
     return ap.parse_args()
+
+
+def copy_probe(mib: int, torch) -> None:
+    """A plain copy kernel of known size: reads and writes exactly `mib` MiB."""
+    n = mib * (1 << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4, "launches": 3}),
+          flush=True)
 
 
 def timed_loop(launch, steps, warmup, torch):
@@ -66,6 +108,30 @@ def timed_loop(launch, steps, warmup, torch):
     wall = (time.perf_counter() - t0) * 1e3 / steps
     per = sum(s.elapsed_time(e) for s, e in ev) / steps
     return wall, per
+
+
+def peak_probes():
+    """Measured issue-rate ceilings of v_dot4_u32_u8 and v_fmac_f32 (32
+    independent chains per lane, 2..16 waves per SIMD); the best rate is the
+    measured ceiling."""
+    import ctypes
+    from cross_correlation_amd import build as b
+
+    lib = ctypes.CDLL(b.PEAK_LIB)
+    lib.xc_peak_probe.restype = ctypes.c_int
+    lib.xc_peak_probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                  ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
+    res = {}
+    for kind, name, per_op in ((0, "dot4_T_per_s", 1.0), (1, "fp32_TFLOP_per_s", 2.0)):
+        rates = {}
+        for w in (2, 4, 8, 16):
+            ms, ops = ctypes.c_double(), ctypes.c_double()
+            if lib.xc_peak_probe(kind, w, 2048, 3, ctypes.byref(ms), ctypes.byref(ops)) != 0:
+                raise RuntimeError("peak probe failed")
+            rates[w] = per_op * ops.value / (ms.value * 1e-3) / 1e12
+        res[name] = {f"waves_per_simd_{w}": round(r, 2) for w, r in rates.items()}
+        res[name]["max"] = round(max(rates.values()), 2)
+    return res
 
 
 def bench_ncc(args, torch, lib, inputs):
@@ -116,7 +182,6 @@ def bench_xcorr(args, torch, lib, inputs):
             "gflops": round(flop / (wall * 1e-3) / 1e9, 1),
             "kernel_gflops": round(flop / (per * 1e-3) / 1e9, 1),
             "frac_of_157.3T": round(flop / (per * 1e-3) / FP32_PEAK, 4),
-            "frac_of_nonpacked_78.6T": round(flop / (per * 1e-3) / FP32_NONPACKED, 4),
             "flop_per_step": flop,
         }
     return res
@@ -130,12 +195,17 @@ def cpu_baseline(args, inputs, oracle_mod):
     case = inputs.workload("ncc_1920x1080_t64")
     oh, ow = case.out_shape
     per_out = 3 * (case.t_width // 4) * case.t_height
+    # probe: 16 output rows, then the whole image once if that is still short
     t0 = time.perf_counter()
-    oracle_mod.ncc_u8(case.image, case.width, case.height, case.tmpl, y_begin=0, y_end=8)
-    t_row = (time.perf_counter() - t0) / 8
+    oracle_mod.ncc_u8(case.image, case.width, case.height, case.tmpl, y_begin=0, y_end=16)
+    t_row = (time.perf_counter() - t0) / 16
+    if t_row * oh < args.cpu_seconds:
+        t0 = time.perf_counter()
+        oracle_mod.ncc_u8(case.image, case.width, case.height, case.tmpl)
+        t_row = (time.perf_counter() - t0) / oh
     want_rows = args.cpu_seconds / max(t_row, 1e-9)
     if want_rows < oh:
-        rows, reps = int(max(8, want_rows)), 1
+        rows, reps = int(max(16, want_rows)), 1
     else:
         rows, reps = oh, int(max(1, round(want_rows / oh)))
     t0 = time.perf_counter()
@@ -160,6 +230,9 @@ def main():
         sys.exit(2)
     import torch
 
+    if args.copy_probe_mib:
+        copy_probe(args.copy_probe_mib, torch)
+        return
     from cross_correlation_amd import _lib, inputs
 
     _lib.load()
@@ -195,13 +268,22 @@ def main():
             "peak": round(DOT4_PEAK / 1e12, 4),
             "unit": "Tdot4/s",
             "frac": round(achieved / DOT4_PEAK, 4),
-            "traffic": None,
+            "traffic": profiled_traffic("ncc_u8_1080p_t64.md", "ncc_u8.hip"),
             "kernel": "ncc_u8_ilp_kernel",
             "kernel_ms": round(r["kernel_ms"], 5),
             "outputs_per_s": round(r["outputs"] / (r["kernel_ms"] * 1e-3), 1),
         }
     if args.only in ("xcorr", "all"):
         out["xcorr"] = bench_xcorr(args, torch, _lib, inputs)
+    if not args.no_peak_probe:
+        out["measured_ceilings"] = peak_probes()
+        if "roofline" in out:
+            ceil = out["measured_ceilings"]["dot4_T_per_s"]["max"]
+            out["roofline"]["frac_of_measured_ceiling"] = round(out["roofline"]["achieved"] / ceil, 4)
+        if "xcorr" in out:
+            ceil = out["measured_ceilings"]["fp32_TFLOP_per_s"]["max"]
+            for v in out["xcorr"].values():
+                v["frac_of_measured_ceiling"] = round(v["kernel_gflops"] / 1e3 / ceil, 4)
     if not args.no_cpu_baseline and args.only in ("ncc", "all"):
         import oracle
 

@@ -16,6 +16,9 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libxcorr_hip.so")
 SOURCES = ["capi.hip", "ncc_u8.hip", "xcorr_f32.hip"]
+# Issue-rate probes used only by the bench harness (not part of the ABI).
+PEAK_LIB = os.path.join(HERE, "libxcorr_peak.so")
+PEAK_SOURCES = ["peak_probe.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -36,8 +39,14 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False, extra: tuple[str, ...] = (), out: str = LIB) -> str:
-    """Compile every HIP source into one shared library (always rebuilds)."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    """Compile the correlation library and the bench's peak probes (always rebuilds)."""
+    _compile(SOURCES, out, verbose, extra)
+    _compile(PEAK_SOURCES, PEAK_LIB, verbose, extra)
+    return out
+
+
+def _compile(sources, out, verbose, extra) -> str:
+    srcs = [os.path.join(CSRC, s) for s in sources]
     tmp = out + ".tmp"
     cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-shared", f"-I{INCLUDE}", f"-I{CSRC}", *srcs, "-o", tmp]
     if verbose:

@@ -51,7 +51,7 @@ int ncc_validate(const uint8_t *image, int width, int height, int pitch_bytes, c
     a.coef = coef;
     a.out_w = (int)out_w;
     a.out_h = (int)out_h;
-    a.hc = a.cw = a.lds_stride = 0;
+    a.hc = a.cw = a.lds_stride = a.t_stride = 0;
     return XC_OK;
 }
 

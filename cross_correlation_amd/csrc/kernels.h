@@ -21,6 +21,7 @@ struct NccArgs {
     int hc;          // template rows per chunk
     int cw;          // template words (4 bytes) per chunk
     int lds_stride;  // LDS words per staged image row
+    int t_stride;    // LDS words per staged template row
 };
 
 hipError_t ncc_launch_ilp(NccArgs a, hipStream_t s);

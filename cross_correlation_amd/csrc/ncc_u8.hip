@@ -107,45 +107,128 @@ __device__ __forceinline__ void ncc_store(const NccArgs &a, size_t o, uint32_t s
     }
 }
 
-// One image row of one template chunk: for each template word k of the chunk
-// load the next aligned image word, form the three shifted words, and for each
-// output row q the row serves, accumulate 3 x 4 dot4 with template row (rl - q).
-template <int Q, int WC, bool FULL>
-__device__ __forceinline__ void ncc_row(const uint32_t *rp, const uint32_t *__restrict__ t0, int nw, int cw,
+// Operands of one block of 4 template words: the lane's next 4 aligned image
+// words and, per output row q, 4 template words (one 16-byte LDS read at a
+// wave-uniform address).
+template <int Q>
+struct NccBlock {
+    uint32_t img[4];
+    uint4 t[Q];
+};
+
+template <int Q, bool FULL>
+__device__ __forceinline__ void ncc_load_block(NccBlock<Q> &blk, const uint32_t *rp, const uint32_t *t0,
+                                               int tstride, int k0, int qlo, int qhi)
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        blk.img[i] = rp[k0 + 1 + i];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        // rows outside the chunk are never used; read a valid row instead
+        const int qq = FULL ? q : min(max(q, qlo), qhi);
+        blk.t[q] = *reinterpret_cast<const uint4 *>(t0 - qq * tstride + k0);
+    }
+}
+
+// 4 template words: form the shifted image words and accumulate 3 x 4 dot4
+// per output row the image row serves.
+template <int Q, bool FULL>
+__device__ __forceinline__ void ncc_do_block(const NccBlock<Q> &blk, uint32_t &w0, int qlo, int qhi,
+                                             uint32_t (&ai)[Q][4], uint32_t (&aq)[Q][4], uint32_t (&at)[Q][4])
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t w1 = blk.img[i];
+        uint32_t s[4];
+        s[0] = w0;
+        s[1] = shift_bytes(w1, w0, 1);
+        s[2] = shift_bytes(w1, w0, 2);
+        s[3] = shift_bytes(w1, w0, 3);
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            if (FULL || (q >= qlo && q <= qhi)) {
+                const uint32_t t = i == 0 ? blk.t[q].x : i == 1 ? blk.t[q].y : i == 2 ? blk.t[q].z : blk.t[q].w;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    ai[q][c] = dot4u(s[c], 0x01010101u, ai[q][c]);
+                    aq[q][c] = dot4u(s[c], s[c], aq[q][c]);
+                    at[q][c] = dot4u(s[c], t, at[q][c]);
+                }
+            }
+        }
+        w0 = w1;
+    }
+}
+
+// One image row of one template chunk (cw words, a multiple of 4): for each
+// template word k load the next aligned image word, form the three shifted
+// words, and for each output row q the row serves accumulate 3 x 4 dot4 with
+// template row (rl - q).  Software-pipelined by one 4-word block: the LDS
+// reads of block b+1 are issued before the 204 VALU operations of block b,
+// alternating between two operand buffers (the loop body holds both, with an
+// exit after each, so no register copies are needed at the back-edge), and a
+// scheduling barrier per block keeps the reads from being hoisted further.
+template <int Q, bool FULL>
+__device__ __forceinline__ void ncc_row(const uint32_t *rp, const uint32_t *t0, int tstride, int cw,
                                         int qlo, int qhi, uint32_t (&ai)[Q][4], uint32_t (&aq)[Q][4],
                                         uint32_t (&at)[Q][4])
 {
+    const int nblk = cw >> 2;
     uint32_t w0 = rp[0];
-    for (int kb = 0; kb < cw; kb += WC) {
+    NccBlock<Q> A, B;
+    ncc_load_block<Q, FULL>(A, rp, t0, tstride, 0, qlo, qhi);
+    for (int bk = 0;; bk += 2) {
+        if (bk + 1 < nblk)
+            ncc_load_block<Q, FULL>(B, rp, t0, tstride, 4 * (bk + 1), qlo, qhi);
+        ncc_do_block<Q, FULL>(A, w0, qlo, qhi, ai, aq, at);
+        __builtin_amdgcn_sched_barrier(0);
+        if (bk + 1 >= nblk)
+            break;
+        if (bk + 2 < nblk)
+            ncc_load_block<Q, FULL>(A, rp, t0, tstride, 4 * (bk + 2), qlo, qhi);
+        ncc_do_block<Q, FULL>(B, w0, qlo, qhi, ai, aq, at);
+        __builtin_amdgcn_sched_barrier(0);
+        if (bk + 2 >= nblk)
+            break;
+    }
+}
+
+// Template rows whose width is not a multiple of 16 bytes: one word at a time.
+template <int Q, bool FULL>
+__device__ __forceinline__ void ncc_row_words(const uint32_t *rp, const uint32_t *t0, int tstride, int cw,
+                                              int qlo, int qhi, uint32_t (&ai)[Q][4], uint32_t (&aq)[Q][4],
+                                              uint32_t (&at)[Q][4])
+{
+    uint32_t w0 = rp[0];
+    for (int k = 0; k < cw; ++k) {
+        const uint32_t w1 = rp[k + 1];
+        uint32_t s[4];
+        s[0] = w0;
+        s[1] = shift_bytes(w1, w0, 1);
+        s[2] = shift_bytes(w1, w0, 2);
+        s[3] = shift_bytes(w1, w0, 3);
 #pragma unroll
-        for (int kk = 0; kk < WC; ++kk) {
-            const int k = kb + kk;
-            const uint32_t w1 = rp[k + 1];
-            uint32_t s[4];
-            s[0] = w0;
-            s[1] = shift_bytes(w1, w0, 1);
-            s[2] = shift_bytes(w1, w0, 2);
-            s[3] = shift_bytes(w1, w0, 3);
+        for (int q = 0; q < Q; ++q) {
+            if (FULL || (q >= qlo && q <= qhi)) {
+                const uint32_t t = t0[k - q * tstride];
 #pragma unroll
-            for (int q = 0; q < Q; ++q) {
-                if (FULL || (q >= qlo && q <= qhi)) {
-                    const uint32_t t = t0[k - q * nw];
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        ai[q][c] = dot4u(s[c], 0x01010101u, ai[q][c]);
-                        aq[q][c] = dot4u(s[c], s[c], aq[q][c]);
-                        at[q][c] = dot4u(s[c], t, at[q][c]);
-                    }
+                for (int c = 0; c < 4; ++c) {
+                    ai[q][c] = dot4u(s[c], 0x01010101u, ai[q][c]);
+                    aq[q][c] = dot4u(s[c], s[c], aq[q][c]);
+                    at[q][c] = dot4u(s[c], t, at[q][c]);
                 }
             }
-            w0 = w1;
         }
+        w0 = w1;
     }
 }
 
 // Main kernel: a workgroup of WV waves covers 256 output columns x WV*Q rows;
 // wave w owns rows [w*Q, w*Q + Q) of the tile, lane l owns columns 4l..4l+3.
-template <int Q, int WV, int WC>
+// LDS: the image tile (WV*Q + hc - 1 rows of `lds_stride` words), then the
+// template chunk (hc rows of `t_stride` words).
+template <int Q, int WV, bool V4>
 __global__ __launch_bounds__(64 * WV) void ncc_u8_ilp_kernel(NccArgs a)
 {
     extern __shared__ uint32_t lds[];
@@ -167,6 +250,8 @@ __global__ __launch_bounds__(64 * WV) void ncc_u8_ilp_kernel(NccArgs a)
             ai[q][c] = aq[q][c] = at[q][c] = 0u;
 
     const int stride = a.lds_stride;
+    const int tstride = a.t_stride;
+    uint32_t *const tl = lds + (WV * Q + a.hc - 1) * stride;
     for (int jc = 0; jc < a.t_height; jc += a.hc) {
         const int hc = min(a.hc, a.t_height - jc);
         for (int ic = 0; ic < nw; ic += a.cw) {
@@ -175,16 +260,28 @@ __global__ __launch_bounds__(64 * WV) void ncc_u8_ilp_kernel(NccArgs a)
             // lane l reads words l + k and l + k + 1, k < cw: 64 + cw words per row
             stage_tile(a.image, a.height, a.pitch, y0 + jc, x0 + 4 * ic, WV * Q + hc - 1,
                        (64 + cw + 3) / 4, lds, stride);
+            for (int t = threadIdx.x; t < hc * cw; t += 64 * WV) {
+                const int r = t / cw;
+                const int c = t - r * cw;
+                tl[r * tstride + c] = tw[(size_t)(jc + r) * nw + ic + c];
+            }
             __syncthreads();
             const uint32_t *wrow = lds + (wave * Q) * stride + lane;
             for (int rl = 0; rl < Q + hc - 1; ++rl) {
                 const int qlo = max(0, rl - hc + 1);
                 const int qhi = min(Q - 1, rl);
-                const uint32_t *t0 = tw + (size_t)(jc + rl) * nw + ic;
-                if (qlo == 0 && qhi == Q - 1)
-                    ncc_row<Q, WC, true>(wrow + rl * stride, t0, nw, cw, qlo, qhi, ai, aq, at);
-                else
-                    ncc_row<Q, WC, false>(wrow + rl * stride, t0, nw, cw, qlo, qhi, ai, aq, at);
+                const uint32_t *t0 = tl + rl * tstride;
+                if (V4) {
+                    if (qlo == 0 && qhi == Q - 1)
+                        ncc_row<Q, true>(wrow + rl * stride, t0, tstride, cw, qlo, qhi, ai, aq, at);
+                    else
+                        ncc_row<Q, false>(wrow + rl * stride, t0, tstride, cw, qlo, qhi, ai, aq, at);
+                } else {
+                    if (qlo == 0 && qhi == Q - 1)
+                        ncc_row_words<Q, true>(wrow + rl * stride, t0, tstride, cw, qlo, qhi, ai, aq, at);
+                    else
+                        ncc_row_words<Q, false>(wrow + rl * stride, t0, tstride, cw, qlo, qhi, ai, aq, at);
+                }
             }
         }
     }
@@ -272,57 +369,51 @@ __global__ __launch_bounds__(256) void ncc_u8_c1_kernel(NccArgs a)
 // ---------------------------------------------------------------------------
 // Host-side launch helpers (called by the C ABI after validation).
 
-template <int Q, int WV, int WC>
+template <int Q, int WV, bool V4>
 static hipError_t launch_ilp(const NccArgs &a, hipStream_t s)
 {
     dim3 grid((a.out_w + 255) / 256, (a.out_h + WV * Q - 1) / (WV * Q));
-    const size_t lds = (size_t)(WV * Q + a.hc - 1) * a.lds_stride * 4;
-    hipLaunchKernelGGL((ncc_u8_ilp_kernel<Q, WV, WC>), grid, dim3(64 * WV), lds, s, a);
+    const size_t lds = ((size_t)(WV * Q + a.hc - 1) * a.lds_stride + (size_t)a.hc * a.t_stride) * 4;
+    hipLaunchKernelGGL((ncc_u8_ilp_kernel<Q, WV, V4>), grid, dim3(64 * WV), lds, s, a);
     return hipGetLastError();
 }
 
 template <int Q, int WV>
-static hipError_t dispatch_wc(const NccArgs &a, int wc, hipStream_t s)
+static hipError_t dispatch_v4(const NccArgs &a, bool v4, hipStream_t s)
 {
-    switch (wc) {
-    case 4: return launch_ilp<Q, WV, 4>(a, s);
-    case 2: return launch_ilp<Q, WV, 2>(a, s);
-    default: return launch_ilp<Q, WV, 1>(a, s);
-    }
+    return v4 ? launch_ilp<Q, WV, true>(a, s) : launch_ilp<Q, WV, false>(a, s);
 }
 
 // Chooses the tile (Q rows per lane, WV waves), the unroll WC and the chunking
-// so that the LDS tile stays within `lds_budget` bytes.
+// so that the LDS tile stays within 64 KiB.
 hipError_t ncc_launch_ilp(NccArgs a, hipStream_t s)
 {
     const int nw = a.t_width / 4;
-    // Unroll of the template-word loop: the largest power of two <= 4 dividing
-    // the words per row (a deeper unroll makes the compiler hold more template
-    // words in SGPRs than fit).
-    int wc = 4;
-    while (nw % wc) wc >>= 1;
+    // Rows of 4-word blocks when every chunk is a multiple of 16 bytes wide.
+    const bool v4 = nw % 4 == 0;
     // Tile shape: the big tile when the image yields enough work to fill
     // 256 CUs, smaller ones for small images.
     int q = 4, wv = 4;
     const long col_tiles = (a.out_w + 255) / 256;
     if (col_tiles * ((a.out_h + 15) / 16) < 256) { q = 2; wv = 2; }
     if (col_tiles * ((a.out_h + 3) / 4) < 256) { q = 1; wv = 1; }
-    const int lds_budget = 64 * 1024;
-    // chunk of template words: a multiple of lcm(wc, 4) words
-    const int unit = wc < 4 ? 4 : wc;
+    const int lds_words = 64 * 1024 / 4;
+    // chunk of template words: a multiple of 4 words (16-byte aligned chunk starts)
     int cw = nw;
-    const int max_cw = 1024 - 64;
-    if (cw > max_cw) cw = max_cw / unit * unit;
+    const int max_cw = 960;
+    if (cw > max_cw) cw = max_cw;
     a.cw = cw;
     a.lds_stride = (64 + cw + 3) / 4 * 4;
+    a.t_stride = (cw + 3) / 4 * 4;
     const int th = wv * q;
-    int hc = lds_budget / (a.lds_stride * 4) - th + 1;
+    // (th + hc - 1) * stride + hc * t_stride <= lds_words
+    int hc = (lds_words - (th - 1) * a.lds_stride) / (a.lds_stride + a.t_stride);
     if (hc < 1) hc = 1;
     if (hc > a.t_height) hc = a.t_height;
     a.hc = hc;
-    if (q == 4) return dispatch_wc<4, 4>(a, wc, s);
-    if (q == 2) return dispatch_wc<2, 2>(a, wc, s);
-    return dispatch_wc<1, 1>(a, wc, s);
+    if (q == 4) return dispatch_v4<4, 4>(a, v4, s);
+    if (q == 2) return dispatch_v4<2, 2>(a, v4, s);
+    return dispatch_v4<1, 1>(a, v4, s);
 }
 
 hipError_t ncc_launch_c1(NccArgs a, bool dot4, hipStream_t s)

@@ -1,0 +1,93 @@
+// peak_probe.hip -- issue-rate probes for the two instructions the hot path
+// is bound by, so that "fraction of peak" can be quoted against a measured
+// ceiling as well as the spec sheet.  Not part of the correlation ABI; only
+// the bench harness loads this library.
+//
+// Each thread runs `iters` rounds of CH independent accumulation chains of
+// one instruction:
+//   kind 0: v_dot4_u32_u8 (unsigned packed-byte dot product, 4 MACs)
+//   kind 1: v_fmac_f32    (fp32 fused multiply-add, 2 flops)
+// A launch has 64-thread workgroups, `waves_per_simd` per SIMD of every CU.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+template <int CH>
+__global__ __launch_bounds__(64) void dot4_probe(uint32_t *out, int iters)
+{
+    uint32_t a = threadIdx.x * 77u, b = a * 2654435761u;
+    uint32_t acc[CH];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) acc[c] = c + threadIdx.x;
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+        for (int c = 0; c < CH; ++c) acc[c] = __builtin_amdgcn_udot4(a, b, acc[c], false);
+        a += 0x01010101u;
+    }
+    uint32_t s = 0;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) s ^= acc[c];
+    out[blockIdx.x * 64 + threadIdx.x] = s;
+}
+
+template <int CH>
+__global__ __launch_bounds__(64) void fma_probe(uint32_t *out, int iters)
+{
+    float a = (float)threadIdx.x, b = 1.0001f;
+    float acc[CH];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) acc[c] = (float)c;
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+        for (int c = 0; c < CH; ++c) acc[c] = fmaf(a, b, acc[c]);
+        a += 1.0f;
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) s += acc[c];
+    out[blockIdx.x * 64 + threadIdx.x] = __float_as_uint(s);
+}
+
+} // namespace
+
+extern "C" {
+
+// Runs the probe `reps` times after one warm-up launch; returns 0 and the mean
+// milliseconds per launch in *ms, or -1 on any HIP error.  ops_per_launch
+// receives the instruction count (lane-operations) of one launch.
+int xc_peak_probe(int kind, int waves_per_simd, int iters, int reps, double *ms, double *ops_per_launch)
+{
+    constexpr int CH = 32;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return -1;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+    const int blocks = cus * 4 * waves_per_simd;
+    uint32_t *buf = nullptr;
+    if (hipMalloc(&buf, (size_t)blocks * 64 * sizeof(uint32_t)) != hipSuccess) return -1;
+    hipEvent_t e0, e1;
+    if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) return -1;
+    auto launch = [&]() {
+        if (kind == 0)
+            hipLaunchKernelGGL(dot4_probe<CH>, dim3(blocks), dim3(64), 0, 0, buf, iters);
+        else
+            hipLaunchKernelGGL(fma_probe<CH>, dim3(blocks), dim3(64), 0, 0, buf, iters);
+    };
+    launch();
+    int st = hipDeviceSynchronize() == hipSuccess ? 0 : -1;
+    float t = 0.0f;
+    if (st == 0) {
+        hipEventRecord(e0, 0);
+        for (int r = 0; r < reps; ++r) launch();
+        hipEventRecord(e1, 0);
+        st = (hipEventSynchronize(e1) == hipSuccess && hipEventElapsedTime(&t, e0, e1) == hipSuccess) ? 0 : -1;
+    }
+    *ms = (double)t / reps;
+    *ops_per_launch = (double)blocks * 64 * iters * CH;
+    hipEventDestroy(e0);
+    hipEventDestroy(e1);
+    if (hipFree(buf) != hipSuccess) st = -1;
+    return st;
+}
+
+} // extern "C"

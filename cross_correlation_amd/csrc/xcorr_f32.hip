@@ -106,51 +106,81 @@ struct BdArgs {
     int n_dgroups;   // ceil(nb / waves per workgroup)
 };
 
-// LDS geometry of one staging buffer for J walk steps.
+// LDS geometry of one staging buffer for J walk steps: per row block, J left
+// columns and J + P - 1 right columns (the window halo), each a float4 of the
+// block's 4 rows.  Strides are odd so lanes on consecutive blocks spread over
+// the banks.
 template <int J>
 struct BdLds {
-    static constexpr int NCL = (J + BD_P - 1) | 1;  // left columns per block (odd: spreads banks)
-    static constexpr int NCR = J | 1;               // right columns per block
-    static constexpr int NLR = J + BD_P - 1;        // left columns actually used
+    static constexpr int NLU = J;                   // left columns used
+    static constexpr int NRU = J + BD_P - 1;        // right columns used
+    static constexpr int NCL = J | 1;               // left stride (float4s)
+    static constexpr int NCR = (J + BD_P) | 1;      // right stride; >= NRU + 1 (pipelined read past the end)
 };
 
-// One walk step range of a chunk: accumulate `nsteps` steps (multiple of P).
+// One walk step: left column u of both left blocks against the P right
+// columns u + roff - p held in the ring; 16 (a, e) row pairs x P FMAs.
+template <int P>
+__device__ __forceinline__ void bd_step(const float4 l1, const float4 l2, const float4 (&ring)[P + 1], int m,
+                                        float (&acc1)[4][P], float (&acc2)[3][P])
+{
+    const float la[4] = {l1.x, l1.y, l1.z, l1.w};
+    const float lb[3] = {l2.x, l2.y, l2.z};
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        // right LDS column m + P - 1 - p lives in ring slot (m + P - 1 - p) mod (P + 1)
+        const float4 rv = ring[(m + P - 1 - p) % (P + 1)];
+        const float re[4] = {rv.x, rv.y, rv.z, rv.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+#pragma unroll
+            for (int ar = 0; ar < 4; ++ar) {
+                if (ar >= e)
+                    acc1[ar - e][p] = fmaf(la[ar], re[e], acc1[ar - e][p]);
+                else
+                    acc2[ar - e + 3][p] = fmaf(lb[ar], re[e], acc2[ar - e + 3][p]);
+            }
+        }
+    }
+}
+
+// Accumulate `nsteps` walk steps (a multiple of P) of one staged chunk.
+// The right-column window lives in a ring of P + 1 slots: during step m the
+// free slot receives the column step m + 1 needs, so reads run one step
+// ahead of the FMAs and no register moves are needed.  The loop body is P + 1
+// groups of P steps (the ring's period), with an exit after every group, so
+// the slot assignment at the back-edge matches the loop head.  A scheduling
+// barrier per step keeps the compiler from hoisting reads further ahead.
 template <int J>
 __device__ __forceinline__ void bd_compute(const float4 *Lb1, const float4 *Lb2, const float4 *Rb, int nsteps,
                                            float (&acc1)[4][BD_P], float (&acc2)[3][BD_P])
 {
     constexpr int P = BD_P;
-    float4 w1[P], w2[P];
+    constexpr int PERIOD = P * (P + 1);
+    float4 ring[P + 1];
 #pragma unroll
-    for (int p = 0; p < P - 1; ++p) {
-        w1[p] = Lb1[p];
-        w2[p] = Lb2[p];
-    }
-    for (int m0 = 0; m0 < nsteps; m0 += P) {
+    for (int r = 0; r < P; ++r)
+        ring[r] = Rb[r];
+    float4 l1 = Lb1[0], l2 = Lb2[0];
+    for (int m0 = 0;; m0 += PERIOD) {
 #pragma unroll
-        for (int sp = 0; sp < P; ++sp) {
-            const int m = m0 + sp;
-            w1[(sp + P - 1) % P] = Lb1[m + P - 1];
-            w2[(sp + P - 1) % P] = Lb2[m + P - 1];
-            const float4 rv = Rb[m];
-            const float re[4] = {rv.x, rv.y, rv.z, rv.w};
+        for (int g = 0; g < P + 1; ++g) {
 #pragma unroll
-            for (int p = 0; p < P; ++p) {
-                const float4 l1 = w1[(sp + p) % P];
-                const float4 l2 = w2[(sp + p) % P];
-                const float la[4] = {l1.x, l1.y, l1.z, l1.w};
-                const float lb[3] = {l2.x, l2.y, l2.z};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-#pragma unroll
-                    for (int ar = 0; ar < 4; ++ar) {
-                        if (ar >= e)
-                            acc1[ar - e][p] = fmaf(la[ar], re[e], acc1[ar - e][p]);
-                        else
-                            acc2[ar - e + 3][p] = fmaf(lb[ar], re[e], acc2[ar - e + 3][p]);
-                    }
-                }
+            for (int sp = 0; sp < P; ++sp) {
+                const int mm = g * P + sp;  // step within the period (compile-time)
+                const int m = m0 + mm;
+                // reads for step m + 1 (the last step of a chunk reads one
+                // column of padding, never used)
+                const float4 n1 = Lb1[m + 1];
+                const float4 n2 = Lb2[m + 1];
+                ring[(mm + P) % (P + 1)] = Rb[m + P];
+                bd_step<P>(l1, l2, ring, mm, acc1, acc2);
+                l1 = n1;
+                l2 = n2;
+                __builtin_amdgcn_sched_barrier(0);
             }
+            if (m0 + (g + 1) * P >= nsteps)
+                return;
         }
     }
 }
@@ -184,23 +214,22 @@ __global__ __launch_bounds__(64 * NW) void xcorr_bd_kernel(BdArgs a)
     const int kb1 = (b + dl) % nb;
     const int kb2 = (b + dl + 1) % nb;
 
-    // LDS: two staging buffers, each L [S][nb][NCL] then R [S][nb][NCR] (a
-    // float4 holds the 4 rows of a row block at one column), then the
-    // reduction area.
+    // LDS: two staging buffers, each L [S][nb][NCL] then R [S][nb][NCR], then
+    // the reduction area.
     const int l_elems = S * nb * G::NCL;
     const int buf_elems = l_elems + S * nb * G::NCR;
     constexpr int NV = 4 * P;  // per-lane partial sums per side: (r, p)
+    constexpr int RS = 65;     // reduction row stride (odd: lanes reading different rows hit different banks)
     float *const red = reinterpret_cast<float *>(smem + 2 * buf_elems);
-    float *const wred = red + wave * (NV * 64 + S * 3 * P);
-    float *const wextra = wred + NV * 64;
+    float *const wred = red + wave * (NV * RS + S * 3 * P);
+    float *const wextra = wred + NV * RS;
 
     // Staging: thread t owns row block sb = t / NW (slot * nb + block, all
     // S*nb <= 64 blocks) and the columns congruent to t mod NW.  One item is
     // the 4 rows of that block at one column, stored as one float4; the NW
     // threads of a block read consecutive columns (coalesced per row).
-    constexpr int LPT = (G::NLR + NW - 1) / NW;  // left items per thread
-    constexpr int RPT = J / NW;                   // right items per thread
-    static_assert(J % NW == 0, "J must be a multiple of the waves per workgroup");
+    constexpr int LPT = (G::NLU + NW - 1) / NW;  // left items per thread
+    constexpr int RPT = (G::NRU + NW - 1) / NW;  // right items per thread
     const int tid = threadIdx.x;
     const int sb = tid / NW;
     const int cres = tid - sb * NW;
@@ -221,11 +250,12 @@ __global__ __launch_bounds__(64 * NW) void xcorr_bd_kernel(BdArgs a)
     const int oh = 2 * rows - 1, ow = 2 * cols - 1;
 
     for (int side = 0; side < 2; ++side) {
-        // Walk of this side: positive dx classes c (j from 0) or negative dx = c - wp.
-        const int j_first = side ? wp - c0 - P : 0;
-        const int j_end = side ? wp : wp - c0;
-        const int nch = (j_end - j_first + J - 1) / J;
-        const int lshift = side ? c0 - wp : c0;  // left column = j + lshift + window position
+        // Walk over left columns u; positive dx = c walks u in [c0, wp),
+        // negative dx = c - wp walks u in [0, c0 + P).  Right column = u + roff - p.
+        const int u_first = side ? 0 : c0;
+        const int u_end = side ? c0 + P : wp;
+        const int roff = side ? wp - c0 : -c0;
+        const int nch = (u_end - u_first + J - 1) / J;
 
         auto load4 = [&](const float *src, int gc) {
             float4 val = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
@@ -238,22 +268,22 @@ __global__ __launch_bounds__(64 * NW) void xcorr_bd_kernel(BdArgs a)
             return val;
         };
         auto load_chunk = [&](int t, float4 (&vl)[LPT], float4 (&vr)[RPT]) {
-            const int ja = j_first + t * J;
+            const int ua = u_first + t * J;
 #pragma unroll
             for (int k = 0; k < LPT; ++k)
-                vl[k] = load4(st_l, ja + lshift + cres + k * NW);
+                vl[k] = load4(st_l, ua + cres + k * NW);
 #pragma unroll
             for (int k = 0; k < RPT; ++k)
-                vr[k] = load4(st_r, ja + cres + k * NW);
+                vr[k] = load4(st_r, ua + roff - (P - 1) + cres + k * NW);
         };
         auto store_chunk = [&](float4 *buf, const float4 (&vl)[LPT], const float4 (&vr)[RPT]) {
             if (sb < S * nb) {
 #pragma unroll
                 for (int k = 0; k < LPT; ++k)
-                    if (cres + k * NW < G::NLR) buf[sb * G::NCL + cres + k * NW] = vl[k];
+                    if (cres + k * NW < G::NLU) buf[sb * G::NCL + cres + k * NW] = vl[k];
 #pragma unroll
                 for (int k = 0; k < RPT; ++k)
-                    buf[l_elems + sb * G::NCR + cres + k * NW] = vr[k];
+                    if (cres + k * NW < G::NRU) buf[l_elems + sb * G::NCR + cres + k * NW] = vr[k];
             }
         };
 
@@ -277,7 +307,7 @@ __global__ __launch_bounds__(64 * NW) void xcorr_bd_kernel(BdArgs a)
             const bool more = t + 1 < nch;
             if (more) load_chunk(t + 1, vl, vr);
             if (wave_on) {
-                const int ns = min(J, j_end - (j_first + t * J));
+                const int ns = min(J, u_end - (u_first + t * J));
                 const float4 *buf = smem + (t & 1) * buf_elems;
                 bd_compute<J>(buf + (s * nb + kb1) * G::NCL, buf + (s * nb + kb2) * G::NCL,
                               buf + l_elems + (s * nb + b) * G::NCR, ns, acc1, acc2);
@@ -296,7 +326,7 @@ __global__ __launch_bounds__(64 * NW) void xcorr_bd_kernel(BdArgs a)
                 for (int r = 0; r < 4; ++r) {
                     float c = acc1[r][p];
                     if (r >= 1 && b != bstar) c += acc2[r - 1][p];
-                    wred[(r * P + p) * 64 + lane] = c;
+                    wred[(r * P + p) * RS + lane] = c;
                 }
             if (b == bstar && lane < S * nb) {
 #pragma unroll
@@ -323,7 +353,7 @@ __global__ __launch_bounds__(64 * NW) void xcorr_bd_kernel(BdArgs a)
                     continue;
                 const int blo = wr ? nb - delta : 0;
                 const int bhi = wr ? nb : nb - delta;
-                const float *col = wred + (r * P + p) * 64 + sl * nb;
+                const float *col = wred + (r * P + p) * RS + sl * nb;
                 float sum = 0.0f;
                 for (int bb = blo; bb < bhi; ++bb)
                     sum += col[bb];
@@ -349,7 +379,7 @@ static hipError_t launch_bd(const BdArgs &b, hipStream_t s)
     using G = BdLds<J>;
     const size_t buf = (size_t)b.S * b.nb * (G::NCL + G::NCR);
     const size_t stage_bytes = 2 * buf * sizeof(float4);
-    const size_t red_bytes = (size_t)NW * (4 * BD_P * 64 + b.S * 3 * BD_P) * sizeof(float);
+    const size_t red_bytes = (size_t)NW * (4 * BD_P * 65 + b.S * 3 * BD_P) * sizeof(float);
     const size_t lds = stage_bytes + red_bytes;
     const unsigned blocks = (unsigned)((int64_t)b.n_groups * b.n_xtiles * b.n_dgroups);
     // Dynamic LDS above 64 KiB must be allowed explicitly (gfx950 has 160 KiB).
