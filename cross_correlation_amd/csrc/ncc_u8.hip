@@ -107,133 +107,94 @@ __device__ __forceinline__ void ncc_store(const NccArgs &a, size_t o, uint32_t s
     }
 }
 
-// Operands of one block of 4 template words: the lane's next 4 aligned image
-// words and, per output row q, 4 template words (one 16-byte LDS read at a
-// wave-uniform address).
-template <int Q>
-struct NccBlock {
-    uint32_t img[4];
-    uint4 t[Q];
-};
-
-template <int Q, bool FULL>
-__device__ __forceinline__ void ncc_load_block(NccBlock<Q> &blk, const uint32_t *rp, const uint32_t *t0,
-                                               int tstride, int k0, int qlo, int qhi)
-{
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        blk.img[i] = rp[k0 + 1 + i];
-#pragma unroll
-    for (int q = 0; q < Q; ++q) {
-        // rows outside the chunk are never used; read a valid row instead
-        const int qq = FULL ? q : min(max(q, qlo), qhi);
-        blk.t[q] = *reinterpret_cast<const uint4 *>(t0 - qq * tstride + k0);
-    }
-}
-
-// 4 template words: form the shifted image words and accumulate 3 x 4 dot4
-// per output row the image row serves.
-template <int Q, bool FULL>
-__device__ __forceinline__ void ncc_do_block(const NccBlock<Q> &blk, uint32_t &w0, int qlo, int qhi,
-                                             uint32_t (&ai)[Q][4], uint32_t (&aq)[Q][4], uint32_t (&at)[Q][4])
-{
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t w1 = blk.img[i];
-        uint32_t s[4];
-        s[0] = w0;
-        s[1] = shift_bytes(w1, w0, 1);
-        s[2] = shift_bytes(w1, w0, 2);
-        s[3] = shift_bytes(w1, w0, 3);
-#pragma unroll
-        for (int q = 0; q < Q; ++q) {
-            if (FULL || (q >= qlo && q <= qhi)) {
-                const uint32_t t = i == 0 ? blk.t[q].x : i == 1 ? blk.t[q].y : i == 2 ? blk.t[q].z : blk.t[q].w;
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    ai[q][c] = dot4u(s[c], 0x01010101u, ai[q][c]);
-                    aq[q][c] = dot4u(s[c], s[c], aq[q][c]);
-                    at[q][c] = dot4u(s[c], t, at[q][c]);
-                }
-            }
-        }
-        w0 = w1;
-    }
-}
-
-// One image row of one template chunk (cw words, a multiple of 4): for each
-// template word k load the next aligned image word, form the three shifted
-// words, and for each output row q the row serves accumulate 3 x 4 dot4 with
-// template row (rl - q).  Software-pipelined by one 4-word block: the LDS
-// reads of block b+1 are issued before the 204 VALU operations of block b,
-// alternating between two operand buffers (the loop body holds both, with an
-// exit after each, so no register copies are needed at the back-edge), and a
-// scheduling barrier per block keeps the reads from being hoisted further.
-template <int Q, bool FULL>
+// One image row of one template chunk: for each template word k of the chunk
+// load the next aligned image word, form the three shifted words, and for each
+// output row q the row serves accumulate 3 x 4 dot4 with template row (rl - q).
+// Image words and template words (at a wave-uniform address) both come from
+// LDS; WC words per unrolled step.
+template <int Q, int WC, bool FULL>
 __device__ __forceinline__ void ncc_row(const uint32_t *rp, const uint32_t *t0, int tstride, int cw,
                                         int qlo, int qhi, uint32_t (&ai)[Q][4], uint32_t (&aq)[Q][4],
                                         uint32_t (&at)[Q][4])
 {
-    const int nblk = cw >> 2;
     uint32_t w0 = rp[0];
-    NccBlock<Q> A, B;
-    ncc_load_block<Q, FULL>(A, rp, t0, tstride, 0, qlo, qhi);
-    for (int bk = 0;; bk += 2) {
-        if (bk + 1 < nblk)
-            ncc_load_block<Q, FULL>(B, rp, t0, tstride, 4 * (bk + 1), qlo, qhi);
-        ncc_do_block<Q, FULL>(A, w0, qlo, qhi, ai, aq, at);
-        __builtin_amdgcn_sched_barrier(0);
-        if (bk + 1 >= nblk)
-            break;
-        if (bk + 2 < nblk)
-            ncc_load_block<Q, FULL>(A, rp, t0, tstride, 4 * (bk + 2), qlo, qhi);
-        ncc_do_block<Q, FULL>(B, w0, qlo, qhi, ai, aq, at);
-        __builtin_amdgcn_sched_barrier(0);
-        if (bk + 2 >= nblk)
-            break;
-    }
-}
-
-// Template rows whose width is not a multiple of 16 bytes: one word at a time.
-template <int Q, bool FULL>
-__device__ __forceinline__ void ncc_row_words(const uint32_t *rp, const uint32_t *t0, int tstride, int cw,
-                                              int qlo, int qhi, uint32_t (&ai)[Q][4], uint32_t (&aq)[Q][4],
-                                              uint32_t (&at)[Q][4])
-{
-    uint32_t w0 = rp[0];
-    for (int k = 0; k < cw; ++k) {
-        const uint32_t w1 = rp[k + 1];
-        uint32_t s[4];
-        s[0] = w0;
-        s[1] = shift_bytes(w1, w0, 1);
-        s[2] = shift_bytes(w1, w0, 2);
-        s[3] = shift_bytes(w1, w0, 3);
+    for (int kb = 0; kb < cw; kb += WC) {
 #pragma unroll
-        for (int q = 0; q < Q; ++q) {
-            if (FULL || (q >= qlo && q <= qhi)) {
-                const uint32_t t = t0[k - q * tstride];
+        for (int kk = 0; kk < WC; ++kk) {
+            const int k = kb + kk;
+            const uint32_t w1 = rp[k + 1];
+            uint32_t s[4];
+            s[0] = w0;
+            s[1] = shift_bytes(w1, w0, 1);
+            s[2] = shift_bytes(w1, w0, 2);
+            s[3] = shift_bytes(w1, w0, 3);
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    ai[q][c] = dot4u(s[c], 0x01010101u, ai[q][c]);
-                    aq[q][c] = dot4u(s[c], s[c], aq[q][c]);
-                    at[q][c] = dot4u(s[c], t, at[q][c]);
+            for (int q = 0; q < Q; ++q) {
+                if (FULL || (q >= qlo && q <= qhi)) {
+                    const uint32_t t = t0[k - q * tstride];
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        ai[q][c] = dot4u(s[c], 0x01010101u, ai[q][c]);
+                        aq[q][c] = dot4u(s[c], s[c], aq[q][c]);
+                        at[q][c] = dot4u(s[c], t, at[q][c]);
+                    }
                 }
             }
+            w0 = w1;
         }
-        w0 = w1;
     }
 }
 
-// Main kernel: a workgroup of WV waves covers 256 output columns x WV*Q rows;
-// wave w owns rows [w*Q, w*Q + Q) of the tile, lane l owns columns 4l..4l+3.
+// A row at the start or end of a template slice serves only output rows
+// q in [qlo, qhi].  The (wave-uniform) test is taken once per q, outside the
+// word loop; the row's words are re-read per q (only 2*(Q-1) rows per slice).
+template <int Q>
+__device__ __forceinline__ void ncc_row_partial(const uint32_t *rp, const uint32_t *t0, int tstride, int cw,
+                                                int qlo, int qhi, uint32_t (&ai)[Q][4],
+                                                uint32_t (&aq)[Q][4], uint32_t (&at)[Q][4])
+{
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        if (q < qlo || q > qhi)
+            continue;
+        const uint32_t *tq = t0 - q * tstride;
+        uint32_t w0 = rp[0];
+        for (int k = 0; k < cw; ++k) {
+            const uint32_t w1 = rp[k + 1];
+            const uint32_t t = tq[k];
+            uint32_t s[4];
+            s[0] = w0;
+            s[1] = shift_bytes(w1, w0, 1);
+            s[2] = shift_bytes(w1, w0, 2);
+            s[3] = shift_bytes(w1, w0, 3);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                ai[q][c] = dot4u(s[c], 0x01010101u, ai[q][c]);
+                aq[q][c] = dot4u(s[c], s[c], aq[q][c]);
+                at[q][c] = dot4u(s[c], t, at[q][c]);
+            }
+            w0 = w1;
+        }
+    }
+}
+
+// Main kernel: a workgroup covers 256 output columns x WV*Q rows with
+// WV*KS waves.  Wave (rw, kh) owns output rows [rw*Q, rw*Q + Q) of the tile
+// and the kh-th of KS slices of the template rows; lane l owns columns
+// 4l..4l+3.  Splitting the template rows over KS waves multiplies the waves
+// in flight per SIMD (the dot4 issue rate needs several) without shrinking
+// the Q*4 outputs a lane's shifted words are shared by.  The KS partial sums
+// are added through LDS before the epilogue.
 // LDS: the image tile (WV*Q + hc - 1 rows of `lds_stride` words), then the
 // template chunk (hc rows of `t_stride` words).
-template <int Q, int WV, bool V4>
-__global__ __launch_bounds__(64 * WV) void ncc_u8_ilp_kernel(NccArgs a)
+template <int Q, int WV, int KS, int WC>
+__global__ __launch_bounds__(64 * WV * KS) void ncc_u8_ilp_kernel(NccArgs a)
 {
     extern __shared__ uint32_t lds[];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int rw = wave % WV;  // output-row group of this wave
+    const int kh = wave / WV;  // template-row slice of this wave
     const int x0 = blockIdx.x * 256;
     const int y0 = blockIdx.y * (WV * Q);
     const int nw = a.t_width >> 2;
@@ -254,35 +215,69 @@ __global__ __launch_bounds__(64 * WV) void ncc_u8_ilp_kernel(NccArgs a)
     uint32_t *const tl = lds + (WV * Q + a.hc - 1) * stride;
     for (int jc = 0; jc < a.t_height; jc += a.hc) {
         const int hc = min(a.hc, a.t_height - jc);
+        // this wave's template rows of the chunk: [j0, j1)
+        const int j0 = hc * kh / KS;
+        const int j1 = hc * (kh + 1) / KS;
         for (int ic = 0; ic < nw; ic += a.cw) {
             const int cw = min(a.cw, nw - ic);
             __syncthreads();
             // lane l reads words l + k and l + k + 1, k < cw: 64 + cw words per row
             stage_tile(a.image, a.height, a.pitch, y0 + jc, x0 + 4 * ic, WV * Q + hc - 1,
                        (64 + cw + 3) / 4, lds, stride);
-            for (int t = threadIdx.x; t < hc * cw; t += 64 * WV) {
+            for (int t = threadIdx.x; t < hc * cw; t += 64 * WV * KS) {
                 const int r = t / cw;
                 const int c = t - r * cw;
                 tl[r * tstride + c] = tw[(size_t)(jc + r) * nw + ic + c];
             }
             __syncthreads();
-            const uint32_t *wrow = lds + (wave * Q) * stride + lane;
-            for (int rl = 0; rl < Q + hc - 1; ++rl) {
-                const int qlo = max(0, rl - hc + 1);
-                const int qhi = min(Q - 1, rl);
-                const uint32_t *t0 = tl + rl * tstride;
-                if (V4) {
-                    if (qlo == 0 && qhi == Q - 1)
-                        ncc_row<Q, true>(wrow + rl * stride, t0, tstride, cw, qlo, qhi, ai, aq, at);
-                    else
-                        ncc_row<Q, false>(wrow + rl * stride, t0, tstride, cw, qlo, qhi, ai, aq, at);
-                } else {
-                    if (qlo == 0 && qhi == Q - 1)
-                        ncc_row_words<Q, true>(wrow + rl * stride, t0, tstride, cw, qlo, qhi, ai, aq, at);
-                    else
-                        ncc_row_words<Q, false>(wrow + rl * stride, t0, tstride, cw, qlo, qhi, ai, aq, at);
-                }
+            if (j1 > j0) {
+                const uint32_t *wrow = lds + (rw * Q) * stride + lane;
+                // Image rows rl (relative to the wave's first output row) meet
+                // template rows j = rl - q with j in [j0, j1).  Three straight
+                // loops -- ramp-up, steady (every q), ramp-down -- so the
+                // accumulators never meet a branch merge inside the row loop.
+                const int steady0 = j0 + Q - 1;
+                for (int rl = j0; rl < min(steady0, j1 + Q - 1); ++rl)
+                    ncc_row_partial<Q>(wrow + rl * stride, tl + rl * tstride, tstride, cw, max(0, rl - j1 + 1),
+                                       min(Q - 1, rl - j0), ai, aq, at);
+                for (int rl = steady0; rl < j1; ++rl)
+                    ncc_row<Q, WC, true>(wrow + rl * stride, tl + rl * tstride, tstride, cw, 0, Q - 1, ai, aq, at);
+                for (int rl = max(j1, steady0); rl < j1 + Q - 1; ++rl)
+                    ncc_row_partial<Q>(wrow + rl * stride, tl + rl * tstride, tstride, cw, max(0, rl - j1 + 1),
+                                       min(Q - 1, rl - j0), ai, aq, at);
             }
+        }
+    }
+
+    if (KS > 1) {
+        // add the slices: waves kh > 0 leave their sums in LDS for wave kh = 0
+        __syncthreads();
+        constexpr int NACC = 3 * 4 * Q;
+        uint32_t *xbuf = lds + (size_t)rw * (KS - 1) * NACC * 64;
+        if (kh > 0) {
+            uint32_t *mine = xbuf + (size_t)(kh - 1) * NACC * 64 + lane;
+#pragma unroll
+            for (int q = 0; q < Q; ++q)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    mine[((q * 4 + c) * 3 + 0) * 64] = ai[q][c];
+                    mine[((q * 4 + c) * 3 + 1) * 64] = aq[q][c];
+                    mine[((q * 4 + c) * 3 + 2) * 64] = at[q][c];
+                }
+        }
+        __syncthreads();
+        if (kh > 0)
+            return;
+        for (int o = 0; o < KS - 1; ++o) {
+            const uint32_t *other = xbuf + (size_t)o * NACC * 64 + lane;
+#pragma unroll
+            for (int q = 0; q < Q; ++q)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    ai[q][c] += other[((q * 4 + c) * 3 + 0) * 64];
+                    aq[q][c] += other[((q * 4 + c) * 3 + 1) * 64];
+                    at[q][c] += other[((q * 4 + c) * 3 + 2) * 64];
+                }
         }
     }
 
@@ -291,7 +286,7 @@ __global__ __launch_bounds__(64 * WV) void ncc_u8_ilp_kernel(NccArgs a)
     const int64_t vt = n * (int64_t)sum_tsq - st64 * st64;
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
-        const int y = y0 + wave * Q + q;
+        const int y = y0 + rw * Q + q;
         if (y >= a.out_h)
             break;
 #pragma unroll
@@ -369,39 +364,50 @@ __global__ __launch_bounds__(256) void ncc_u8_c1_kernel(NccArgs a)
 // ---------------------------------------------------------------------------
 // Host-side launch helpers (called by the C ABI after validation).
 
-template <int Q, int WV, bool V4>
+template <int Q, int WV, int KS, int WC>
 static hipError_t launch_ilp(const NccArgs &a, hipStream_t s)
 {
     dim3 grid((a.out_w + 255) / 256, (a.out_h + WV * Q - 1) / (WV * Q));
-    const size_t lds = ((size_t)(WV * Q + a.hc - 1) * a.lds_stride + (size_t)a.hc * a.t_stride) * 4;
-    hipLaunchKernelGGL((ncc_u8_ilp_kernel<Q, WV, V4>), grid, dim3(64 * WV), lds, s, a);
+    size_t lds = ((size_t)(WV * Q + a.hc - 1) * a.lds_stride + (size_t)a.hc * a.t_stride) * 4;
+    const size_t xchg = (size_t)WV * (KS - 1) * 3 * 4 * Q * 64 * 4;  // slice exchange, reuses the tile
+    if (xchg > lds) lds = xchg;
+    hipLaunchKernelGGL((ncc_u8_ilp_kernel<Q, WV, KS, WC>), grid, dim3(64 * WV * KS), lds, s, a);
     return hipGetLastError();
 }
 
-template <int Q, int WV>
-static hipError_t dispatch_v4(const NccArgs &a, bool v4, hipStream_t s)
+template <int Q, int WV, int KS>
+static hipError_t dispatch_wc(const NccArgs &a, int wc, hipStream_t s)
 {
-    return v4 ? launch_ilp<Q, WV, true>(a, s) : launch_ilp<Q, WV, false>(a, s);
+    switch (wc) {
+    case 4: return launch_ilp<Q, WV, KS, 4>(a, s);
+    case 2: return launch_ilp<Q, WV, KS, 2>(a, s);
+    default: return launch_ilp<Q, WV, KS, 1>(a, s);
+    }
 }
 
-// Chooses the tile (Q rows per lane, WV waves), the unroll WC and the chunking
-// so that the LDS tile stays within 64 KiB.
+// Chooses the tile (Q rows per lane, WV row waves, KS template slices), the
+// unroll WC and the chunking so that the LDS tile stays within 64 KiB.
 hipError_t ncc_launch_ilp(NccArgs a, hipStream_t s)
 {
     const int nw = a.t_width / 4;
-    // Rows of 4-word blocks when every chunk is a multiple of 16 bytes wide.
-    const bool v4 = nw % 4 == 0;
+    // Unroll of the template-word loop: the largest power of two <= 4 that
+    // divides the words per template row (every chunk is a multiple of it).
+    int wc = 4;
+    while (nw % wc) wc >>= 1;
     // Tile shape: the big tile when the image yields enough work to fill
-    // 256 CUs, smaller ones for small images.
+    // 256 CUs, smaller ones for small images; the template-row split when
+    // the template is tall enough to give each slice several rows.
     int q = 4, wv = 4;
     const long col_tiles = (a.out_w + 255) / 256;
     if (col_tiles * ((a.out_h + 15) / 16) < 256) { q = 2; wv = 2; }
     if (col_tiles * ((a.out_h + 3) / 4) < 256) { q = 1; wv = 1; }
+    const int ks = (q == 4 && a.t_height >= 16) ? 2 : 1;
     const int lds_words = 64 * 1024 / 4;
-    // chunk of template words: a multiple of 4 words (16-byte aligned chunk starts)
+    // chunk of template words: a multiple of lcm(wc, 4) words (16-byte aligned chunk starts)
+    const int unit = 4;
     int cw = nw;
     const int max_cw = 960;
-    if (cw > max_cw) cw = max_cw;
+    if (cw > max_cw) cw = max_cw / unit * unit;
     a.cw = cw;
     a.lds_stride = (64 + cw + 3) / 4 * 4;
     a.t_stride = (cw + 3) / 4 * 4;
@@ -411,9 +417,9 @@ hipError_t ncc_launch_ilp(NccArgs a, hipStream_t s)
     if (hc < 1) hc = 1;
     if (hc > a.t_height) hc = a.t_height;
     a.hc = hc;
-    if (q == 4) return dispatch_v4<4, 4>(a, v4, s);
-    if (q == 2) return dispatch_v4<2, 2>(a, v4, s);
-    return dispatch_v4<1, 1>(a, v4, s);
+    if (q == 4) return ks == 2 ? dispatch_wc<4, 4, 2>(a, wc, s) : dispatch_wc<4, 4, 1>(a, wc, s);
+    if (q == 2) return dispatch_wc<2, 2, 1>(a, wc, s);
+    return dispatch_wc<1, 1, 1>(a, wc, s);
 }
 
 hipError_t ncc_launch_c1(NccArgs a, bool dot4, hipStream_t s)
