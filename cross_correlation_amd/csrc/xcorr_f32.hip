@@ -101,9 +101,11 @@ struct BdArgs {
     int nb;          // row blocks of 4 (rows padded with zero rows to 4*nb)
     int wp;          // columns padded with zero columns to a multiple of BD_P
     int S;           // pairs per wave (slots); S * nb <= 64
+    int nls;         // distinct left matrices a pair group can touch (LDS slots)
     int n_groups;    // pair groups of S pairs
     int n_xtiles;    // wp / BD_P
     int n_dgroups;   // ceil(nb / waves per workgroup)
+    int n_sides;     // 1: a workgroup walks both dx signs; 2: one sign each
 };
 
 // LDS geometry of one staging buffer for J walk steps: per row block, J left
@@ -185,44 +187,152 @@ __device__ __forceinline__ void bd_compute(const float4 *Lb1, const float4 *Lb2,
     }
 }
 
+// Geometry shared by both staging modes: which pairs, diagonal and column
+// tile a workgroup / wave / lane works on.
+struct BdWho {
+    int lane, wave, grp, c0, delta, s, b, kb1, kb2, ls, bstar, side_lo, side_hi;
+    bool wave_on;
+};
+
+template <int NW>
+__device__ __forceinline__ BdWho bd_who(const BdArgs &a)
+{
+    BdWho w;
+    w.lane = threadIdx.x & 63;
+    w.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    int bid = blockIdx.x;
+    const int side = bid % a.n_sides;
+    bid /= a.n_sides;
+    const int dgrp = bid % a.n_dgroups;
+    bid /= a.n_dgroups;
+    const int xt = bid % a.n_xtiles;
+    w.grp = bid / a.n_xtiles;
+    w.c0 = xt * BD_P;
+    w.side_lo = a.n_sides == 2 ? side : 0;
+    w.side_hi = a.n_sides == 2 ? side + 1 : 2;
+    w.delta = dgrp * NW + w.wave;  // this wave's block diagonal
+    w.wave_on = w.delta < a.nb;
+    const int nb = a.nb;
+    int sl = w.lane / nb;
+    w.b = w.lane - sl * nb;
+    if (sl >= a.S) sl = a.S - 1;  // spare lanes shadow the last slot; never stored
+    w.s = sl;
+    const int dl = w.wave_on ? w.delta : 0;
+    w.kb1 = (w.b + dl) % nb;
+    w.kb2 = (w.b + dl + 1) % nb;
+    // left-matrix slot: distinct left matrices of the group, in order
+    const int64_t p0 = (int64_t)w.grp * a.S;
+    const int64_t np = (int64_t)a.x.n_left * a.x.n_right;
+    const int64_t ps = min(p0 + sl, np - 1);
+    w.ls = (int)(ps / a.x.n_right - p0 / a.x.n_right);
+    w.bstar = nb - dl - 1;  // the lane whose block 1 is unwrapped and block 2 wrapped
+    return w;
+}
+
+// Cross-lane reduction of one side's partial sums, in a fixed order, then the
+// stores.  Each wave uses only its own LDS area, so a wave-level barrier
+// suffices.  comb = block-1 sums plus block-2 sums when both blocks share the
+// wrap status (every lane but bstar); bstar keeps its block-2 sums apart.
+__device__ __forceinline__ void bd_reduce_store(const BdArgs &a, const BdWho &w, int side, float *wred,
+                                                float *wextra, const float (&acc1)[4][BD_P],
+                                                const float (&acc2)[3][BD_P])
+{
+    constexpr int P = BD_P;
+    constexpr int NV = 4 * P;
+    constexpr int RS = 65;  // row stride: lanes reading different rows hit different banks
+    const int nb = a.nb, S = a.S;
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float c = acc1[r][p];
+            if (r >= 1 && w.b != w.bstar) c += acc2[r - 1][p];
+            wred[(r * P + p) * RS + w.lane] = c;
+        }
+    if (w.b == w.bstar && w.lane < S * nb) {
+#pragma unroll
+        for (int p = 0; p < P; ++p)
+#pragma unroll
+            for (int r = 0; r < 3; ++r)
+                wextra[(w.s * 3 + r) * P + p] = acc2[r][p];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int rows = a.x.rows, cols = a.x.cols, h4 = 4 * nb;
+    const int oh = 2 * rows - 1, ow = 2 * cols - 1;
+    const int64_t npairs = (int64_t)a.x.n_left * a.x.n_right;
+    const int per_slot = NV * 2;  // (r, wrapped, p), p fastest: 4 lanes store 16 contiguous bytes
+    for (int o = w.lane; o < S * per_slot; o += 64) {
+        const int sl = o / per_slot;
+        const int q = o - sl * per_slot;
+        const int p = q % P;
+        const int wr = (q / P) & 1;
+        const int r = q / (2 * P);
+        const int64_t pair = (int64_t)w.grp * S + sl;
+        const int dy = 4 * w.delta + r - (wr ? h4 : 0);
+        const int c = w.c0 + p;
+        const int dx = side ? c - a.wp : c;
+        const bool keep = pair < npairs && dy > -rows && dy < rows && dx > -cols && dx < cols;
+        const int blo = wr ? nb - w.delta : 0;
+        const int bhi = wr ? nb : nb - w.delta;
+        const float *col = wred + (r * P + p) * RS + sl * nb;
+        // eight independent partial sums, combined in a fixed tree order
+        float part[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) part[i] = 0.0f;
+        for (int bb = blo; bb < bhi; bb += 8) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if (bb + i < bhi) part[i] += col[bb + i];
+        }
+        float sum = ((part[0] + part[1]) + (part[2] + part[3])) + ((part[4] + part[5]) + (part[6] + part[7]));
+        if (wr && r >= 1)
+            sum += wextra[(sl * 3 + (r - 1)) * P + p];
+        if (keep)
+            a.x.out[((size_t)pair * oh + (dy + rows - 1)) * ow + (dx + cols - 1)] = sum;
+    }
+    // the next side's writes come after these reads in every lane's program
+    // order and LDS serves one wave in order
+    __builtin_amdgcn_wave_barrier();
+}
+
+// Reduction area per wave (floats).
+__host__ __device__ constexpr int bd_red_floats(int S) { return 4 * BD_P * 65 + S * 3 * BD_P; }
+
+// The 4 rows of a row block at one column (zero outside the matrix).
+__device__ __forceinline__ float4 bd_load4(const float *src, int nrow_ok, int gc, int cols, bool on)
+{
+    float4 val = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (on && nrow_ok > 0 && gc >= 0 && gc < cols) {
+        val.x = src[gc];
+        if (nrow_ok > 1) val.y = src[(size_t)cols + gc];
+        if (nrow_ok > 2) val.z = src[(size_t)2 * cols + gc];
+        if (nrow_ok > 3) val.w = src[(size_t)3 * cols + gc];
+    }
+    return val;
+}
+
+// ---- chunked staging: columns pass through LDS J walk steps at a time ----
 template <int NW, int J>
-__global__ __launch_bounds__(64 * NW) void xcorr_bd_kernel(BdArgs a)
+__global__ __launch_bounds__(64 * NW) void xcorr_bd_chunk_kernel(BdArgs a)
 {
     constexpr int P = BD_P;
     using G = BdLds<J>;
     extern __shared__ float4 smem[];
-
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    int bid = blockIdx.x;
-    const int dgrp = bid % a.n_dgroups;
-    bid /= a.n_dgroups;
-    const int xt = bid % a.n_xtiles;
-    const int grp = bid / a.n_xtiles;
-    const int c0 = xt * P;
+    const BdWho w = bd_who<NW>(a);
     const int nb = a.nb, S = a.S, wp = a.wp;
     const int rows = a.x.rows, cols = a.x.cols;
-    const int h4 = 4 * nb;
     const int64_t npairs = (int64_t)a.x.n_left * a.x.n_right;
-    const int delta = dgrp * NW + wave;  // this wave's block diagonal
-    const bool wave_on = delta < nb;
 
-    int s = lane / nb;
-    const int b = lane - s * nb;
-    if (s >= S) s = S - 1;  // spare lanes shadow the last slot; never stored
-    const int dl = wave_on ? delta : 0;
-    const int kb1 = (b + dl) % nb;
-    const int kb2 = (b + dl + 1) % nb;
-
-    // LDS: two staging buffers, each L [S][nb][NCL] then R [S][nb][NCR], then
-    // the reduction area.
+    // LDS: two staging buffers, each L [S][nb][NCL] then R [S][nb][NCR].  A
+    // side's reduction runs in the staging area once its last chunk is done
+    // (a barrier separates it from the next side's staging).
     const int l_elems = S * nb * G::NCL;
     const int buf_elems = l_elems + S * nb * G::NCR;
-    constexpr int NV = 4 * P;  // per-lane partial sums per side: (r, p)
-    constexpr int RS = 65;     // reduction row stride (odd: lanes reading different rows hit different banks)
-    float *const red = reinterpret_cast<float *>(smem + 2 * buf_elems);
-    float *const wred = red + wave * (NV * RS + S * 3 * P);
-    float *const wextra = wred + NV * RS;
+    float *const red = reinterpret_cast<float *>(smem);
+    float *const wred = red + w.wave * bd_red_floats(S);
+    float *const wextra = wred + 4 * P * 65;
 
     // Staging: thread t owns row block sb = t / NW (slot * nb + block, all
     // S*nb <= 64 blocks) and the columns congruent to t mod NW.  One item is
@@ -235,7 +345,7 @@ __global__ __launch_bounds__(64 * NW) void xcorr_bd_kernel(BdArgs a)
     const int cres = tid - sb * NW;
     const int st_slot = sb / nb;
     const int st_row0 = 4 * (sb - st_slot * nb);
-    const int64_t st_pair = (int64_t)grp * S + st_slot;
+    const int64_t st_pair = (int64_t)w.grp * S + st_slot;
     const bool st_on = sb < S * nb && st_pair < npairs;
     const float *st_l = a.x.left;
     const float *st_r = a.x.right;
@@ -245,36 +355,24 @@ __global__ __launch_bounds__(64 * NW) void xcorr_bd_kernel(BdArgs a)
         st_l += ((size_t)l * rows + st_row0) * cols;
         st_r += ((size_t)r * rows + st_row0) * cols;
     }
-    const int nrow_ok = min(4, rows - st_row0);  // rows of the block inside the matrix
-    const int bstar = nb - dl - 1;  // the lane whose block 1 is unwrapped and block 2 wrapped
-    const int oh = 2 * rows - 1, ow = 2 * cols - 1;
+    const int nrow_ok = min(4, rows - st_row0);
 
-    for (int side = 0; side < 2; ++side) {
+    for (int side = w.side_lo; side < w.side_hi; ++side) {
         // Walk over left columns u; positive dx = c walks u in [c0, wp),
         // negative dx = c - wp walks u in [0, c0 + P).  Right column = u + roff - p.
-        const int u_first = side ? 0 : c0;
-        const int u_end = side ? c0 + P : wp;
-        const int roff = side ? wp - c0 : -c0;
+        const int u_first = side ? 0 : w.c0;
+        const int u_end = side ? w.c0 + P : wp;
+        const int roff = side ? wp - w.c0 : -w.c0;
         const int nch = (u_end - u_first + J - 1) / J;
 
-        auto load4 = [&](const float *src, int gc) {
-            float4 val = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-            if (st_on && nrow_ok > 0 && gc >= 0 && gc < cols) {
-                val.x = src[gc];
-                if (nrow_ok > 1) val.y = src[(size_t)cols + gc];
-                if (nrow_ok > 2) val.z = src[(size_t)2 * cols + gc];
-                if (nrow_ok > 3) val.w = src[(size_t)3 * cols + gc];
-            }
-            return val;
-        };
         auto load_chunk = [&](int t, float4 (&vl)[LPT], float4 (&vr)[RPT]) {
             const int ua = u_first + t * J;
 #pragma unroll
             for (int k = 0; k < LPT; ++k)
-                vl[k] = load4(st_l, ua + cres + k * NW);
+                vl[k] = bd_load4(st_l, nrow_ok, ua + cres + k * NW, cols, st_on);
 #pragma unroll
             for (int k = 0; k < RPT; ++k)
-                vr[k] = load4(st_r, ua + roff - (P - 1) + cres + k * NW);
+                vr[k] = bd_load4(st_r, nrow_ok, ua + roff - (P - 1) + cres + k * NW, cols, st_on);
         };
         auto store_chunk = [&](float4 *buf, const float4 (&vl)[LPT], const float4 (&vr)[RPT]) {
             if (sb < S * nb) {
@@ -306,64 +404,110 @@ __global__ __launch_bounds__(64 * NW) void xcorr_bd_kernel(BdArgs a)
             float4 vl[LPT], vr[RPT];
             const bool more = t + 1 < nch;
             if (more) load_chunk(t + 1, vl, vr);
-            if (wave_on) {
+            if (w.wave_on) {
                 const int ns = min(J, u_end - (u_first + t * J));
                 const float4 *buf = smem + (t & 1) * buf_elems;
-                bd_compute<J>(buf + (s * nb + kb1) * G::NCL, buf + (s * nb + kb2) * G::NCL,
-                              buf + l_elems + (s * nb + b) * G::NCR, ns, acc1, acc2);
+                bd_compute<J>(buf + (w.s * nb + w.kb1) * G::NCL, buf + (w.s * nb + w.kb2) * G::NCL,
+                              buf + l_elems + (w.s * nb + w.b) * G::NCR, ns, acc1, acc2);
             }
             if (more) store_chunk(smem + ((t + 1) & 1) * buf_elems, vl, vr);
             __syncthreads();
         }
+        if (w.wave_on)
+            bd_reduce_store(a, w, side, wred, wextra, acc1, acc2);
+        __syncthreads();  // reduction reads done before the next side stages
+    }
+}
 
-        // ---- cross-lane reduction in a fixed order, then store ----
-        // comb: block-1 sums plus block-2 sums when both blocks share the wrap
-        // status (every lane but bstar); bstar keeps its block-2 sums apart.
-        if (wave_on) {
+// ---- whole staging: both matrices of every pair of the group (with zero
+// column halos) are staged once; every wave then walks both dx signs straight
+// from LDS, with no further workgroup barrier ----
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void xcorr_bd_whole_kernel(BdArgs a)
+{
+    constexpr int P = BD_P;
+    extern __shared__ float4 smem[];
+    const BdWho w = bd_who<NW>(a);
+    const int nb = a.nb, S = a.S, wp = a.wp;
+    const int rows = a.x.rows, cols = a.x.cols;
+    const int64_t npairs = (int64_t)a.x.n_left * a.x.n_right;
+    // left: nls slots x nb blocks x LW columns (column u at index u; index wp
+    // is padding read by the pipelined walk); right: S slots x nb blocks x RW
+    // columns (right column c at index c + P - 1, zero halos on both sides).
+    const int LW = (wp + 1) | 1;
+    const int RW = (wp + 2 * P) | 1;
+    const int l_elems = a.nls * nb * LW;
+    float4 *const Ls = smem;
+    float4 *const Rs = smem + l_elems;
+    float *const red = reinterpret_cast<float *>(smem + l_elems + S * nb * RW);
+    float *const wred = red + w.wave * bd_red_floats(S);
+    float *const wextra = wred + 4 * P * 65;
+
+    const int64_t p0 = (int64_t)w.grp * S;
+    const int l_first = (int)(p0 / a.x.n_right);
+    const int nthreads = 64 * NW;
+    // Items: (left slot, block, column) then (pair slot, block, column index
+    // c + P - 1).  Each thread takes items in batches of SB: all loads of a
+    // batch are issued before any of its LDS stores, so the global-memory
+    // latency is paid once per batch rather than once per item.
+    const int nli = a.nls * nb * LW;
+    const int nit = nli + S * nb * RW;
+    constexpr int SB = 8;
+    for (int it0 = threadIdx.x; it0 < nit; it0 += SB * nthreads) {
+        float4 v[SB];
 #pragma unroll
-            for (int p = 0; p < P; ++p)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    float c = acc1[r][p];
-                    if (r >= 1 && b != bstar) c += acc2[r - 1][p];
-                    wred[(r * P + p) * RS + lane] = c;
-                }
-            if (b == bstar && lane < S * nb) {
-#pragma unroll
-                for (int p = 0; p < P; ++p)
-#pragma unroll
-                    for (int r = 0; r < 3; ++r)
-                        wextra[(s * 3 + r) * P + p] = acc2[r][p];
+        for (int k = 0; k < SB; ++k) {
+            const int it = it0 + k * nthreads;
+            v[k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            if (it < nli) {
+                const int blk = it / LW;
+                const int col = it - blk * LW;
+                const int lsl = blk / nb;
+                const int row0 = 4 * (blk - lsl * nb);
+                const int l = l_first + lsl;
+                const bool on = l < a.x.n_left && col < wp;
+                const float *src = a.x.left + ((size_t)(on ? l : 0) * rows + row0) * cols;
+                v[k] = bd_load4(src, min(4, rows - row0), col, cols, on);
+            } else if (it < nit) {
+                const int it2 = it - nli;
+                const int blk = it2 / RW;
+                const int col = it2 - blk * RW;
+                const int sl = blk / nb;
+                const int row0 = 4 * (blk - sl * nb);
+                const int64_t pair = p0 + sl;
+                const bool on = pair < npairs;
+                const int r = on ? (int)(pair % a.x.n_right) : 0;
+                const float *src = a.x.right + ((size_t)r * rows + row0) * cols;
+                v[k] = bd_load4(src, min(4, rows - row0), col - (P - 1), cols, on);
             }
         }
-        __syncthreads();
-        if (wave_on) {
-            const int per_slot = NV * 2;  // (r, p, wrapped)
-            for (int o = lane; o < S * per_slot; o += 64) {
-                const int sl = o / per_slot;
-                const int q = o - sl * per_slot;
-                const int wr = q & 1;
-                const int p = (q >> 1) % P;
-                const int r = (q >> 1) / P;
-                const int64_t pair = (int64_t)grp * S + sl;
-                const int dy = 4 * delta + r - (wr ? h4 : 0);
-                const int c = c0 + p;
-                const int dx = side ? c - wp : c;
-                if (pair >= npairs || dy <= -rows || dy >= rows || dx <= -cols || dx >= cols)
-                    continue;
-                const int blo = wr ? nb - delta : 0;
-                const int bhi = wr ? nb : nb - delta;
-                const float *col = wred + (r * P + p) * RS + sl * nb;
-                float sum = 0.0f;
-                for (int bb = blo; bb < bhi; ++bb)
-                    sum += col[bb];
-                if (wr && r >= 1)
-                    sum += wextra[(sl * 3 + (r - 1)) * P + p];
-                a.x.out[((size_t)pair * oh + (dy + rows - 1)) * ow + (dx + cols - 1)] = sum;
-            }
+#pragma unroll
+        for (int k = 0; k < SB; ++k) {
+            const int it = it0 + k * nthreads;
+            if (it < nit)
+                smem[it] = v[k];  // left items then right items are contiguous in LDS
         }
-        // The next side's first barrier orders these reads before the
-        // reduction area is written again.
+    }
+    __syncthreads();
+    if (!w.wave_on)
+        return;
+    for (int side = w.side_lo; side < w.side_hi; ++side) {
+        const int u_first = side ? 0 : w.c0;
+        const int u_end = side ? w.c0 + P : wp;
+        const int roff = side ? wp - w.c0 : -w.c0;
+        float acc1[4][P], acc2[3][P];
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc1[r][p] = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 3; ++r) acc2[r][p] = 0.0f;
+        }
+        // ring preload reads right columns u_first + roff - (P-1) .. u_first + roff,
+        // i.e. indices u_first + roff .. + P - 1 (>= 0: roff >= -c0 and u_first >= c0 on side 0)
+        bd_compute<16>(Ls + (w.ls * nb + w.kb1) * LW + u_first, Ls + (w.ls * nb + w.kb2) * LW + u_first,
+                       Rs + (w.s * nb + w.b) * RW + u_first + roff, u_end - u_first, acc1, acc2);
+        bd_reduce_store(a, w, side, wred, wextra, acc1, acc2);
     }
 }
 
@@ -373,25 +517,61 @@ bool xcorr_blockdiag_supported(const XcorrArgs &a)
     return nb >= 4 && nb <= 64;
 }
 
+template <typename K>
+static hipError_t allow_lds(K kernel)
+{
+    // Dynamic LDS above 64 KiB must be allowed explicitly (gfx950 has 160 KiB).
+    return hipFuncSetAttribute(reinterpret_cast<const void *>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                               160 * 1024);
+}
+
+constexpr size_t BD_LDS_MAX = 160 * 1024;
+
+static size_t bd_whole_lds(const BdArgs &b, int nw)
+{
+    const size_t LW = (size_t)((b.wp + 1) | 1), RW = (size_t)((b.wp + 2 * BD_P) | 1);
+    return (b.nls * b.nb * LW + (size_t)b.S * b.nb * RW) * sizeof(float4) +
+           (size_t)nw * bd_red_floats(b.S) * sizeof(float);
+}
+
 template <int NW, int J>
-static hipError_t launch_bd(const BdArgs &b, hipStream_t s)
+static size_t bd_chunk_lds(const BdArgs &b)
 {
     using G = BdLds<J>;
-    const size_t buf = (size_t)b.S * b.nb * (G::NCL + G::NCR);
-    const size_t stage_bytes = 2 * buf * sizeof(float4);
-    const size_t red_bytes = (size_t)NW * (4 * BD_P * 65 + b.S * 3 * BD_P) * sizeof(float);
-    const size_t lds = stage_bytes + red_bytes;
-    const unsigned blocks = (unsigned)((int64_t)b.n_groups * b.n_xtiles * b.n_dgroups);
-    // Dynamic LDS above 64 KiB must be allowed explicitly (gfx950 has 160 KiB).
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&xcorr_bd_kernel<NW, J>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        if (e != hipSuccess)
-            return e;
-        attr_set = true;
+    const size_t stage = 2 * (size_t)b.S * b.nb * (G::NCL + G::NCR) * sizeof(float4);
+    const size_t red = (size_t)NW * bd_red_floats(b.S) * sizeof(float);
+    return stage > red ? stage : red;
+}
+
+template <int NW>
+static hipError_t launch_whole(BdArgs b, hipStream_t s)
+{
+    static bool attr = false;
+    if (!attr) {
+        const hipError_t e = allow_lds(&xcorr_bd_whole_kernel<NW>);
+        if (e != hipSuccess) return e;
+        attr = true;
     }
-    hipLaunchKernelGGL((xcorr_bd_kernel<NW, J>), dim3(blocks), dim3(64 * NW), lds, s, b);
+    b.n_dgroups = (b.nb + NW - 1) / NW;
+    const unsigned blocks = (unsigned)((int64_t)b.n_groups * b.n_xtiles * b.n_dgroups * b.n_sides);
+    const size_t lds = bd_whole_lds(b, NW);
+    hipLaunchKernelGGL((xcorr_bd_whole_kernel<NW>), dim3(blocks), dim3(64 * NW), lds, s, b);
+    return hipGetLastError();
+}
+
+template <int NW, int J>
+static hipError_t launch_chunk(BdArgs b, hipStream_t s)
+{
+    static bool attr = false;
+    if (!attr) {
+        const hipError_t e = allow_lds(&xcorr_bd_chunk_kernel<NW, J>);
+        if (e != hipSuccess) return e;
+        attr = true;
+    }
+    b.n_dgroups = (b.nb + NW - 1) / NW;
+    const unsigned blocks = (unsigned)((int64_t)b.n_groups * b.n_xtiles * b.n_dgroups * b.n_sides);
+    const size_t lds = bd_chunk_lds<NW, J>(b);
+    hipLaunchKernelGGL((xcorr_bd_chunk_kernel<NW, J>), dim3(blocks), dim3(64 * NW), lds, s, b);
     return hipGetLastError();
 }
 
@@ -405,18 +585,37 @@ hipError_t xcorr_launch_blockdiag(const XcorrArgs &a, hipStream_t s)
     const int64_t npairs = (int64_t)a.n_left * a.n_right;
     b.n_groups = (int)((npairs + b.S - 1) / b.S);
     b.n_xtiles = b.wp / BD_P;
-    // Largest workgroup (more waves share one staged chunk) that still gives
-    // at least 256 workgroups.
+    // distinct left matrices one group of S consecutive pairs can touch
+    int nls = (b.S + a.n_right - 1) / a.n_right + 1;
+    if (nls > b.S) nls = b.S;
+    if (nls > a.n_left) nls = a.n_left;
+    b.nls = nls;
+    const int64_t per_side = (int64_t)b.n_groups * b.n_xtiles;
+    // Waves per workgroup: the most (they share one staging) that keeps at
+    // least 256 workgroups; walk the two dx signs in separate workgroups when
+    // that is needed to reach 256.
+    auto pick = [&](int nw) { return per_side * ((b.nb + nw - 1) / nw); };
     int nw = 4;
-    const int64_t base = (int64_t)b.n_groups * b.n_xtiles;
-    if (b.nb >= 16 && base * ((b.nb + 15) / 16) >= 256)
-        nw = 16;
-    else if (b.nb >= 8 && base * ((b.nb + 7) / 8) >= 256)
-        nw = 8;
-    b.n_dgroups = (b.nb + nw - 1) / nw;
-    if (nw == 16) return launch_bd<16, 16>(b, s);
-    if (nw == 8) return launch_bd<8, 8>(b, s);
-    return launch_bd<4, 8>(b, s);
+    if (b.nb >= 16 && pick(16) >= 256) nw = 16;
+    else if (b.nb >= 8 && pick(8) >= 256) nw = 8;
+    // split the two dx signs over workgroups when the grid would hold fewer
+    // than 4096 waves (4 per SIMD)
+    b.n_sides = pick(nw) * nw >= 4096 ? 1 : 2;
+    // Up to 8 diagonals: one 8-wave workgroup holds them all and shares one
+    // staging; the dx signs go to separate workgroups.
+    if (b.nb <= 8 && bd_whole_lds(b, 8) <= BD_LDS_MAX) {
+        b.n_sides = 2;
+        return launch_whole<8>(b, s);
+    }
+    if (nw == 16 && bd_whole_lds(b, 16) <= BD_LDS_MAX) return launch_whole<16>(b, s);
+    if (nw >= 8 && bd_whole_lds(b, 8) <= BD_LDS_MAX) {
+        if (nw == 16) b.n_sides = 2;  // half the waves per workgroup: keep the wave count
+        return launch_whole<8>(b, s);
+    }
+    if (nw == 4 && bd_whole_lds(b, 4) <= BD_LDS_MAX) return launch_whole<4>(b, s);
+    if (nw == 16) return launch_chunk<16, 16>(b, s);
+    if (nw == 8) return launch_chunk<8, 8>(b, s);
+    return launch_chunk<4, 8>(b, s);
 }
 
 } // namespace xc

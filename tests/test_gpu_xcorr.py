@@ -55,7 +55,13 @@ def test_xcorr_edge_shapes(shape, algo):
 
 
 @pytest.mark.parametrize("shape", [(1, 1, 16, 16), (2, 3, 37, 5), (1, 5, 64, 63), (3, 7, 32, 33),
-                                   (1, 1, 255, 3), (1, 1, 256, 1), (2, 2, 24, 40), (4, 3, 200, 12)])
+                                   (1, 1, 255, 3), (1, 1, 256, 1), (2, 2, 24, 40), (4, 3, 200, 12),
+                                   # too wide to stage whole: the chunked staging path (16, 8
+                                   # and 4 waves per workgroup, one or two dx signs each)
+                                   (2, 3, 100, 200), (1, 1, 60, 300), (1, 3, 13, 1000),
+                                   (1, 1, 35, 600), (2, 3, 41, 600), (2, 3, 65, 260),
+                                   # 16 diagonals whose whole staging only fits at 8 waves
+                                   (3, 3, 85, 72)])
 def test_xcorr_blockdiag_edge_shapes(shape):
     nl, nr, rows, cols = shape
     rng = np.random.default_rng(rows * 31 + cols)
