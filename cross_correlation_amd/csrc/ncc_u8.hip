@@ -23,8 +23,12 @@
 //     row), so the shifts are amortised over 12*Q dot4 per word.  The 3*4*Q
 //     accumulator chains are independent, which supplies the ILP the page
 //     found essential.
-//   * The template row for each (image row, output row) pair is wave-uniform,
-//     so it is read with scalar loads and fed to v_dot4 straight from SGPRs.
+//   * The template row for each (image row, output row) pair is wave-uniform:
+//     it is staged in LDS beside the image tile and read at a wave-uniform
+//     address (a broadcast read, no bank conflicts).
+//   * Tall templates split their rows over two waves that share a tile
+//     (KS = 2); their partial sums meet in LDS before the epilogue, which
+//     doubles the waves per SIMD without a second copy of the tile.
 //   * Image tiles are staged into LDS with 16-byte loads (the page's uint4
 //     versus int finding: wide coalesced copies into on-chip memory).
 //   * The epilogue forms num, vI, vT exactly in 64-bit integers and divides in

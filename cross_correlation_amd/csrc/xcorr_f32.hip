@@ -11,7 +11,8 @@
 // * xcorr_overlap_kernel -- the overlap-wise baseline the page compares
 //   against: one thread per output shift, no data reuse.
 //
-// * xcorr_bd_kernel -- the register-blocked kernel.  The page's kernels give
+// * xcorr_bd_whole_kernel / xcorr_bd_chunk_kernel -- the register-blocked
+//   (block-diagonal) kernel, in two staging modes.  The page's kernels give
 //   each thread one or several neighbouring overlaps and cache the left rows
 //   in warp-wide register buffers moved by shuffles; a thread-per-overlap
 //   mapping leaves SIMT lanes idle wherever neighbouring overlaps have
@@ -37,9 +38,17 @@
 //     - The per-lane partial sums of the same output are reduced across the
 //       wave through LDS in a fixed order (deterministic, no atomics): the
 //       split of one overlap over several lanes is the page's split-row idea.
-//   Left and right columns are staged into LDS chunk by chunk (double
-//   buffered, transposed to [block][column][4 rows] so one 16-byte read gives
-//   a lane its 4 rows of a column).
+//   Staging (columns transposed to [block][column][4 rows], so one 16-byte
+//   LDS read gives a lane its 4 rows of a column):
+//     - whole: when every matrix a workgroup touches fits in LDS with zero
+//       column halos, it is staged once (left matrices shared by consecutive
+//       pairs only once) and the waves walk both dx signs from LDS with no
+//       further workgroup barrier;
+//     - chunk: otherwise columns pass through two LDS buffers J walk steps at
+//       a time, the next chunk prefetched into registers during the FMAs.
+//   The host picks waves per workgroup (16, 8 or 4 diagonals sharing one
+//   staging) and whether the two dx signs go to separate workgroups, so that
+//   small groupings still put enough waves on the 256 CUs.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
