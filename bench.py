@@ -34,18 +34,23 @@ METRIC = "u8 NCC Gdot4/s & fp32 xcorr GFLOP/s, % of gfx950 peak, 1 GPU"
 CUS, CLOCK_HZ, LANES = 256, 2.4e9, 64
 DOT4_PEAK = CUS * LANES * CLOCK_HZ  # one v_dot4_u32_u8 per lane per clock: 39.32 T/s
 FP32_PEAK = 157.3e12                # spec FP32 vector peak (2 FMA per lane per clock)
+I8_MFMA_PEAK = 5.0e15               # spec dense int8 matrix-core peak (ops/s)
 
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "cross_correlation_amd", "csrc")
 
 
-def source_digest(name: str) -> str:
+def source_digest(names) -> str:
+    """First 16 hex digits of the sha256 of the named kernel sources, in order."""
     import hashlib
-    with open(os.path.join(CSRC, name), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for name in ([names] if isinstance(names, str) else names):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
-def profiled_traffic(profile: str, source: str):
+def profiled_traffic(profile: str, source):
     """HBM bytes per launch from a committed rocprofv3 counter summary, or None
     when the kernel source changed since the counters were taken."""
     path = os.path.join(PROFILES, profile)
@@ -134,7 +139,9 @@ def peak_probes():
     return res
 
 
-def bench_ncc(args, torch, lib, inputs):
+def bench_ncc(args, torch, lib, inputs, variant=0, steps=None, warmup=None):
+    steps = args.steps if steps is None else steps
+    warmup = args.warmup if warmup is None else warmup
     case = inputs.workload("ncc_1920x1080_t64")
     dev = torch.device("cuda:0")
     img = torch.from_numpy(case.image).to(dev)
@@ -147,11 +154,11 @@ def bench_ncc(args, torch, lib, inputs):
          outs[0].data_ptr(), outs[1].data_ptr(), outs[2].data_ptr(), coef.data_ptr()]
 
     def launch():
-        st = lib.ncc_u8_run(*p, stream=stream)
+        st = lib.ncc_u8_run(*p, stream=stream, variant=variant)
         if st != 0:
             raise RuntimeError(lib.status_str(st))
 
-    wall, per = timed_loop(launch, args.steps, args.warmup, torch)
+    wall, per = timed_loop(launch, steps, warmup, torch)
     dot4 = 3 * (case.t_width // 4) * case.t_height * oh * ow
     bytes_alg = case.height * case.width + case.t_width * case.t_height + 16 * oh * ow
     return case, dict(wall_ms=wall, kernel_ms=per, dot4=dot4, outputs=oh * ow, bytes=bytes_alg)
@@ -268,11 +275,33 @@ def main():
             "peak": round(DOT4_PEAK / 1e12, 4),
             "unit": "Tdot4/s",
             "frac": round(achieved / DOT4_PEAK, 4),
-            "traffic": profiled_traffic("ncc_u8_1080p_t64.md", "ncc_u8.hip"),
+            "traffic": profiled_traffic("ncc_u8_1080p_t64.md", ["ncc_u8.hip", "ncc_common.h"]),
             "kernel": "ncc_u8_ilp_kernel",
             "kernel_ms": round(r["kernel_ms"], 5),
             "outputs_per_s": round(r["outputs"] / (r["kernel_ms"] * 1e-3), 1),
         }
+        # The same workload through the other kernel variants (every variant
+        # returns identical outputs): the page's ablation points and the
+        # matrix-core recast of SumIT.
+        variants = {"dot4_c1": _lib.XC_NCC_DOT4_C1, "scalar_c1": _lib.XC_NCC_SCALAR_C1, "mfma": _lib.XC_NCC_MFMA}
+        out["ncc_variants"] = {"dot4_ilp": {"kernel_ms": round(r["kernel_ms"], 5), "speedup_vs_dot4_ilp": 1.0}}
+        for name, v in variants.items():
+            k = min(args.steps, 10) if name != "mfma" else args.steps
+            _, rv = bench_ncc(args, torch, _lib, inputs, variant=v, steps=k, warmup=min(args.warmup, 3))
+            out["ncc_variants"][name] = {
+                "kernel_ms": round(rv["kernel_ms"], 5),
+                "nominal_Gdot4_per_s": round(rv["dot4"] / (rv["kernel_ms"] * 1e-3) / 1e9, 2),
+                "outputs_per_s": round(rv["outputs"] / (rv["kernel_ms"] * 1e-3), 1),
+                "speedup_vs_dot4_ilp": round(r["kernel_ms"] / rv["kernel_ms"], 3),
+            }
+        m = out["ncc_variants"]["mfma"]
+        # Matrix-core accounting: the SumIT products the method defines (2
+        # int8 ops per template pixel per output) over the kernel time.
+        ops = 2 * case.t_width * case.t_height * r["outputs"]
+        mf_achieved = ops / (m["kernel_ms"] * 1e-3)
+        m["roofline"] = {"bound": "mfma", "achieved": round(mf_achieved / 1e12, 2), "peak": I8_MFMA_PEAK / 1e12,
+                         "unit": "TOP/s", "frac": round(mf_achieved / I8_MFMA_PEAK, 4),
+                         "kernel": "ncc_u8_mfma_kernel"}
     if args.only in ("xcorr", "all"):
         out["xcorr"] = bench_xcorr(args, torch, _lib, inputs)
     if not args.no_peak_probe:

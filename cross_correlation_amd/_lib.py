@@ -26,6 +26,7 @@ XC_NCC_AUTO = 0
 XC_NCC_DOT4_ILP = 1
 XC_NCC_DOT4_C1 = 2
 XC_NCC_SCALAR_C1 = 3
+XC_NCC_MFMA = 4
 
 XC_XCORR_AUTO = 0
 XC_XCORR_OVERLAP = 1

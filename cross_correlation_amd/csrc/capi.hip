@@ -101,6 +101,10 @@ int ncc_u8_run_variant(const uint8_t *image, int width, int height, int pitch_by
         return hip_status(xc::ncc_launch_c1(a, true, s));
     case XC_NCC_SCALAR_C1:
         return hip_status(xc::ncc_launch_c1(a, false, s));
+    case XC_NCC_MFMA:
+        if (!xc::ncc_mfma_supported(a))
+            return XC_ERR_SHAPE;
+        return hip_status(xc::ncc_launch_mfma(a, s));
     default:
         return XC_ERR_VARIANT;
     }

@@ -26,6 +26,9 @@ struct NccArgs {
 
 hipError_t ncc_launch_ilp(NccArgs a, hipStream_t s);
 hipError_t ncc_launch_c1(NccArgs a, bool dot4, hipStream_t s);
+// SumIT on the i8 matrix cores; takes template rows up to 256 bytes.
+hipError_t ncc_launch_mfma(NccArgs a, hipStream_t s);
+bool ncc_mfma_supported(const NccArgs &a);
 
 // Arguments of the fp32 cross-correlation kernels (validated on the host).
 struct XcorrArgs {

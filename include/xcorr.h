@@ -90,11 +90,18 @@ int ncc_u8_run(const uint8_t *image, int width, int height, int pitch_bytes,
  *   XC_NCC_DOT4_ILP      packed-byte dot products, 4 columns x several rows per lane
  *   XC_NCC_DOT4_C1       packed-byte dot products, one output per lane
  *   XC_NCC_SCALAR_C1     byte-at-a-time multiply-adds, one output per lane
+ *   XC_NCC_MFMA          SumIT as a signed-byte matrix product on the matrix
+ *                        cores (pixels and template biased by -128, corrected
+ *                        exactly with SumI and SumT), SumI and SumISq as
+ *                        separable box sums; t_width <= 256 only, else
+ *                        XC_ERR_SHAPE.  A recast of the page's computation,
+ *                        not its DP4A method.
  */
 #define XC_NCC_AUTO 0
 #define XC_NCC_DOT4_ILP 1
 #define XC_NCC_DOT4_C1 2
 #define XC_NCC_SCALAR_C1 3
+#define XC_NCC_MFMA 4
 int ncc_u8_run_variant(const uint8_t *image, int width, int height, int pitch_bytes,
                        const uint8_t *tmpl, int t_width, int t_height,
                        uint32_t *sum_i, uint32_t *sum_isq, uint32_t *sum_it, float *coef,

@@ -13,7 +13,9 @@ import _gpu
 
 pytestmark = pytest.mark.gpu
 
-VARIANTS = [_lib.XC_NCC_AUTO, _lib.XC_NCC_DOT4_C1, _lib.XC_NCC_SCALAR_C1]
+VARIANTS = [_lib.XC_NCC_AUTO, _lib.XC_NCC_DOT4_C1, _lib.XC_NCC_SCALAR_C1, _lib.XC_NCC_MFMA]
+# template rows the matrix-core variant takes
+MFMA_MAX_T_WIDTH = 256
 
 
 def _case_from(img, tmpl, name="t", pitch=None):
@@ -44,7 +46,7 @@ def test_ncc_1080p_t64_full():
     assert res["coef"][oy, ox] == np.float32(1.0)
 
 
-@pytest.mark.parametrize("variant", [_lib.XC_NCC_DOT4_C1, _lib.XC_NCC_SCALAR_C1])
+@pytest.mark.parametrize("variant", [_lib.XC_NCC_DOT4_C1, _lib.XC_NCC_SCALAR_C1, _lib.XC_NCC_MFMA])
 def test_ncc_1080p_variants_sampled(variant):
     """Ablation variants at full size: compare against the auto path bit for bit."""
     case = workload("ncc_1920x1080_t64")
@@ -148,7 +150,51 @@ def test_ncc_edge_shapes(shape, variant):
     tmpl = u8_uniform(rng, (th, tw))
     case = _case_from(img, tmpl, pitch=pitch_for(w) + extra)
     _gpu.log(f"ncc edge shape {shape} variant={variant}")
+    if variant == _lib.XC_NCC_MFMA and tw > MFMA_MAX_T_WIDTH:
+        with pytest.raises(_lib.XcError) as e:
+            _gpu.run_ncc(case, variant)
+        assert e.value.status == _lib.XC_ERR_SHAPE
+        return
     _gpu.check_ncc(case, _gpu.run_ncc(case, variant))
+
+
+@pytest.mark.parametrize("shape", [
+    # (height, width, t_height, t_width): template widths on both sides of the
+    # 64-byte blocks, ragged 256-column and 16-row tiles, template-row chunks
+    (40, 300, 16, 4),
+    (31, 290, 9, 60),
+    (47, 529, 17, 64),
+    (33, 400, 5, 68),
+    (70, 700, 33, 132),
+    (29, 600, 2, 196),
+    (64, 800, 16, 252),
+    (20, 600, 3, 256),
+    (300, 60, 290, 8),        # 290 rows: two row chunks
+    (300, 300, 258, 256),     # the largest template (66,048 pixels): many chunks
+    (1, 1024, 1, 128),        # one output row
+    (600, 64, 100, 64),       # one output column
+])
+def test_ncc_mfma_shapes(shape):
+    h, w, th, tw = shape
+    rng = np.random.default_rng(h * 131 + w * 7 + th)
+    img = u8_uniform(rng, (h, w))
+    tmpl = u8_uniform(rng, (th, tw))
+    case = _case_from(img, tmpl)
+    _gpu.log(f"ncc mfma shape {shape}")
+    _gpu.check_ncc(case, _gpu.run_ncc(case, _lib.XC_NCC_MFMA))
+
+
+def test_ncc_mfma_extreme_pixels():
+    """All-255 and all-0 windows against 0/255 templates: the -128 bias and its
+    exact correction at the ends of the byte range."""
+    for iv, tv in ((255, 255), (0, 255), (255, 0), (0, 0)):
+        img = np.full((40, 300), iv, np.uint8)
+        img[::7, ::5] = 255 - iv
+        tmpl = np.full((12, 64), tv, np.uint8)
+        tmpl[0, 0] = 255 - tv
+        case = _case_from(img, tmpl)
+        _gpu.log(f"ncc mfma extremes image={iv} template={tv}")
+        _gpu.check_ncc(case, _gpu.run_ncc(case, _lib.XC_NCC_MFMA))
 
 
 def test_ncc_output_subsets():
