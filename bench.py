@@ -3,8 +3,13 @@
 Headline (``value``): u8 normalized correlation of a 1920x1080 image with a
 64x64 template cut from it (valid-mode output 1857x1017, all four outputs:
 SumI, SumISq, SumIT and the coefficient), in nominal Gdot4/s:
-3 * (t_width/4) * t_height packed-byte dot products per output.  One step is
-one ncc_u8_run call on that image with inputs resident in HBM.
+3 * (t_width/4) * t_height packed-byte dot products per output, through the
+packed-byte (DP4A-style) kernel the method describes.  One step is one
+ncc_u8_run_variant(..., XC_NCC_DOT4_ILP) call on that image with inputs
+resident in HBM.  The other kernel variants (the page's ablation points and
+the matrix-core recast, which ncc_u8_run picks for this template) are timed
+on the same workload under "ncc_variants"; every variant returns identical
+outputs.
 
 The fp32 cross-correlation form is timed in the same run (its own loops,
 reported under "xcorr"): one-to-one 256x256, one-to-many 1x64 of 64x64 and
@@ -116,9 +121,10 @@ def timed_loop(launch, steps, warmup, torch):
 
 
 def peak_probes():
-    """Measured issue-rate ceilings of v_dot4_u32_u8 and v_fmac_f32 (32
-    independent chains per lane, 2..16 waves per SIMD); the best rate is the
-    measured ceiling."""
+    """Measured issue-rate ceilings of v_dot4_u32_u8, v_fmac_f32 (32
+    independent chains per lane) and the two signed-byte MFMA shapes (8 or 4
+    independent accumulators per wave), 2..16 waves per SIMD; the best rate is
+    the measured ceiling."""
     import ctypes
     from cross_correlation_amd import build as b
 
@@ -127,7 +133,8 @@ def peak_probes():
     lib.xc_peak_probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                   ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
     res = {}
-    for kind, name, per_op in ((0, "dot4_T_per_s", 1.0), (1, "fp32_TFLOP_per_s", 2.0)):
+    for kind, name, per_op in ((0, "dot4_T_per_s", 1.0), (1, "fp32_TFLOP_per_s", 2.0),
+                               (2, "mfma_i8_16x16x64_TOP_per_s", 1.0), (3, "mfma_i8_32x32x32_TOP_per_s", 1.0)):
         rates = {}
         for w in (2, 4, 8, 16):
             ms, ops = ctypes.c_double(), ctypes.c_double()
@@ -265,7 +272,7 @@ def main():
         "device": {"name": props.name, "cus": props.multi_processor_count},
     }
     if args.only in ("ncc", "all"):
-        case, r = bench_ncc(args, torch, _lib, inputs)
+        case, r = bench_ncc(args, torch, _lib, inputs, variant=_lib.XC_NCC_DOT4_ILP)
         out["value"] = round(r["dot4"] / (r["wall_ms"] * 1e-3) / 1e9, 2)
         out["ms_per_step"] = round(r["wall_ms"], 5)
         achieved = r["dot4"] / (r["kernel_ms"] * 1e-3)
@@ -283,10 +290,11 @@ def main():
         # The same workload through the other kernel variants (every variant
         # returns identical outputs): the page's ablation points and the
         # matrix-core recast of SumIT.
-        variants = {"dot4_c1": _lib.XC_NCC_DOT4_C1, "scalar_c1": _lib.XC_NCC_SCALAR_C1, "mfma": _lib.XC_NCC_MFMA}
+        variants = {"dot4_c1": _lib.XC_NCC_DOT4_C1, "scalar_c1": _lib.XC_NCC_SCALAR_C1, "mfma": _lib.XC_NCC_MFMA,
+                    "auto": _lib.XC_NCC_AUTO}
         out["ncc_variants"] = {"dot4_ilp": {"kernel_ms": round(r["kernel_ms"], 5), "speedup_vs_dot4_ilp": 1.0}}
         for name, v in variants.items():
-            k = min(args.steps, 10) if name != "mfma" else args.steps
+            k = args.steps if name in ("mfma", "auto") else min(args.steps, 10)
             _, rv = bench_ncc(args, torch, _lib, inputs, variant=v, steps=k, warmup=min(args.warmup, 3))
             out["ncc_variants"][name] = {
                 "kernel_ms": round(rv["kernel_ms"], 5),
@@ -301,11 +309,17 @@ def main():
         mf_achieved = ops / (m["kernel_ms"] * 1e-3)
         m["roofline"] = {"bound": "mfma", "achieved": round(mf_achieved / 1e12, 2), "peak": I8_MFMA_PEAK / 1e12,
                          "unit": "TOP/s", "frac": round(mf_achieved / I8_MFMA_PEAK, 4),
-                         "kernel": "ncc_u8_mfma_kernel"}
+                         "kernel": "ncc_u8_mfma_kernel",
+                         "note": "matrix-core instructions take ~1 us of the kernel; VALU issue and "
+                                 "LDS/barrier latency bound it"}
     if args.only in ("xcorr", "all"):
         out["xcorr"] = bench_xcorr(args, torch, _lib, inputs)
     if not args.no_peak_probe:
         out["measured_ceilings"] = peak_probes()
+        if "ncc_variants" in out:
+            ceil = out["measured_ceilings"]["mfma_i8_16x16x64_TOP_per_s"]["max"]
+            mr = out["ncc_variants"]["mfma"]["roofline"]
+            mr["frac_of_measured_ceiling"] = round(mr["achieved"] / ceil, 4)
         if "roofline" in out:
             ceil = out["measured_ceilings"]["dot4_T_per_s"]["max"]
             out["roofline"]["frac_of_measured_ceiling"] = round(out["roofline"]["achieved"] / ceil, 4)

@@ -21,12 +21,18 @@
 //     the window sum over every template row (B is the template placed
 //     Toeplitz-wise along the output rows); a fraction 15/(t_height + 15) of
 //     the products is against zero rows.
-//   * SumI and SumISq: column sums over the template height for the 16 output
-//     rows (sliding down the tile, unsigned), then inclusive prefix sums along
-//     each row, so a window sum is the difference of two prefix entries; all
-//     unsigned 32-bit, exact because every final sum is below 2^32.
-//   * The epilogue is the packed-byte kernels' exact one (64-bit integers,
-//     fp64 divide and square root, one fp32 rounding).
+//   * SumI and SumISq: while the matrix cores run, the first lanes of each
+//     wave walk the tile's image words (4 columns each) down the template's
+//     rows, keeping running sums of pixels and of squares per column (the
+//     window of output row 0).  A short sliding pass then moves the window
+//     down the 16 output rows (add the row entering, remove the row leaving;
+//     the tile's first 15 rows are kept for that), and prefix sums along each
+//     row give the window sums as differences of two entries.  All unsigned
+//     32-bit, exact because every final sum is below 2^32.
+//   * The coefficient follows the packed-byte kernels' exact formula: num, vI
+//     and vT are exact integers (held in fp64 here, formed with fused
+//     multiply-adds), then an IEEE fp64 divide and square root and one fp32
+//     rounding, so both paths return the same bits.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -39,18 +45,29 @@ typedef int mf_v4i __attribute__((ext_vector_type(4)));
 
 constexpr int MF_TY = 16;          // output rows per workgroup (MFMA N)
 constexpr int MF_TX = 256;         // output columns per workgroup (4 waves x 64)
+constexpr int MF_THREADS = 256;
 constexpr int MF_MAX_NKB = 4;      // template rows up to 256 bytes
-constexpr int MF_MAX_HC = 256;     // template rows per chunk (16-bit column sums)
+constexpr int MF_MAX_HC = 256;     // template rows per chunk
 constexpr int MF_ACC_STRIDE = 257; // i32 words per output row of the SumIT staging
 
-// LDS plan of one workgroup (host and device agree through these helpers).
+// LDS plan of one workgroup (host and device agree through these helpers):
+//   V     2*MF_TY rows x vs u32: column sums of pixels (rows 0..15) and of
+//         squares (rows 16..31), then their row prefix
+//   img   the staged image tile plus one spare row; after the walk, the
+//         SumIT' staging of MF_TY x MF_ACC_STRIDE i32
+//   tpl   template rows with zero rows around them (trows rows of tsb bytes)
+//   head  the tile's first MF_TY - 1 image rows (words 0..nwd-1), kept for
+//         the sliding pass when the template comes in several chunks
+//   tsum  SumT and SumTSq
 struct MfPlan {
     int nkb;      // 64-byte blocks per template row
     int hc;       // template rows per chunk
     int sw;       // image LDS words per row
     int tsb;      // template LDS bytes per row
-    int nwd;      // image words covered by the box sums
-    int vs;       // u32 per row of the column-sum arrays (odd: spreads banks)
+    int trows;    // template LDS rows
+    int nwd;      // image words covered by the column sums
+    int cw;       // column-walk words per wave
+    int vs;       // u32 per row of V (a multiple of 4: 16-byte stores)
     int img_words;
     size_t bytes;
 };
@@ -62,12 +79,15 @@ __host__ __device__ inline MfPlan mf_plan(int t_width, int hc)
     p.hc = hc;
     p.sw = 64 + 16 * p.nkb + 4;
     p.tsb = 64 * p.nkb + 16;
+    p.trows = hc + 2 * MF_TY - 1;
     p.nwd = 64 + t_width / 4;
-    p.vs = 4 * p.nwd + 1;
-    int img = (MF_TY - 1 + hc) * p.sw;
-    if (img < MF_TY * MF_ACC_STRIDE) img = MF_TY * MF_ACC_STRIDE;  // reused for SumIT staging
+    p.cw = (p.nwd + 3) / 4;
+    p.vs = 4 * p.nwd + 4;
+    int img = (MF_TY + hc) * p.sw;  // staged rows + one spare row
+    if (img < MF_TY * MF_ACC_STRIDE) img = MF_TY * MF_ACC_STRIDE;
     p.img_words = img;
-    p.bytes = (size_t)2 * MF_TY * p.vs * 4 + (size_t)img * 4 + (size_t)(hc + 1) * p.tsb;
+    p.bytes = (size_t)2 * MF_TY * p.vs * 4 + (size_t)img * 4 + (size_t)p.trows * p.tsb +
+              (size_t)(MF_TY - 1) * p.nwd * 4 + 8;
     return p;
 }
 
@@ -94,124 +114,146 @@ __device__ __forceinline__ void mf_stage_image(const uint8_t *__restrict__ image
     }
 }
 
-// Template rows [j0, j0 + hcur) biased to signed bytes, zero beyond t_width up
-// to the 64-byte block; row hcur is all zero (the rows that do not exist).
+// Template rows [j0, j0 + hcur) biased to signed bytes at LDS rows
+// [MF_TY - 1, MF_TY - 1 + hcur), with MF_TY - 1 zero rows before and MF_TY
+// after (the template rows that do not exist for some output row of the tile,
+// and the spare row the pipelined walk reads last) and zero bytes beyond
+// t_width up to the 64-byte block.
 __device__ __forceinline__ void mf_stage_template(const uint8_t *__restrict__ tmpl, int t_width, int j0, int hcur,
-                                                  int kw, uint8_t *tpl, int tsb)
+                                                  int kw, uint8_t *tpl, int tsb, int trows)
 {
     const int wpr = kw / 4;  // words per staged row
     const int twords = t_width / 4;
-    const int total = (hcur + 1) * wpr;
+    const int total = trows * wpr;
     for (int i = threadIdx.x; i < total; i += blockDim.x) {
         const int r = i / wpr;
         const int k = i - r * wpr;
+        const int j = r - (MF_TY - 1);
         uint32_t v = 0u;
-        if (r < hcur && k < twords)
-            v = reinterpret_cast<const uint32_t *>(tmpl + (size_t)(j0 + r) * t_width)[k] ^ 0x80808080u;
+        if (j >= 0 && j < hcur && k < twords)
+            v = reinterpret_cast<const uint32_t *>(tmpl + (size_t)(j0 + j) * t_width)[k] ^ 0x80808080u;
         *reinterpret_cast<uint32_t *>(tpl + r * tsb + 4 * k) = v;
     }
 }
 
-// Column sums of one template-row chunk, added into V1 (pixels) and V2
-// (squares): V[n][c] += sum_{j in chunk} I[n + j][c] for the 16 output rows.
-// Thread (part p, word wd): the chunk's rows are split into np parts; each
-// part slides down the 16 output rows (add the row entering, remove the row
-// leaving) with pixel sums in two 16-bit lanes per register.
-__device__ __forceinline__ void mf_box_chunk(const uint32_t *img, int sw, int hcur, int nwd, uint32_t *V1,
-                                             uint32_t *V2, int vs)
+// Running column sums: add the pixels and squares of one image word (4
+// columns) into pi / pq.
+__device__ __forceinline__ void mf_col_add(uint32_t biased, uint32_t (&pi)[4], uint32_t (&pq)[4])
 {
-    const int np = blockDim.x / nwd;
-    const int p = threadIdx.x / nwd;
-    const int wd = threadIdx.x - p * nwd;
-    if (p >= np)
-        return;
-    const int jlo = p * hcur / np, jhi = (p + 1) * hcur / np;
-    if (jlo >= jhi)
-        return;
-    const uint32_t *col = img + wd;
-    uint32_t lo = 0u, hi = 0u;     // bytes 0,2 and 1,3 of the word, 16 bits each
-    uint32_t qa[4] = {0u, 0u, 0u, 0u}, qr[4] = {0u, 0u, 0u, 0u};  // squares added / removed
-    auto add = [&](uint32_t w) {
-        w ^= 0x80808080u;
-        lo += w & 0x00FF00FFu;
-        hi += (w >> 8) & 0x00FF00FFu;
+    const uint32_t w = biased ^ 0x80808080u;
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-            qa[k] = dot4u(w & (0xFFu << (8 * k)), w, qa[k]);
-    };
-    auto remove = [&](uint32_t w) {
-        w ^= 0x80808080u;
-        lo -= w & 0x00FF00FFu;
-        hi -= (w >> 8) & 0x00FF00FFu;
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            qr[k] = dot4u(w & (0xFFu << (8 * k)), w, qr[k]);
-    };
-    auto emit = [&](int n) {
-        uint32_t *v1 = V1 + n * vs + 4 * wd;
-        uint32_t *v2 = V2 + n * vs + 4 * wd;
-        atomicAdd(v1 + 0, lo & 0xFFFFu);
-        atomicAdd(v1 + 1, hi & 0xFFFFu);
-        atomicAdd(v1 + 2, lo >> 16);
-        atomicAdd(v1 + 3, hi >> 16);
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            atomicAdd(v2 + k, qa[k] - qr[k]);
-    };
-    for (int j = jlo; j < jhi; ++j)
-        add(col[j * sw]);
-    emit(0);
-    for (int n = 1; n < MF_TY; ++n) {
-        add(col[(n - 1 + jhi) * sw]);
-        remove(col[(n - 1 + jlo) * sw]);
-        emit(n);
+    for (int k = 0; k < 4; ++k) {
+        pi[k] = dot4u(w, 1u << (8 * k), pi[k]);
+        pq[k] = dot4u(w & (0xFFu << (8 * k)), w, pq[k]);
     }
 }
 
-// The MFMA walk of one chunk for one wave: every image row of the chunk's tile
-// against the template rows it meets, NKB 64-byte blocks per row.
+// The walk of one template-row chunk for one wave.  Matrix cores: every image
+// row of the chunk's tile against the template rows it meets, NKB 64-byte
+// blocks per row; rows go in pairs through two register sets, the next row's
+// LDS words read while the current row's products issue (the read after the
+// last row lands in the spare row each LDS area keeps).  Column sums: walker
+// lanes add image row rr of word wd for rr < hcur (absolute rows j0 + rr), and
+// keep the first MF_TY - 1 absolute rows in `head`.
 template <int NKB>
-__device__ __forceinline__ void mf_mfma_chunk(const uint32_t *img, int sw, const uint8_t *tpl, int tsb, int hcur,
-                                              mf_v4i (&acc)[4])
+__device__ __forceinline__ void mf_walk_chunk(const uint32_t *img, int sw, const uint8_t *tpl, int tsb, int hcur,
+                                              int j0, bool walker, int wd, uint32_t *head, int nwd,
+                                              mf_v4i (&at)[4], uint32_t (&pi)[4], uint32_t (&pq)[4])
 {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int m = lane & 15, g = lane >> 4;
     // A: output column x0 + 64*wave + 4m + t reads image words from 16*wave + m
-    // (+ 4g for its 16 bytes of the 64-byte block); B: template row rr - n.
-    const uint32_t *ibase = img + 16 * wave + m + 4 * g;
-    const uint8_t *tbase = tpl + 16 * g;
-    const int n = m;  // B column = output row
+    // (+ 4g for its 16 bytes of the 64-byte block).  B: output row n = m meets
+    // template row rr - n, staged at LDS row rr - n + MF_TY - 1.
+    const uint32_t *ip = img + 16 * wave + m + 4 * g;
+    const uint8_t *tp = tpl + (MF_TY - 1 - m) * tsb + 16 * g;
+    const uint32_t *cp = img + (walker ? wd : 0);
     const int nrows = MF_TY - 1 + hcur;
-    for (int rr = 0; rr < nrows; ++rr) {
-        const int jr = rr - n;
-        const uint8_t *trow = tbase + (jr >= 0 && jr < hcur ? jr : hcur) * tsb;
-        const uint32_t *irow = ibase + rr * sw;
+
+    auto load = [&](uint32_t (&w)[NKB][5], mf_v4i (&b)[NKB], uint32_t &cw) {
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
-            uint32_t w[5];
 #pragma unroll
             for (int k = 0; k < 5; ++k)
-                w[k] = irow[16 * kb + k];
-            const mf_v4i b = *reinterpret_cast<const mf_v4i *>(trow + 64 * kb);
-            mf_v4i a0, a1, a2, a3;
+                w[kb][k] = ip[16 * kb + k];
+            b[kb] = *reinterpret_cast<const mf_v4i *>(tp + 64 * kb);
+        }
+        cw = *cp;
+        ip += sw;
+        tp += tsb;
+        cp += sw;
+    };
+    auto compute = [&](int rr, const uint32_t (&w)[NKB][5], const mf_v4i (&b)[NKB], uint32_t cw) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            mf_v4i a[4];
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                a0[k] = (int)w[k];
-                a1[k] = (int)shift_bytes(w[k + 1], w[k], 1);
-                a2[k] = (int)shift_bytes(w[k + 1], w[k], 2);
-                a3[k] = (int)shift_bytes(w[k + 1], w[k], 3);
+                a[0][k] = (int)w[kb][k];
+                a[1][k] = (int)shift_bytes(w[kb][k + 1], w[kb][k], 1);
+                a[2][k] = (int)shift_bytes(w[kb][k + 1], w[kb][k], 2);
+                a[3][k] = (int)shift_bytes(w[kb][k + 1], w[kb][k], 3);
             }
-            acc[0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b, acc[0], 0, 0, 0);
-            acc[1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b, acc[1], 0, 0, 0);
-            acc[2] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a2, b, acc[2], 0, 0, 0);
-            acc[3] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a3, b, acc[3], 0, 0, 0);
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                at[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[t], b[kb], at[t], 0, 0, 0);
         }
+        if (walker && rr < hcur) {
+            mf_col_add(cw, pi, pq);
+            if (j0 + rr < MF_TY - 1)
+                head[(j0 + rr) * nwd + wd] = cw;
+        }
+    };
+    uint32_t wa[NKB][5], wb[NKB][5], ca, cb;
+    mf_v4i ba[NKB], bb[NKB];
+    load(wa, ba, ca);
+    int rr = 0;
+    for (; rr + 2 <= nrows; rr += 2) {
+        load(wb, bb, cb);  // row rr + 1
+        compute(rr, wa, ba, ca);
+        load(wa, ba, ca);  // row rr + 2 (the spare row when rr + 2 == nrows)
+        compute(rr + 1, wb, bb, cb);
+    }
+    if (rr < nrows)
+        compute(rr, wa, ba, ca);
+}
+
+// The sliding pass of walker word wd after the last chunk's walk: pi / pq hold
+// the column sums of absolute rows [0, th), i.e. output row 0's window.  Row
+// n's window adds absolute row n + th - 1 (tile row hcur + n - 1 of the last
+// chunk) and drops absolute row n - 1 (tile row n - 1 when the template came
+// in one chunk, else the saved head row).
+__device__ __forceinline__ void mf_slide(const uint32_t *img, int sw, int hcur, bool one_chunk, const uint32_t *head,
+                                         int nwd, int wd, uint32_t *V1, uint32_t *V2, int vs, uint32_t (&pi)[4],
+                                         uint32_t (&pq)[4])
+{
+    uint32_t in[MF_TY - 1], out[MF_TY - 1];
+#pragma unroll
+    for (int n = 1; n < MF_TY; ++n) {
+        in[n - 1] = img[(hcur + n - 1) * sw + wd];
+        out[n - 1] = one_chunk ? img[(n - 1) * sw + wd] : head[(n - 1) * nwd + wd];
+    }
+    *reinterpret_cast<uint4 *>(V1 + 4 * wd) = make_uint4(pi[0], pi[1], pi[2], pi[3]);
+    *reinterpret_cast<uint4 *>(V2 + 4 * wd) = make_uint4(pq[0], pq[1], pq[2], pq[3]);
+#pragma unroll
+    for (int n = 1; n < MF_TY; ++n) {
+        uint32_t ri[4] = {0u, 0u, 0u, 0u}, rq[4] = {0u, 0u, 0u, 0u};
+        mf_col_add(in[n - 1], pi, pq);
+        mf_col_add(out[n - 1], ri, rq);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            pi[k] -= ri[k];
+            pq[k] -= rq[k];
+        }
+        *reinterpret_cast<uint4 *>(V1 + n * vs + 4 * wd) = make_uint4(pi[0], pi[1], pi[2], pi[3]);
+        *reinterpret_cast<uint4 *>(V2 + n * vs + 4 * wd) = make_uint4(pq[0], pq[1], pq[2], pq[3]);
     }
 }
 
-// In-place inclusive prefix sums along each of the 32 rows (16 of V1, 16 of
-// V2) over `ncols` columns: 8 threads per row, each a contiguous segment.
+// In-place inclusive prefix sums along each of the 2*MF_TY rows of V over
+// `ncols` columns: 8 threads per row, each a contiguous segment read and
+// written 8 entries at a time.  Every thread must call it (it holds barriers).
 __device__ __forceinline__ void mf_row_prefix(uint32_t *V, int vs, int ncols)
 {
     const int row = threadIdx.x >> 3;  // 0..31
@@ -220,9 +262,20 @@ __device__ __forceinline__ void mf_row_prefix(uint32_t *V, int vs, int ncols)
     const int c0 = seg * len, c1 = min(ncols, c0 + len);
     uint32_t *r = V + row * vs;
     uint32_t s = 0u;
-    for (int c = c0; c < c1; ++c) {
-        s += r[c];
-        r[c] = s;
+    for (int c = c0; c < c1; c += 8) {
+        uint32_t v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            v[u] = c + u < c1 ? r[c + u] : 0u;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            s += v[u];
+            v[u] = s;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (c + u < c1)
+                r[c + u] = v[u];
     }
     __syncthreads();
     uint32_t off = 0u;
@@ -238,7 +291,7 @@ __device__ __forceinline__ void mf_row_prefix(uint32_t *V, int vs, int ncols)
 }
 
 template <int NKB>
-__global__ __launch_bounds__(256) void ncc_u8_mfma_kernel(NccArgs a)
+__global__ __launch_bounds__(MF_THREADS) void ncc_u8_mfma_kernel(NccArgs a)
 {
     extern __shared__ uint4 mf_smem[];
     const MfPlan P = mf_plan(a.t_width, a.hc);
@@ -246,66 +299,103 @@ __global__ __launch_bounds__(256) void ncc_u8_mfma_kernel(NccArgs a)
     uint32_t *const V2 = V1 + MF_TY * P.vs;
     uint32_t *const img = V2 + MF_TY * P.vs;
     uint8_t *const tpl = reinterpret_cast<uint8_t *>(img + P.img_words);
-    int32_t *const accbuf = reinterpret_cast<int32_t *>(img);
+    uint32_t *const head = reinterpret_cast<uint32_t *>(tpl + P.trows * P.tsb);
+    uint32_t *const tsum = head + (MF_TY - 1) * P.nwd;
+    int32_t *const acc_it = reinterpret_cast<int32_t *>(img);
 
     const int x0 = blockIdx.x * MF_TX, y0 = blockIdx.y * MF_TY;
     const int tw = a.t_width, th = a.t_height;
+    const int twords = tw / 4;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wd = wave * P.cw + lane;              // column-walk word of this lane
+    const bool walker = lane < P.cw && wd < P.nwd;
 
-    for (int i = threadIdx.x; i < 2 * MF_TY * P.vs; i += blockDim.x)
-        V1[i] = 0u;
+    if (threadIdx.x < 2)
+        tsum[threadIdx.x] = 0u;
 
-    mf_v4i acc[4];
+    mf_v4i at[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
-        acc[t] = mf_v4i{0, 0, 0, 0};
+        at[t] = mf_v4i{0, 0, 0, 0};
+    uint32_t pi[4] = {0u, 0u, 0u, 0u}, pq[4] = {0u, 0u, 0u, 0u};
+    uint32_t ts = 0u, tq = 0u;
 
     const int nchunks16 = (64 + 16 * NKB) / 4;  // 16-byte chunks per staged image row
     for (int j0 = 0; j0 < th; j0 += P.hc) {
         const int hcur = min(P.hc, th - j0);
-        __syncthreads();  // the previous chunk's readers are done (and V is zeroed)
+        __syncthreads();  // the previous chunk's readers are done
         mf_stage_image(a.image, a.height, a.pitch, y0 + j0, x0, MF_TY - 1 + hcur, nchunks16, img, P.sw);
-        mf_stage_template(a.tmpl, tw, j0, hcur, 64 * NKB, tpl, P.tsb);
+        mf_stage_template(a.tmpl, tw, j0, hcur, 64 * NKB, tpl, P.tsb, P.trows);
         __syncthreads();
-        mf_box_chunk(img, P.sw, hcur, P.nwd, V1, V2, P.vs);
-        mf_mfma_chunk<NKB>(img, P.sw, tpl, P.tsb, hcur, acc);
+        // template sums from the staged (biased) rows of this chunk
+        for (int i = threadIdx.x; i < hcur * twords; i += MF_THREADS) {
+            const int r = i / twords;
+            const uint32_t w =
+                *reinterpret_cast<const uint32_t *>(tpl + (MF_TY - 1 + r) * P.tsb + 4 * (i - r * twords)) ^
+                0x80808080u;
+            ts = dot4u(w, 0x01010101u, ts);
+            tq = dot4u(w, w, tq);
+        }
+        mf_walk_chunk<NKB>(img, P.sw, tpl, P.tsb, hcur, j0, walker, wd, head, P.nwd, at, pi, pq);
+        if (j0 + hcur == th && walker)
+            mf_slide(img, P.sw, hcur, j0 == 0, head, P.nwd, wd, V1, V2, P.vs, pi, pq);
+    }
+    ts = wave_sum_u32(ts);
+    tq = wave_sum_u32(tq);
+    if (lane == 0) {
+        atomicAdd(tsum + 0, ts);
+        atomicAdd(tsum + 1, tq);
     }
     __syncthreads();
 
     // SumIT' to LDS: lane (g, n) holds columns 64*wave + 16g + 4i + t of row n.
     {
-        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
         const int n = lane & 15, g = lane >> 4;
-        int32_t *row = accbuf + n * MF_ACC_STRIDE + 64 * wave + 16 * g;
+        const int base = n * MF_ACC_STRIDE + 64 * wave + 16 * g;
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                row[4 * i + t] = acc[t][i];
+            for (int t = 0; t < 4; ++t)
+                acc_it[base + 4 * i + t] = at[t][i];
     }
     // Window sums from prefix sums of the column sums (V1 and V2 rows are
     // contiguous, so one pass covers both).
     mf_row_prefix(V1, P.vs, 4 * P.nwd);
-
-    uint32_t sum_t, sum_tsq;
-    template_sums(reinterpret_cast<const uint32_t *>(a.tmpl), tw * th / 4, sum_t, sum_tsq);
-    const int64_t nn = (int64_t)tw * th;
-    const int64_t vt = nn * (int64_t)sum_tsq - (int64_t)sum_t * (int64_t)sum_t;
-    const uint32_t bias = 128u * sum_t - 16384u * (uint32_t)nn;
     __syncthreads();
+
+    const uint32_t sum_t = tsum[0], sum_tsq = tsum[1];
+    const uint32_t nn = (uint32_t)(tw * th);
+    const uint32_t bias = 128u * sum_t - 16384u * nn;
+    // num, vI, vT are integers below 2^50 (N <= 66,051 and every sum below
+    // 2^32), so fp64 fused multiply-adds form them exactly: the same doubles,
+    // hence the same coefficient, as the 64-bit integer form.
+    const double nd = (double)nn, std_ = (double)sum_t;
+    const double vt = fma(nd, (double)sum_tsq, -(std_ * std_));
 
     const int x = threadIdx.x;
     const int gx = x0 + x;
     if (gx < a.out_w) {
-        for (int n = 0; n < MF_TY; ++n) {
-            const int gy = y0 + n;
-            if (gy >= a.out_h)
+        size_t o = (size_t)y0 * a.out_w + gx;
+        for (int n = 0; n < MF_TY; ++n, o += a.out_w) {
+            if (y0 + n >= a.out_h)
                 break;
             const uint32_t *q1 = V1 + n * P.vs;
             const uint32_t *q2 = V2 + n * P.vs;
             const uint32_t si = q1[x + tw - 1] - (x > 0 ? q1[x - 1] : 0u);
             const uint32_t sq = q2[x + tw - 1] - (x > 0 ? q2[x - 1] : 0u);
-            const uint32_t st = (uint32_t)accbuf[n * MF_ACC_STRIDE + x] + 128u * si + bias;
-            ncc_store(a, (size_t)gy * a.out_w + gx, si, sq, st, nn, (int64_t)sum_t, vt);
+            const uint32_t st = (uint32_t)acc_it[n * MF_ACC_STRIDE + x] + 128u * si + bias;
+            if (a.sum_i) a.sum_i[o] = si;
+            if (a.sum_isq) a.sum_isq[o] = sq;
+            if (a.sum_it) a.sum_it[o] = st;
+            if (a.coef) {
+                const double sid = (double)si;
+                const double num = fma(nd, (double)st, -(sid * std_));
+                const double vi = fma(nd, (double)sq, -(sid * sid));
+                double c = 0.0;
+                if (vi != 0.0 && vt != 0.0)
+                    c = num / sqrt(vi * vt);
+                a.coef[o] = (float)c;
+            }
         }
     }
 }
@@ -347,7 +437,7 @@ static hipError_t mf_launch(const NccArgs &a, hipStream_t s)
     }
     const size_t lds = mf_plan(a.t_width, a.hc).bytes;
     const dim3 grid((a.out_w + MF_TX - 1) / MF_TX, (a.out_h + MF_TY - 1) / MF_TY);
-    hipLaunchKernelGGL((ncc_u8_mfma_kernel<NKB>), grid, dim3(256), lds, s, a);
+    hipLaunchKernelGGL((ncc_u8_mfma_kernel<NKB>), grid, dim3(MF_THREADS), lds, s, a);
     return hipGetLastError();
 }
 

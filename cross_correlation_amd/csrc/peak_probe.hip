@@ -7,6 +7,9 @@
 // one instruction:
 //   kind 0: v_dot4_u32_u8 (unsigned packed-byte dot product, 4 MACs)
 //   kind 1: v_fmac_f32    (fp32 fused multiply-add, 2 flops)
+//   kind 2: v_mfma_i32_16x16x64_i8 (16x16x64 signed-byte MACs per wave)
+//   kind 3: v_mfma_i32_32x32x32_i8 (32x32x32 signed-byte MACs per wave)
+// (the matrix-core kinds run 8 and 4 independent accumulators per wave).
 // A launch has 64-thread workgroups, `waves_per_simd` per SIMD of every CU.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -49,13 +52,56 @@ __global__ __launch_bounds__(64) void fma_probe(uint32_t *out, int iters)
     out[blockIdx.x * 64 + threadIdx.x] = __float_as_uint(s);
 }
 
+typedef int probe_v4i __attribute__((ext_vector_type(4)));
+typedef int probe_v16i __attribute__((ext_vector_type(16)));
+
+__global__ __launch_bounds__(64) void mfma16_probe(uint32_t *out, int iters)
+{
+    constexpr int NA = 8;
+    probe_v4i a = {(int)threadIdx.x, 3, 5, 7}, b = {11, 13, (int)threadIdx.x * 3, 17};
+    probe_v4i acc[NA];
+#pragma unroll
+    for (int c = 0; c < NA; ++c) acc[c] = probe_v4i{c, 0, 0, 0};
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+        for (int c = 0; c < NA; ++c) acc[c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[c], 0, 0, 0);
+        a[0] += 0x01010101;
+    }
+    int s = 0;
+#pragma unroll
+    for (int c = 0; c < NA; ++c) s ^= acc[c][0] ^ acc[c][1] ^ acc[c][2] ^ acc[c][3];
+    out[blockIdx.x * 64 + threadIdx.x] = (uint32_t)s;
+}
+
+__global__ __launch_bounds__(64) void mfma32_probe(uint32_t *out, int iters)
+{
+    constexpr int NA = 4;
+    probe_v4i a = {(int)threadIdx.x, 3, 5, 7}, b = {11, 13, (int)threadIdx.x * 3, 17};
+    probe_v16i acc[NA];
+#pragma unroll
+    for (int c = 0; c < NA; ++c) {
+        acc[c] = probe_v16i{};
+        acc[c][0] = c;
+    }
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+        for (int c = 0; c < NA; ++c) acc[c] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, acc[c], 0, 0, 0);
+        a[0] += 0x01010101;
+    }
+    int s = 0;
+#pragma unroll
+    for (int c = 0; c < NA; ++c)
+#pragma unroll
+        for (int k = 0; k < 16; ++k) s ^= acc[c][k];
+    out[blockIdx.x * 64 + threadIdx.x] = (uint32_t)s;
+}
+
 } // namespace
 
 extern "C" {
 
 // Runs the probe `reps` times after one warm-up launch; returns 0 and the mean
-// milliseconds per launch in *ms, or -1 on any HIP error.  ops_per_launch
-// receives the instruction count (lane-operations) of one launch.
+// milliseconds per launch in *ms, or -1 on any HIP error or unknown kind.
 int xc_peak_probe(int kind, int waves_per_simd, int iters, int reps, double *ms, double *ops_per_launch)
 {
     constexpr int CH = 32;
@@ -67,11 +113,16 @@ int xc_peak_probe(int kind, int waves_per_simd, int iters, int reps, double *ms,
     if (hipMalloc(&buf, (size_t)blocks * 64 * sizeof(uint32_t)) != hipSuccess) return -1;
     hipEvent_t e0, e1;
     if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) return -1;
+    if (kind < 0 || kind > 3) return -1;
     auto launch = [&]() {
         if (kind == 0)
             hipLaunchKernelGGL(dot4_probe<CH>, dim3(blocks), dim3(64), 0, 0, buf, iters);
-        else
+        else if (kind == 1)
             hipLaunchKernelGGL(fma_probe<CH>, dim3(blocks), dim3(64), 0, 0, buf, iters);
+        else if (kind == 2)
+            hipLaunchKernelGGL(mfma16_probe, dim3(blocks), dim3(64), 0, 0, buf, iters);
+        else
+            hipLaunchKernelGGL(mfma32_probe, dim3(blocks), dim3(64), 0, 0, buf, iters);
     };
     launch();
     int st = hipDeviceSynchronize() == hipSuccess ? 0 : -1;
@@ -83,7 +134,14 @@ int xc_peak_probe(int kind, int waves_per_simd, int iters, int reps, double *ms,
         st = (hipEventSynchronize(e1) == hipSuccess && hipEventElapsedTime(&t, e0, e1) == hipSuccess) ? 0 : -1;
     }
     *ms = (double)t / reps;
-    *ops_per_launch = (double)blocks * 64 * iters * CH;
+    // lane-operations for kinds 0 and 1; int8 operations (2 per MAC) for the
+    // matrix-core kinds
+    if (kind <= 1)
+        *ops_per_launch = (double)blocks * 64 * iters * CH;
+    else if (kind == 2)
+        *ops_per_launch = (double)blocks * iters * 8 * (16.0 * 16 * 64) * 2;
+    else
+        *ops_per_launch = (double)blocks * iters * 4 * (32.0 * 32 * 32) * 2;
     hipEventDestroy(e0);
     hipEventDestroy(e1);
     if (hipFree(buf) != hipSuccess) st = -1;
