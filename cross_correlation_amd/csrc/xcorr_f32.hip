@@ -520,10 +520,205 @@ __global__ __launch_bounds__(64 * NW) void xcorr_bd_whole_kernel(BdArgs a)
     }
 }
 
+// ---- more than 64 row blocks: passes over 64-block ranges ----
+// One pair per workgroup, NW consecutive diagonals per workgroup (S = 1).
+// Pass q covers right blocks [64q, 64q + 64): lane b walks right block
+// B = 64q + b against left blocks kb1 = (B + delta) mod nb and kb2 = kb1 + 1
+// (mod nb), which lie in the window of BIG_LW blocks starting at
+// (64q + delta0) mod nb (delta0 = the workgroup's first diagonal), at window
+// index b + wave and b + wave + 1.  Columns stream through two LDS buffers J
+// walk steps at a time.  After each side of each pass the wave reduces its
+// lanes in a fixed order and stores (pass 0) or adds to (later passes) its
+// output rows, which no other wave writes: the result does not depend on
+// scheduling.
+template <int NW>
+struct BdBig {
+    static constexpr int LW = 64 + NW + 1;  // left window blocks
+};
+
+__device__ __forceinline__ void bd_big_reduce_store(const BdArgs &a, int lane, int delta, int c0, int side, int64_t pair,
+                                                    int q, float *wred, float *wextra,
+                                                    const float (&acc1)[4][BD_P], const float (&acc2)[3][BD_P])
+{
+    constexpr int P = BD_P;
+    constexpr int RS = 65;
+    const int nb = a.nb;
+    const int B = 64 * q + lane;
+    const int bstar = nb - delta - 1;  // block 1 unwrapped, block 2 wrapped
+    const bool star_here = bstar >= 64 * q && bstar < 64 * q + 64;
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float c = acc1[r][p];
+            if (r >= 1 && B != bstar) c += acc2[r - 1][p];
+            wred[(r * P + p) * RS + lane] = c;
+        }
+    if (B == bstar) {
+#pragma unroll
+        for (int p = 0; p < P; ++p)
+#pragma unroll
+            for (int r = 0; r < 3; ++r)
+                wextra[r * P + p] = acc2[r][p];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int rows = a.x.rows, cols = a.x.cols, h4 = 4 * nb;
+    const int oh = 2 * rows - 1, ow = 2 * cols - 1;
+    if (lane < 8 * P) {
+        const int p = lane % P;
+        const int wr = (lane / P) & 1;
+        const int r = lane / (2 * P);
+        const int dy = 4 * delta + r - (wr ? h4 : 0);
+        const int c = c0 + p;
+        const int dx = side ? c - a.wp : c;
+        const bool keep = dy > -rows && dy < rows && dx > -cols && dx < cols;
+        // lanes of this pass that add to (r, wr): blocks [blo, bhi) shifted
+        const int blo = max(wr ? nb - delta : 0, 64 * q) - 64 * q;
+        const int bhi = min(wr ? nb : nb - delta, 64 * q + 64) - 64 * q;
+        const float *col = wred + (r * P + p) * RS;
+        float part[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) part[i] = 0.0f;
+        for (int bb = blo; bb < bhi; bb += 8) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if (bb + i < bhi) part[i] += col[bb + i];
+        }
+        float sum = ((part[0] + part[1]) + (part[2] + part[3])) + ((part[4] + part[5]) + (part[6] + part[7]));
+        if (wr && r >= 1 && star_here)
+            sum += wextra[(r - 1) * P + p];
+        if (keep) {
+            float *o = a.x.out + ((size_t)pair * oh + (dy + rows - 1)) * ow + (dx + cols - 1);
+            *o = q == 0 ? sum : *o + sum;
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+}
+
+template <int NW, int J>
+__global__ __launch_bounds__(64 * NW) void xcorr_bd_big_kernel(BdArgs a)
+{
+    constexpr int P = BD_P;
+    using G = BdLds<J>;
+    constexpr int LW = BdBig<NW>::LW;
+    extern __shared__ float4 smem[];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    int bid = blockIdx.x;
+    const int side_sel = bid % a.n_sides;
+    bid /= a.n_sides;
+    const int dgrp = bid % a.n_dgroups;
+    bid /= a.n_dgroups;
+    const int xt = bid % a.n_xtiles;
+    const int64_t pair = bid / a.n_xtiles;
+    const int c0 = xt * P;
+    const int side_lo = a.n_sides == 2 ? side_sel : 0;
+    const int side_hi = a.n_sides == 2 ? side_sel + 1 : 2;
+    const int nb = a.nb, wp = a.wp, rows = a.x.rows, cols = a.x.cols;
+    const int delta0 = dgrp * NW;
+    const int delta = delta0 + wave;
+    const bool wave_on = delta < nb;
+    const int npass = (nb + 63) / 64;
+
+    const int l = (int)(pair / a.x.n_right);
+    const int r = (int)(pair - (int64_t)l * a.x.n_right);
+    const float *lmat = a.x.left + (size_t)l * rows * cols;
+    const float *rmat = a.x.right + (size_t)r * rows * cols;
+
+    // LDS: two staging buffers, each L [LW][NCL] then R [64][NCR]; the
+    // per-wave reduction runs in the staging area once a side is done.
+    constexpr int L_ELEMS = LW * G::NCL;
+    constexpr int BUF = L_ELEMS + 64 * G::NCR;
+    float *const wred = reinterpret_cast<float *>(smem) + wave * bd_red_floats(1);
+    float *const wextra = wred + 4 * P * 65;
+
+    // Staging items: left (window block, column) then right (block, column).
+    constexpr int NL_ITEMS = LW * G::NLU;
+    constexpr int N_ITEMS = NL_ITEMS + 64 * G::NRU;
+    constexpr int IPT = (N_ITEMS + 64 * NW - 1) / (64 * NW);
+
+    for (int q = 0; q < npass; ++q) {
+        const int L0 = (64 * q + delta0) % nb;
+        for (int side = side_lo; side < side_hi; ++side) {
+            const int u_first = side ? 0 : c0;
+            const int u_end = side ? c0 + P : wp;
+            const int roff = side ? wp - c0 : -c0;
+            const int nch = (u_end - u_first + J - 1) / J;
+
+            auto load_chunk = [&](int t, float4 (&v)[IPT]) {
+                const int ua = u_first + t * J;
+#pragma unroll
+                for (int k = 0; k < IPT; ++k) {
+                    const int i = threadIdx.x + k * 64 * NW;
+                    v[k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                    if (i < NL_ITEMS) {
+                        const int blk = i / G::NLU, cc = i - blk * G::NLU;
+                        const int kb = (L0 + blk) % nb;
+                        v[k] = bd_load4(lmat + (size_t)4 * kb * cols, min(4, rows - 4 * kb), ua + cc, cols, true);
+                    } else if (i < N_ITEMS) {
+                        const int j = i - NL_ITEMS;
+                        const int blk = j / G::NRU, cc = j - blk * G::NRU;
+                        const int rb = 64 * q + blk;
+                        v[k] = bd_load4(rmat + (size_t)4 * rb * cols, min(4, rows - 4 * rb),
+                                        ua + roff - (P - 1) + cc, cols, rb < nb);
+                    }
+                }
+            };
+            auto store_chunk = [&](float4 *buf, const float4 (&v)[IPT]) {
+#pragma unroll
+                for (int k = 0; k < IPT; ++k) {
+                    const int i = threadIdx.x + k * 64 * NW;
+                    if (i < NL_ITEMS) {
+                        const int blk = i / G::NLU, cc = i - blk * G::NLU;
+                        buf[blk * G::NCL + cc] = v[k];
+                    } else if (i < N_ITEMS) {
+                        const int j = i - NL_ITEMS;
+                        const int blk = j / G::NRU, cc = j - blk * G::NRU;
+                        buf[L_ELEMS + blk * G::NCR + cc] = v[k];
+                    }
+                }
+            };
+
+            float acc1[4][P], acc2[3][P];
+#pragma unroll
+            for (int p = 0; p < P; ++p) {
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) acc1[rr][p] = 0.0f;
+#pragma unroll
+                for (int rr = 0; rr < 3; ++rr) acc2[rr][p] = 0.0f;
+            }
+            {
+                float4 v[IPT];
+                load_chunk(0, v);
+                store_chunk(smem, v);
+            }
+            __syncthreads();
+            for (int t = 0; t < nch; ++t) {
+                float4 v[IPT];
+                const bool more = t + 1 < nch;
+                if (more) load_chunk(t + 1, v);
+                if (wave_on) {
+                    const int ns = min(J, u_end - (u_first + t * J));
+                    const float4 *buf = smem + (t & 1) * BUF;
+                    bd_compute<J>(buf + (lane + wave) * G::NCL, buf + (lane + wave + 1) * G::NCL,
+                                  buf + L_ELEMS + lane * G::NCR, ns, acc1, acc2);
+                }
+                if (more) store_chunk(smem + ((t + 1) & 1) * BUF, v);
+                __syncthreads();
+            }
+            if (wave_on)
+                bd_big_reduce_store(a, lane, delta, c0, side, pair, q, wred, wextra, acc1, acc2);
+            __syncthreads();  // reduction reads done before the next staging
+        }
+    }
+}
+
 bool xcorr_blockdiag_supported(const XcorrArgs &a)
 {
     const int nb = (a.rows + 3) / 4;
-    return nb >= 4 && nb <= 64;
+    return nb >= 4;
 }
 
 template <typename K>
@@ -584,14 +779,49 @@ static hipError_t launch_chunk(BdArgs b, hipStream_t s)
     return hipGetLastError();
 }
 
+template <int NW, int J>
+static size_t bd_big_lds()
+{
+    using G = BdLds<J>;
+    const size_t stage = 2 * ((size_t)BdBig<NW>::LW * G::NCL + 64 * G::NCR) * sizeof(float4);
+    const size_t red = (size_t)NW * bd_red_floats(1) * sizeof(float);
+    return stage > red ? stage : red;
+}
+
+template <int NW, int J>
+static hipError_t launch_big(BdArgs b, hipStream_t s)
+{
+    static bool attr = false;
+    if (!attr) {
+        const hipError_t e = allow_lds(&xcorr_bd_big_kernel<NW, J>);
+        if (e != hipSuccess) return e;
+        attr = true;
+    }
+    b.n_dgroups = (b.nb + NW - 1) / NW;
+    const int64_t per = (int64_t)b.n_groups * b.n_xtiles * b.n_dgroups;
+    b.n_sides = per >= 1024 ? 1 : 2;
+    const unsigned blocks = (unsigned)(per * b.n_sides);
+    const size_t lds = bd_big_lds<NW, J>();
+    hipLaunchKernelGGL((xcorr_bd_big_kernel<NW, J>), dim3(blocks), dim3(64 * NW), lds, s, b);
+    return hipGetLastError();
+}
+
 hipError_t xcorr_launch_blockdiag(const XcorrArgs &a, hipStream_t s)
 {
     BdArgs b;
     b.x = a;
     b.nb = (a.rows + 3) / 4;
     b.wp = (a.cols + BD_P - 1) / BD_P * BD_P;
-    b.S = 64 / b.nb;
     const int64_t npairs = (int64_t)a.n_left * a.n_right;
+    if (b.nb > 64) {
+        // more row blocks than lanes: one pair per workgroup, passes of 64 blocks
+        b.S = 1;
+        b.nls = 1;
+        b.n_groups = (int)npairs;
+        b.n_xtiles = b.wp / BD_P;
+        return launch_big<16, 8>(b, s);
+    }
+    b.S = 64 / b.nb;
     b.n_groups = (int)((npairs + b.S - 1) / b.S);
     b.n_xtiles = b.wp / BD_P;
     // distinct left matrices one group of S consecutive pairs can touch

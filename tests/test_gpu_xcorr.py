@@ -61,7 +61,12 @@ def test_xcorr_edge_shapes(shape, algo):
                                    (2, 3, 100, 200), (1, 1, 60, 300), (1, 3, 13, 1000),
                                    (1, 1, 35, 600), (2, 3, 41, 600), (2, 3, 65, 260),
                                    # 16 diagonals whose whole staging only fits at 8 waves
-                                   (3, 3, 85, 72)])
+                                   (3, 3, 85, 72),
+                                   # more than 64 row blocks: passes of 64 blocks; 65 blocks
+                                   # (the left window wraps onto itself), odd rows, 2-3 passes,
+                                   # several pairs, wide rows
+                                   (1, 1, 257, 19), (1, 1, 260, 40), (1, 1, 300, 17), (2, 3, 272, 9),
+                                   (1, 2, 513, 6), (1, 1, 384, 64), (2, 1, 290, 33)])
 def test_xcorr_blockdiag_edge_shapes(shape):
     nl, nr, rows, cols = shape
     rng = np.random.default_rng(rows * 31 + cols)
@@ -145,3 +150,49 @@ def test_xcorr_invalid_arguments_rejected_before_launch():
     assert e.value.status == _lib.XC_ERR_SHAPE
     st = _lib.xcorr_f32_run(L.data_ptr() + 4, 1, L.data_ptr(), 1, 8, 8, L.data_ptr())
     assert st == _lib.XC_ERR_ALIGN
+
+
+def test_xcorr_large_one_to_one_sampled():
+    """512x512 one-to-one (two passes of 64 row blocks) against the oracle at
+    sampled outputs: every row and column of the output grid, plus random ones."""
+    rng = np.random.default_rng(402)
+    rows = cols = 512
+    L = f32_uniform(rng, (1, rows, cols))
+    R = f32_uniform(rng, (1, rows, cols))
+    _gpu.log("xcorr 512x512 one-to-one, sampled")
+    got = _gpu.run_xcorr(L, R)
+    oh, ow = 2 * rows - 1, 2 * cols - 1
+    ys = np.concatenate([np.arange(oh), rng.integers(0, oh, 600)])
+    xs = np.concatenate([rng.integers(0, ow, oh), rng.integers(0, ow, 600)])
+    ys = np.concatenate([ys, rng.integers(0, oh, ow)])
+    xs = np.concatenate([xs, np.arange(ow)])
+    flat = ys * ow + xs
+    ref, ab = oracle.xcorr_f32_points(L, R, flat)
+    g = got.reshape(-1)[flat].astype(np.float64)
+    err = np.abs(g - ref)
+    assert np.all(err <= 1e-5 * ab + 1e-30), f"max excess {np.max(err - 1e-5 * ab)}"
+
+
+def test_xcorr_large_small_integers_exact():
+    """Rows beyond 256 with small-integer inputs: exact in any summation order."""
+    rng = np.random.default_rng(403)
+    L = rng.integers(-2, 3, size=(2, 300, 24)).astype(np.float32)
+    R = rng.integers(-2, 3, size=(1, 300, 24)).astype(np.float32)
+    _gpu.log("xcorr 300-row small-integer exact")
+    ref, _ = oracle.xcorr_f32(L, R)
+    got = _gpu.run_xcorr(L, R, _lib.XC_XCORR_BLOCKDIAG)
+    assert np.array_equal(got.astype(np.float64), ref)
+
+
+def test_xcorr_large_delta_orientation():
+    rows, cols = 270, 12
+    for (a, b, c, d) in ((0, 0, 269, 11), (269, 11, 0, 0), (100, 3, 7, 9), (257, 0, 256, 11)):
+        L = np.zeros((1, rows, cols), np.float32)
+        R = np.zeros((1, rows, cols), np.float32)
+        L[0, a, b] = 1.0
+        R[0, c, d] = 1.0
+        _gpu.log(f"xcorr 270-row delta ({a},{b}) ({c},{d})")
+        got = _gpu.run_xcorr(L, R, _lib.XC_XCORR_BLOCKDIAG)
+        expect = np.zeros((2 * rows - 1, 2 * cols - 1), np.float32)
+        expect[a - c + rows - 1, b - d + cols - 1] = 1.0
+        assert np.array_equal(got[0, 0], expect)
