@@ -15,8 +15,8 @@ The fp32 cross-correlation form is timed in the same run (its own loops,
 reported under "xcorr"): one-to-one 256x256, one-to-many 1x64 of 64x64 and
 n-to-m 8x16 of 32x32, in GFLOP/s counted as 2*rows^2*cols^2 per pair.
 
-Kernel durations come from HIP events recorded on the stream the kernels run
-on, around every launch of the timed region.  The CPU oracle is timed on a
+Kernel durations come from two HIP events recorded on the stream the kernels
+run on, around the back-to-back launches of the timed region.  The CPU oracle is timed on a
 bounded sample of the same workload on this host ("cpu_baseline").
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
@@ -102,21 +102,27 @@ def copy_probe(mib: int, torch) -> None:
 
 
 def timed_loop(launch, steps, warmup, torch):
-    """Run `launch` warmup + steps times; return (wall ms per step, mean event ms per launch)."""
+    """Run `launch` warmup + steps times; return (wall ms per step, event ms per launch).
+
+    The timed launches run back to back on the current stream between two HIP
+    events recorded on that stream; the event time divided by the number of
+    launches is the mean launch duration (it includes the gaps between
+    dispatches but no per-launch event overhead, so it agrees with a
+    rocprofv3 kernel trace of back-to-back launches)."""
     for _ in range(warmup):
         launch()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s, e in ev:
-        s.record(stream)
+    start.record(stream)
+    for _ in range(steps):
         launch()
-        e.record(stream)
+    end.record(stream)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
-    per = sum(s.elapsed_time(e) for s, e in ev) / steps
+    per = start.elapsed_time(end) / steps
     return wall, per
 
 
