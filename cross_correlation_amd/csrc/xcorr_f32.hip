@@ -115,7 +115,26 @@ struct BdArgs {
     int n_xtiles;    // wp / BD_P
     int n_dgroups;   // ceil(nb / waves per workgroup)
     int n_sides;     // 1: a workgroup walks both dx signs; 2: one sign each
+    // multipliers for division by nb and by the whole-staging row widths
+    uint32_t m_nb, m_nr;  // fast_div_m(nb), small_div_m16(n_right)
 };
+
+// floor(x / d) as one high multiply, with m = fast_div_m(d); exact whenever
+// x * d < 2^32 (m = (2^32 + e) / d with 0 < e <= d, so the product
+// overshoots x / d by less than x / 2^32 < 1 / d).  d >= 2.
+__host__ __device__ constexpr uint32_t fast_div_m(uint32_t d) { return 0xFFFFFFFFu / d + 1u; }
+__device__ __forceinline__ int fast_div(int x, uint32_t m) { return (int)__umulhi((uint32_t)x, m); }
+
+// floor(x / d) for 0 <= x < d + 64 (a pair offset within a group over the
+// right-matrix count), with m16 = small_div_m16(d): for d >= 64 the quotient
+// is 0 or 1; below that (x * m16) >> 16 with m16 = ceil(2^16 / d) overshoots
+// x / d by less than x / 2^16 < 1 / d (x * d < 2^13), so it is exact.
+__host__ __device__ constexpr uint32_t small_div_m16(uint32_t d) { return d >= 64 ? 0u : (65535u + d) / d; }
+__device__ __forceinline__ int small_div(int x, int d, uint32_t m16)
+{
+    const int q_small = (int)(((uint32_t)x * m16) >> 16);
+    return d >= 64 ? (x >= d ? 1 : 0) : q_small;
+}
 
 // LDS geometry of one staging buffer for J walk steps: per row block, J left
 // columns and J + P - 1 right columns (the window halo), each a float4 of the
@@ -222,18 +241,25 @@ __device__ __forceinline__ BdWho bd_who(const BdArgs &a)
     w.delta = dgrp * NW + w.wave;  // this wave's block diagonal
     w.wave_on = w.delta < a.nb;
     const int nb = a.nb;
-    int sl = w.lane / nb;
+    int sl = fast_div(w.lane, a.m_nb);
     w.b = w.lane - sl * nb;
     if (sl >= a.S) sl = a.S - 1;  // spare lanes shadow the last slot; never stored
     w.s = sl;
     const int dl = w.wave_on ? w.delta : 0;
-    w.kb1 = (w.b + dl) % nb;
-    w.kb2 = (w.b + dl + 1) % nb;
-    // left-matrix slot: distinct left matrices of the group, in order
+    int k1 = w.b + dl;  // b, dl < nb: at most one wrap
+    k1 -= k1 >= nb ? nb : 0;
+    int k2 = k1 + 1;
+    k2 -= k2 >= nb ? nb : 0;
+    w.kb1 = k1;
+    w.kb2 = k2;
+    // left-matrix slot: distinct left matrices of the group, in order.  The
+    // group's first pair p0 is (l_first, r_first); pair p0 + d (d < 64) has
+    // left matrix l_first + (r_first + d) / n_right.
     const int64_t p0 = (int64_t)w.grp * a.S;
     const int64_t np = (int64_t)a.x.n_left * a.x.n_right;
-    const int64_t ps = min(p0 + sl, np - 1);
-    w.ls = (int)(ps / a.x.n_right - p0 / a.x.n_right);
+    const unsigned r_first = (unsigned)(p0 % a.x.n_right);
+    const unsigned d = (unsigned)min((int64_t)sl, np - 1 - p0);
+    w.ls = small_div((int)(r_first + d), a.x.n_right, a.m_nr);
     w.bstar = nb - dl - 1;  // the lane whose block 1 is unwrapped and block 2 wrapped
     return w;
 }
@@ -286,14 +312,20 @@ __device__ __forceinline__ void bd_reduce_store(const BdArgs &a, const BdWho &w,
         const int blo = wr ? nb - w.delta : 0;
         const int bhi = wr ? nb : nb - w.delta;
         const float *col = wred + (r * P + p) * RS + sl * nb;
-        // eight independent partial sums, combined in a fixed tree order
+        // eight independent partial sums (block b into part[b % 8]),
+        // combined in a fixed tree order; the reads are unconditional (index
+        // clamped into the slot) so they are all in flight together
         float part[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) part[i] = 0.0f;
-        for (int bb = blo; bb < bhi; bb += 8) {
+        for (int bb = blo & ~7; bb < bhi; bb += 8) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-                if (bb + i < bhi) part[i] += col[bb + i];
+            for (int i = 0; i < 8; ++i) {
+                const int b = bb + i;
+                const float v = col[min(b, nb - 1)];
+                const int keep_b = -(int)((b >= blo) & (b < bhi));  // all ones or zero
+                part[i] += __int_as_float(__float_as_int(v) & keep_b);
+            }
         }
         float sum = ((part[0] + part[1]) + (part[2] + part[3])) + ((part[4] + part[5]) + (part[6] + part[7]));
         if (wr && r >= 1)
@@ -306,20 +338,29 @@ __device__ __forceinline__ void bd_reduce_store(const BdArgs &a, const BdWho &w,
     __builtin_amdgcn_wave_barrier();
 }
 
+// Whole staging: LDS columns per staged row block (P - 1 zero columns each
+// side of the wp data columns, one padding column, odd for the banks).
+__host__ __device__ constexpr int bd_whole_w(int wp) { return (wp + 2 * BD_P) | 1; }
+
 // Reduction area per wave (floats).
 __host__ __device__ constexpr int bd_red_floats(int S) { return 4 * BD_P * 65 + S * 3 * BD_P; }
 
-// The 4 rows of a row block at one column (zero outside the matrix).
-__device__ __forceinline__ float4 bd_load4(const float *src, int nrow_ok, int gc, int cols, bool on)
+// The 4 rows of a row block at one column (zero outside the matrix).  The
+// four loads are issued unconditionally, from `safe` (any readable float)
+// where the element is outside the matrix, and the zeros are selected
+// afterwards: with no branch around them, the loads of several items stay
+// in flight together instead of waiting for each other.
+__device__ __forceinline__ float4 bd_load4(const float *src, const float *safe, int nrow_ok, int gc, int cols,
+                                           bool on)
 {
-    float4 val = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    if (on && nrow_ok > 0 && gc >= 0 && gc < cols) {
-        val.x = src[gc];
-        if (nrow_ok > 1) val.y = src[(size_t)cols + gc];
-        if (nrow_ok > 2) val.z = src[(size_t)2 * cols + gc];
-        if (nrow_ok > 3) val.w = src[(size_t)3 * cols + gc];
-    }
-    return val;
+    const bool ok = on && nrow_ok > 0 && gc >= 0 && gc < cols;
+    const float *p = ok ? src + gc : safe;
+    const bool ok1 = ok && nrow_ok > 1, ok2 = ok && nrow_ok > 2, ok3 = ok && nrow_ok > 3;
+    const float x = p[0];
+    const float y = p[ok1 ? cols : 0];
+    const float z = p[ok2 ? 2 * cols : 0];
+    const float w = p[ok3 ? 3 * cols : 0];
+    return make_float4(ok ? x : 0.0f, ok1 ? y : 0.0f, ok2 ? z : 0.0f, ok3 ? w : 0.0f);
 }
 
 // ---- chunked staging: columns pass through LDS J walk steps at a time ----
@@ -378,10 +419,10 @@ __global__ __launch_bounds__(64 * NW) void xcorr_bd_chunk_kernel(BdArgs a)
             const int ua = u_first + t * J;
 #pragma unroll
             for (int k = 0; k < LPT; ++k)
-                vl[k] = bd_load4(st_l, nrow_ok, ua + cres + k * NW, cols, st_on);
+                vl[k] = bd_load4(st_l, a.x.left, nrow_ok, ua + cres + k * NW, cols, st_on);
 #pragma unroll
             for (int k = 0; k < RPT; ++k)
-                vr[k] = bd_load4(st_r, nrow_ok, ua + roff - (P - 1) + cres + k * NW, cols, st_on);
+                vr[k] = bd_load4(st_r, a.x.right, nrow_ok, ua + roff - (P - 1) + cres + k * NW, cols, st_on);
         };
         auto store_chunk = [&](float4 *buf, const float4 (&vl)[LPT], const float4 (&vr)[RPT]) {
             if (sb < S * nb) {
@@ -440,61 +481,94 @@ __global__ __launch_bounds__(64 * NW) void xcorr_bd_whole_kernel(BdArgs a)
     const int nb = a.nb, S = a.S, wp = a.wp;
     const int rows = a.x.rows, cols = a.x.cols;
     const int64_t npairs = (int64_t)a.x.n_left * a.x.n_right;
-    // left: nls slots x nb blocks x LW columns (column u at index u; index wp
-    // is padding read by the pipelined walk); right: S slots x nb blocks x RW
-    // columns (right column c at index c + P - 1, zero halos on both sides).
-    const int LW = (wp + 1) | 1;
-    const int RW = (wp + 2 * P) | 1;
-    const int l_elems = a.nls * nb * LW;
+    // Every staged row block ("unit") is W LDS columns wide, left and right
+    // alike: source column g at index g + P - 1, zero halos on both sides
+    // (index wp + P - 1 is padding read by the pipelined walk).  Units: nls
+    // left slots x nb blocks, then S pair slots x nb blocks.
+    const int W = bd_whole_w(wp);
+    const int n_lu = a.nls * nb;
+    const int l_elems = n_lu * W;
     float4 *const Ls = smem;
     float4 *const Rs = smem + l_elems;
-    float *const red = reinterpret_cast<float *>(smem + l_elems + S * nb * RW);
+    float *const red = reinterpret_cast<float *>(smem + l_elems + S * nb * W);
     float *const wred = red + w.wave * bd_red_floats(S);
     float *const wextra = wred + 4 * P * 65;
 
     const int64_t p0 = (int64_t)w.grp * S;
     const int l_first = (int)(p0 / a.x.n_right);
-    const int nthreads = 64 * NW;
-    // Items: (left slot, block, column) then (pair slot, block, column index
-    // c + P - 1).  Each thread takes items in batches of SB: all loads of a
-    // batch are issued before any of its LDS stores, so the global-memory
-    // latency is paid once per batch rather than once per item.
-    const int nli = a.nls * nb * LW;
-    const int nit = nli + S * nb * RW;
-    constexpr int SB = 8;
-    for (int it0 = threadIdx.x; it0 < nit; it0 += SB * nthreads) {
-        float4 v[SB];
-#pragma unroll
-        for (int k = 0; k < SB; ++k) {
-            const int it = it0 + k * nthreads;
-            v[k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-            if (it < nli) {
-                const int blk = it / LW;
-                const int col = it - blk * LW;
-                const int lsl = blk / nb;
-                const int row0 = 4 * (blk - lsl * nb);
-                const int l = l_first + lsl;
-                const bool on = l < a.x.n_left && col < wp;
-                const float *src = a.x.left + ((size_t)(on ? l : 0) * rows + row0) * cols;
-                v[k] = bd_load4(src, min(4, rows - row0), col, cols, on);
-            } else if (it < nit) {
-                const int it2 = it - nli;
-                const int blk = it2 / RW;
-                const int col = it2 - blk * RW;
-                const int sl = blk / nb;
-                const int row0 = 4 * (blk - sl * nb);
-                const int64_t pair = p0 + sl;
-                const bool on = pair < npairs;
-                const int r = on ? (int)(pair % a.x.n_right) : 0;
-                const float *src = a.x.right + ((size_t)r * rows + row0) * cols;
-                v[k] = bd_load4(src, min(4, rows - row0), col - (P - 1), cols, on);
-            }
+    const int r_first = (int)(p0 % a.x.n_right);  // right matrix of the group's first pair
+    // Staging, in two steps.  (1) The first threads build a table in the
+    // (still unused) reduction area: for each unit, the offset of its first
+    // source row in the left or right array and the number of source rows
+    // (0: an empty slot, all zeros).  (2) Waves then take whole units, wave-uniform: the table entry
+    // goes to scalar registers and a lane only adds its own column, so a
+    // unit costs a lane a handful of instructions; the loads of KB units are
+    // issued before any of their LDS stores, so they are in flight together.
+    // Lanes below W - cols also write the unit's zero halo columns.
+    const int n_units = n_lu + S * nb;
+    uint4 *const table = reinterpret_cast<uint4 *>(red);
+    if ((int)threadIdx.x < n_units) {
+        const int u = threadIdx.x;
+        const bool is_l = u < n_lu;
+        const int ur = is_l ? u : u - n_lu;
+        const int sl = fast_div(ur, a.m_nb);
+        const int row0 = 4 * (ur - sl * nb);
+        int mat;
+        bool on;
+        if (is_l) {
+            // left slot sl: matrix l_first + sl
+            mat = l_first + sl;
+            on = mat < a.x.n_left;
+        } else {
+            // pair slot sl: pair p0 + sl, right matrix (r_first + sl) mod n_right
+            const int rq = r_first + sl;
+            mat = rq - small_div(rq, a.x.n_right, a.m_nr) * a.x.n_right;
+            on = p0 + sl < npairs;
         }
+        const uint64_t off = (uint64_t)(on ? mat : 0) * rows * cols + (uint64_t)row0 * cols;  // elements
+        table[u] = make_uint4((uint32_t)off, (uint32_t)(off >> 32), on ? (uint32_t)min(4, rows - row0) : 0u,
+                              is_l ? 1u : 0u);
+    }
+    __syncthreads();
+    {
+        constexpr int KB = 8;
+        const int n_halo = W - cols;  // P - 1 columns left of the data, the rest right of it
+        const int halo_c = w.lane < P - 1 ? w.lane : cols + w.lane;
+        for (int cp = 0; cp * 64 < cols; ++cp) {
+            const int gc = cp * 64 + w.lane;  // source column
+            const bool col_ok = gc < cols;
+            for (int u0 = w.wave; u0 < n_units; u0 += NW * KB) {
+                float4 v[KB];
 #pragma unroll
-        for (int k = 0; k < SB; ++k) {
-            const int it = it0 + k * nthreads;
-            if (it < nit)
-                smem[it] = v[k];  // left items then right items are contiguous in LDS
+                for (int k = 0; k < KB; ++k) {
+                    const int u = u0 + k * NW;  // wave-uniform
+                    v[k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                    if (u < n_units) {
+                        const uint4 e = table[u];
+                        const uint32_t lo = __builtin_amdgcn_readfirstlane(e.x);
+                        const uint32_t hi = __builtin_amdgcn_readfirstlane(e.y);
+                        const int nrow = (int)__builtin_amdgcn_readfirstlane(e.z);
+                        const bool t_l = __builtin_amdgcn_readfirstlane(e.w) != 0;
+                        const float *src = (t_l ? a.x.left : a.x.right) + (((uint64_t)hi << 32) | lo);
+                        if (col_ok && nrow > 0) {
+                            v[k].x = src[gc];
+                            if (nrow > 1) v[k].y = src[cols + gc];
+                            if (nrow > 2) v[k].z = src[2 * cols + gc];
+                            if (nrow > 3) v[k].w = src[3 * cols + gc];
+                        }
+                    }
+                }
+#pragma unroll
+                for (int k = 0; k < KB; ++k) {
+                    const int u = u0 + k * NW;
+                    if (u < n_units) {
+                        if (col_ok)
+                            smem[u * W + (P - 1) + gc] = v[k];
+                        if (cp == 0 && w.lane < n_halo)
+                            smem[u * W + halo_c] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                    }
+                }
+            }
         }
     }
     __syncthreads();
@@ -514,8 +588,9 @@ __global__ __launch_bounds__(64 * NW) void xcorr_bd_whole_kernel(BdArgs a)
         }
         // ring preload reads right columns u_first + roff - (P-1) .. u_first + roff,
         // i.e. indices u_first + roff .. + P - 1 (>= 0: roff >= -c0 and u_first >= c0 on side 0)
-        bd_compute<16>(Ls + (w.ls * nb + w.kb1) * LW + u_first, Ls + (w.ls * nb + w.kb2) * LW + u_first,
-                       Rs + (w.s * nb + w.b) * RW + u_first + roff, u_end - u_first, acc1, acc2);
+        bd_compute<16>(Ls + (w.ls * nb + w.kb1) * W + (P - 1) + u_first,
+                       Ls + (w.ls * nb + w.kb2) * W + (P - 1) + u_first,
+                       Rs + (w.s * nb + w.b) * W + u_first + roff, u_end - u_first, acc1, acc2);
         bd_reduce_store(a, w, side, wred, wextra, acc1, acc2);
     }
 }
@@ -581,10 +656,14 @@ __device__ __forceinline__ void bd_big_reduce_store(const BdArgs &a, int lane, i
         float part[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) part[i] = 0.0f;
-        for (int bb = blo; bb < bhi; bb += 8) {
+        for (int bb = blo & ~7; bb < bhi; bb += 8) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-                if (bb + i < bhi) part[i] += col[bb + i];
+            for (int i = 0; i < 8; ++i) {
+                const int b = bb + i;
+                const float v = col[min(b, 63)];
+                const int keep_b = -(int)((b >= blo) & (b < bhi));  // all ones or zero
+                part[i] += __int_as_float(__float_as_int(v) & keep_b);
+            }
         }
         float sum = ((part[0] + part[1]) + (part[2] + part[3])) + ((part[4] + part[5]) + (part[6] + part[7]));
         if (wr && r >= 1 && star_here)
@@ -651,19 +730,22 @@ __global__ __launch_bounds__(64 * NW) void xcorr_bd_big_kernel(BdArgs a)
                 const int ua = u_first + t * J;
 #pragma unroll
                 for (int k = 0; k < IPT; ++k) {
+                    // left (window block, column) or right (block, column):
+                    // parameters selected, one unconditional load sequence
                     const int i = threadIdx.x + k * 64 * NW;
-                    v[k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-                    if (i < NL_ITEMS) {
-                        const int blk = i / G::NLU, cc = i - blk * G::NLU;
-                        const int kb = (L0 + blk) % nb;
-                        v[k] = bd_load4(lmat + (size_t)4 * kb * cols, min(4, rows - 4 * kb), ua + cc, cols, true);
-                    } else if (i < N_ITEMS) {
-                        const int j = i - NL_ITEMS;
-                        const int blk = j / G::NRU, cc = j - blk * G::NRU;
-                        const int rb = 64 * q + blk;
-                        v[k] = bd_load4(rmat + (size_t)4 * rb * cols, min(4, rows - 4 * rb),
-                                        ua + roff - (P - 1) + cc, cols, rb < nb);
-                    }
+                    const bool is_l = i < NL_ITEMS;
+                    const int j = is_l ? i : i - NL_ITEMS;
+                    const int blk = is_l ? j / G::NLU : j / G::NRU;
+                    const int cc = j - blk * (is_l ? G::NLU : G::NRU);
+                    int kb = L0 + blk;  // L0 < nb, blk < 81 < 2 nb: at most two wraps
+                    kb -= kb >= nb ? nb : 0;
+                    kb -= kb >= nb ? nb : 0;
+                    const int rb = 64 * q + blk;
+                    const bool on = is_l || (i < N_ITEMS && rb < nb);
+                    const int row0 = 4 * (is_l ? kb : rb);
+                    const float *src = (is_l ? lmat : rmat) + (size_t)row0 * cols;
+                    const int gc = is_l ? ua + cc : ua + roff - (P - 1) + cc;
+                    v[k] = bd_load4(src, is_l ? a.x.left : a.x.right, min(4, rows - row0), gc, cols, on);
                 }
             };
             auto store_chunk = [&](float4 *buf, const float4 (&v)[IPT]) {
@@ -733,8 +815,7 @@ constexpr size_t BD_LDS_MAX = 160 * 1024;
 
 static size_t bd_whole_lds(const BdArgs &b, int nw)
 {
-    const size_t LW = (size_t)((b.wp + 1) | 1), RW = (size_t)((b.wp + 2 * BD_P) | 1);
-    return (b.nls * b.nb * LW + (size_t)b.S * b.nb * RW) * sizeof(float4) +
+    return (size_t)(b.nls + b.S) * b.nb * bd_whole_w(b.wp) * sizeof(float4) +
            (size_t)nw * bd_red_floats(b.S) * sizeof(float);
 }
 
@@ -812,6 +893,9 @@ hipError_t xcorr_launch_blockdiag(const XcorrArgs &a, hipStream_t s)
     b.x = a;
     b.nb = (a.rows + 3) / 4;
     b.wp = (a.cols + BD_P - 1) / BD_P * BD_P;
+    b.m_nb = fast_div_m((uint32_t)b.nb);
+    b.m_nr = small_div_m16((uint32_t)a.n_right);
+
     const int64_t npairs = (int64_t)a.n_left * a.n_right;
     if (b.nb > 64) {
         // more row blocks than lanes: one pair per workgroup, passes of 64 blocks
