@@ -11,6 +11,9 @@ the matrix-core recast, which ncc_u8_run picks for this template) are timed
 on the same workload under "ncc_variants"; every variant returns identical
 outputs.
 
+The generalizations (best-match search, a 63 x 63 template) are timed on the
+same image under "ncc_ext".
+
 The fp32 cross-correlation form is timed in the same run (its own loops,
 reported under "xcorr"): one-to-one 256x256, one-to-many 1x64 of 64x64 and
 n-to-m 8x16 of 32x32, in GFLOP/s counted as 2*rows^2*cols^2 per pair.
@@ -177,6 +180,52 @@ def bench_ncc(args, torch, lib, inputs, variant=0, steps=None, warmup=None):
     return case, dict(wall_ms=wall, kernel_ms=per, dot4=dot4, outputs=oh * ow, bytes=bytes_alg)
 
 
+def bench_ncc_ext(args, torch, lib, inputs):
+    """The generalizations on the headline image: the best-match search
+    (ncc_u8_peak, with and without the coefficient map) and a template width
+    that is not a multiple of four (63 x 63, the last packed word of each
+    template row masked), next to the 64 x 64 template."""
+    from cross_correlation_amd.inputs import ncc_case
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream().cuda_stream
+    res = {}
+    steps, warmup = min(args.steps, 50), min(args.warmup, 5)
+    case = inputs.workload("ncc_1920x1080_t64")
+    img = torch.from_numpy(case.image).to(dev)
+    tm = torch.from_numpy(case.tmpl).to(dev)
+    oh, ow = case.out_shape
+    coef = torch.empty((oh, ow), dtype=torch.float32, device=dev)
+    peak = torch.empty(lib.PEAK_BYTES // 8, dtype=torch.int64, device=dev)
+    for name, cptr in (("peak_only", 0), ("peak_and_coef", coef.data_ptr())):
+        def launch():
+            st = lib.ncc_u8_peak(img.data_ptr(), case.width, case.height, case.pitch, tm.data_ptr(), case.t_width,
+                                 case.t_height, 0, 0, 0, cptr, peak.data_ptr(), stream=stream)
+            if st != 0:
+                raise RuntimeError(lib.status_str(st))
+        wall, per = timed_loop(launch, steps, warmup, torch)
+        res[name] = {"ms_per_step": round(wall, 5), "launches_ms": round(per, 5),
+                     "outputs_per_s": round(oh * ow / (per * 1e-3), 1)}
+    odd = ncc_case("ncc_1920x1080_t63", 2, 1080, 1920, 63, 63, image_kind="gradient", cut=True)
+    img63 = torch.from_numpy(odd.image).to(dev)
+    tm63 = torch.from_numpy(odd.tmpl).to(dev)
+    oh63, ow63 = odd.out_shape
+    outs = [torch.empty((oh63, ow63), dtype=torch.int32, device=dev) for _ in range(3)]
+    coef63 = torch.empty((oh63, ow63), dtype=torch.float32, device=dev)
+    for vname, v in (("dot4_ilp", lib.XC_NCC_DOT4_ILP), ("auto", lib.XC_NCC_AUTO)):
+        def launch():
+            st = lib.ncc_u8_run(img63.data_ptr(), odd.width, odd.height, odd.pitch, tm63.data_ptr(), odd.t_width,
+                                odd.t_height, outs[0].data_ptr(), outs[1].data_ptr(), outs[2].data_ptr(),
+                                coef63.data_ptr(), stream=stream, variant=v)
+            if st != 0:
+                raise RuntimeError(lib.status_str(st))
+        wall, per = timed_loop(launch, steps, warmup, torch)
+        # packed-byte work: 3 dot4 per packed word (16 per row, the last one masked) per output
+        dot4 = 3 * ((odd.t_width + 3) // 4) * odd.t_height * oh63 * ow63
+        res[f"t63x63_{vname}"] = {"kernel_ms": round(per, 5), "outputs_per_s": round(oh63 * ow63 / (per * 1e-3), 1),
+                                  "issued_Gdot4_per_s": round(dot4 / (per * 1e-3) / 1e9, 2)}
+    return res
+
+
 def bench_xcorr(args, torch, lib, inputs):
     dev = torch.device("cuda:0")
     res = {}
@@ -318,6 +367,7 @@ def main():
                          "kernel": "ncc_u8_mfma_kernel",
                          "note": "matrix-core instructions take ~1 us of the kernel; VALU issue and "
                                  "LDS/barrier latency bound it"}
+        out["ncc_ext"] = bench_ncc_ext(args, torch, _lib, inputs)
     if args.only in ("xcorr", "all"):
         out["xcorr"] = bench_xcorr(args, torch, _lib, inputs)
     if not args.no_peak_probe:

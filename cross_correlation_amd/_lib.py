@@ -35,7 +35,11 @@ XC_XCORR_BLOCKDIAG = 2
 XC_NCC_MAX_TEMPLATE_PIXELS = 66051
 
 # Every symbol the public header declares.
-EXPORTED = ("ncc_u8_run", "ncc_u8_run_variant", "xcorr_f32_run", "xcorr_f32_run_algo", "xc_status_str")
+EXPORTED = ("ncc_u8_run", "ncc_u8_run_variant", "ncc_u8_peak", "xcorr_f32_run", "xcorr_f32_run_algo",
+            "xc_status_str")
+
+# xc_ncc_peak (include/xcorr.h): key u64, y i32, x i32, coef f32, reserved i32
+PEAK_BYTES = 24
 
 
 class XcError(RuntimeError):
@@ -66,6 +70,8 @@ def load(path: str = LIB_PATH):
     lib.ncc_u8_run.argtypes = [_vp, _i, _i, _i, _vp, _i, _i, _vp, _vp, _vp, _vp, _vp]
     lib.ncc_u8_run_variant.restype = _i
     lib.ncc_u8_run_variant.argtypes = [_vp, _i, _i, _i, _vp, _i, _i, _vp, _vp, _vp, _vp, _i, _vp]
+    lib.ncc_u8_peak.restype = _i
+    lib.ncc_u8_peak.argtypes = [_vp, _i, _i, _i, _vp, _i, _i, _vp, _vp, _vp, _vp, _vp, _i, _vp]
     lib.xcorr_f32_run.restype = _i
     lib.xcorr_f32_run.argtypes = [_vp, _i, _vp, _i, _i, _i, _vp, _vp]
     lib.xcorr_f32_run_algo.restype = _i
@@ -91,6 +97,22 @@ def ncc_u8_run(image, width, height, pitch, tmpl, t_width, t_height, sum_i, sum_
     return load().ncc_u8_run_variant(image, width, height, pitch, tmpl, t_width, t_height,
                                      sum_i or None, sum_isq or None, sum_it or None, coef or None,
                                      variant, stream or None)
+
+
+def ncc_u8_peak(image, width, height, pitch, tmpl, t_width, t_height, sum_i, sum_isq, sum_it, coef, peak,
+                stream=None, variant=XC_NCC_AUTO) -> int:
+    """Raw call with integer device addresses (0 for NULL; ``peak`` points to
+    PEAK_BYTES of device memory); returns the status."""
+    return load().ncc_u8_peak(image, width, height, pitch, tmpl, t_width, t_height,
+                              sum_i or None, sum_isq or None, sum_it or None, coef or None, peak or None,
+                              variant, stream or None)
+
+
+def decode_peak(raw: bytes) -> tuple[int, int, float]:
+    """(y, x, coef) from the PEAK_BYTES of an xc_ncc_peak read back to the host."""
+    import struct
+    _key, y, x, coef, _res = struct.unpack("<QiifI", bytes(raw[:PEAK_BYTES]))
+    return y, x, coef
 
 
 def xcorr_f32_run(left, n_left, right, n_right, rows, cols, out, stream=None, algo=XC_XCORR_AUTO) -> int:

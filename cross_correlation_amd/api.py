@@ -28,7 +28,7 @@ def ncc_u8(image: torch.Tensor, tmpl: torch.Tensor, *, width: int | None = None,
 
     ``image`` is a [height, pitch] uint8 CUDA tensor (rows contiguous, pitch a
     multiple of 16 bytes, only the first ``width`` columns are pixels);
-    ``tmpl`` a dense [t_height, t_width] uint8 CUDA tensor.  Returns a dict of
+    ``tmpl`` a dense [t_height, t_width] uint8 CUDA tensor (any width).  Returns a dict of
     the requested outputs, each [out_h, out_w]; pass ``out`` to reuse buffers.
     """
     _device_u8(image, "image")
@@ -50,6 +50,41 @@ def ncc_u8(image: torch.Tensor, tmpl: torch.Tensor, *, width: int | None = None,
                          _stream_handle(stream), variant)
     _lib.check(st, "ncc_u8_run")
     return out
+
+
+def ncc_u8_peak(image: torch.Tensor, tmpl: torch.Tensor, *, width: int | None = None, outputs=(),
+                variant: int = _lib.XC_NCC_AUTO, out: dict | None = None, peak: torch.Tensor | None = None,
+                stream=None) -> dict:
+    """Best match of the valid-mode u8 normalized correlation.
+
+    Same inputs as :func:`ncc_u8`; ``outputs`` (default none) selects maps to
+    return as well.  The result dict holds those maps and ``"peak"``, the
+    device tensor of the xc_ncc_peak (decode it with
+    ``_lib.decode_peak(peak.cpu().numpy().tobytes())`` after synchronizing).
+    """
+    _device_u8(image, "image")
+    _device_u8(tmpl, "tmpl")
+    if image.dim() != 2 or image.stride(1) != 1 or tmpl.dim() != 2 or not tmpl.is_contiguous():
+        raise ValueError("image must be 2D with unit column stride; tmpl must be 2D contiguous")
+    height, pitch = image.shape[0], image.stride(0)
+    width = image.shape[1] if width is None else width
+    th, tw = tmpl.shape
+    oh, ow = height - th + 1, width - tw + 1
+    if out is None:
+        out = {}
+        for k in outputs:
+            dt = torch.float32 if k == "coef" else torch.int32
+            out[k] = torch.empty((max(oh, 0), max(ow, 0)), dtype=dt, device=image.device)
+    if peak is None:
+        peak = torch.empty(_lib.PEAK_BYTES // 8, dtype=torch.int64, device=image.device)
+    ptr = {k: (out[k].data_ptr() if k in out else 0) for k in ("sum_i", "sum_isq", "sum_it", "coef")}
+    st = _lib.ncc_u8_peak(image.data_ptr(), width, height, pitch, tmpl.data_ptr(), tw, th,
+                          ptr["sum_i"], ptr["sum_isq"], ptr["sum_it"], ptr["coef"], peak.data_ptr(),
+                          _stream_handle(stream), variant)
+    _lib.check(st, "ncc_u8_peak")
+    res = dict(out)
+    res["peak"] = peak
+    return res
 
 
 def xcorr_f32(left: torch.Tensor, right: torch.Tensor, *, algo: int = _lib.XC_XCORR_AUTO,

@@ -16,24 +16,22 @@ int hip_status(hipError_t e) { return e == hipSuccess ? XC_OK : XC_ERR_HIP; }
 // Host-side validation shared by both NCC entry points; fills `a` on success.
 int ncc_validate(const uint8_t *image, int width, int height, int pitch_bytes, const uint8_t *tmpl,
                  int t_width, int t_height, uint32_t *sum_i, uint32_t *sum_isq, uint32_t *sum_it,
-                 float *coef, xc::NccArgs &a)
+                 float *coef, bool need_map, xc::NccArgs &a)
 {
     if (!image || !tmpl)
         return XC_ERR_NULL;
-    if (!sum_i && !sum_isq && !sum_it && !coef)
+    if (need_map && !sum_i && !sum_isq && !sum_it && !coef)
         return XC_ERR_NULL;
     if (width <= 0 || height <= 0 || t_width <= 0 || t_height <= 0 || pitch_bytes <= 0)
         return XC_ERR_SHAPE;
     if (t_width > width || t_height > height || pitch_bytes < width)
         return XC_ERR_SHAPE;
-    if (t_width % 4 != 0)
-        return XC_ERR_TEMPLATE_WIDTH;
     if ((int64_t)t_width * t_height > XC_NCC_MAX_TEMPLATE_PIXELS)
         return XC_ERR_OVERFLOW;
     const int64_t out_w = width - t_width + 1, out_h = height - t_height + 1;
     if (out_w * out_h > INT32_MAX || (int64_t)height * pitch_bytes > ((int64_t)1 << 40))
         return XC_ERR_OVERFLOW;
-    if (!aligned(image, 16) || pitch_bytes % 16 != 0 || !aligned(tmpl, 4))
+    if (!aligned(image, 16) || pitch_bytes % 16 != 0)
         return XC_ERR_ALIGN;
     if ((sum_i && !aligned(sum_i, 4)) || (sum_isq && !aligned(sum_isq, 4)) || (sum_it && !aligned(sum_it, 4)) ||
         (coef && !aligned(coef, 4)))
@@ -49,6 +47,7 @@ int ncc_validate(const uint8_t *image, int width, int height, int pitch_bytes, c
     a.sum_isq = sum_isq;
     a.sum_it = sum_it;
     a.coef = coef;
+    a.peak = nullptr;
     a.out_w = (int)out_w;
     a.out_h = (int)out_h;
     a.hc = a.cw = a.lds_stride = a.t_stride = 0;
@@ -79,27 +78,16 @@ int xcorr_validate(const float *left, int n_left, const float *right, int n_righ
     return XC_OK;
 }
 
-} // namespace
-
-extern "C" {
-
-int ncc_u8_run_variant(const uint8_t *image, int width, int height, int pitch_bytes, const uint8_t *tmpl,
-                       int t_width, int t_height, uint32_t *sum_i, uint32_t *sum_isq, uint32_t *sum_it,
-                       float *coef, int variant, void *stream)
+// Launch the chosen variant on validated arguments.
+int ncc_dispatch(const xc::NccArgs &a, int variant, hipStream_t s)
 {
-    xc::NccArgs a;
-    const int st = ncc_validate(image, width, height, pitch_bytes, tmpl, t_width, t_height, sum_i, sum_isq,
-                                sum_it, coef, a);
-    if (st != XC_OK)
-        return st;
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     switch (variant) {
     case XC_NCC_AUTO:
         // The matrix-core recast has a fixed cost per tile of about the
         // packed-byte kernel's time for a 16x16 template; it wins from about
         // 512 template pixels on (measured on MI355X: 2.2x at 32x32, 6.4x at
         // 64x64, 10x at 256x128 over a 1920x1080 image).
-        if ((int64_t)t_width * t_height >= 512 && xc::ncc_mfma_supported(a))
+        if ((int64_t)a.t_width * a.t_height >= 512 && xc::ncc_mfma_supported(a))
             return hip_status(xc::ncc_launch_mfma(a, s));
         return hip_status(xc::ncc_launch_ilp(a, s));
     case XC_NCC_DOT4_ILP:
@@ -109,12 +97,63 @@ int ncc_u8_run_variant(const uint8_t *image, int width, int height, int pitch_by
     case XC_NCC_SCALAR_C1:
         return hip_status(xc::ncc_launch_c1(a, false, s));
     case XC_NCC_MFMA:
-        if (!xc::ncc_mfma_supported(a))
-            return XC_ERR_SHAPE;
         return hip_status(xc::ncc_launch_mfma(a, s));
     default:
         return XC_ERR_VARIANT;
     }
+}
+
+// Variant check done before anything is enqueued.
+int ncc_variant_ok(const xc::NccArgs &a, int variant)
+{
+    if (variant < XC_NCC_AUTO || variant > XC_NCC_MFMA)
+        return XC_ERR_VARIANT;
+    if (variant == XC_NCC_MFMA && !xc::ncc_mfma_supported(a))
+        return XC_ERR_SHAPE;
+    return XC_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+int ncc_u8_run_variant(const uint8_t *image, int width, int height, int pitch_bytes, const uint8_t *tmpl,
+                       int t_width, int t_height, uint32_t *sum_i, uint32_t *sum_isq, uint32_t *sum_it,
+                       float *coef, int variant, void *stream)
+{
+    xc::NccArgs a;
+    int st = ncc_validate(image, width, height, pitch_bytes, tmpl, t_width, t_height, sum_i, sum_isq, sum_it,
+                          coef, true, a);
+    if (st != XC_OK)
+        return st;
+    if ((st = ncc_variant_ok(a, variant)) != XC_OK)
+        return st;
+    return ncc_dispatch(a, variant, reinterpret_cast<hipStream_t>(stream));
+}
+
+int ncc_u8_peak(const uint8_t *image, int width, int height, int pitch_bytes, const uint8_t *tmpl, int t_width,
+                int t_height, uint32_t *sum_i, uint32_t *sum_isq, uint32_t *sum_it, float *coef,
+                xc_ncc_peak *peak, int variant, void *stream)
+{
+    if (!peak)
+        return XC_ERR_NULL;
+    xc::NccArgs a;
+    int st = ncc_validate(image, width, height, pitch_bytes, tmpl, t_width, t_height, sum_i, sum_isq, sum_it,
+                          coef, false, a);
+    if (st != XC_OK)
+        return st;
+    if (!aligned(peak, 8))
+        return XC_ERR_ALIGN;
+    if ((st = ncc_variant_ok(a, variant)) != XC_OK)
+        return st;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    static_assert(sizeof(peak->key) == sizeof(unsigned long long), "64-bit key");
+    a.peak = reinterpret_cast<unsigned long long *>(&peak->key);
+    if ((st = hip_status(xc::ncc_peak_init(peak, s))) != XC_OK)
+        return st;
+    if ((st = ncc_dispatch(a, variant, s)) != XC_OK)
+        return st;
+    return hip_status(xc::ncc_peak_finish(peak, a.out_w, s));
 }
 
 int ncc_u8_run(const uint8_t *image, int width, int height, int pitch_bytes, const uint8_t *tmpl, int t_width,
@@ -160,7 +199,7 @@ const char *xc_status_str(int status)
     case XC_OK: return "success";
     case XC_ERR_NULL: return "a required pointer is NULL, or no output was requested";
     case XC_ERR_SHAPE: return "a size is not positive, the template is larger than the image, or the shape is not supported by the chosen algorithm";
-    case XC_ERR_TEMPLATE_WIDTH: return "template width is not a multiple of 4";
+    case XC_ERR_TEMPLATE_WIDTH: return "reserved (template widths are no longer restricted)";
     case XC_ERR_OVERFLOW: return "template area over 66,051 pixels (32-bit sums could wrap) or an index range exceeded";
     case XC_ERR_ALIGN: return "a base pointer or the row pitch is not suitably aligned (16 bytes for images and matrices)";
     case XC_ERR_HIP: return "HIP launch or runtime error (or no device)";

@@ -16,6 +16,7 @@ struct NccArgs {
     int t_width, t_height;
     uint32_t *sum_i, *sum_isq, *sum_it;
     float *coef;
+    unsigned long long *peak;  // best-match key (see peak_key), or NULL
     int out_w, out_h;
     // chunking of the template, chosen by the launcher
     int hc;          // template rows per chunk
@@ -29,6 +30,11 @@ hipError_t ncc_launch_c1(NccArgs a, bool dot4, hipStream_t s);
 // SumIT on the i8 matrix cores; takes template rows up to 256 bytes.
 hipError_t ncc_launch_mfma(NccArgs a, hipStream_t s);
 bool ncc_mfma_supported(const NccArgs &a);
+// Best-match search around a correlation launch: set the key to 0 before it,
+// decode the key into (y, x, coefficient) after it.  `peak` points to an
+// xc_ncc_peak (include/xcorr.h).
+hipError_t ncc_peak_init(void *peak, hipStream_t s);
+hipError_t ncc_peak_finish(void *peak, int out_w, hipStream_t s);
 
 // Arguments of the fp32 cross-correlation kernels (validated on the host).
 struct XcorrArgs {

@@ -38,6 +38,7 @@
 
 #include "kernels.h"
 #include "ncc_common.h"
+#include "xcorr.h"
 
 namespace xc {
 
@@ -45,46 +46,60 @@ namespace xc {
 // load the next aligned image word, form the three shifted words, and for each
 // output row q the row serves accumulate 3 x 4 dot4 with template row (rl - q).
 // Image words and template words (at a wave-uniform address) both come from
-// LDS; WC words per unrolled step.
+// LDS; WC words per unrolled step.  When the chunk ends with the last word of
+// a template row whose width is not a multiple of 4 (tmask != ~0), that word
+// goes last, its shifted image words masked to the template's bytes (the
+// template word is zero beyond them), so every sum counts exactly the
+// template's pixels.
+template <int Q>
+__device__ __forceinline__ void ncc_word(uint32_t w1, uint32_t w0, uint32_t mask, const uint32_t *t0, int k,
+                                         int tstride, int qlo, int qhi, bool full, uint32_t (&ai)[Q][4],
+                                         uint32_t (&aq)[Q][4], uint32_t (&at)[Q][4])
+{
+    uint32_t s[4];
+    s[0] = w0 & mask;
+    s[1] = shift_bytes(w1, w0, 1) & mask;
+    s[2] = shift_bytes(w1, w0, 2) & mask;
+    s[3] = shift_bytes(w1, w0, 3) & mask;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        if (full || (q >= qlo && q <= qhi)) {
+            const uint32_t t = t0[k - q * tstride];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                ai[q][c] = dot4u(s[c], 0x01010101u, ai[q][c]);
+                aq[q][c] = dot4u(s[c], s[c], aq[q][c]);
+                at[q][c] = dot4u(s[c], t, at[q][c]);
+            }
+        }
+    }
+}
+
 template <int Q, int WC, bool FULL>
-__device__ __forceinline__ void ncc_row(const uint32_t *rp, const uint32_t *t0, int tstride, int cw,
-                                        int qlo, int qhi, uint32_t (&ai)[Q][4], uint32_t (&aq)[Q][4],
-                                        uint32_t (&at)[Q][4])
+__device__ __forceinline__ void ncc_row(const uint32_t *rp, const uint32_t *t0, int tstride, int cw_main,
+                                        uint32_t tmask, int qlo, int qhi, uint32_t (&ai)[Q][4],
+                                        uint32_t (&aq)[Q][4], uint32_t (&at)[Q][4])
 {
     uint32_t w0 = rp[0];
-    for (int kb = 0; kb < cw; kb += WC) {
+    for (int kb = 0; kb < cw_main; kb += WC) {
 #pragma unroll
         for (int kk = 0; kk < WC; ++kk) {
             const int k = kb + kk;
             const uint32_t w1 = rp[k + 1];
-            uint32_t s[4];
-            s[0] = w0;
-            s[1] = shift_bytes(w1, w0, 1);
-            s[2] = shift_bytes(w1, w0, 2);
-            s[3] = shift_bytes(w1, w0, 3);
-#pragma unroll
-            for (int q = 0; q < Q; ++q) {
-                if (FULL || (q >= qlo && q <= qhi)) {
-                    const uint32_t t = t0[k - q * tstride];
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        ai[q][c] = dot4u(s[c], 0x01010101u, ai[q][c]);
-                        aq[q][c] = dot4u(s[c], s[c], aq[q][c]);
-                        at[q][c] = dot4u(s[c], t, at[q][c]);
-                    }
-                }
-            }
+            ncc_word<Q>(w1, w0, 0xFFFFFFFFu, t0, k, tstride, qlo, qhi, FULL, ai, aq, at);
             w0 = w1;
         }
     }
+    if (tmask != 0xFFFFFFFFu)
+        ncc_word<Q>(rp[cw_main + 1], w0, tmask, t0, cw_main, tstride, qlo, qhi, FULL, ai, aq, at);
 }
 
 // A row at the start or end of a template slice serves only output rows
 // q in [qlo, qhi].  The (wave-uniform) test is taken once per q, outside the
 // word loop; the row's words are re-read per q (only 2*(Q-1) rows per slice).
 template <int Q>
-__device__ __forceinline__ void ncc_row_partial(const uint32_t *rp, const uint32_t *t0, int tstride, int cw,
-                                                int qlo, int qhi, uint32_t (&ai)[Q][4],
+__device__ __forceinline__ void ncc_row_partial(const uint32_t *rp, const uint32_t *t0, int tstride, int cw_main,
+                                                uint32_t tmask, int qlo, int qhi, uint32_t (&ai)[Q][4],
                                                 uint32_t (&aq)[Q][4], uint32_t (&at)[Q][4])
 {
 #pragma unroll
@@ -93,7 +108,7 @@ __device__ __forceinline__ void ncc_row_partial(const uint32_t *rp, const uint32
             continue;
         const uint32_t *tq = t0 - q * tstride;
         uint32_t w0 = rp[0];
-        for (int k = 0; k < cw; ++k) {
+        for (int k = 0; k < cw_main; ++k) {
             const uint32_t w1 = rp[k + 1];
             const uint32_t t = tq[k];
             uint32_t s[4];
@@ -108,6 +123,22 @@ __device__ __forceinline__ void ncc_row_partial(const uint32_t *rp, const uint32
                 at[q][c] = dot4u(s[c], t, at[q][c]);
             }
             w0 = w1;
+        }
+        if (tmask != 0xFFFFFFFFu) {
+            // the row's partial last word: only the template's bytes count
+            const uint32_t w1 = rp[cw_main + 1];
+            const uint32_t t = tq[cw_main];
+            uint32_t s[4];
+            s[0] = w0 & tmask;
+            s[1] = shift_bytes(w1, w0, 1) & tmask;
+            s[2] = shift_bytes(w1, w0, 2) & tmask;
+            s[3] = shift_bytes(w1, w0, 3) & tmask;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                ai[q][c] = dot4u(s[c], 0x01010101u, ai[q][c]);
+                aq[q][c] = dot4u(s[c], s[c], aq[q][c]);
+                at[q][c] = dot4u(s[c], t, at[q][c]);
+            }
         }
     }
 }
@@ -131,11 +162,12 @@ __global__ __launch_bounds__(64 * WV * KS) void ncc_u8_ilp_kernel(NccArgs a)
     const int kh = wave / WV;  // template-row slice of this wave
     const int x0 = blockIdx.x * 256;
     const int y0 = blockIdx.y * (WV * Q);
-    const int nw = a.t_width >> 2;
-    const uint32_t *__restrict__ tw = reinterpret_cast<const uint32_t *>(a.tmpl);
+    const int nw = (a.t_width + 3) >> 2;  // packed words per template row
+    const uint32_t tm = tail_mask(a.t_width);
+    const bool word_rows = tmpl_word_rows(a.tmpl, a.t_width);
 
     uint32_t sum_t, sum_tsq;
-    template_sums(tw, nw * a.t_height, sum_t, sum_tsq);
+    template_sums(a.tmpl, a.t_width, a.t_height, sum_t, sum_tsq);
 
     uint32_t ai[Q][4], aq[Q][4], at[Q][4];
 #pragma unroll
@@ -161,9 +193,12 @@ __global__ __launch_bounds__(64 * WV * KS) void ncc_u8_ilp_kernel(NccArgs a)
             for (int t = threadIdx.x; t < hc * cw; t += 64 * WV * KS) {
                 const int r = t / cw;
                 const int c = t - r * cw;
-                tl[r * tstride + c] = tw[(size_t)(jc + r) * nw + ic + c];
+                tl[r * tstride + c] = tmpl_word(a.tmpl, a.t_width, word_rows, jc + r, ic + c);
             }
             __syncthreads();
+            // the chunk holding a row's last word ends with the masked tail word
+            const uint32_t cm = ic + cw == nw ? tm : 0xFFFFFFFFu;
+            const int cw_main = cw - (cm != 0xFFFFFFFFu ? 1 : 0);
             if (j1 > j0) {
                 const uint32_t *wrow = lds + (rw * Q) * stride + lane;
                 // Image rows rl (relative to the wave's first output row) meet
@@ -172,13 +207,14 @@ __global__ __launch_bounds__(64 * WV * KS) void ncc_u8_ilp_kernel(NccArgs a)
                 // accumulators never meet a branch merge inside the row loop.
                 const int steady0 = j0 + Q - 1;
                 for (int rl = j0; rl < min(steady0, j1 + Q - 1); ++rl)
-                    ncc_row_partial<Q>(wrow + rl * stride, tl + rl * tstride, tstride, cw, max(0, rl - j1 + 1),
-                                       min(Q - 1, rl - j0), ai, aq, at);
+                    ncc_row_partial<Q>(wrow + rl * stride, tl + rl * tstride, tstride, cw_main, cm,
+                                       max(0, rl - j1 + 1), min(Q - 1, rl - j0), ai, aq, at);
                 for (int rl = steady0; rl < j1; ++rl)
-                    ncc_row<Q, WC, true>(wrow + rl * stride, tl + rl * tstride, tstride, cw, 0, Q - 1, ai, aq, at);
+                    ncc_row<Q, WC, true>(wrow + rl * stride, tl + rl * tstride, tstride, cw_main, cm, 0, Q - 1, ai,
+                                         aq, at);
                 for (int rl = max(j1, steady0); rl < j1 + Q - 1; ++rl)
-                    ncc_row_partial<Q>(wrow + rl * stride, tl + rl * tstride, tstride, cw, max(0, rl - j1 + 1),
-                                       min(Q - 1, rl - j0), ai, aq, at);
+                    ncc_row_partial<Q>(wrow + rl * stride, tl + rl * tstride, tstride, cw_main, cm,
+                                       max(0, rl - j1 + 1), min(Q - 1, rl - j0), ai, aq, at);
             }
         }
     }
@@ -218,6 +254,7 @@ __global__ __launch_bounds__(64 * WV * KS) void ncc_u8_ilp_kernel(NccArgs a)
     const int64_t n = (int64_t)a.t_width * a.t_height;
     const int64_t st64 = sum_t;
     const int64_t vt = n * (int64_t)sum_tsq - st64 * st64;
+    unsigned long long best = 0ull;
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
         const int y = y0 + rw * Q + q;
@@ -227,16 +264,18 @@ __global__ __launch_bounds__(64 * WV * KS) void ncc_u8_ilp_kernel(NccArgs a)
         for (int c = 0; c < 4; ++c) {
             const int x = x0 + 4 * lane + c;
             if (x < a.out_w)
-                ncc_store(a, (size_t)y * a.out_w + x, ai[q][c], aq[q][c], at[q][c], n, st64, vt);
+                ncc_store(a, (size_t)y * a.out_w + x, ai[q][c], aq[q][c], at[q][c], n, st64, vt, best);
         }
     }
+    if (a.peak)
+        peak_commit(a.peak, best);
 }
 
 // Ablation kernels: one output per thread, a 64 x 4 tile per workgroup, the
 // image tile in LDS.  DOT4 selects packed-byte dot products; otherwise the
 // bytes are multiplied and added one at a time.  Each thread runs one
 // dependent chain per sum, as the page's baseline kernels do.
-template <bool DOT4>
+template <bool DOT4, bool WORD_ROWS>
 __global__ __launch_bounds__(256) void ncc_u8_c1_kernel(NccArgs a)
 {
     extern __shared__ uint32_t lds[];
@@ -244,11 +283,11 @@ __global__ __launch_bounds__(256) void ncc_u8_c1_kernel(NccArgs a)
     const int ty = threadIdx.x >> 6;
     const int x0 = blockIdx.x * 64;
     const int y0 = blockIdx.y * 4;
-    const int nw = a.t_width >> 2;
-    const uint32_t *__restrict__ tw = reinterpret_cast<const uint32_t *>(a.tmpl);
+    const int nw = (a.t_width + 3) >> 2;  // packed words per template row
+    const uint32_t tm = tail_mask(a.t_width);
 
     uint32_t sum_t, sum_tsq;
-    template_sums(tw, nw * a.t_height, sum_t, sum_tsq);
+    template_sums(a.tmpl, a.t_width, a.t_height, sum_t, sum_tsq);
 
     uint32_t si = 0, sq = 0, st = 0;
     const int stride = a.lds_stride;
@@ -264,10 +303,8 @@ __global__ __launch_bounds__(256) void ncc_u8_c1_kernel(NccArgs a)
             __syncthreads();
             for (int j = 0; j < hc; ++j) {
                 const uint32_t *rp = lds + (ty + j) * stride + (tx >> 2);
-                const uint32_t *tr = tw + (size_t)(jc + j) * nw + ic;
-                for (int k = 0; k < cw; ++k) {
-                    const uint32_t i4 = shift_bytes(rp[k + 1], rp[k], sh);
-                    const uint32_t t4 = tr[k];
+                const uint8_t *trow = a.tmpl + (size_t)(jc + j) * a.t_width;
+                auto mac = [&](uint32_t i4, uint32_t t4) {
                     if (DOT4) {
                         si = dot4u(i4, 0x01010101u, si);
                         sq = dot4u(i4, i4, sq);
@@ -282,17 +319,56 @@ __global__ __launch_bounds__(256) void ncc_u8_c1_kernel(NccArgs a)
                             st += p * t;
                         }
                     }
+                };
+                if (WORD_ROWS) {
+                    // whole-word rows: the (wave-uniform) template words load directly
+                    const uint32_t *tw = reinterpret_cast<const uint32_t *>(trow) + ic;
+                    for (int k = 0; k < cw; ++k)
+                        mac(shift_bytes(rp[k + 1], rp[k], sh), tw[k]);
+                } else {
+                    // gathered words, the row's partial last word with its image bytes masked
+                    const int cw_main = cw - (ic + cw == nw && tm != 0xFFFFFFFFu ? 1 : 0);
+                    for (int k = 0; k < cw_main; ++k)
+                        mac(shift_bytes(rp[k + 1], rp[k], sh), tmpl_row_word(trow, a.t_width, false, ic + k));
+                    if (cw_main < cw)
+                        mac(shift_bytes(rp[cw_main + 1], rp[cw_main], sh) & tm,
+                            tmpl_row_word(trow, a.t_width, false, ic + cw_main));
                 }
             }
         }
     }
     const int y = y0 + ty;
     const int x = x0 + tx;
+    unsigned long long best = 0ull;
     if (y < a.out_h && x < a.out_w) {
         const int64_t n = (int64_t)a.t_width * a.t_height;
         const int64_t st64 = sum_t;
-        ncc_store(a, (size_t)y * a.out_w + x, si, sq, st, n, st64, n * (int64_t)sum_tsq - st64 * st64);
+        ncc_store(a, (size_t)y * a.out_w + x, si, sq, st, n, st64, n * (int64_t)sum_tsq - st64 * st64, best);
     }
+    if (a.peak)
+        peak_commit(a.peak, best);
+}
+
+// Best match: clear the key before the correlation launch, decode it after.
+__global__ void ncc_peak_init_kernel(xc_ncc_peak *p)
+{
+    p->key = 0ull;
+    p->y = -1;
+    p->x = -1;
+    p->coef = 0.0f;
+    p->reserved = 0;
+}
+
+__global__ void ncc_peak_finish_kernel(xc_ncc_peak *p, int out_w)
+{
+    const unsigned long long k = p->key;
+    if (k == 0ull)
+        return;
+    const uint32_t idx = 0xFFFFFFFFu - (uint32_t)k;
+    const uint32_t ord = (uint32_t)(k >> 32);
+    p->y = (int32_t)(idx / (uint32_t)out_w);
+    p->x = (int32_t)(idx % (uint32_t)out_w);
+    p->coef = __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
 }
 
 // ---------------------------------------------------------------------------
@@ -323,11 +399,13 @@ static hipError_t dispatch_wc(const NccArgs &a, int wc, hipStream_t s)
 // unroll WC and the chunking so that the LDS tile stays within 64 KiB.
 hipError_t ncc_launch_ilp(NccArgs a, hipStream_t s)
 {
-    const int nw = a.t_width / 4;
+    const int nw = (a.t_width + 3) / 4;  // packed words per row, the last one partial when t_width % 4 != 0
     // Unroll of the template-word loop: the largest power of two <= 4 that
-    // divides the words per template row (every chunk is a multiple of it).
+    // divides the whole words per template row (every chunk's whole words are
+    // a multiple of it; a partial last word goes after them).
+    const int nw_whole = a.t_width / 4;
     int wc = 4;
-    while (nw % wc) wc >>= 1;
+    while (wc > 1 && nw_whole % wc) wc >>= 1;
     // Tile shape: the big tile when the image yields enough work to fill
     // 256 CUs, smaller ones for small images; the template-row split when
     // the template is tall enough to give each slice several rows.
@@ -356,9 +434,21 @@ hipError_t ncc_launch_ilp(NccArgs a, hipStream_t s)
     return dispatch_wc<1, 1, 1>(a, wc, s);
 }
 
+hipError_t ncc_peak_init(void *peak, hipStream_t s)
+{
+    hipLaunchKernelGGL(ncc_peak_init_kernel, dim3(1), dim3(1), 0, s, static_cast<xc_ncc_peak *>(peak));
+    return hipGetLastError();
+}
+
+hipError_t ncc_peak_finish(void *peak, int out_w, hipStream_t s)
+{
+    hipLaunchKernelGGL(ncc_peak_finish_kernel, dim3(1), dim3(1), 0, s, static_cast<xc_ncc_peak *>(peak), out_w);
+    return hipGetLastError();
+}
+
 hipError_t ncc_launch_c1(NccArgs a, bool dot4, hipStream_t s)
 {
-    const int nw = a.t_width / 4;
+    const int nw = (a.t_width + 3) / 4;
     int cw = nw;
     if (cw > 512) cw = 512;
     a.cw = cw;
@@ -369,10 +459,15 @@ hipError_t ncc_launch_c1(NccArgs a, bool dot4, hipStream_t s)
     a.hc = hc;
     dim3 grid((a.out_w + 63) / 64, (a.out_h + 3) / 4);
     const size_t lds = (size_t)(4 + hc - 1) * a.lds_stride * 4;
-    if (dot4)
-        hipLaunchKernelGGL((ncc_u8_c1_kernel<true>), grid, dim3(256), lds, s, a);
+    const bool word_rows = a.t_width % 4 == 0 && (reinterpret_cast<uintptr_t>(a.tmpl) & 3) == 0;
+    if (dot4 && word_rows)
+        hipLaunchKernelGGL((ncc_u8_c1_kernel<true, true>), grid, dim3(256), lds, s, a);
+    else if (dot4)
+        hipLaunchKernelGGL((ncc_u8_c1_kernel<true, false>), grid, dim3(256), lds, s, a);
+    else if (word_rows)
+        hipLaunchKernelGGL((ncc_u8_c1_kernel<false, true>), grid, dim3(256), lds, s, a);
     else
-        hipLaunchKernelGGL((ncc_u8_c1_kernel<false>), grid, dim3(256), lds, s, a);
+        hipLaunchKernelGGL((ncc_u8_c1_kernel<false, false>), grid, dim3(256), lds, s, a);
     return hipGetLastError();
 }
 

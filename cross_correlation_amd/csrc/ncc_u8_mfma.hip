@@ -80,7 +80,7 @@ __host__ __device__ inline MfPlan mf_plan(int t_width, int hc)
     p.sw = 64 + 16 * p.nkb + 4;
     p.tsb = 64 * p.nkb + 16;
     p.trows = hc + 2 * MF_TY - 1;
-    p.nwd = 64 + t_width / 4;
+    p.nwd = 64 + (t_width + 2) / 4;  // words holding columns 0 .. 255 + t_width - 1
     p.cw = (p.nwd + 3) / 4;
     p.vs = 4 * p.nwd + 4;
     int img = (MF_TY + hc) * p.sw;  // staged rows + one spare row
@@ -118,21 +118,36 @@ __device__ __forceinline__ void mf_stage_image(const uint8_t *__restrict__ image
 // [MF_TY - 1, MF_TY - 1 + hcur), with MF_TY - 1 zero rows before and MF_TY
 // after (the template rows that do not exist for some output row of the tile,
 // and the spare row the pipelined walk reads last) and zero bytes beyond
-// t_width up to the 64-byte block.
+// t_width up to the 64-byte block (a zero byte of T' adds nothing to sum I'T').
 __device__ __forceinline__ void mf_stage_template(const uint8_t *__restrict__ tmpl, int t_width, int j0, int hcur,
                                                   int kw, uint8_t *tpl, int tsb, int trows)
 {
     const int wpr = kw / 4;  // words per staged row
-    const int twords = t_width / 4;
+    const int twords = (t_width + 3) / 4;
     const int total = trows * wpr;
-    for (int i = threadIdx.x; i < total; i += blockDim.x) {
-        const int r = i / wpr;
-        const int k = i - r * wpr;
-        const int j = r - (MF_TY - 1);
-        uint32_t v = 0u;
-        if (j >= 0 && j < hcur && k < twords)
-            v = reinterpret_cast<const uint32_t *>(tmpl + (size_t)(j0 + j) * t_width)[k] ^ 0x80808080u;
-        *reinterpret_cast<uint32_t *>(tpl + r * tsb + 4 * k) = v;
+    if (tmpl_word_rows(tmpl, t_width)) {
+        // whole-word rows
+        for (int i = threadIdx.x; i < total; i += blockDim.x) {
+            const int r = i / wpr;
+            const int k = i - r * wpr;
+            const int j = r - (MF_TY - 1);
+            uint32_t v = 0u;
+            if (j >= 0 && j < hcur && k < twords)
+                v = reinterpret_cast<const uint32_t *>(tmpl + (size_t)(j0 + j) * t_width)[k] ^ 0x80808080u;
+            *reinterpret_cast<uint32_t *>(tpl + r * tsb + 4 * k) = v;
+        }
+    } else {
+        // gathered words; the partial last word is biased on its template bytes only
+        const uint32_t tm = tail_mask(t_width);
+        for (int i = threadIdx.x; i < total; i += blockDim.x) {
+            const int r = i / wpr;
+            const int k = i - r * wpr;
+            const int j = r - (MF_TY - 1);
+            uint32_t v = 0u;
+            if (j >= 0 && j < hcur && k < twords)
+                v = tmpl_word(tmpl, t_width, false, j0 + j, k) ^ (k == twords - 1 ? 0x80808080u & tm : 0x80808080u);
+            *reinterpret_cast<uint32_t *>(tpl + r * tsb + 4 * k) = v;
+        }
     }
 }
 
@@ -305,7 +320,8 @@ __global__ __launch_bounds__(MF_THREADS) void ncc_u8_mfma_kernel(NccArgs a)
 
     const int x0 = blockIdx.x * MF_TX, y0 = blockIdx.y * MF_TY;
     const int tw = a.t_width, th = a.t_height;
-    const int twords = tw / 4;
+    const int twords = (tw + 3) / 4;  // packed words per template row (the last one partial when tw % 4 != 0)
+    const uint32_t tm = tail_mask(tw);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wd = wave * P.cw + lane;              // column-walk word of this lane
     const bool walker = lane < P.cw && wd < P.nwd;
@@ -327,12 +343,14 @@ __global__ __launch_bounds__(MF_THREADS) void ncc_u8_mfma_kernel(NccArgs a)
         mf_stage_image(a.image, a.height, a.pitch, y0 + j0, x0, MF_TY - 1 + hcur, nchunks16, img, P.sw);
         mf_stage_template(a.tmpl, tw, j0, hcur, 64 * NKB, tpl, P.tsb, P.trows);
         __syncthreads();
-        // template sums from the staged (biased) rows of this chunk
+        // template sums from the staged (biased) rows of this chunk; the
+        // partial last word of a row (tm != ~0) is unbiased on its template
+        // bytes only, its padding stays zero
         for (int i = threadIdx.x; i < hcur * twords; i += MF_THREADS) {
             const int r = i / twords;
-            const uint32_t w =
-                *reinterpret_cast<const uint32_t *>(tpl + (MF_TY - 1 + r) * P.tsb + 4 * (i - r * twords)) ^
-                0x80808080u;
+            const int k = i - r * twords;
+            const uint32_t unbias = tm == 0xFFFFFFFFu || k != twords - 1 ? 0x80808080u : 0x80808080u & tm;
+            const uint32_t w = *reinterpret_cast<const uint32_t *>(tpl + (MF_TY - 1 + r) * P.tsb + 4 * k) ^ unbias;
             ts = dot4u(w, 0x01010101u, ts);
             tq = dot4u(w, w, tq);
         }
@@ -374,6 +392,7 @@ __global__ __launch_bounds__(MF_THREADS) void ncc_u8_mfma_kernel(NccArgs a)
 
     const int x = threadIdx.x;
     const int gx = x0 + x;
+    unsigned long long best = 0ull;
     if (gx < a.out_w) {
         size_t o = (size_t)y0 * a.out_w + gx;
         for (int n = 0; n < MF_TY; ++n, o += a.out_w) {
@@ -387,17 +406,23 @@ __global__ __launch_bounds__(MF_THREADS) void ncc_u8_mfma_kernel(NccArgs a)
             if (a.sum_i) a.sum_i[o] = si;
             if (a.sum_isq) a.sum_isq[o] = sq;
             if (a.sum_it) a.sum_it[o] = st;
-            if (a.coef) {
+            if (a.coef || a.peak) {
                 const double sid = (double)si;
                 const double num = fma(nd, (double)st, -(sid * std_));
                 const double vi = fma(nd, (double)sq, -(sid * sid));
                 double c = 0.0;
                 if (vi != 0.0 && vt != 0.0)
                     c = num / sqrt(vi * vt);
-                a.coef[o] = (float)c;
+                if (a.coef) a.coef[o] = (float)c;
+                if (a.peak) {
+                    const unsigned long long k = peak_key((float)c, (uint32_t)o);
+                    best = k > best ? k : best;
+                }
             }
         }
     }
+    if (a.peak)
+        peak_commit(a.peak, best);
 }
 
 // Template rows per chunk: the most that fit two workgroups per CU (80 KiB

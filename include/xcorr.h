@@ -8,8 +8,10 @@
  *                  "Instruction-Level Parallelism and DP4A": per window the
  *                  unsigned 32-bit sums SumI (pixels), SumISq (squared pixels)
  *                  and SumIT (pixel times template pixel) over unsigned bytes,
- *                  the template width a multiple of four, then a correlation
- *                  coefficient from those sums and the template sums.
+ *                  then a correlation coefficient from those sums and the
+ *                  template sums.  The page packs template rows whose width is
+ *                  a multiple of four; here any width is taken (the last
+ *                  packed word of a row is masked to the template's bytes).
  *
  *   xcorr_f32_run  fp32 full 2D cross-correlation over every shift at which
  *                  two matrices overlap, for one-to-one, one-to-many and
@@ -45,7 +47,7 @@ extern "C" {
 #define XC_OK 0
 #define XC_ERR_NULL (-1)           /* a required pointer is NULL, or no output requested        */
 #define XC_ERR_SHAPE (-2)          /* a size is <= 0, or the template is larger than the image */
-#define XC_ERR_TEMPLATE_WIDTH (-3) /* t_width is not a multiple of 4                           */
+#define XC_ERR_TEMPLATE_WIDTH (-3) /* reserved: template widths are not restricted any more     */
 #define XC_ERR_OVERFLOW (-4)       /* sums could wrap 32 bits, or an index range is exceeded    */
 #define XC_ERR_ALIGN (-5)          /* a base pointer or the pitch is not 16-byte aligned        */
 #define XC_ERR_HIP (-6)            /* HIP launch or runtime error (including: no device)        */
@@ -59,9 +61,10 @@ extern "C" {
  *
  * image   [height][pitch_bytes] u8, row-major; pixel (y, x) at image[y*pitch + x]
  *         for x < width.  Base and pitch_bytes must be multiples of 16.
- * tmpl    [t_height][t_width] u8, dense row-major; 4-byte aligned.
- *         Requires 0 < t_width <= width, 0 < t_height <= height,
- *         t_width % 4 == 0 and t_width * t_height <= 66,051.
+ * tmpl    [t_height][t_width] u8, dense row-major, any alignment.
+ *         Requires 0 < t_width <= width, 0 < t_height <= height and
+ *         t_width * t_height <= 66,051 (any width; rows are packed into
+ *         4-byte words, the last one masked to the row's bytes).
  * Outputs dense row-major [out_h][out_w], out_h = height - t_height + 1,
  *         out_w = width - t_width + 1; entry (y, x) is the window whose
  *         top-left pixel is image (y, x):
@@ -108,6 +111,39 @@ int ncc_u8_run_variant(const uint8_t *image, int width, int height, int pitch_by
                        const uint8_t *tmpl, int t_width, int t_height,
                        uint32_t *sum_i, uint32_t *sum_isq, uint32_t *sum_it, float *coef,
                        int variant, void *stream);
+
+/*
+ * ncc_u8_peak -- best match: the window with the largest coefficient.
+ *
+ * Computes what ncc_u8_run_variant computes (the same arguments and rules; the
+ * four map outputs are optional here, all of them may be NULL) and also the
+ * best match over all out_h x out_w windows:
+ *   peak   DEVICE pointer to one xc_ncc_peak, 8-byte aligned, caller-owned.
+ *          On completion peak->y, peak->x are the top-left pixel of the window
+ *          with the largest coefficient (the coefficient ncc_u8_run returns,
+ *          as an fp32 value) and peak->coef is that coefficient.  Among
+ *          windows with equal coefficients the first in row-major order
+ *          (smallest y * out_w + x) is returned, so the result is unique and
+ *          deterministic.  peak->key is the library's working value (the
+ *          packed coefficient and position) and peak->reserved is 0.
+ * Three launches are enqueued on `stream` (clear the key, correlate, decode);
+ * the library still allocates nothing.  Concurrent calls must not share one
+ * xc_ncc_peak.  Errors as ncc_u8_run_variant, plus XC_ERR_NULL for a NULL peak
+ * and XC_ERR_ALIGN for a misaligned one.
+ * The pages describe the correlation only; the search is the usual last step
+ * of template matching, fused into the correlation's epilogue here (each wave
+ * reduces its windows, then one 64-bit atomic maximum).
+ */
+typedef struct {
+    uint64_t key;
+    int32_t y, x;
+    float coef;
+    int32_t reserved;
+} xc_ncc_peak;
+int ncc_u8_peak(const uint8_t *image, int width, int height, int pitch_bytes,
+                const uint8_t *tmpl, int t_width, int t_height,
+                uint32_t *sum_i, uint32_t *sum_isq, uint32_t *sum_it, float *coef,
+                xc_ncc_peak *peak, int variant, void *stream);
 
 /*
  * xcorr_f32_run -- fp32 full 2D cross-correlation of every (left, right) pair.

@@ -10,6 +10,9 @@ Functions follow the definitions cited in ``oracle.c``:
 * :func:`ncc_u8` -- u8 normalized correlation, "The CUDA Handbook" section
   15.5 "Instruction-Level Parallelism and DP4A" (the SumI / SumISq / SumIT
   accumulators over unsigned 8-bit pixels), coefficient read as Pearson's r.
+* :func:`ncc_peak` -- the best match of a coefficient map (first entry, in
+  row-major order, holding the maximum), the usual last step of template
+  matching.
 * :func:`xcorr_f32` -- full 2D cross-correlation over all overlaps, JPDC 2023
   artifact README (each thread computes one overlap; one-to-one, one-to-many
   and multi-matrix-both groupings), accumulated in fp64.
@@ -73,6 +76,8 @@ def _bind(path: str):
     lib.oracle_ncc_u8_points.argtypes = [
         _u8p, ctypes.c_int, ctypes.c_int, ctypes.c_int, _u8p, ctypes.c_int, ctypes.c_int,
         _i32p, _i32p, ctypes.c_int64, _u32p, _u32p, _u32p, _f32p, _f64p, ctypes.c_int]
+    lib.oracle_ncc_peak.restype = ctypes.c_int
+    lib.oracle_ncc_peak.argtypes = [_f32p, ctypes.c_int64, _i64p, _f32p]
     lib.oracle_xcorr_f32.restype = ctypes.c_int
     lib.oracle_xcorr_f32.argtypes = [
         _f32p, ctypes.c_int, _f32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, _f64p, _f64p, ctypes.c_int]
@@ -166,6 +171,21 @@ def ncc_u8_points(image: np.ndarray, width: int, height: int, tmpl: np.ndarray,
     if st != ORACLE_OK:
         raise ValueError(f"oracle_ncc_u8_points: bad arguments (status {st})")
     return res
+
+
+def ncc_peak(coef: np.ndarray, *, lib=None):
+    """Best match of a coefficient map: ``(y, x, value)`` of the first entry
+    (row-major) holding the largest coefficient."""
+    coef = np.ascontiguousarray(coef, dtype=np.float32)
+    if coef.ndim != 2 or coef.size == 0:
+        raise ValueError("coef must be a non-empty 2D map")
+    idx = np.zeros(1, dtype=np.int64)
+    val = np.zeros(1, dtype=np.float32)
+    st = (lib or _load()).oracle_ncc_peak(_ptr(coef, _f32p), coef.size, _ptr(idx, _i64p), _ptr(val, _f32p))
+    if st != ORACLE_OK:
+        raise ValueError(f"oracle_ncc_peak: bad arguments (status {st})")
+    y, x = divmod(int(idx[0]), coef.shape[1])
+    return y, x, float(val[0])
 
 
 def xcorr_f32(left: np.ndarray, right: np.ndarray, *, with_abs: bool = True, nthreads: int = 0, lib=None):

@@ -177,6 +177,26 @@ int oracle_ncc_u8_points(const uint8_t *image, int width, int height, int pitch,
     return bad ? ORACLE_ERR_U32 : ORACLE_OK;
 }
 
+/*
+ * Best match over a coefficient map of n entries (row-major): the index of
+ * the first entry holding the largest value, and that value.  A plain scan.
+ * The pages stop at the coefficient; finding its maximum is the usual last
+ * step of template matching, and "first in row-major order" is the reading
+ * taken for ties.
+ */
+int oracle_ncc_peak(const float *coef, int64_t n, int64_t *idx, float *val)
+{
+    if (!coef || n <= 0 || !idx || !val)
+        return ORACLE_ERR_ARG;
+    int64_t best = 0;
+    for (int64_t k = 1; k < n; ++k)
+        if (coef[k] > coef[best])
+            best = k;
+    *idx = best;
+    *val = coef[best];
+    return ORACLE_OK;
+}
+
 /* One output of one pair: the overlap sum in fp64, plus the sum of |l*r|. */
 static void one_shift(const float *L, const float *R, int rows, int cols, int dy, int dx,
                       double *o_val, double *o_abs)

@@ -8,10 +8,13 @@ fixture, closed forms, invariants, brute force through numpy primitives and
 Definition followed: "The CUDA Handbook", section 15.5 "Instruction-Level
 Parallelism and DP4A" -- per window the unsigned sums SumI, SumISq, SumIT over
 8-bit pixels (the two-column accumulator fragment and the three DP4A lines);
-the template width is a multiple of four and the unsigned byte product is
-required (pixels above 127 must not turn negative); only SumIT pairs image and
-template lanes, so a byte-order slip shows in SumIT alone.  The coefficient is
-read as Pearson's r from the five sums, with 0 where a variance is zero.
+the page packs templates whose width is a multiple of four, and the sums are
+defined for any width (the oracle sums pixels one by one); the unsigned byte
+product is required (pixels above 127 must not turn negative); only SumIT
+pairs image and template lanes, so a byte-order slip shows in SumIT alone.
+The coefficient is read as Pearson's r from the five sums, with 0 where a
+variance is zero.  The best match is the first window (row-major) holding the
+largest coefficient.
 """
 from __future__ import annotations
 
@@ -217,6 +220,69 @@ def pin_points_and_rows(lib=None):
         assert np.array_equal(pts[k], full[k][ys, xs])
 
 
+def pin_sums_bruteforce_any_width(lib=None):
+    """Template widths that are not multiples of four (and below four)."""
+    rng = np.random.default_rng(114)
+    for tw in (1, 2, 3, 5, 6, 7, 9, 11, 13):
+        th = int(rng.integers(1, 6))
+        h = th + int(rng.integers(0, 7))
+        w = tw + int(rng.integers(0, 11))
+        img = u8_uniform(rng, (h, w))
+        tmpl = u8_uniform(rng, (th, tw))
+        r = _run(img, tmpl, lib)
+        si, sq, st = _numpy_sums(img, tmpl)
+        assert np.array_equal(r["sum_i"].astype(np.int64), si), tw
+        assert np.array_equal(r["sum_isq"].astype(np.int64), sq), tw
+        assert np.array_equal(r["sum_it"].astype(np.int64), st), tw
+
+
+def pin_cut_template_any_width(lib=None):
+    """A template cut from the image correlates to exactly 1 at its offset, at
+    odd widths too, and there the sums close: SumI = SumT, SumISq = SumIT = SumTSq."""
+    for k, tw in enumerate((2, 3, 5, 7, 13, 21)):
+        case = ncc_case("t", 120 + k, 24, 40, 3 + k % 3, tw, cut=True)
+        r = oracle.ncc_u8(case.image, case.width, case.height, case.tmpl, lib=lib)
+        oy, ox = case.cut
+        t = case.tmpl.astype(np.int64)
+        assert r["coef"][oy, ox] == np.float32(1.0), tw
+        assert int(r["sum_i"][oy, ox]) == int(t.sum())
+        assert int(r["sum_isq"][oy, ox]) == int((t * t).sum()) == int(r["sum_it"][oy, ox])
+
+
+def pin_peak_argmax(lib=None):
+    """The best match against numpy.argmax (documented to return the first
+    occurrence), on random maps with planted ties before and after the
+    maximum, and on all-negative and constant maps."""
+    rng = np.random.default_rng(115)
+    for h, w in ((1, 1), (1, 7), (5, 1), (9, 13), (31, 17)):
+        m = rng.uniform(-1, 1, size=(h, w)).astype(np.float32)
+        y, x, v = oracle.ncc_peak(m, lib=lib)
+        k = int(np.argmax(m))
+        assert (y, x, v) == (k // w, k % w, float(m.flat[k]))
+        if m.size >= 3:
+            m2 = m.copy()
+            top = np.float32(2.0)
+            slots = rng.choice(m.size, 3, replace=False)
+            m2.flat[slots] = top
+            y, x, v = oracle.ncc_peak(m2, lib=lib)
+            assert y * w + x == int(slots.min()) == int(np.argmax(m2)) and v == 2.0
+        neg = -np.abs(m) - np.float32(0.5)
+        y, x, _ = oracle.ncc_peak(neg, lib=lib)
+        assert y * w + x == int(np.argmax(neg))
+    y, x, v = oracle.ncc_peak(np.zeros((4, 6), np.float32), lib=lib)
+    assert (y, x, v) == (0, 0, 0.0)
+
+
+def pin_peak_cut(lib=None):
+    """The best match of a template cut from a noisy image is the cut offset,
+    with coefficient exactly 1 (the largest any window can reach)."""
+    for k, (th, tw) in enumerate(((4, 4), (5, 7), (8, 3))):
+        case = ncc_case("t", 130 + k, 40, 60, th, tw, cut=True)
+        r = oracle.ncc_u8(case.image, case.width, case.height, case.tmpl, lib=lib)
+        y, x, v = oracle.ncc_peak(r["coef"], lib=lib)
+        assert (y, x) == case.cut and v == 1.0
+
+
 ALL_PINS = [
     pin_hand_worked,
     pin_sums_bruteforce,
@@ -230,4 +296,8 @@ ALL_PINS = [
     pin_constant,
     pin_bounded,
     pin_points_and_rows,
+    pin_sums_bruteforce_any_width,
+    pin_cut_template_any_width,
+    pin_peak_argmax,
+    pin_peak_cut,
 ]

@@ -44,11 +44,9 @@ FAKE = 1 << 20  # a 16-byte aligned non-null address; never dereferenced (valida
     (dict(t_width=80), _lib.XC_ERR_SHAPE),
     (dict(t_height=70), _lib.XC_ERR_SHAPE),
     (dict(pitch=32), _lib.XC_ERR_SHAPE),
-    (dict(t_width=6), _lib.XC_ERR_TEMPLATE_WIDTH),
     (dict(width=70000, pitch=70016, height=2, t_width=33028, t_height=2), _lib.XC_ERR_OVERFLOW),
     (dict(image=FAKE + 4), _lib.XC_ERR_ALIGN),
     (dict(pitch=72), _lib.XC_ERR_ALIGN),
-    (dict(tmpl=FAKE + 2), _lib.XC_ERR_ALIGN),
     (dict(coef=FAKE + 2), _lib.XC_ERR_ALIGN),
     (dict(variant=42), _lib.XC_ERR_VARIANT),
 ])
@@ -59,6 +57,29 @@ def test_ncc_validation(args, expect):
     st = _lib.ncc_u8_run(a["image"], a["width"], a["height"], a["pitch"], a["tmpl"], a["t_width"], a["t_height"],
                          a["sum_i"], a["sum_isq"], a["sum_it"], a["coef"], None, a["variant"])
     assert st == expect, _lib.status_str(st)
+
+
+@pytest.mark.parametrize("args,expect", [
+    (dict(peak=0), _lib.XC_ERR_NULL),
+    (dict(image=0), _lib.XC_ERR_NULL),
+    (dict(peak=FAKE + 4), _lib.XC_ERR_ALIGN),
+    (dict(t_width=80), _lib.XC_ERR_SHAPE),
+    (dict(variant=42), _lib.XC_ERR_VARIANT),
+    (dict(t_width=300, width=400, pitch=400, variant=_lib.XC_NCC_MFMA), _lib.XC_ERR_SHAPE),
+])
+def test_ncc_peak_validation(args, expect):
+    """The best-match entry point: the maps are optional, the peak is not."""
+    a = dict(image=FAKE, width=64, height=64, pitch=64, tmpl=FAKE, t_width=8, t_height=8, peak=FAKE, variant=0)
+    a.update(args)
+    st = _lib.ncc_u8_peak(a["image"], a["width"], a["height"], a["pitch"], a["tmpl"], a["t_width"],
+                          a["t_height"], 0, 0, 0, 0, a["peak"], None, a["variant"])
+    assert st == expect, _lib.status_str(st)
+
+
+def test_decode_peak_layout():
+    import struct
+    raw = struct.pack("<QiifI", 123, 7, 9, 0.5, 0)
+    assert _lib.decode_peak(raw) == (7, 9, 0.5)
 
 
 @pytest.mark.parametrize("args,expect", [

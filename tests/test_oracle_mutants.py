@@ -29,6 +29,8 @@ MUTANTS = {
     "ncc_zero_var_rule": ("if (vi != 0 && vt != 0)", "if (vt != 0)", "ncc"),
     "ncc_single_precision": ("c = (double)num / sqrt((double)vi * (double)vt);",
                              "c = (float)num / sqrtf((float)vi * (float)vt);", "ncc"),
+    "ncc_peak_last_of_ties": ("if (coef[k] > coef[best])", "if (coef[k] >= coef[best])", "ncc"),
+    "ncc_peak_minimum": ("if (coef[k] > coef[best])", "if (coef[k] < coef[best])", "ncc"),
     # fp32 cross-correlation
     "xcorr_operands_swapped": ("one_shift(L, R, rows, cols, y - (rows - 1), x - (cols - 1), out + base + x,",
                                "one_shift(R, L, rows, cols, y - (rows - 1), x - (cols - 1), out + base + x,", "xcorr"),
