@@ -85,6 +85,8 @@ def parse():
     ap.add_argument("--only", choices=["ncc", "xcorr", "all"], default="all")
     ap.add_argument("--json-out", default=None)
     ap.add_argument("--no-peak-probe", action="store_true", help="skip the measured issue-rate ceilings")
+    ap.add_argument("--no-ext", action="store_true",
+                    help="skip the ncc_ext timings (profiling runs: each kernel then sees one workload)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (a known-size kernel that "
                          "calibrates the FETCH_SIZE / WRITE_SIZE counters), then exit")
@@ -367,7 +369,8 @@ def main():
                          "kernel": "ncc_u8_mfma_kernel",
                          "note": "matrix-core instructions take ~1 us of the kernel; VALU issue and "
                                  "LDS/barrier latency bound it"}
-        out["ncc_ext"] = bench_ncc_ext(args, torch, _lib, inputs)
+        if not args.no_ext:
+            out["ncc_ext"] = bench_ncc_ext(args, torch, _lib, inputs)
     if args.only in ("xcorr", "all"):
         out["xcorr"] = bench_xcorr(args, torch, _lib, inputs)
     if not args.no_peak_probe:

@@ -215,6 +215,19 @@ __device__ __forceinline__ void bd_compute(const float4 *Lb1, const float4 *Lb2,
     }
 }
 
+// Workgroups are dispatched round-robin over the chip's 8 XCDs, each with
+// its own L2.  Logical ids are renumbered so each XCD runs one contiguous
+// range of them: neighbouring column tiles, which write parts of the same
+// output cache lines and read the same matrices, then meet in one L2 instead
+// of writing back partial lines from eight.  A bijection on [0, n), so
+// results do not depend on it.
+__device__ __forceinline__ int xcd_logical_id(int b, int n)
+{
+    const int q = n >> 3, r = n & 7;  // XCDs 0..r-1 run q + 1 workgroups, the others q
+    const int xcd = b & 7, slot = b >> 3;
+    return (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + slot;
+}
+
 // Geometry shared by both staging modes: which pairs, diagonal and column
 // tile a workgroup / wave / lane works on.
 struct BdWho {
@@ -228,7 +241,7 @@ __device__ __forceinline__ BdWho bd_who(const BdArgs &a)
     BdWho w;
     w.lane = threadIdx.x & 63;
     w.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    int bid = blockIdx.x;
+    int bid = xcd_logical_id(blockIdx.x, gridDim.x);
     const int side = bid % a.n_sides;
     bid /= a.n_sides;
     const int dgrp = bid % a.n_dgroups;
@@ -685,7 +698,7 @@ __global__ __launch_bounds__(64 * NW) void xcorr_bd_big_kernel(BdArgs a)
     extern __shared__ float4 smem[];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    int bid = blockIdx.x;
+    int bid = xcd_logical_id(blockIdx.x, gridDim.x);
     const int side_sel = bid % a.n_sides;
     bid /= a.n_sides;
     const int dgrp = bid % a.n_dgroups;
