@@ -12,7 +12,8 @@ on the same workload under "ncc_variants"; every variant returns identical
 outputs.
 
 The generalizations (best-match search, a 63 x 63 template) are timed on the
-same image under "ncc_ext".
+same image under "ncc_ext"; one-to-one pairs of 512 and 1024 rows under
+"xcorr_large".
 
 The fp32 cross-correlation form is timed in the same run (its own loops,
 reported under "xcorr"): one-to-one 256x256, one-to-many 1x64 of 64x64 and
@@ -228,6 +229,34 @@ def bench_ncc_ext(args, torch, lib, inputs):
     return res
 
 
+def bench_xcorr_large(args, torch, lib, inputs):
+    """One-to-one pairs beyond 256 rows (the block-diagonal kernel in passes of
+    64 row blocks), with the overlap-wise baseline on the smaller one."""
+    from cross_correlation_amd.inputs import xcorr_case
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream().cuda_stream
+    res = {}
+    for n, seed, algos in ((512, 6, ("auto", "overlap")), (1024, 7, ("auto",))):
+        c = xcorr_case(f"xcorr_1to1_{n}", seed, 1, 1, n, n)
+        L = torch.from_numpy(c.left).to(dev)
+        R = torch.from_numpy(c.right).to(dev)
+        out = torch.empty(c.out_shape, dtype=torch.float32, device=dev)
+        flop = 2.0 * n ** 4
+        for an in algos:
+            algo = lib.XC_XCORR_AUTO if an == "auto" else lib.XC_XCORR_OVERLAP
+
+            def launch():
+                st = lib.xcorr_f32_run(L.data_ptr(), 1, R.data_ptr(), 1, n, n, out.data_ptr(), stream=stream, algo=algo)
+                if st != 0:
+                    raise RuntimeError(lib.status_str(st))
+
+            steps = 5 if n >= 1024 or an == "overlap" else min(args.steps, 20)
+            _, per = timed_loop(launch, steps, 1, torch)
+            res[f"xcorr_1to1_{n}_{an}"] = {"kernel_ms": round(per, 4), "gflops": round(flop / (per * 1e-3) / 1e9, 1),
+                                           "frac_of_157.3T": round(flop / (per * 1e-3) / FP32_PEAK, 4)}
+    return res
+
+
 def bench_xcorr(args, torch, lib, inputs):
     dev = torch.device("cuda:0")
     res = {}
@@ -373,6 +402,8 @@ def main():
             out["ncc_ext"] = bench_ncc_ext(args, torch, _lib, inputs)
     if args.only in ("xcorr", "all"):
         out["xcorr"] = bench_xcorr(args, torch, _lib, inputs)
+        if not args.no_ext:
+            out["xcorr_large"] = bench_xcorr_large(args, torch, _lib, inputs)
     if not args.no_peak_probe:
         out["measured_ceilings"] = peak_probes()
         if "ncc_variants" in out:
