@@ -196,3 +196,19 @@ def test_xcorr_large_delta_orientation():
         expect = np.zeros((2 * rows - 1, 2 * cols - 1), np.float32)
         expect[a - c + rows - 1, b - d + cols - 1] = 1.0
         assert np.array_equal(got[0, 0], expect)
+
+
+@pytest.mark.parametrize("shape", [
+    # (n_left, n_right, rows, cols): pair groups that span several left matrices
+    # (n_right below the pairs per wave), one right matrix, and n_right of 64
+    # and more (the group's right index wraps at most once)
+    (6, 3, 16, 16), (9, 2, 13, 20), (40, 1, 32, 8), (2, 70, 16, 16), (3, 65, 32, 32), (7, 5, 20, 4),
+])
+def test_xcorr_groupings(shape):
+    nl, nr, rows, cols = shape
+    rng = np.random.default_rng(1000 + nl * 97 + nr * 13 + rows)
+    L = f32_uniform(rng, (nl, rows, cols))
+    R = f32_uniform(rng, (nr, rows, cols))
+    _gpu.log(f"xcorr grouping {shape}")
+    ref, ab = oracle.xcorr_f32(L, R)
+    _gpu.check_xcorr(_gpu.run_xcorr(L, R, _lib.XC_XCORR_BLOCKDIAG), ref, ab)
