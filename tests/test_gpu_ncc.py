@@ -228,3 +228,24 @@ def test_ncc_invalid_arguments_rejected_before_launch():
     with pytest.raises(_lib.XcError) as e:
         api.ncc_u8(img[:, 1:], torch.zeros((4, 8), dtype=torch.uint8, device="cuda"))
     assert e.value.status == _lib.XC_ERR_ALIGN
+
+
+@pytest.mark.parametrize("th,tw", [(257, 257), (258, 256)])
+def test_ncc_largest_template_near_u32_limit(th, tw):
+    """Templates at the area limit (66,049 and 66,048 pixels of 66,051) over a
+    nearly saturated image: SumISq reaches 255^2 * N, just below 2^32, in every
+    variant that takes the width (the matrix-core kernel up to 256 bytes)."""
+    rng = np.random.default_rng(330 + tw)
+    img = np.full((th + 40, tw + 60), 255, np.uint8)
+    img[::9, ::7] = u8_uniform(rng, img[::9, ::7].shape)
+    tmpl = u8_uniform(rng, (th, tw))
+    case = _case_from(img, tmpl)
+    ref = None
+    variants = [_lib.XC_NCC_AUTO, _lib.XC_NCC_DOT4_ILP, _lib.XC_NCC_DOT4_C1]
+    if tw <= 256:
+        variants.append(_lib.XC_NCC_MFMA)
+    for v in variants:
+        _gpu.log(f"ncc largest template {th}x{tw} variant {v}")
+        res = _gpu.run_ncc(case, v)
+        ref = _gpu.check_ncc(case, res, ref)
+    assert int(ref["sum_isq"].max()) > 4_200_000_000  # far above 2^31: a signed 32-bit slip would show
