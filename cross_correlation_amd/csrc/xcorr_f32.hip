@@ -6,13 +6,14 @@
 // overlap:  out[y][x] = sum_{i,j} L[i+dy][j+dx] * R[i][j],
 // dy = y - (rows-1), dx = x - (cols-1).
 //
-// Two kernels:
+// Kernels:
 //
 // * xcorr_overlap_kernel -- the overlap-wise baseline the page compares
 //   against: one thread per output shift, no data reuse.
 //
-// * xcorr_bd_whole_kernel / xcorr_bd_chunk_kernel -- the register-blocked
-//   (block-diagonal) kernel, in two staging modes.  The page's kernels give
+// * xcorr_bd_whole_kernel / xcorr_bd_chunk_kernel / xcorr_bd_big_kernel --
+//   the register-blocked (block-diagonal) kernel, in two staging modes for up
+//   to 64 row blocks and in passes of 64 row blocks beyond.  The page's kernels give
 //   each thread one or several neighbouring overlaps and cache the left rows
 //   in warp-wide register buffers moved by shuffles; a thread-per-overlap
 //   mapping leaves SIMT lanes idle wherever neighbouring overlaps have
@@ -29,10 +30,10 @@
 //       16 (a, e) row pairs cover every row pair exactly once over all
 //       diagonals, so no lane ever multiplies outside the overlap in y.
 //     - Columns: a lane owns P shift classes c0 .. c0+P-1; class c yields
-//       dx = c (summed over j < w - c) and dx = c - w (j >= w - c).  Both are
-//       one walk over j with a P-wide sliding window of left columns kept in
-//       registers (the register buffer of the page, per lane instead of per
-//       warp); zero-filled LDS columns make the border exact.
+//       dx = c and dx = c - w.  Both are one walk over the left columns u with
+//       a P-wide sliding window of the right columns u - dx kept in registers
+//       (the register buffer of the page, per lane instead of per warp);
+//       zero-filled LDS columns make the border exact.
 //     - Each step: one float4 of each of the two left blocks and one of the
 //       right block from LDS, 16 x P fp32 FMAs.
 //     - The per-lane partial sums of the same output are reduced across the
@@ -48,7 +49,8 @@
 //       a time, the next chunk prefetched into registers during the FMAs.
 //   The host picks waves per workgroup (16, 8 or 4 diagonals sharing one
 //   staging) and whether the two dx signs go to separate workgroups, so that
-//   small groupings still put enough waves on the 256 CUs.
+//   small groupings still put enough waves on the 256 CUs; workgroup ids are
+//   renumbered so each XCD (own L2) runs a contiguous range of tiles.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
