@@ -6,7 +6,31 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace xc {
+
+// Allow `kernel` up to 160 KiB of dynamic LDS (gfx950's per-CU size) on the
+// current device, once per device: `done` holds one bit per device id below
+// 64 (higher ids make the call every time).  Thread-safe: concurrent first
+// calls may both make the (idempotent) attribute call; the bit is set after
+// a successful one.
+template <typename K>
+inline hipError_t allow_lds_once(K kernel, std::atomic<uint64_t> &done)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    const uint64_t bit = dev < 64 ? 1ull << dev : 0ull;
+    if (bit && (done.load(std::memory_order_acquire) & bit))
+        return hipSuccess;
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            160 * 1024);
+    if (e == hipSuccess && bit)
+        done.fetch_or(bit, std::memory_order_release);
+    return e;
+}
 
 // Arguments of every u8 normalized-correlation kernel (validated on the host).
 struct NccArgs {

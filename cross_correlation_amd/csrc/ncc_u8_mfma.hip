@@ -452,14 +452,11 @@ bool ncc_mfma_supported(const NccArgs &a)
 template <int NKB>
 static hipError_t mf_launch(const NccArgs &a, hipStream_t s)
 {
-    static bool attr = false;
-    if (!attr) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&ncc_u8_mfma_kernel<NKB>),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        if (e != hipSuccess)
-            return e;
-        attr = true;
-    }
+    // dynamic LDS above 64 KiB must be allowed explicitly
+    static std::atomic<uint64_t> lds_allowed{0};
+    const hipError_t e = allow_lds_once(&ncc_u8_mfma_kernel<NKB>, lds_allowed);
+    if (e != hipSuccess)
+        return e;
     const size_t lds = mf_plan(a.t_width, a.hc).bytes;
     const dim3 grid((a.out_w + MF_TX - 1) / MF_TX, (a.out_h + MF_TY - 1) / MF_TY);
     hipLaunchKernelGGL((ncc_u8_mfma_kernel<NKB>), grid, dim3(MF_THREADS), lds, s, a);

@@ -818,14 +818,6 @@ bool xcorr_blockdiag_supported(const XcorrArgs &a)
     return nb >= 4;
 }
 
-template <typename K>
-static hipError_t allow_lds(K kernel)
-{
-    // Dynamic LDS above 64 KiB must be allowed explicitly (gfx950 has 160 KiB).
-    return hipFuncSetAttribute(reinterpret_cast<const void *>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-                               160 * 1024);
-}
-
 constexpr size_t BD_LDS_MAX = 160 * 1024;
 
 static size_t bd_whole_lds(const BdArgs &b, int nw)
@@ -846,12 +838,10 @@ static size_t bd_chunk_lds(const BdArgs &b)
 template <int NW>
 static hipError_t launch_whole(BdArgs b, hipStream_t s)
 {
-    static bool attr = false;
-    if (!attr) {
-        const hipError_t e = allow_lds(&xcorr_bd_whole_kernel<NW>);
-        if (e != hipSuccess) return e;
-        attr = true;
-    }
+    // dynamic LDS above 64 KiB must be allowed explicitly
+    static std::atomic<uint64_t> lds_allowed{0};
+    const hipError_t e = allow_lds_once(&xcorr_bd_whole_kernel<NW>, lds_allowed);
+    if (e != hipSuccess) return e;
     b.n_dgroups = (b.nb + NW - 1) / NW;
     const unsigned blocks = (unsigned)((int64_t)b.n_groups * b.n_xtiles * b.n_dgroups * b.n_sides);
     const size_t lds = bd_whole_lds(b, NW);
@@ -862,12 +852,10 @@ static hipError_t launch_whole(BdArgs b, hipStream_t s)
 template <int NW, int J>
 static hipError_t launch_chunk(BdArgs b, hipStream_t s)
 {
-    static bool attr = false;
-    if (!attr) {
-        const hipError_t e = allow_lds(&xcorr_bd_chunk_kernel<NW, J>);
-        if (e != hipSuccess) return e;
-        attr = true;
-    }
+    // dynamic LDS above 64 KiB must be allowed explicitly
+    static std::atomic<uint64_t> lds_allowed{0};
+    const hipError_t e = allow_lds_once(&xcorr_bd_chunk_kernel<NW, J>, lds_allowed);
+    if (e != hipSuccess) return e;
     b.n_dgroups = (b.nb + NW - 1) / NW;
     const unsigned blocks = (unsigned)((int64_t)b.n_groups * b.n_xtiles * b.n_dgroups * b.n_sides);
     const size_t lds = bd_chunk_lds<NW, J>(b);
@@ -887,12 +875,10 @@ static size_t bd_big_lds()
 template <int NW, int J>
 static hipError_t launch_big(BdArgs b, hipStream_t s)
 {
-    static bool attr = false;
-    if (!attr) {
-        const hipError_t e = allow_lds(&xcorr_bd_big_kernel<NW, J>);
-        if (e != hipSuccess) return e;
-        attr = true;
-    }
+    // dynamic LDS above 64 KiB must be allowed explicitly
+    static std::atomic<uint64_t> lds_allowed{0};
+    const hipError_t e = allow_lds_once(&xcorr_bd_big_kernel<NW, J>, lds_allowed);
+    if (e != hipSuccess) return e;
     b.n_dgroups = (b.nb + NW - 1) / NW;
     const int64_t per = (int64_t)b.n_groups * b.n_xtiles * b.n_dgroups;
     b.n_sides = per >= 1024 ? 1 : 2;
