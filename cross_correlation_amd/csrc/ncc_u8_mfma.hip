@@ -94,23 +94,42 @@ __host__ __device__ inline MfPlan mf_plan(int t_width, int hc)
 // Image rows [gy0, gy0 + nrows) x words [0, 4*nchunks) from column gx0, biased
 // to signed bytes; rows at or past `height` and chunks at or past `pitch` are
 // zero-filled, so no load leaves the image allocation.
+// Each thread takes its items in batches of 8, all loads of a batch issued
+// before any of its LDS stores (one memory round trip per batch); a chunk
+// outside the image loads from the image base and is zeroed afterwards.
 __device__ __forceinline__ void mf_stage_image(const uint8_t *__restrict__ image, int height, int pitch, int gy0,
                                                int gx0, int nrows, int nchunks, uint32_t *lds, int stride)
 {
+    constexpr int SB = 8;
     const int total = nrows * nchunks;
-    for (int i = threadIdx.x; i < total; i += blockDim.x) {
-        const int r = i / nchunks;
-        const int b = i - r * nchunks;
-        const int gy = gy0 + r;
-        const int gx = gx0 + 16 * b;
-        uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        if (gy < height && gx < pitch)
-            v = *reinterpret_cast<const uint4 *>(image + (size_t)gy * pitch + gx);
-        v.x ^= 0x80808080u;
-        v.y ^= 0x80808080u;
-        v.z ^= 0x80808080u;
-        v.w ^= 0x80808080u;
-        *reinterpret_cast<uint4 *>(lds + r * stride + 4 * b) = v;
+    for (int i0 = threadIdx.x; i0 < total; i0 += SB * MF_THREADS) {
+        uint4 v[SB];
+#pragma unroll
+        for (int k = 0; k < SB; ++k) {
+            const int i = i0 + k * MF_THREADS;
+            const int r = i / nchunks;
+            const int b = i - r * nchunks;
+            const int gy = gy0 + r;
+            const int gx = gx0 + 16 * b;
+            const bool ok = i < total && gy < height && gx < pitch;
+            v[k] = *reinterpret_cast<const uint4 *>(image + (ok ? (size_t)gy * pitch + gx : 0));
+            if (!ok)
+                v[k] = make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int k = 0; k < SB; ++k) {
+            const int i = i0 + k * MF_THREADS;
+            if (i < total) {
+                const int r = i / nchunks;
+                const int b = i - r * nchunks;
+                uint4 w = v[k];
+                w.x ^= 0x80808080u;
+                w.y ^= 0x80808080u;
+                w.z ^= 0x80808080u;
+                w.w ^= 0x80808080u;
+                *reinterpret_cast<uint4 *>(lds + r * stride + 4 * b) = w;
+            }
+        }
     }
 }
 
@@ -126,15 +145,29 @@ __device__ __forceinline__ void mf_stage_template(const uint8_t *__restrict__ tm
     const int twords = (t_width + 3) / 4;
     const int total = trows * wpr;
     if (tmpl_word_rows(tmpl, t_width)) {
-        // whole-word rows
-        for (int i = threadIdx.x; i < total; i += blockDim.x) {
-            const int r = i / wpr;
-            const int k = i - r * wpr;
-            const int j = r - (MF_TY - 1);
-            uint32_t v = 0u;
-            if (j >= 0 && j < hcur && k < twords)
-                v = reinterpret_cast<const uint32_t *>(tmpl + (size_t)(j0 + j) * t_width)[k] ^ 0x80808080u;
-            *reinterpret_cast<uint32_t *>(tpl + r * tsb + 4 * k) = v;
+        // whole-word rows, in batches of 8 (loads first, then the LDS stores)
+        constexpr int SB = 8;
+        for (int i0 = threadIdx.x; i0 < total; i0 += SB * MF_THREADS) {
+            uint32_t v[SB];
+#pragma unroll
+            for (int q = 0; q < SB; ++q) {
+                const int i = i0 + q * MF_THREADS;
+                const int r = i / wpr;
+                const int k = i - r * wpr;
+                const int j = r - (MF_TY - 1);
+                const bool ok = i < total && j >= 0 && j < hcur && k < twords;
+                v[q] = reinterpret_cast<const uint32_t *>(tmpl)[ok ? (size_t)(j0 + j) * (t_width >> 2) + k : 0];
+                v[q] = ok ? v[q] ^ 0x80808080u : 0u;
+            }
+#pragma unroll
+            for (int q = 0; q < SB; ++q) {
+                const int i = i0 + q * MF_THREADS;
+                if (i < total) {
+                    const int r = i / wpr;
+                    const int k = i - r * wpr;
+                    *reinterpret_cast<uint32_t *>(tpl + r * tsb + 4 * k) = v[q];
+                }
+            }
         }
     } else {
         // gathered words; the partial last word is biased on its template bytes only
@@ -267,42 +300,66 @@ __device__ __forceinline__ void mf_slide(const uint32_t *img, int sw, int hcur, 
 }
 
 // In-place inclusive prefix sums along each of the 2*MF_TY rows of V over
-// `ncols` columns: 8 threads per row, each a contiguous segment read and
-// written 8 entries at a time.  Every thread must call it (it holds barriers).
+// `ncols` columns.  Each wave scans its own MF_TY/2 rows: lane l takes the K
+// contiguous columns [l*K, l*K + K) of a row (K odd, so the lanes' reads fall
+// in different banks; 64*K covers the widest rows of NKB template blocks).
+// Pass 1 sums each lane's columns for every row; one shuffle scan over the
+// lanes then serves all the wave's rows at once; pass 2 re-reads the columns,
+// scans them and adds the sum of the lanes before.  Reads are unconditional
+// (index clamped, value masked) so they are in flight together.  No
+// workgroup barrier inside; the caller synchronizes before reading V.
+template <int NKB>
 __device__ __forceinline__ void mf_row_prefix(uint32_t *V, int vs, int ncols)
 {
-    const int row = threadIdx.x >> 3;  // 0..31
-    const int seg = threadIdx.x & 7;
-    const int len = (ncols + 7) / 8;
-    const int c0 = seg * len, c1 = min(ncols, c0 + len);
-    uint32_t *r = V + row * vs;
-    uint32_t s = 0u;
-    for (int c = c0; c < c1; c += 8) {
-        uint32_t v[8];
+    constexpr int K = ((256 + 64 * NKB + 63) / 64) | 1;  // ncols <= 256 + 64 * NKB
+    constexpr int RPW = 2 * MF_TY / (MF_THREADS / 64);    // rows per wave
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int c0 = lane * K;
+    uint32_t *const r0 = V + wave * RPW * vs;
+    uint32_t keep[K];  // all ones for the lane's columns inside the row
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-            v[u] = c + u < c1 ? r[c + u] : 0u;
+    for (int u = 0; u < K; ++u)
+        keep[u] = c0 + u < ncols ? 0xFFFFFFFFu : 0u;
+    uint32_t tot[RPW];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            s += v[u];
-            v[u] = s;
+    for (int q = 0; q < RPW; ++q) {
+        uint32_t t = 0u;
+#pragma unroll
+        for (int u = 0; u < K; ++u)
+            t += r0[q * vs + min(c0 + u, ncols - 1)] & keep[u];
+        tot[q] = t;
+    }
+    uint32_t incl[RPW];
+#pragma unroll
+    for (int q = 0; q < RPW; ++q)
+        incl[q] = tot[q];
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        uint32_t o[RPW];
+#pragma unroll
+        for (int q = 0; q < RPW; ++q)
+            o[q] = (uint32_t)__shfl_up((int)incl[q], d, 64);
+#pragma unroll
+        for (int q = 0; q < RPW; ++q)
+            if (lane >= d)
+                incl[q] += o[q];
+    }
+#pragma unroll
+    for (int q = 0; q < RPW; ++q) {
+        uint32_t *r = r0 + q * vs;
+        uint32_t x[K];
+#pragma unroll
+        for (int u = 0; u < K; ++u)
+            x[u] = r[min(c0 + u, ncols - 1)] & keep[u];
+        uint32_t run = incl[q] - tot[q];  // sum of the lanes before this one
+#pragma unroll
+        for (int u = 0; u < K; ++u) {
+            run += x[u];
+            if (c0 + u < ncols)
+                r[c0 + u] = run;
         }
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-            if (c + u < c1)
-                r[c + u] = v[u];
     }
-    __syncthreads();
-    uint32_t off = 0u;
-    for (int k = 0; k < seg; ++k) {
-        const int e = min(ncols, (k + 1) * len) - 1;
-        if (e >= k * len)
-            off += r[e];
-    }
-    __syncthreads();
-    if (off)
-        for (int c = c0; c < c1; ++c)
-            r[c] += off;
 }
 
 template <int NKB>
@@ -378,7 +435,7 @@ __global__ __launch_bounds__(MF_THREADS) void ncc_u8_mfma_kernel(NccArgs a)
     }
     // Window sums from prefix sums of the column sums (V1 and V2 rows are
     // contiguous, so one pass covers both).
-    mf_row_prefix(V1, P.vs, 4 * P.nwd);
+    mf_row_prefix<NKB>(V1, P.vs, 4 * P.nwd);
     __syncthreads();
 
     const uint32_t sum_t = tsum[0], sum_tsq = tsum[1];
@@ -395,13 +452,17 @@ __global__ __launch_bounds__(MF_THREADS) void ncc_u8_mfma_kernel(NccArgs a)
     unsigned long long best = 0ull;
     if (gx < a.out_w) {
         size_t o = (size_t)y0 * a.out_w + gx;
+        // window sums as prefix differences; the entry left of column 0 is
+        // read from column 0 and masked to zero, so every read is unconditional
+        const int xl = x > 0 ? x - 1 : 0;
+        const uint32_t left_keep = x > 0 ? 0xFFFFFFFFu : 0u;
         for (int n = 0; n < MF_TY; ++n, o += a.out_w) {
             if (y0 + n >= a.out_h)
                 break;
             const uint32_t *q1 = V1 + n * P.vs;
             const uint32_t *q2 = V2 + n * P.vs;
-            const uint32_t si = q1[x + tw - 1] - (x > 0 ? q1[x - 1] : 0u);
-            const uint32_t sq = q2[x + tw - 1] - (x > 0 ? q2[x - 1] : 0u);
+            const uint32_t si = q1[x + tw - 1] - (q1[xl] & left_keep);
+            const uint32_t sq = q2[x + tw - 1] - (q2[xl] & left_keep);
             const uint32_t st = (uint32_t)acc_it[n * MF_ACC_STRIDE + x] + 128u * si + bias;
             if (a.sum_i) a.sum_i[o] = si;
             if (a.sum_isq) a.sum_isq[o] = sq;
