@@ -21,14 +21,17 @@
 //     the window sum over every template row (B is the template placed
 //     Toeplitz-wise along the output rows); a fraction 15/(t_height + 15) of
 //     the products is against zero rows.
-//   * SumI and SumISq: while the matrix cores run, the first lanes of each
-//     wave walk the tile's image words (4 columns each) down the template's
-//     rows, keeping running sums of pixels and of squares per column (the
-//     window of output row 0).  A short sliding pass then moves the window
-//     down the 16 output rows (add the row entering, remove the row leaving;
-//     the tile's first 15 rows are kept for that), and prefix sums along each
-//     row give the window sums as differences of two entries.  All unsigned
-//     32-bit, exact because every final sum is below 2^32.
+//   * SumI and SumISq: while four waves of the workgroup run the matrix
+//     cores, four more walk the tile's image words (4 columns each) down the
+//     template's rows, keeping running sums per column of pixels (two waves,
+//     half of the words each) and of squares (two more): the window of output
+//     row 0.  Each then slides its window down the 16 output rows (add the
+//     row entering, remove the row leaving; the tile's first 15 rows are kept
+//     for that when the template comes in several chunks) and takes prefix
+//     sums along each row of its half, so a window sum is the difference of
+//     two entries (plus the first half's row total where a window spans both
+//     halves).  All unsigned 32-bit, exact because every final sum is below
+//     2^32.
 //   * The coefficient follows the packed-byte kernels' exact formula: num, vI
 //     and vT are exact integers (held in fp64 here, formed with fused
 //     multiply-adds), then an IEEE fp64 divide and square root and one fp32
@@ -45,14 +48,15 @@ typedef int mf_v4i __attribute__((ext_vector_type(4)));
 
 constexpr int MF_TY = 16;          // output rows per workgroup (MFMA N)
 constexpr int MF_TX = 256;         // output columns per workgroup (4 waves x 64)
-constexpr int MF_THREADS = 256;
+constexpr int MF_MMA_WAVES = 4;    // matrix-core waves
+constexpr int MF_THREADS = 64 * (MF_MMA_WAVES + 4);  // plus the four column-sum waves
 constexpr int MF_MAX_NKB = 4;      // template rows up to 256 bytes
 constexpr int MF_MAX_HC = 256;     // template rows per chunk
 constexpr int MF_ACC_STRIDE = 257; // i32 words per output row of the SumIT staging
 
 // LDS plan of one workgroup (host and device agree through these helpers):
 //   V     2*MF_TY rows x vs u32: column sums of pixels (rows 0..15) and of
-//         squares (rows 16..31), then their row prefix
+//         squares (rows 16..31), then their row prefix (per half of the words)
 //   img   the staged image tile plus one spare row; after the walk, the
 //         SumIT' staging of MF_TY x MF_ACC_STRIDE i32
 //   tpl   template rows with zero rows around them (trows rows of tsb bytes)
@@ -65,8 +69,7 @@ struct MfPlan {
     int sw;       // image LDS words per row
     int tsb;      // template LDS bytes per row
     int trows;    // template LDS rows
-    int nwd;      // image words covered by the column sums
-    int cw;       // column-walk words per wave
+    int nwd;      // image words covered by the column sums (64 .. 128)
     int vs;       // u32 per row of V (a multiple of 4: 16-byte stores)
     int img_words;
     size_t bytes;
@@ -81,7 +84,6 @@ __host__ __device__ inline MfPlan mf_plan(int t_width, int hc)
     p.tsb = 64 * p.nkb + 16;
     p.trows = hc + 2 * MF_TY - 1;
     p.nwd = 64 + (t_width + 2) / 4;  // words holding columns 0 .. 255 + t_width - 1
-    p.cw = (p.nwd + 3) / 4;
     p.vs = 4 * p.nwd + 4;
     int img = (MF_TY + hc) * p.sw;  // staged rows + one spare row
     if (img < MF_TY * MF_ACC_STRIDE) img = MF_TY * MF_ACC_STRIDE;
@@ -94,13 +96,13 @@ __host__ __device__ inline MfPlan mf_plan(int t_width, int hc)
 // Image rows [gy0, gy0 + nrows) x words [0, 4*nchunks) from column gx0, biased
 // to signed bytes; rows at or past `height` and chunks at or past `pitch` are
 // zero-filled, so no load leaves the image allocation.
-// Each thread takes its items in batches of 8, all loads of a batch issued
+// Each thread takes its items in batches of 4, all loads of a batch issued
 // before any of its LDS stores (one memory round trip per batch); a chunk
 // outside the image loads from the image base and is zeroed afterwards.
 __device__ __forceinline__ void mf_stage_image(const uint8_t *__restrict__ image, int height, int pitch, int gy0,
                                                int gx0, int nrows, int nchunks, uint32_t *lds, int stride)
 {
-    constexpr int SB = 8;
+    constexpr int SB = 4;
     const int total = nrows * nchunks;
     for (int i0 = threadIdx.x; i0 < total; i0 += SB * MF_THREADS) {
         uint4 v[SB];
@@ -145,8 +147,8 @@ __device__ __forceinline__ void mf_stage_template(const uint8_t *__restrict__ tm
     const int twords = (t_width + 3) / 4;
     const int total = trows * wpr;
     if (tmpl_word_rows(tmpl, t_width)) {
-        // whole-word rows, in batches of 8 (loads first, then the LDS stores)
-        constexpr int SB = 8;
+        // whole-word rows, in batches of 4 (loads first, then the LDS stores)
+        constexpr int SB = 4;
         for (int i0 = threadIdx.x; i0 < total; i0 += SB * MF_THREADS) {
             uint32_t v[SB];
 #pragma unroll
@@ -184,42 +186,36 @@ __device__ __forceinline__ void mf_stage_template(const uint8_t *__restrict__ tm
     }
 }
 
-// Running column sums: add the pixels and squares of one image word (4
-// columns) into pi / pq.
-__device__ __forceinline__ void mf_col_add(uint32_t biased, uint32_t (&pi)[4], uint32_t (&pq)[4])
+// Column sums of field F over one image word (4 columns), into c[0..3]:
+// F = 0 adds the pixels, F = 1 their squares.
+template <int F>
+__device__ __forceinline__ void mf_col_add(uint32_t biased, uint32_t (&c)[4])
 {
     const uint32_t w = biased ^ 0x80808080u;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        pi[k] = dot4u(w, 1u << (8 * k), pi[k]);
-        pq[k] = dot4u(w & (0xFFu << (8 * k)), w, pq[k]);
-    }
+    for (int k = 0; k < 4; ++k)
+        c[k] = F == 0 ? dot4u(w, 1u << (8 * k), c[k]) : dot4u(w & (0xFFu << (8 * k)), w, c[k]);
 }
 
-// The walk of one template-row chunk for one wave.  Matrix cores: every image
+// The matrix-core walk of one template-row chunk for one wave: every image
 // row of the chunk's tile against the template rows it meets, NKB 64-byte
 // blocks per row; rows go in pairs through two register sets, the next row's
 // LDS words read while the current row's products issue (the read after the
-// last row lands in the spare row each LDS area keeps).  Column sums: walker
-// lanes add image row rr of word wd for rr < hcur (absolute rows j0 + rr), and
-// keep the first MF_TY - 1 absolute rows in `head`.
+// last row lands in the spare row each LDS area keeps).
 template <int NKB>
 __device__ __forceinline__ void mf_walk_chunk(const uint32_t *img, int sw, const uint8_t *tpl, int tsb, int hcur,
-                                              int j0, bool walker, int wd, uint32_t *head, int nwd,
-                                              mf_v4i (&at)[4], uint32_t (&pi)[4], uint32_t (&pq)[4])
+                                              int wave, mf_v4i (&at)[4])
 {
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
     const int m = lane & 15, g = lane >> 4;
     // A: output column x0 + 64*wave + 4m + t reads image words from 16*wave + m
     // (+ 4g for its 16 bytes of the 64-byte block).  B: output row n = m meets
     // template row rr - n, staged at LDS row rr - n + MF_TY - 1.
     const uint32_t *ip = img + 16 * wave + m + 4 * g;
     const uint8_t *tp = tpl + (MF_TY - 1 - m) * tsb + 16 * g;
-    const uint32_t *cp = img + (walker ? wd : 0);
     const int nrows = MF_TY - 1 + hcur;
 
-    auto load = [&](uint32_t (&w)[NKB][5], mf_v4i (&b)[NKB], uint32_t &cw) {
+    auto load = [&](uint32_t (&w)[NKB][5], mf_v4i (&b)[NKB]) {
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
@@ -227,54 +223,77 @@ __device__ __forceinline__ void mf_walk_chunk(const uint32_t *img, int sw, const
                 w[kb][k] = ip[16 * kb + k];
             b[kb] = *reinterpret_cast<const mf_v4i *>(tp + 64 * kb);
         }
-        cw = *cp;
         ip += sw;
         tp += tsb;
-        cp += sw;
     };
-    auto compute = [&](int rr, const uint32_t (&w)[NKB][5], const mf_v4i (&b)[NKB], uint32_t cw) {
+    auto compute = [&](const uint32_t (&w)[NKB][5], const mf_v4i (&b)[NKB]) {
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
-            mf_v4i a[4];
+            mf_v4i av[4];
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                a[0][k] = (int)w[kb][k];
-                a[1][k] = (int)shift_bytes(w[kb][k + 1], w[kb][k], 1);
-                a[2][k] = (int)shift_bytes(w[kb][k + 1], w[kb][k], 2);
-                a[3][k] = (int)shift_bytes(w[kb][k + 1], w[kb][k], 3);
+                av[0][k] = (int)w[kb][k];
+                av[1][k] = (int)shift_bytes(w[kb][k + 1], w[kb][k], 1);
+                av[2][k] = (int)shift_bytes(w[kb][k + 1], w[kb][k], 2);
+                av[3][k] = (int)shift_bytes(w[kb][k + 1], w[kb][k], 3);
             }
 #pragma unroll
             for (int t = 0; t < 4; ++t)
-                at[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[t], b[kb], at[t], 0, 0, 0);
-        }
-        if (walker && rr < hcur) {
-            mf_col_add(cw, pi, pq);
-            if (j0 + rr < MF_TY - 1)
-                head[(j0 + rr) * nwd + wd] = cw;
+                at[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[t], b[kb], at[t], 0, 0, 0);
         }
     };
-    uint32_t wa[NKB][5], wb[NKB][5], ca, cb;
+    uint32_t wa[NKB][5], wb[NKB][5];
     mf_v4i ba[NKB], bb[NKB];
-    load(wa, ba, ca);
+    load(wa, ba);
     int rr = 0;
     for (; rr + 2 <= nrows; rr += 2) {
-        load(wb, bb, cb);  // row rr + 1
-        compute(rr, wa, ba, ca);
-        load(wa, ba, ca);  // row rr + 2 (the spare row when rr + 2 == nrows)
-        compute(rr + 1, wb, bb, cb);
+        load(wb, bb);  // row rr + 1
+        compute(wa, ba);
+        load(wa, ba);  // row rr + 2 (the spare row when rr + 2 == nrows)
+        compute(wb, bb);
     }
     if (rr < nrows)
-        compute(rr, wa, ba, ca);
+        compute(wa, ba);
 }
 
-// The sliding pass of walker word wd after the last chunk's walk: pi / pq hold
+// The column walk of field F over tile rows [0, hcur) of one chunk (absolute
+// rows j0 .. j0 + hcur - 1) for image word wd of this lane, into c.  With
+// save_head the raw words of the first MF_TY - 1 absolute rows go to `head`
+// for the sliding pass of the last chunk (only when `keep`: lanes past their
+// wave's words read a clamped word and store nothing).
+template <int F>
+__device__ __forceinline__ void mf_col_walk(const uint32_t *img, int sw, int hcur, int j0, bool save_head,
+                                            uint32_t *head, int nwd, int wd, bool keep, uint32_t (&c)[4])
+{
+    const uint32_t *p = img + wd;
+    constexpr int U = 4;
+    int rr = 0;
+    for (; rr + U <= hcur; rr += U) {
+        uint32_t u[U];
+#pragma unroll
+        for (int q = 0; q < U; ++q)
+            u[q] = p[(rr + q) * sw];
+#pragma unroll
+        for (int q = 0; q < U; ++q)
+            mf_col_add<F>(u[q], c);
+    }
+    for (; rr < hcur; ++rr)
+        mf_col_add<F>(p[rr * sw], c);
+    if (save_head && keep)
+        for (rr = 0; rr < hcur && j0 + rr < MF_TY - 1; ++rr)
+            head[(j0 + rr) * nwd + wd] = p[rr * sw];
+}
+
+// The sliding pass of field F for word wd after the last chunk's walk: c holds
 // the column sums of absolute rows [0, th), i.e. output row 0's window.  Row
 // n's window adds absolute row n + th - 1 (tile row hcur + n - 1 of the last
 // chunk) and drops absolute row n - 1 (tile row n - 1 when the template came
-// in one chunk, else the saved head row).
-__device__ __forceinline__ void mf_slide(const uint32_t *img, int sw, int hcur, bool one_chunk, const uint32_t *head,
-                                         int nwd, int wd, uint32_t *V1, uint32_t *V2, int vs, uint32_t (&pi)[4],
-                                         uint32_t (&pq)[4])
+// in one chunk, else the saved head row).  Rows n = 0 .. MF_TY - 1 go to V
+// (row stride vs) when `keep`; reads are unconditional.
+template <int F>
+__device__ __forceinline__ void mf_slide_word(const uint32_t *img, int sw, int hcur, bool one_chunk,
+                                              const uint32_t *head, int nwd, int wd, bool keep, uint32_t *V, int vs,
+                                              uint32_t (&c)[4])
 {
     uint32_t in[MF_TY - 1], out[MF_TY - 1];
 #pragma unroll
@@ -282,72 +301,76 @@ __device__ __forceinline__ void mf_slide(const uint32_t *img, int sw, int hcur, 
         in[n - 1] = img[(hcur + n - 1) * sw + wd];
         out[n - 1] = one_chunk ? img[(n - 1) * sw + wd] : head[(n - 1) * nwd + wd];
     }
-    *reinterpret_cast<uint4 *>(V1 + 4 * wd) = make_uint4(pi[0], pi[1], pi[2], pi[3]);
-    *reinterpret_cast<uint4 *>(V2 + 4 * wd) = make_uint4(pq[0], pq[1], pq[2], pq[3]);
+    if (keep)
+        *reinterpret_cast<uint4 *>(V + 4 * wd) = make_uint4(c[0], c[1], c[2], c[3]);
 #pragma unroll
     for (int n = 1; n < MF_TY; ++n) {
-        uint32_t ri[4] = {0u, 0u, 0u, 0u}, rq[4] = {0u, 0u, 0u, 0u};
-        mf_col_add(in[n - 1], pi, pq);
-        mf_col_add(out[n - 1], ri, rq);
+        uint32_t r[4] = {0u, 0u, 0u, 0u};
+        mf_col_add<F>(in[n - 1], c);
+        mf_col_add<F>(out[n - 1], r);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            pi[k] -= ri[k];
-            pq[k] -= rq[k];
-        }
-        *reinterpret_cast<uint4 *>(V1 + n * vs + 4 * wd) = make_uint4(pi[0], pi[1], pi[2], pi[3]);
-        *reinterpret_cast<uint4 *>(V2 + n * vs + 4 * wd) = make_uint4(pq[0], pq[1], pq[2], pq[3]);
+        for (int k = 0; k < 4; ++k)
+            c[k] -= r[k];
+        if (keep)
+            *reinterpret_cast<uint4 *>(V + n * vs + 4 * wd) = make_uint4(c[0], c[1], c[2], c[3]);
     }
 }
 
-// In-place inclusive prefix sums along each of the 2*MF_TY rows of V over
-// `ncols` columns.  Each wave scans its own MF_TY/2 rows: lane l takes the K
-// contiguous columns [l*K, l*K + K) of a row (K odd, so the lanes' reads fall
-// in different banks; 64*K covers the widest rows of NKB template blocks).
-// Pass 1 sums each lane's columns for every row; one shuffle scan over the
-// lanes then serves all the wave's rows at once; pass 2 re-reads the columns,
+// In-place inclusive prefix sums along the MF_TY rows of V (row stride vs)
+// over `ncols` columns, by one wave, half the rows at a time: lane l takes the
+// K contiguous columns [l*K, l*K + K) of a row (K odd, so the lanes' reads
+// fall in different banks; 64*K covers the widest half of NKB template
+// blocks).  Pass 1 sums each lane's columns for every row; one scan over the
+// lanes then serves all rows at once; pass 2 re-reads the columns,
 // scans them and adds the sum of the lanes before.  Reads are unconditional
-// (index clamped, value masked) so they are in flight together.  No
-// workgroup barrier inside; the caller synchronizes before reading V.
-template <int NKB>
-__device__ __forceinline__ void mf_row_prefix(uint32_t *V, int vs, int ncols)
+// (index clamped, value masked) so they are in flight together.  Each lane
+// writes only its own columns; the caller orders V's writers before and its
+// readers after.
+// Inclusive prefix sum over the 64 lanes of a wave in DPP moves: shifts by
+// 1, 2, 4 and 8 lanes within each row of 16 (lanes shifted in from outside
+// the row read 0), then lane 15's total added to rows 1 and 3 and lane 31's
+// to rows 2 and 3.
+__device__ __forceinline__ uint32_t mf_wave_scan(uint32_t v)
 {
-    constexpr int K = ((256 + 64 * NKB + 63) / 64) | 1;  // ncols <= 256 + 64 * NKB
-    constexpr int RPW = 2 * MF_TY / (MF_THREADS / 64);    // rows per wave
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, true);   // row_shr:1
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, true);   // row_shr:2
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, true);   // row_shr:4
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, true);   // row_shr:8
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+    return v;
+}
+
+template <int NKB>
+__device__ __forceinline__ void mf_row_prefix_half(uint32_t *V, int vs, int ncols)
+{
+    constexpr int K = ((4 * (32 + 8 * NKB) + 63) / 64) | 1;  // ncols <= 4 * ceil(nwd / 2)
+    constexpr int R = MF_TY / 2;
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
     const int c0 = lane * K;
-    uint32_t *const r0 = V + wave * RPW * vs;
     uint32_t keep[K];  // all ones for the lane's columns inside the row
 #pragma unroll
     for (int u = 0; u < K; ++u)
         keep[u] = c0 + u < ncols ? 0xFFFFFFFFu : 0u;
-    uint32_t tot[RPW];
+    uint32_t tot[R];
 #pragma unroll
-    for (int q = 0; q < RPW; ++q) {
+    for (int q = 0; q < R; ++q) {
         uint32_t t = 0u;
 #pragma unroll
         for (int u = 0; u < K; ++u)
-            t += r0[q * vs + min(c0 + u, ncols - 1)] & keep[u];
+            t += V[q * vs + min(c0 + u, ncols - 1)] & keep[u];
         tot[q] = t;
     }
-    uint32_t incl[RPW];
+    uint32_t incl[R];
 #pragma unroll
-    for (int q = 0; q < RPW; ++q)
+    for (int q = 0; q < R; ++q)
         incl[q] = tot[q];
 #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        uint32_t o[RPW];
+    for (int q = 0; q < R; ++q)
+        incl[q] = mf_wave_scan(incl[q]);
 #pragma unroll
-        for (int q = 0; q < RPW; ++q)
-            o[q] = (uint32_t)__shfl_up((int)incl[q], d, 64);
-#pragma unroll
-        for (int q = 0; q < RPW; ++q)
-            if (lane >= d)
-                incl[q] += o[q];
-    }
-#pragma unroll
-    for (int q = 0; q < RPW; ++q) {
-        uint32_t *r = r0 + q * vs;
+    for (int q = 0; q < R; ++q) {
+        uint32_t *r = V + q * vs;
         uint32_t x[K];
 #pragma unroll
         for (int u = 0; u < K; ++u)
@@ -363,7 +386,46 @@ __device__ __forceinline__ void mf_row_prefix(uint32_t *V, int vs, int ncols)
 }
 
 template <int NKB>
-__global__ __launch_bounds__(MF_THREADS) void ncc_u8_mfma_kernel(NccArgs a)
+__device__ __forceinline__ void mf_row_prefix(uint32_t *V, int vs, int ncols)
+{
+#pragma nounroll
+    for (int h = 0; h < 2; ++h)
+        mf_row_prefix_half<NKB>(V + h * (MF_TY / 2) * vs, vs, ncols);
+}
+
+// Column walk, sliding pass and row prefix of field F over words
+// [w0, w0 + cnt) by one column-sum wave for one chunk (the last two after the
+// last chunk only).  The prefix runs over the wave's own columns
+// [4*w0, 4*(w0 + cnt)), starting from zero.
+template <int NKB, int F>
+__device__ __forceinline__ void mf_field_chunk(const uint32_t *img, int sw, int hcur, int j0, bool last,
+                                               bool one_chunk, uint32_t *head, int nwd, int w0, int cnt,
+                                               uint32_t *V, int vs, uint32_t (&c)[4])
+{
+    const int lane = threadIdx.x & 63;
+    const int wd = w0 + min(lane, cnt - 1);
+    const bool keep = lane < cnt;
+    mf_col_walk<F>(img, sw, hcur, j0, !one_chunk, head, nwd, wd, keep, c);
+    if (!last)
+        return;
+    mf_slide_word<F>(img, sw, hcur, one_chunk, head, nwd, wd, keep, V, vs, c);
+    // the slide's stores (other lanes' columns) before the scan's reads
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    mf_row_prefix<NKB>(V + 4 * w0, vs, 4 * cnt);
+}
+
+// Workgroup roles (wave-uniform): waves 0 .. MF_MMA_WAVES - 1 run the matrix
+// cores, 64 output columns each; the next four keep the column sums, one wave
+// per field (pixels, squared pixels) and half of the image words (the first
+// pixel wave also sums the template), so the vector work of SumI and SumISq
+// runs beside the matrix products instead of inside their loop.  Every wave
+// takes part in the staging and in the epilogue.  The row prefix of each half
+// starts from zero; the epilogue adds the first half's row total where a
+// window reaches from the first half into the second.
+template <int NKB>
+__global__ __launch_bounds__(MF_THREADS) __attribute__((amdgpu_waves_per_eu(NKB == 1 ? 4 : 1)))
+void ncc_u8_mfma_kernel(NccArgs a)
 {
     extern __shared__ uint4 mf_smem[];
     const MfPlan P = mf_plan(a.t_width, a.hc);
@@ -379,52 +441,72 @@ __global__ __launch_bounds__(MF_THREADS) void ncc_u8_mfma_kernel(NccArgs a)
     const int tw = a.t_width, th = a.t_height;
     const int twords = (tw + 3) / 4;  // packed words per template row (the last one partial when tw % 4 != 0)
     const uint32_t tm = tail_mask(tw);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wd = wave * P.cw + lane;              // column-walk word of this lane
-    const bool walker = lane < P.cw && wd < P.nwd;
-
-    if (threadIdx.x < 2)
-        tsum[threadIdx.x] = 0u;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const bool one_chunk = th <= P.hc;
+    const int half = (P.nwd + 1) / 2;  // words of the first half (<= 64)
+    const int ce = 4 * half;           // first column of the second half
 
     mf_v4i at[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
         at[t] = mf_v4i{0, 0, 0, 0};
-    uint32_t pi[4] = {0u, 0u, 0u, 0u}, pq[4] = {0u, 0u, 0u, 0u};
+    uint32_t c[4] = {0u, 0u, 0u, 0u};
     uint32_t ts = 0u, tq = 0u;
 
     const int nchunks16 = (64 + 16 * NKB) / 4;  // 16-byte chunks per staged image row
     for (int j0 = 0; j0 < th; j0 += P.hc) {
         const int hcur = min(P.hc, th - j0);
+        const bool last = j0 + hcur == th;
         __syncthreads();  // the previous chunk's readers are done
         mf_stage_image(a.image, a.height, a.pitch, y0 + j0, x0, MF_TY - 1 + hcur, nchunks16, img, P.sw);
         mf_stage_template(a.tmpl, tw, j0, hcur, 64 * NKB, tpl, P.tsb, P.trows);
         __syncthreads();
-        // template sums from the staged (biased) rows of this chunk; the
-        // partial last word of a row (tm != ~0) is unbiased on its template
-        // bytes only, its padding stays zero
-        for (int i = threadIdx.x; i < hcur * twords; i += MF_THREADS) {
-            const int r = i / twords;
-            const int k = i - r * twords;
-            const uint32_t unbias = tm == 0xFFFFFFFFu || k != twords - 1 ? 0x80808080u : 0x80808080u & tm;
-            const uint32_t w = *reinterpret_cast<const uint32_t *>(tpl + (MF_TY - 1 + r) * P.tsb + 4 * k) ^ unbias;
-            ts = dot4u(w, 0x01010101u, ts);
-            tq = dot4u(w, w, tq);
+        if (wave < MF_MMA_WAVES) {
+            mf_walk_chunk<NKB>(img, P.sw, tpl, P.tsb, hcur, wave, at);
+        } else {
+            // the column-sum waves issue first on their SIMD: the matrix
+            // waves lose little (their products keep the matrix cores busy)
+            // and the sums are ready when the products are
+            __builtin_amdgcn_s_setprio(2);
+            const int h = (wave - MF_MMA_WAVES) & 1;
+            const int w0 = h * half, cnt = h ? P.nwd - half : half;
+            if (wave < MF_MMA_WAVES + 2) {
+                if (h == 0) {
+                    // template sums from the staged (biased) rows of this
+                    // chunk; the partial last word of a row (tm != ~0) is
+                    // unbiased on its template bytes only, its padding stays zero
+                    for (int i = lane; i < hcur * twords; i += 64) {
+                        const int r = i / twords;
+                        const int k = i - r * twords;
+                        const uint32_t unbias =
+                            tm == 0xFFFFFFFFu || k != twords - 1 ? 0x80808080u : 0x80808080u & tm;
+                        const uint32_t w =
+                            *reinterpret_cast<const uint32_t *>(tpl + (MF_TY - 1 + r) * P.tsb + 4 * k) ^ unbias;
+                        ts = dot4u(w, 0x01010101u, ts);
+                        tq = dot4u(w, w, tq);
+                    }
+                }
+                mf_field_chunk<NKB, 0>(img, P.sw, hcur, j0, last, one_chunk, head, P.nwd, w0, cnt, V1, P.vs, c);
+            } else {
+                mf_field_chunk<NKB, 1>(img, P.sw, hcur, j0, last, one_chunk, head, P.nwd, w0, cnt, V2, P.vs, c);
+            }
+            __builtin_amdgcn_s_setprio(0);
         }
-        mf_walk_chunk<NKB>(img, P.sw, tpl, P.tsb, hcur, j0, walker, wd, head, P.nwd, at, pi, pq);
-        if (j0 + hcur == th && walker)
-            mf_slide(img, P.sw, hcur, j0 == 0, head, P.nwd, wd, V1, V2, P.vs, pi, pq);
     }
-    ts = wave_sum_u32(ts);
-    tq = wave_sum_u32(tq);
-    if (lane == 0) {
-        atomicAdd(tsum + 0, ts);
-        atomicAdd(tsum + 1, tq);
+    if (wave == MF_MMA_WAVES) {
+        ts = wave_sum_u32(ts);
+        tq = wave_sum_u32(tq);
+        if (lane == 0) {
+            tsum[0] = ts;
+            tsum[1] = tq;
+        }
     }
-    __syncthreads();
+    __syncthreads();  // every reader of the image tile is done; V, tsum written
 
-    // SumIT' to LDS: lane (g, n) holds columns 64*wave + 16g + 4i + t of row n.
-    {
+    // SumIT' to LDS (over the image tile): lane (g, n) holds columns
+    // 64*wave + 16g + 4i + t of row n.
+    if (wave < MF_MMA_WAVES) {
         const int n = lane & 15, g = lane >> 4;
         const int base = n * MF_ACC_STRIDE + 64 * wave + 16 * g;
 #pragma unroll
@@ -433,9 +515,6 @@ __global__ __launch_bounds__(MF_THREADS) void ncc_u8_mfma_kernel(NccArgs a)
             for (int t = 0; t < 4; ++t)
                 acc_it[base + 4 * i + t] = at[t][i];
     }
-    // Window sums from prefix sums of the column sums (V1 and V2 rows are
-    // contiguous, so one pass covers both).
-    mf_row_prefix<NKB>(V1, P.vs, 4 * P.nwd);
     __syncthreads();
 
     const uint32_t sum_t = tsum[0], sum_tsq = tsum[1];
@@ -447,38 +526,40 @@ __global__ __launch_bounds__(MF_THREADS) void ncc_u8_mfma_kernel(NccArgs a)
     const double nd = (double)nn, std_ = (double)sum_t;
     const double vt = fma(nd, (double)sum_tsq, -(std_ * std_));
 
-    const int x = threadIdx.x;
-    const int gx = x0 + x;
+    // Each wave takes 64 consecutive columns of one output row at a time.
     unsigned long long best = 0ull;
-    if (gx < a.out_w) {
-        size_t o = (size_t)y0 * a.out_w + gx;
-        // window sums as prefix differences; the entry left of column 0 is
-        // read from column 0 and masked to zero, so every read is unconditional
-        const int xl = x > 0 ? x - 1 : 0;
+    for (int i = threadIdx.x; i < MF_TY * MF_TX; i += MF_THREADS) {
+        const int n = i / MF_TX, x = i % MF_TX;
+        const int gx = x0 + x;
+        if (gx >= a.out_w || y0 + n >= a.out_h)
+            continue;
+        const size_t o = (size_t)(y0 + n) * a.out_w + gx;
+        // window sums as differences of the row prefix at columns hi and lo:
+        // the entry left of column 0 is read from column 0 and masked to
+        // zero, and the first half's row total (at ce - 1) is added when hi
+        // is in the second half and lo is not; every read is unconditional
+        const int hi = x + tw - 1, xl = x > 0 ? x - 1 : 0;
         const uint32_t left_keep = x > 0 ? 0xFFFFFFFFu : 0u;
-        for (int n = 0; n < MF_TY; ++n, o += a.out_w) {
-            if (y0 + n >= a.out_h)
-                break;
-            const uint32_t *q1 = V1 + n * P.vs;
-            const uint32_t *q2 = V2 + n * P.vs;
-            const uint32_t si = q1[x + tw - 1] - (q1[xl] & left_keep);
-            const uint32_t sq = q2[x + tw - 1] - (q2[xl] & left_keep);
-            const uint32_t st = (uint32_t)acc_it[n * MF_ACC_STRIDE + x] + 128u * si + bias;
-            if (a.sum_i) a.sum_i[o] = si;
-            if (a.sum_isq) a.sum_isq[o] = sq;
-            if (a.sum_it) a.sum_it[o] = st;
-            if (a.coef || a.peak) {
-                const double sid = (double)si;
-                const double num = fma(nd, (double)st, -(sid * std_));
-                const double vi = fma(nd, (double)sq, -(sid * sid));
-                double c = 0.0;
-                if (vi != 0.0 && vt != 0.0)
-                    c = num / sqrt(vi * vt);
-                if (a.coef) a.coef[o] = (float)c;
-                if (a.peak) {
-                    const unsigned long long k = peak_key((float)c, (uint32_t)o);
-                    best = k > best ? k : best;
-                }
+        const uint32_t join_keep = hi >= ce && (x == 0 || x - 1 < ce) ? 0xFFFFFFFFu : 0u;
+        const uint32_t *q1 = V1 + n * P.vs;
+        const uint32_t *q2 = V2 + n * P.vs;
+        const uint32_t si = q1[hi] - (q1[xl] & left_keep) + (q1[ce - 1] & join_keep);
+        const uint32_t sq = q2[hi] - (q2[xl] & left_keep) + (q2[ce - 1] & join_keep);
+        const uint32_t st = (uint32_t)acc_it[n * MF_ACC_STRIDE + x] + 128u * si + bias;
+        if (a.sum_i) a.sum_i[o] = si;
+        if (a.sum_isq) a.sum_isq[o] = sq;
+        if (a.sum_it) a.sum_it[o] = st;
+        if (a.coef || a.peak) {
+            const double sid = (double)si;
+            const double num = fma(nd, (double)st, -(sid * std_));
+            const double vi = fma(nd, (double)sq, -(sid * sid));
+            double cf = 0.0;
+            if (vi != 0.0 && vt != 0.0)
+                cf = num / sqrt(vi * vt);
+            if (a.coef) a.coef[o] = (float)cf;
+            if (a.peak) {
+                const unsigned long long k = peak_key((float)cf, (uint32_t)o);
+                best = k > best ? k : best;
             }
         }
     }
