@@ -139,6 +139,34 @@ __device__ __forceinline__ void peak_commit(unsigned long long *peak, unsigned l
         atomicMax(peak, v);
 }
 
+// Largest key of the workgroup, then one 64-bit atomic maximum for it (one
+// per workgroup instead of one per wave: the atomics on the single key
+// serialize).  Every thread of the workgroup must call it.  `slots` is LDS
+// for one key per wave; it may overlay any LDS the workgroup does not read
+// after the call (a barrier separates the earlier reads from its writes).
+__device__ __forceinline__ void peak_commit_wg(unsigned long long *peak, unsigned long long v,
+                                               unsigned long long *slots)
+{
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m, 64);
+        const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m, 64);
+        const unsigned long long o = ((unsigned long long)hi << 32) | lo;
+        v = o > v ? o : v;
+    }
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0)
+        slots[threadIdx.x >> 6] = v;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const int nwaves = (int)(blockDim.x >> 6);
+        for (int w = 1; w < nwaves; ++w)
+            v = slots[w] > v ? slots[w] : v;
+        if (v != 0ull)
+            atomicMax(peak, v);
+    }
+}
+
 // Exact epilogue for one window; writes whichever outputs are requested and
 // folds the window into `best` when the best match is requested.
 __device__ __forceinline__ void ncc_store(const NccArgs &a, size_t o, uint32_t si, uint32_t sq, uint32_t st,

@@ -564,7 +564,7 @@ void ncc_u8_mfma_kernel(NccArgs a)
         }
     }
     if (a.peak)
-        peak_commit(a.peak, best);
+        peak_commit_wg(a.peak, best, reinterpret_cast<unsigned long long *>(tpl));
 }
 
 // Template rows per chunk: the most that fit two workgroups per CU (80 KiB
