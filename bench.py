@@ -396,8 +396,9 @@ def main():
         m["roofline"] = {"bound": "mfma", "achieved": round(mf_achieved / 1e12, 2), "peak": I8_MFMA_PEAK / 1e12,
                          "unit": "TOP/s", "frac": round(mf_achieved / I8_MFMA_PEAK, 4),
                          "kernel": "ncc_u8_mfma_kernel",
-                         "note": "matrix-core instructions take ~1 us of the kernel; VALU issue and "
-                                 "LDS/barrier latency bound it"}
+                         "note": "matrix-core and vector instructions of a SIMD take turns: the byte "
+                                 "alignment of the A operand, the column sums and the fp64 epilogue "
+                                 "lengthen the product walk"}
         if not args.no_ext:
             out["ncc_ext"] = bench_ncc_ext(args, torch, _lib, inputs)
     if args.only in ("xcorr", "all"):

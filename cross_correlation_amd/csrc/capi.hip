@@ -83,13 +83,21 @@ int ncc_dispatch(const xc::NccArgs &a, int variant, hipStream_t s)
 {
     switch (variant) {
     case XC_NCC_AUTO:
-        // The matrix-core recast has a fixed cost per tile of about the
-        // packed-byte kernel's time for a 16x16 template; it wins from about
-        // 512 template pixels on (measured on MI355X: 2.2x at 32x32, 6.4x at
-        // 64x64, 10x at 256x128 over a 1920x1080 image).
-        if ((int64_t)a.t_width * a.t_height >= 512 && xc::ncc_mfma_supported(a))
-            return hip_status(xc::ncc_launch_mfma(a, s));
-        return hip_status(xc::ncc_launch_ilp(a, s));
+        // The matrix-core recast costs a nearly fixed time per output tile,
+        // the packed-byte kernel a time that grows with the template; the
+        // recast wins from 512 template pixels at any image size, and from
+        // about 96 pixels once there are 400K outputs to spread its fixed
+        // cost over (measured on MI355X, packed-byte / recast: 1920x1080
+        // with 8x8 0.95, 10x10 1.15, 16x16 1.48, 64x64 8.3; 512x512 with
+        // 16x16 0.78, 24x24 1.18; 768x768 with 16x16 1.24; 256x256 with
+        // 16x16 0.71, 24x24 1.09).
+        {
+            const int64_t npix = (int64_t)a.t_width * a.t_height;
+            const int64_t nout = (int64_t)a.out_w * a.out_h;
+            if ((npix >= 512 || (npix >= 96 && nout >= 400000)) && xc::ncc_mfma_supported(a))
+                return hip_status(xc::ncc_launch_mfma(a, s));
+            return hip_status(xc::ncc_launch_ilp(a, s));
+        }
     case XC_NCC_DOT4_ILP:
         return hip_status(xc::ncc_launch_ilp(a, s));
     case XC_NCC_DOT4_C1:

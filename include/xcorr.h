@@ -90,8 +90,9 @@ int ncc_u8_run(const uint8_t *image, int width, int height, int pitch_bytes,
  * ncc_u8_run_variant -- the same computation through a chosen kernel variant,
  * for ablation studies.  Every variant returns identical outputs.
  *   XC_NCC_AUTO          the library's choice (what ncc_u8_run uses): XC_NCC_MFMA
- *                        for templates of at least 512 pixels it takes, else
- *                        XC_NCC_DOT4_ILP
+ *                        where it takes the template and the template has at
+ *                        least 512 pixels, or at least 96 pixels with at least
+ *                        400,000 outputs; else XC_NCC_DOT4_ILP
  *   XC_NCC_DOT4_ILP      packed-byte dot products, 4 columns x several rows per lane
  *   XC_NCC_DOT4_C1       packed-byte dot products, one output per lane
  *   XC_NCC_SCALAR_C1     byte-at-a-time multiply-adds, one output per lane
