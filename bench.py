@@ -374,10 +374,13 @@ def main():
             "outputs_per_s": round(r["outputs"] / (r["kernel_ms"] * 1e-3), 1),
         }
         # The same workload through the other kernel variants (every variant
-        # returns identical outputs): the page's ablation points and the
-        # matrix-core recast of SumIT.
-        variants = {"dot4_c1": _lib.XC_NCC_DOT4_C1, "scalar_c1": _lib.XC_NCC_SCALAR_C1, "mfma": _lib.XC_NCC_MFMA,
-                    "auto": _lib.XC_NCC_AUTO}
+        # returns identical outputs): the page's ablation points (one output
+        # per lane, byte-wise or packed-byte), the ILP series (4 columns x Q
+        # rows per lane, no template-row split) and the matrix-core recast of
+        # SumIT.
+        variants = {"dot4_c1": _lib.XC_NCC_DOT4_C1, "scalar_c1": _lib.XC_NCC_SCALAR_C1,
+                    "dot4_ilp_q1": _lib.XC_NCC_DOT4_ILP_Q1, "dot4_ilp_q2": _lib.XC_NCC_DOT4_ILP_Q2,
+                    "dot4_ilp_q4": _lib.XC_NCC_DOT4_ILP_Q4, "mfma": _lib.XC_NCC_MFMA, "auto": _lib.XC_NCC_AUTO}
         out["ncc_variants"] = {"dot4_ilp": {"kernel_ms": round(r["kernel_ms"], 5), "speedup_vs_dot4_ilp": 1.0}}
         for name, v in variants.items():
             k = args.steps if name in ("mfma", "auto") else min(args.steps, 10)

@@ -27,6 +27,9 @@ XC_NCC_DOT4_ILP = 1
 XC_NCC_DOT4_C1 = 2
 XC_NCC_SCALAR_C1 = 3
 XC_NCC_MFMA = 4
+XC_NCC_DOT4_ILP_Q1 = 5
+XC_NCC_DOT4_ILP_Q2 = 6
+XC_NCC_DOT4_ILP_Q4 = 7
 
 XC_XCORR_AUTO = 0
 XC_XCORR_OVERLAP = 1

@@ -106,6 +106,12 @@ int ncc_dispatch(const xc::NccArgs &a, int variant, hipStream_t s)
         return hip_status(xc::ncc_launch_c1(a, false, s));
     case XC_NCC_MFMA:
         return hip_status(xc::ncc_launch_mfma(a, s));
+    case XC_NCC_DOT4_ILP_Q1:
+        return hip_status(xc::ncc_launch_ilp(a, s, 1));
+    case XC_NCC_DOT4_ILP_Q2:
+        return hip_status(xc::ncc_launch_ilp(a, s, 2));
+    case XC_NCC_DOT4_ILP_Q4:
+        return hip_status(xc::ncc_launch_ilp(a, s, 4));
     default:
         return XC_ERR_VARIANT;
     }
@@ -114,7 +120,7 @@ int ncc_dispatch(const xc::NccArgs &a, int variant, hipStream_t s)
 // Variant check done before anything is enqueued.
 int ncc_variant_ok(const xc::NccArgs &a, int variant)
 {
-    if (variant < XC_NCC_AUTO || variant > XC_NCC_MFMA)
+    if (variant < XC_NCC_AUTO || variant > XC_NCC_DOT4_ILP_Q4)
         return XC_ERR_VARIANT;
     if (variant == XC_NCC_MFMA && !xc::ncc_mfma_supported(a))
         return XC_ERR_SHAPE;

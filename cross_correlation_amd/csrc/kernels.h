@@ -49,7 +49,9 @@ struct NccArgs {
     int t_stride;    // LDS words per staged template row
 };
 
-hipError_t ncc_launch_ilp(NccArgs a, hipStream_t s);
+// force_q = 0: the tile picked for the shape; 1, 2 or 4: Q rows per lane
+// (and as many row waves), no template-row split.
+hipError_t ncc_launch_ilp(NccArgs a, hipStream_t s, int force_q = 0);
 hipError_t ncc_launch_c1(NccArgs a, bool dot4, hipStream_t s);
 // SumIT on the i8 matrix cores; takes template rows up to 256 bytes.
 hipError_t ncc_launch_mfma(NccArgs a, hipStream_t s);

@@ -397,7 +397,7 @@ static hipError_t dispatch_wc(const NccArgs &a, int wc, hipStream_t s)
 
 // Chooses the tile (Q rows per lane, WV row waves, KS template slices), the
 // unroll WC and the chunking so that the LDS tile stays within 64 KiB.
-hipError_t ncc_launch_ilp(NccArgs a, hipStream_t s)
+hipError_t ncc_launch_ilp(NccArgs a, hipStream_t s, int force_q)
 {
     const int nw = (a.t_width + 3) / 4;  // packed words per row, the last one partial when t_width % 4 != 0
     // Unroll of the template-word loop: the largest power of two <= 4 that
@@ -413,7 +413,11 @@ hipError_t ncc_launch_ilp(NccArgs a, hipStream_t s)
     const long col_tiles = (a.out_w + 255) / 256;
     if (col_tiles * ((a.out_h + 15) / 16) < 256) { q = 2; wv = 2; }
     if (col_tiles * ((a.out_h + 3) / 4) < 256) { q = 1; wv = 1; }
-    const int ks = (q == 4 && a.t_height >= 16) ? 2 : 1;
+    int ks = (q == 4 && a.t_height >= 16) ? 2 : 1;
+    if (force_q) {  // the ablation series: Q rows per lane, no template-row split
+        q = wv = force_q;
+        ks = 1;
+    }
     const int lds_words = 64 * 1024 / 4;
     // chunk of template words: a multiple of lcm(wc, 4) words (16-byte aligned chunk starts)
     const int unit = 4;

@@ -102,12 +102,20 @@ int ncc_u8_run(const uint8_t *image, int width, int height, int pitch_bytes,
  *                        separable box sums; t_width <= 256 only, else
  *                        XC_ERR_SHAPE.  A recast of the page's computation,
  *                        not its DP4A method.
+ *   XC_NCC_DOT4_ILP_Q1   the ILP series of the ablation: packed-byte dot
+ *   XC_NCC_DOT4_ILP_Q2   products, 4 columns x Q = 1, 2 or 4 rows per lane,
+ *   XC_NCC_DOT4_ILP_Q4   each lane walking every template row itself (no split
+ *                        of the template rows over waves, which
+ *                        XC_NCC_DOT4_ILP adds for templates of 16 or more rows)
  */
 #define XC_NCC_AUTO 0
 #define XC_NCC_DOT4_ILP 1
 #define XC_NCC_DOT4_C1 2
 #define XC_NCC_SCALAR_C1 3
 #define XC_NCC_MFMA 4
+#define XC_NCC_DOT4_ILP_Q1 5
+#define XC_NCC_DOT4_ILP_Q2 6
+#define XC_NCC_DOT4_ILP_Q4 7
 int ncc_u8_run_variant(const uint8_t *image, int width, int height, int pitch_bytes,
                        const uint8_t *tmpl, int t_width, int t_height,
                        uint32_t *sum_i, uint32_t *sum_isq, uint32_t *sum_it, float *coef,

@@ -26,6 +26,14 @@ def test_header_symbols_exported():
         assert hasattr(lib, n), n
 
 
+def test_header_constants_match_binding():
+    """Every XC_ constant the header defines has the same value in the binding."""
+    found = re.findall(r"^#define (XC_\w+) \(?(-?\d+)\)?", open(HEADER).read(), re.M)
+    assert len(found) >= 20
+    for name, value in found:
+        assert getattr(_lib, name) == int(value), name
+
+
 def test_status_strings():
     for code in range(0, -8, -1):
         assert _lib.status_str(code) and _lib.status_str(code) != "unknown status"
@@ -49,6 +57,8 @@ FAKE = 1 << 20  # a 16-byte aligned non-null address; never dereferenced (valida
     (dict(pitch=72), _lib.XC_ERR_ALIGN),
     (dict(coef=FAKE + 2), _lib.XC_ERR_ALIGN),
     (dict(variant=42), _lib.XC_ERR_VARIANT),
+    (dict(variant=_lib.XC_NCC_DOT4_ILP_Q4 + 1), _lib.XC_ERR_VARIANT),
+    (dict(variant=-1), _lib.XC_ERR_VARIANT),
 ])
 def test_ncc_validation(args, expect):
     a = dict(image=FAKE, width=64, height=64, pitch=64, tmpl=FAKE, t_width=8, t_height=8,

@@ -13,7 +13,8 @@ import _gpu
 
 pytestmark = pytest.mark.gpu
 
-VARIANTS = [_lib.XC_NCC_AUTO, _lib.XC_NCC_DOT4_ILP, _lib.XC_NCC_DOT4_C1, _lib.XC_NCC_SCALAR_C1, _lib.XC_NCC_MFMA]
+VARIANTS = [_lib.XC_NCC_AUTO, _lib.XC_NCC_DOT4_ILP, _lib.XC_NCC_DOT4_C1, _lib.XC_NCC_SCALAR_C1, _lib.XC_NCC_MFMA,
+            _lib.XC_NCC_DOT4_ILP_Q1, _lib.XC_NCC_DOT4_ILP_Q2, _lib.XC_NCC_DOT4_ILP_Q4]
 # template rows the matrix-core variant takes
 MFMA_MAX_T_WIDTH = 256
 
@@ -46,7 +47,8 @@ def test_ncc_1080p_t64_full():
     assert res["coef"][oy, ox] == np.float32(1.0)
 
 
-@pytest.mark.parametrize("variant", [_lib.XC_NCC_DOT4_ILP, _lib.XC_NCC_DOT4_C1, _lib.XC_NCC_SCALAR_C1, _lib.XC_NCC_MFMA])
+@pytest.mark.parametrize("variant", [_lib.XC_NCC_DOT4_ILP, _lib.XC_NCC_DOT4_C1, _lib.XC_NCC_SCALAR_C1, _lib.XC_NCC_MFMA,
+                                     _lib.XC_NCC_DOT4_ILP_Q1, _lib.XC_NCC_DOT4_ILP_Q2, _lib.XC_NCC_DOT4_ILP_Q4])
 def test_ncc_1080p_variants_sampled(variant):
     """Ablation variants at full size: compare against the auto path bit for bit."""
     case = workload("ncc_1920x1080_t64")

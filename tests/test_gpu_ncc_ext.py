@@ -18,6 +18,9 @@ VARIANTS = {
     "c1": _lib.XC_NCC_DOT4_C1,
     "scalar": _lib.XC_NCC_SCALAR_C1,
     "mfma": _lib.XC_NCC_MFMA,
+    "ilp_q1": _lib.XC_NCC_DOT4_ILP_Q1,
+    "ilp_q2": _lib.XC_NCC_DOT4_ILP_Q2,
+    "ilp_q4": _lib.XC_NCC_DOT4_ILP_Q4,
 }
 
 
