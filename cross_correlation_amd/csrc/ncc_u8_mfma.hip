@@ -75,13 +75,18 @@ struct MfPlan {
     size_t bytes;
 };
 
+// LDS row strides for NKB 64-byte template blocks (compile-time in the
+// kernels, so consecutive rows are immediate offsets of one address)
+__host__ __device__ constexpr int mf_sw(int nkb) { return 64 + 16 * nkb + 4; }
+__host__ __device__ constexpr int mf_tsb(int nkb) { return 64 * nkb + 16; }
+
 __host__ __device__ inline MfPlan mf_plan(int t_width, int hc)
 {
     MfPlan p;
     p.nkb = (t_width + 63) / 64;
     p.hc = hc;
-    p.sw = 64 + 16 * p.nkb + 4;
-    p.tsb = 64 * p.nkb + 16;
+    p.sw = mf_sw(p.nkb);
+    p.tsb = mf_tsb(p.nkb);
     p.trows = hc + 2 * MF_TY - 1;
     p.nwd = 64 + (t_width + 2) / 4;  // words holding columns 0 .. 255 + t_width - 1
     p.vs = 4 * p.nwd + 4;
@@ -203,9 +208,10 @@ __device__ __forceinline__ void mf_col_add(uint32_t biased, uint32_t (&c)[4])
 // LDS words read while the current row's products issue (the read after the
 // last row lands in the spare row each LDS area keeps).
 template <int NKB>
-__device__ __forceinline__ void mf_walk_chunk(const uint32_t *img, int sw, const uint8_t *tpl, int tsb, int hcur,
-                                              int wave, mf_v4i (&at)[4])
+__device__ __forceinline__ void mf_walk_chunk(const uint32_t *img, const uint8_t *tpl, int hcur, int wave,
+                                              mf_v4i (&at)[4])
 {
+    constexpr int sw = mf_sw(NKB), tsb = mf_tsb(NKB);
     const int lane = threadIdx.x & 63;
     const int m = lane & 15, g = lane >> 4;
     // A: output column x0 + 64*wave + 4m + t reads image words from 16*wave + m
@@ -463,7 +469,7 @@ void ncc_u8_mfma_kernel(NccArgs a)
         mf_stage_template(a.tmpl, tw, j0, hcur, 64 * NKB, tpl, P.tsb, P.trows);
         __syncthreads();
         if (wave < MF_MMA_WAVES) {
-            mf_walk_chunk<NKB>(img, P.sw, tpl, P.tsb, hcur, wave, at);
+            mf_walk_chunk<NKB>(img, tpl, hcur, wave, at);
         } else {
             // the column-sum waves issue first on their SIMD: the matrix
             // waves lose little (their products keep the matrix cores busy)
