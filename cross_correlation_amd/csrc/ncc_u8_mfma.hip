@@ -267,10 +267,11 @@ __device__ __forceinline__ void mf_walk_chunk(const uint32_t *img, const uint8_t
 // save_head the raw words of the first MF_TY - 1 absolute rows go to `head`
 // for the sliding pass of the last chunk (only when `keep`: lanes past their
 // wave's words read a clamped word and store nothing).
-template <int F>
-__device__ __forceinline__ void mf_col_walk(const uint32_t *img, int sw, int hcur, int j0, bool save_head,
-                                            uint32_t *head, int nwd, int wd, bool keep, uint32_t (&c)[4])
+template <int NKB, int F>
+__device__ __forceinline__ void mf_col_walk(const uint32_t *img, int hcur, int j0, bool save_head, uint32_t *head,
+                                            int nwd, int wd, bool keep, uint32_t (&c)[4])
 {
+    constexpr int sw = mf_sw(NKB);
     const uint32_t *p = img + wd;
     constexpr int U = 4;
     int rr = 0;
@@ -296,11 +297,11 @@ __device__ __forceinline__ void mf_col_walk(const uint32_t *img, int sw, int hcu
 // chunk) and drops absolute row n - 1 (tile row n - 1 when the template came
 // in one chunk, else the saved head row).  Rows n = 0 .. MF_TY - 1 go to V
 // (row stride vs) when `keep`; reads are unconditional.
-template <int F>
-__device__ __forceinline__ void mf_slide_word(const uint32_t *img, int sw, int hcur, bool one_chunk,
-                                              const uint32_t *head, int nwd, int wd, bool keep, uint32_t *V, int vs,
-                                              uint32_t (&c)[4])
+template <int NKB, int F>
+__device__ __forceinline__ void mf_slide_word(const uint32_t *img, int hcur, bool one_chunk, const uint32_t *head,
+                                              int nwd, int wd, bool keep, uint32_t *V, int vs, uint32_t (&c)[4])
 {
+    constexpr int sw = mf_sw(NKB);
     uint32_t in[MF_TY - 1], out[MF_TY - 1];
 #pragma unroll
     for (int n = 1; n < MF_TY; ++n) {
@@ -404,17 +405,17 @@ __device__ __forceinline__ void mf_row_prefix(uint32_t *V, int vs, int ncols)
 // last chunk only).  The prefix runs over the wave's own columns
 // [4*w0, 4*(w0 + cnt)), starting from zero.
 template <int NKB, int F>
-__device__ __forceinline__ void mf_field_chunk(const uint32_t *img, int sw, int hcur, int j0, bool last,
-                                               bool one_chunk, uint32_t *head, int nwd, int w0, int cnt,
-                                               uint32_t *V, int vs, uint32_t (&c)[4])
+__device__ __forceinline__ void mf_field_chunk(const uint32_t *img, int hcur, int j0, bool last, bool one_chunk,
+                                               uint32_t *head, int nwd, int w0, int cnt, uint32_t *V, int vs,
+                                               uint32_t (&c)[4])
 {
     const int lane = threadIdx.x & 63;
     const int wd = w0 + min(lane, cnt - 1);
     const bool keep = lane < cnt;
-    mf_col_walk<F>(img, sw, hcur, j0, !one_chunk, head, nwd, wd, keep, c);
+    mf_col_walk<NKB, F>(img, hcur, j0, !one_chunk, head, nwd, wd, keep, c);
     if (!last)
         return;
-    mf_slide_word<F>(img, sw, hcur, one_chunk, head, nwd, wd, keep, V, vs, c);
+    mf_slide_word<NKB, F>(img, hcur, one_chunk, head, nwd, wd, keep, V, vs, c);
     // the slide's stores (other lanes' columns) before the scan's reads
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
     __builtin_amdgcn_wave_barrier();
@@ -493,9 +494,9 @@ void ncc_u8_mfma_kernel(NccArgs a)
                         tq = dot4u(w, w, tq);
                     }
                 }
-                mf_field_chunk<NKB, 0>(img, P.sw, hcur, j0, last, one_chunk, head, P.nwd, w0, cnt, V1, P.vs, c);
+                mf_field_chunk<NKB, 0>(img, hcur, j0, last, one_chunk, head, P.nwd, w0, cnt, V1, P.vs, c);
             } else {
-                mf_field_chunk<NKB, 1>(img, P.sw, hcur, j0, last, one_chunk, head, P.nwd, w0, cnt, V2, P.vs, c);
+                mf_field_chunk<NKB, 1>(img, hcur, j0, last, one_chunk, head, P.nwd, w0, cnt, V2, P.vs, c);
             }
             __builtin_amdgcn_s_setprio(0);
         }
