@@ -23,15 +23,16 @@
 //     the products is against zero rows.
 //   * SumI and SumISq: while four waves of the workgroup run the matrix
 //     cores, four more walk the tile's image words (4 columns each) down the
-//     template's rows, keeping running sums per column of pixels (two waves,
-//     half of the words each) and of squares (two more): the window of output
-//     row 0.  Each then slides its window down the 16 output rows (add the
+//     template's rows, keeping running sums per column of the biased pixels
+//     s = I - 128 (two waves, half of the words each) and of s^2 (two more),
+//     with signed v_dot4 on the staged bytes: the window of output row 0.  Each then slides its window down the 16 output rows (add the
 //     row entering, remove the row leaving; the tile's first 15 rows are kept
 //     for that when the template comes in several chunks) and takes prefix
 //     sums along each row of its half, so a window sum is the difference of
 //     two entries (plus the first half's row total where a window spans both
-//     halves).  All unsigned 32-bit, exact because every final sum is below
-//     2^32.
+//     halves).  SumI = sum s + 128 N and SumISq = sum s^2 + 256 SumI -
+//     16384 N, all in wrapping 32-bit arithmetic, exact because every final
+//     sum is below 2^32.
 //   * The coefficient follows the packed-byte kernels' exact formula: num, vI
 //     and vT are exact integers (held in fp64 here, formed with fused
 //     multiply-adds), then an IEEE fp64 divide and square root and one fp32
@@ -191,15 +192,18 @@ __device__ __forceinline__ void mf_stage_template(const uint8_t *__restrict__ tm
     }
 }
 
-// Column sums of field F over one image word (4 columns), into c[0..3]:
-// F = 0 adds the pixels, F = 1 their squares.
+// Column sums of field F over one staged image word (4 columns of biased
+// pixels s = I - 128, signed bytes), into c[0..3]: F = 0 adds s, F = 1 adds
+// s^2 (v_dot4_i32_i8, wrapping 32-bit sums).  The epilogue recovers
+// SumI = sum s + 128 N and SumISq = sum s^2 + 256 SumI - 16384 N exactly.
 template <int F>
 __device__ __forceinline__ void mf_col_add(uint32_t biased, uint32_t (&c)[4])
 {
-    const uint32_t w = biased ^ 0x80808080u;
 #pragma unroll
     for (int k = 0; k < 4; ++k)
-        c[k] = F == 0 ? dot4u(w, 1u << (8 * k), c[k]) : dot4u(w & (0xFFu << (8 * k)), w, c[k]);
+        c[k] = (uint32_t)__builtin_amdgcn_sdot4(
+            F == 0 ? (int)biased : (int)(biased & (0xFFu << (8 * k))), F == 0 ? (int)(1u << (8 * k)) : (int)biased,
+            (int)c[k], false);
 }
 
 // The matrix-core walk of one template-row chunk for one wave: every image
@@ -550,8 +554,9 @@ void ncc_u8_mfma_kernel(NccArgs a)
         const uint32_t join_keep = hi >= ce && (x == 0 || x - 1 < ce) ? 0xFFFFFFFFu : 0u;
         const uint32_t *q1 = V1 + n * P.vs;
         const uint32_t *q2 = V2 + n * P.vs;
-        const uint32_t si = q1[hi] - (q1[xl] & left_keep) + (q1[ce - 1] & join_keep);
-        const uint32_t sq = q2[hi] - (q2[xl] & left_keep) + (q2[ce - 1] & join_keep);
+        // the column sums are of s = I - 128 and of s^2
+        const uint32_t si = q1[hi] - (q1[xl] & left_keep) + (q1[ce - 1] & join_keep) + 128u * nn;
+        const uint32_t sq = q2[hi] - (q2[xl] & left_keep) + (q2[ce - 1] & join_keep) + 256u * si - 16384u * nn;
         const uint32_t st = (uint32_t)acc_it[n * MF_ACC_STRIDE + x] + 128u * si + bias;
         if (a.sum_i) a.sum_i[o] = si;
         if (a.sum_isq) a.sum_isq[o] = sq;
