@@ -10,6 +10,11 @@ Functions follow the definitions cited in ``oracle.c``:
 * :func:`ncc_u8` -- u8 normalized correlation, "The CUDA Handbook" section
   15.5 "Instruction-Level Parallelism and DP4A" (the SumI / SumISq / SumIT
   accumulators over unsigned 8-bit pixels), coefficient read as Pearson's r.
+* :func:`ncc_u8_mode` -- the same correlation over other output domains: the
+  pages define the windows inside the image only; "same" and "full" read
+  pixels outside the image as 0 (counted among the window's pixels), the
+  zero-padding convention of scipy.signal.correlate2d, i.e. the valid-mode
+  definition applied to the image with zero borders.
 * :func:`ncc_peak` -- the best match of a coefficient map (first entry, in
   row-major order, holding the maximum), the usual last step of template
   matching.
@@ -148,6 +153,37 @@ def ncc_u8(image: np.ndarray, width: int, height: int, tmpl: np.ndarray, *,
     if st != ORACLE_OK:
         raise ValueError(f"oracle_ncc_u8_rows: bad arguments (status {st})")
     return res
+
+
+MODE_VALID, MODE_SAME, MODE_FULL = 0, 1, 2
+
+
+def ncc_mode_geometry(width: int, height: int, t_width: int, t_height: int, mode: int):
+    """(out_h, out_w, pad_top, pad_left) of an output mode: output (y, x) is
+    the window whose top-left pixel is (y - pad_top, x - pad_left)."""
+    if mode == MODE_VALID:
+        return height - t_height + 1, width - t_width + 1, 0, 0
+    if mode == MODE_SAME:
+        return height, width, (t_height - 1) // 2, (t_width - 1) // 2
+    if mode == MODE_FULL:
+        return height + t_height - 1, width + t_width - 1, t_height - 1, t_width - 1
+    raise ValueError(f"unknown mode {mode}")
+
+
+def ncc_u8_mode(image: np.ndarray, width: int, height: int, tmpl: np.ndarray, mode: int, *,
+                nthreads: int = 0, lib=None) -> dict:
+    """u8 normalized correlation in an output mode, written out as its
+    definition: the image placed at (pad_top, pad_left) of a zero image large
+    enough for every window of the mode, then the valid-mode oracle on it
+    (so outside pixels are 0 and count among the window's pixels)."""
+    image, tmpl = _image_args(image, width, height, tmpl)
+    th, tw = tmpl.shape
+    if mode == MODE_VALID:
+        return ncc_u8(image, width, height, tmpl, nthreads=nthreads, lib=lib)
+    out_h, out_w, pt, pl = ncc_mode_geometry(width, height, tw, th, mode)
+    padded = np.zeros((out_h + th - 1, out_w + tw - 1), dtype=np.uint8)
+    padded[pt:pt + height, pl:pl + width] = image[:, :width]
+    return ncc_u8(padded, padded.shape[1], padded.shape[0], tmpl, nthreads=nthreads, lib=lib)
 
 
 def ncc_u8_points(image: np.ndarray, width: int, height: int, tmpl: np.ndarray,

@@ -283,6 +283,49 @@ def pin_peak_cut(lib=None):
         assert (y, x) == case.cut and v == 1.0
 
 
+def pin_modes_scipy(lib=None):
+    """Same and full modes: SumIT, SumI and SumISq equal
+    scipy.signal.correlate2d of the image with the template, with a template
+    of ones, and of the squared image with ones, in that mode (zero padding,
+    scipy's anchoring), for odd and even template sizes and for templates
+    larger than the image."""
+    import scipy.signal as ss
+    rng = np.random.default_rng(140)
+    for (h, w, th, tw) in ((9, 13, 3, 4), (10, 8, 4, 5), (6, 7, 6, 7), (5, 6, 7, 9), (1, 9, 1, 4), (12, 5, 2, 2)):
+        img = u8_uniform(rng, (h, w))
+        tmpl = u8_uniform(rng, (th, tw))
+        ones = np.ones((th, tw), dtype=np.int64)
+        i64 = img.astype(np.int64)
+        for mode, name in ((oracle.MODE_SAME, "same"), (oracle.MODE_FULL, "full")):
+            r = oracle.ncc_u8_mode(_pad(img), w, h, tmpl, mode, lib=lib)
+            assert np.array_equal(r["sum_it"].astype(np.int64), ss.correlate2d(i64, tmpl.astype(np.int64), name)), name
+            assert np.array_equal(r["sum_i"].astype(np.int64), ss.correlate2d(i64, ones, name)), name
+            assert np.array_equal(r["sum_isq"].astype(np.int64), ss.correlate2d(i64 * i64, ones, name)), name
+
+
+def pin_modes_contain_valid(lib=None):
+    """The full-mode output at (y + th - 1, x + tw - 1) and the same-mode
+    output at (y + (th - 1)/2, x + (tw - 1)/2) are the valid-mode output at
+    (y, x), all four quantities; the full-mode corner (0, 0) is the window
+    holding only pixel (0, 0), against the template's last pixel."""
+    rng = np.random.default_rng(141)
+    img = u8_uniform(rng, (23, 31))
+    tmpl = u8_uniform(rng, (6, 9))
+    th, tw = tmpl.shape
+    v = _run(img, tmpl, lib)
+    f = oracle.ncc_u8_mode(_pad(img), 31, 23, tmpl, oracle.MODE_FULL, lib=lib)
+    s = oracle.ncc_u8_mode(_pad(img), 31, 23, tmpl, oracle.MODE_SAME, lib=lib)
+    vh, vw = v["sum_i"].shape
+    for k in ("sum_i", "sum_isq", "sum_it", "coef"):
+        assert np.array_equal(f[k][th - 1:th - 1 + vh, tw - 1:tw - 1 + vw], v[k]), k
+        a, b = (th - 1) // 2, (tw - 1) // 2
+        assert np.array_equal(s[k][a:a + vh, b:b + vw], v[k]), k
+    p = int(img[0, 0])
+    assert int(f["sum_i"][0, 0]) == p and int(f["sum_isq"][0, 0]) == p * p
+    assert int(f["sum_it"][0, 0]) == p * int(tmpl[th - 1, tw - 1])
+    assert f["sum_i"].shape == (23 + th - 1, 31 + tw - 1) and s["sum_i"].shape == (23, 31)
+
+
 ALL_PINS = [
     pin_hand_worked,
     pin_sums_bruteforce,
@@ -300,4 +343,6 @@ ALL_PINS = [
     pin_cut_template_any_width,
     pin_peak_argmax,
     pin_peak_cut,
+    pin_modes_scipy,
+    pin_modes_contain_valid,
 ]
