@@ -185,9 +185,11 @@ def bench_ncc(args, torch, lib, inputs, variant=0, steps=None, warmup=None):
 
 def bench_ncc_ext(args, torch, lib, inputs):
     """The generalizations on the headline image: the best-match search
-    (ncc_u8_peak, with and without the coefficient map) and a template width
+    (ncc_u8_peak, with and without the coefficient map), a template width
     that is not a multiple of four (63 x 63, the last packed word of each
-    template row masked), next to the 64 x 64 template."""
+    template row masked), next to the 64 x 64 template, and the same and full
+    output modes (ncc_u8_run_mode: the zero-padded copy, then the automatic
+    variant; all four outputs)."""
     from cross_correlation_amd.inputs import ncc_case
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream().cuda_stream
@@ -226,6 +228,24 @@ def bench_ncc_ext(args, torch, lib, inputs):
         dot4 = 3 * ((odd.t_width + 3) // 4) * odd.t_height * oh63 * ow63
         res[f"t63x63_{vname}"] = {"kernel_ms": round(per, 5), "outputs_per_s": round(oh63 * ow63 / (per * 1e-3), 1),
                                   "issued_Gdot4_per_s": round(dot4 / (per * 1e-3) / 1e9, 2)}
+    for mname, mode in (("same_mode", lib.XC_NCC_MODE_SAME), ("full_mode", lib.XC_NCC_MODE_FULL)):
+        st, nbytes = lib.ncc_u8_mode_workspace(case.width, case.height, case.t_width, case.t_height, mode)
+        if st != 0:
+            raise RuntimeError(lib.status_str(st))
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        moh, mow = lib.ncc_mode_shape(case.width, case.height, case.t_width, case.t_height, mode)
+        mouts = [torch.empty((moh, mow), dtype=torch.int32, device=dev) for _ in range(3)]
+        mcoef = torch.empty((moh, mow), dtype=torch.float32, device=dev)
+
+        def launch():
+            st = lib.ncc_u8_run_mode(img.data_ptr(), case.width, case.height, case.pitch, tm.data_ptr(),
+                                     case.t_width, case.t_height, mode, ws.data_ptr(), nbytes, mouts[0].data_ptr(),
+                                     mouts[1].data_ptr(), mouts[2].data_ptr(), mcoef.data_ptr(), stream=stream)
+            if st != 0:
+                raise RuntimeError(lib.status_str(st))
+        wall, per = timed_loop(launch, steps, warmup, torch)
+        res[mname] = {"launches_ms": round(per, 5), "out_shape": [moh, mow],
+                      "outputs_per_s": round(moh * mow / (per * 1e-3), 1)}
     return res
 
 

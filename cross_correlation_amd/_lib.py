@@ -31,6 +31,10 @@ XC_NCC_DOT4_ILP_Q1 = 5
 XC_NCC_DOT4_ILP_Q2 = 6
 XC_NCC_DOT4_ILP_Q4 = 7
 
+XC_NCC_MODE_VALID = 0
+XC_NCC_MODE_SAME = 1
+XC_NCC_MODE_FULL = 2
+
 XC_XCORR_AUTO = 0
 XC_XCORR_OVERLAP = 1
 XC_XCORR_BLOCKDIAG = 2
@@ -38,8 +42,8 @@ XC_XCORR_BLOCKDIAG = 2
 XC_NCC_MAX_TEMPLATE_PIXELS = 66051
 
 # Every symbol the public header declares.
-EXPORTED = ("ncc_u8_run", "ncc_u8_run_variant", "ncc_u8_peak", "xcorr_f32_run", "xcorr_f32_run_algo",
-            "xc_status_str")
+EXPORTED = ("ncc_u8_run", "ncc_u8_run_variant", "ncc_u8_peak", "ncc_u8_mode_workspace", "ncc_u8_run_mode",
+            "xcorr_f32_run", "xcorr_f32_run_algo", "xc_status_str")
 
 # xc_ncc_peak (include/xcorr.h): key u64, y i32, x i32, coef f32, reserved i32
 PEAK_BYTES = 24
@@ -75,6 +79,11 @@ def load(path: str = LIB_PATH):
     lib.ncc_u8_run_variant.argtypes = [_vp, _i, _i, _i, _vp, _i, _i, _vp, _vp, _vp, _vp, _i, _vp]
     lib.ncc_u8_peak.restype = _i
     lib.ncc_u8_peak.argtypes = [_vp, _i, _i, _i, _vp, _i, _i, _vp, _vp, _vp, _vp, _vp, _i, _vp]
+    lib.ncc_u8_mode_workspace.restype = _i
+    lib.ncc_u8_mode_workspace.argtypes = [_i, _i, _i, _i, _i, ctypes.POINTER(ctypes.c_size_t)]
+    lib.ncc_u8_run_mode.restype = _i
+    lib.ncc_u8_run_mode.argtypes = [_vp, _i, _i, _i, _vp, _i, _i, _i, _vp, ctypes.c_size_t, _vp, _vp, _vp, _vp, _i,
+                                    _vp]
     lib.xcorr_f32_run.restype = _i
     lib.xcorr_f32_run.argtypes = [_vp, _i, _vp, _i, _i, _i, _vp, _vp]
     lib.xcorr_f32_run_algo.restype = _i
@@ -109,6 +118,30 @@ def ncc_u8_peak(image, width, height, pitch, tmpl, t_width, t_height, sum_i, sum
     return load().ncc_u8_peak(image, width, height, pitch, tmpl, t_width, t_height,
                               sum_i or None, sum_isq or None, sum_it or None, coef or None, peak or None,
                               variant, stream or None)
+
+
+def ncc_u8_mode_workspace(width, height, t_width, t_height, mode) -> tuple[int, int]:
+    """(status, workspace bytes) for an output mode."""
+    n = ctypes.c_size_t(0)
+    st = load().ncc_u8_mode_workspace(width, height, t_width, t_height, mode, ctypes.byref(n))
+    return st, n.value
+
+
+def ncc_mode_shape(width, height, t_width, t_height, mode) -> tuple[int, int]:
+    """(out_h, out_w) of an output mode (include/xcorr.h, ncc_u8_run_mode)."""
+    if mode == XC_NCC_MODE_SAME:
+        return height, width
+    if mode == XC_NCC_MODE_FULL:
+        return height + t_height - 1, width + t_width - 1
+    return height - t_height + 1, width - t_width + 1
+
+
+def ncc_u8_run_mode(image, width, height, pitch, tmpl, t_width, t_height, mode, workspace, workspace_bytes,
+                    sum_i, sum_isq, sum_it, coef, stream=None, variant=XC_NCC_AUTO) -> int:
+    """Raw call with integer device addresses (0 for NULL); returns the status."""
+    return load().ncc_u8_run_mode(image, width, height, pitch, tmpl, t_width, t_height, mode, workspace or None,
+                                  workspace_bytes, sum_i or None, sum_isq or None, sum_it or None, coef or None,
+                                  variant, stream or None)
 
 
 def decode_peak(raw: bytes) -> tuple[int, int, float]:

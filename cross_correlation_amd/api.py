@@ -87,6 +87,43 @@ def ncc_u8_peak(image: torch.Tensor, tmpl: torch.Tensor, *, width: int | None = 
     return res
 
 
+def ncc_u8_mode(image: torch.Tensor, tmpl: torch.Tensor, mode: int, *, width: int | None = None,
+                outputs=("sum_i", "sum_isq", "sum_it", "coef"), variant: int = _lib.XC_NCC_AUTO,
+                out: dict | None = None, workspace: torch.Tensor | None = None, stream=None) -> dict:
+    """u8 normalized correlation in an output mode (``_lib.XC_NCC_MODE_*``):
+    valid, same or full, the last two over the image with zero borders.
+
+    Same inputs as :func:`ncc_u8`; ``workspace`` (a uint8 CUDA tensor of at
+    least ``_lib.ncc_u8_mode_workspace(...)`` bytes) is allocated here when
+    not given.  Returns the requested outputs, each [out_h, out_w].
+    """
+    _device_u8(image, "image")
+    _device_u8(tmpl, "tmpl")
+    if image.dim() != 2 or image.stride(1) != 1 or tmpl.dim() != 2 or not tmpl.is_contiguous():
+        raise ValueError("image must be 2D with unit column stride; tmpl must be 2D contiguous")
+    height, pitch = image.shape[0], image.stride(0)
+    width = image.shape[1] if width is None else width
+    th, tw = tmpl.shape
+    st, nbytes = _lib.ncc_u8_mode_workspace(width, height, tw, th, mode)
+    _lib.check(st, "ncc_u8_mode_workspace")
+    if workspace is None and nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=image.device)
+    oh, ow = _lib.ncc_mode_shape(width, height, tw, th, mode)
+    if out is None:
+        out = {}
+        for k in outputs:
+            dt = torch.float32 if k == "coef" else torch.int32
+            out[k] = torch.empty((max(oh, 0), max(ow, 0)), dtype=dt, device=image.device)
+    ptr = {k: (out[k].data_ptr() if k in out else 0) for k in ("sum_i", "sum_isq", "sum_it", "coef")}
+    ws_ptr = workspace.data_ptr() if workspace is not None else 0
+    ws_bytes = workspace.numel() if workspace is not None else 0
+    st = _lib.ncc_u8_run_mode(image.data_ptr(), width, height, pitch, tmpl.data_ptr(), tw, th, mode, ws_ptr,
+                              ws_bytes, ptr["sum_i"], ptr["sum_isq"], ptr["sum_it"], ptr["coef"],
+                              _stream_handle(stream), variant)
+    _lib.check(st, "ncc_u8_run_mode")
+    return out
+
+
 def xcorr_f32(left: torch.Tensor, right: torch.Tensor, *, algo: int = _lib.XC_XCORR_AUTO,
               out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """Full cross-correlation of every (left, right) pair.

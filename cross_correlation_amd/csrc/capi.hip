@@ -54,6 +54,47 @@ int ncc_validate(const uint8_t *image, int width, int height, int pitch_bytes, c
     return XC_OK;
 }
 
+// Geometry of an output mode: the output size, and the zero-padded image the
+// valid-mode kernels run on (the image placed at (pad_top, pad_left)).
+struct NccModeGeom {
+    int out_w, out_h;        // output size
+    int pw, ph, ppitch;      // padded image: width, height, pitch in bytes
+    int pad_top, pad_left;   // where the image sits in it
+    size_t bytes;            // workspace: ph * ppitch
+};
+
+int ncc_mode_geom(int width, int height, int t_width, int t_height, int mode, NccModeGeom &g)
+{
+    if (mode != XC_NCC_MODE_VALID && mode != XC_NCC_MODE_SAME && mode != XC_NCC_MODE_FULL)
+        return XC_ERR_VARIANT;
+    if (width <= 0 || height <= 0 || t_width <= 0 || t_height <= 0)
+        return XC_ERR_SHAPE;
+    if ((int64_t)t_width * t_height > XC_NCC_MAX_TEMPLATE_PIXELS)
+        return XC_ERR_OVERFLOW;
+    int64_t ow, oh, pl, pt;
+    if (mode == XC_NCC_MODE_VALID) {
+        if (t_width > width || t_height > height)
+            return XC_ERR_SHAPE;
+        ow = width - t_width + 1, oh = height - t_height + 1, pl = pt = 0;
+    } else if (mode == XC_NCC_MODE_SAME) {
+        ow = width, oh = height, pl = (t_width - 1) / 2, pt = (t_height - 1) / 2;
+    } else {
+        ow = (int64_t)width + t_width - 1, oh = (int64_t)height + t_height - 1, pl = t_width - 1, pt = t_height - 1;
+    }
+    const int64_t pw = ow + t_width - 1, ph = oh + t_height - 1, pp = (pw + 15) / 16 * 16;
+    if (ow * oh > INT32_MAX || pp > INT32_MAX || ph > INT32_MAX || ph * pp > ((int64_t)1 << 40))
+        return XC_ERR_OVERFLOW;
+    g.out_w = (int)ow;
+    g.out_h = (int)oh;
+    g.pw = (int)pw;
+    g.ph = (int)ph;
+    g.ppitch = (int)pp;
+    g.pad_top = (int)pt;
+    g.pad_left = (int)pl;
+    g.bytes = mode == XC_NCC_MODE_VALID ? 0 : (size_t)(ph * pp);
+    return XC_OK;
+}
+
 int xcorr_validate(const float *left, int n_left, const float *right, int n_right, int rows, int cols,
                    float *out, xc::XcorrArgs &a)
 {
@@ -168,6 +209,52 @@ int ncc_u8_peak(const uint8_t *image, int width, int height, int pitch_bytes, co
     if ((st = ncc_dispatch(a, variant, s)) != XC_OK)
         return st;
     return hip_status(xc::ncc_peak_finish(peak, a.out_w, s));
+}
+
+int ncc_u8_mode_workspace(int width, int height, int t_width, int t_height, int mode, size_t *bytes)
+{
+    if (!bytes)
+        return XC_ERR_NULL;
+    NccModeGeom g;
+    const int st = ncc_mode_geom(width, height, t_width, t_height, mode, g);
+    if (st != XC_OK)
+        return st;
+    *bytes = g.bytes;
+    return XC_OK;
+}
+
+int ncc_u8_run_mode(const uint8_t *image, int width, int height, int pitch_bytes, const uint8_t *tmpl, int t_width,
+                    int t_height, int mode, void *workspace, size_t workspace_bytes, uint32_t *sum_i,
+                    uint32_t *sum_isq, uint32_t *sum_it, float *coef, int variant, void *stream)
+{
+    if (mode == XC_NCC_MODE_VALID)
+        return ncc_u8_run_variant(image, width, height, pitch_bytes, tmpl, t_width, t_height, sum_i, sum_isq, sum_it,
+                                  coef, variant, stream);
+    NccModeGeom g;
+    int st = ncc_mode_geom(width, height, t_width, t_height, mode, g);
+    if (st != XC_OK)
+        return st;
+    if (!image || !tmpl || !workspace)
+        return XC_ERR_NULL;
+    if (pitch_bytes < width || (int64_t)height * pitch_bytes > ((int64_t)1 << 40))
+        return XC_ERR_SHAPE;
+    if (!aligned(image, 16) || pitch_bytes % 16 != 0 || !aligned(workspace, 16))
+        return XC_ERR_ALIGN;
+    if (workspace_bytes < g.bytes)
+        return XC_ERR_SHAPE;
+    // the valid-mode computation on the padded image, which lives in the workspace
+    uint8_t *const padded = static_cast<uint8_t *>(workspace);
+    xc::NccArgs a;
+    st = ncc_validate(padded, g.pw, g.ph, g.ppitch, tmpl, t_width, t_height, sum_i, sum_isq, sum_it, coef, true, a);
+    if (st != XC_OK)
+        return st;
+    if ((st = ncc_variant_ok(a, variant)) != XC_OK)
+        return st;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if ((st = hip_status(xc::ncc_pad_image(image, width, height, pitch_bytes, padded, g.pw, g.ph, g.ppitch, g.pad_top,
+                                           g.pad_left, s))) != XC_OK)
+        return st;
+    return ncc_dispatch(a, variant, s);
 }
 
 int ncc_u8_run(const uint8_t *image, int width, int height, int pitch_bytes, const uint8_t *tmpl, int t_width,

@@ -60,6 +60,11 @@ bool ncc_mfma_supported(const NccArgs &a);
 // decode the key into (y, x, coefficient) after it.  `peak` points to an
 // xc_ncc_peak (include/xcorr.h).
 hipError_t ncc_peak_init(void *peak, hipStream_t s);
+// Zero-padded copy of an image for the same and full output modes:
+// out[r][c] = image[r - pad_top][c - pad_left] where that pixel exists, else
+// 0, for r < out_h and c < out_pitch (out_pitch a multiple of 16).
+hipError_t ncc_pad_image(const uint8_t *image, int width, int height, int pitch, uint8_t *out, int out_w, int out_h,
+                         int out_pitch, int pad_top, int pad_left, hipStream_t s);
 hipError_t ncc_peak_finish(void *peak, int out_w, hipStream_t s);
 
 // Arguments of the fp32 cross-correlation kernels (validated on the host).

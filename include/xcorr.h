@@ -37,6 +37,7 @@
 #ifndef XCORR_MI355X_H
 #define XCORR_MI355X_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -51,7 +52,7 @@ extern "C" {
 #define XC_ERR_OVERFLOW (-4)       /* sums could wrap 32 bits, or an index range is exceeded    */
 #define XC_ERR_ALIGN (-5)          /* a base pointer or the pitch is not 16-byte aligned        */
 #define XC_ERR_HIP (-6)            /* HIP launch or runtime error (including: no device)        */
-#define XC_ERR_VARIANT (-7)        /* unknown variant / algorithm selector                      */
+#define XC_ERR_VARIANT (-7)        /* unknown variant / algorithm / output-mode selector        */
 
 /* Largest template area for which the u32 sums cannot wrap: N * 255^2 < 2^32. */
 #define XC_NCC_MAX_TEMPLATE_PIXELS 66051
@@ -153,6 +154,44 @@ int ncc_u8_peak(const uint8_t *image, int width, int height, int pitch_bytes,
                 const uint8_t *tmpl, int t_width, int t_height,
                 uint32_t *sum_i, uint32_t *sum_isq, uint32_t *sum_it, float *coef,
                 xc_ncc_peak *peak, int variant, void *stream);
+
+/*
+ * ncc_u8_run_mode -- the 8-bit normalized correlation with a choice of output
+ * domain.  The pages define only the windows inside the image (valid mode);
+ * same and full modes follow the zero-padding convention of
+ * scipy.signal.correlate2d: pixels outside the image are 0 and count among
+ * the window's N = t_width * t_height pixels, so every output is the valid-mode
+ * result on the image with zero borders.
+ *   XC_NCC_MODE_VALID  out_h x out_w = (height - t_height + 1) x (width - t_width + 1);
+ *                      output (y, x) is the window with top-left pixel (y, x)
+ *                      (what ncc_u8_run computes; no workspace)
+ *   XC_NCC_MODE_SAME   out_h x out_w = height x width; window top-left
+ *                      (y - (t_height - 1) / 2, x - (t_width - 1) / 2)
+ *   XC_NCC_MODE_FULL   out_h x out_w = (height + t_height - 1) x (width + t_width - 1);
+ *                      window top-left (y - t_height + 1, x - t_width + 1)
+ * In same and full modes the template may be larger than the image.
+ *
+ * ncc_u8_mode_workspace stores in *bytes the workspace a mode needs for these
+ * sizes (0 for valid mode), or returns the error the shape would get.
+ * ncc_u8_run_mode takes the arguments of ncc_u8_run_variant plus the mode and
+ * a caller-owned DEVICE workspace of at least that many bytes, 16-byte
+ * aligned (NULL allowed in valid mode): a first launch copies the image into
+ * it with zero borders, the chosen variant then runs on that copy, both on
+ * `stream`.  Outputs are out_h x out_w dense row-major as above, with the
+ * coefficient rule of ncc_u8_run.  Errors: as ncc_u8_run_variant, plus
+ * XC_ERR_VARIANT for an unknown mode, XC_ERR_NULL for a missing workspace,
+ * XC_ERR_ALIGN for a misaligned one and XC_ERR_SHAPE for one too small.
+ * Concurrent calls must not share a workspace.
+ */
+#define XC_NCC_MODE_VALID 0
+#define XC_NCC_MODE_SAME 1
+#define XC_NCC_MODE_FULL 2
+int ncc_u8_mode_workspace(int width, int height, int t_width, int t_height, int mode, size_t *bytes);
+int ncc_u8_run_mode(const uint8_t *image, int width, int height, int pitch_bytes,
+                    const uint8_t *tmpl, int t_width, int t_height, int mode,
+                    void *workspace, size_t workspace_bytes,
+                    uint32_t *sum_i, uint32_t *sum_isq, uint32_t *sum_it, float *coef,
+                    int variant, void *stream);
 
 /*
  * xcorr_f32_run -- fp32 full 2D cross-correlation of every (left, right) pair.

@@ -15,7 +15,7 @@ HEADER = os.path.join(ROOT, "include", "xcorr.h")
 
 def _declared():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:int|const char \*)\s*(\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|const char \*|size_t)\s*(\w+)\s*\(", text, re.M)))
 
 
 def test_header_symbols_exported():
@@ -109,3 +109,40 @@ def test_xcorr_validation(args, expect):
     st = _lib.xcorr_f32_run(a["left"], a["n_left"], a["right"], a["n_right"], a["rows"], a["cols"], a["out"],
                             None, a["algo"])
     assert st == expect, _lib.status_str(st)
+
+
+@pytest.mark.parametrize("args,expect", [
+    (dict(mode=3), _lib.XC_ERR_VARIANT),
+    (dict(mode=-1), _lib.XC_ERR_VARIANT),
+    (dict(workspace=0), _lib.XC_ERR_NULL),
+    (dict(workspace=FAKE + 8), _lib.XC_ERR_ALIGN),
+    (dict(workspace_bytes=100), _lib.XC_ERR_SHAPE),
+    (dict(image=FAKE + 4), _lib.XC_ERR_ALIGN),
+    (dict(pitch=32), _lib.XC_ERR_SHAPE),
+    (dict(t_width=300, t_height=300), _lib.XC_ERR_OVERFLOW),
+    (dict(sum_i=0, coef=0), _lib.XC_ERR_NULL),
+    (dict(variant=42), _lib.XC_ERR_VARIANT),
+    (dict(mode=0, t_width=80), _lib.XC_ERR_SHAPE),
+])
+def test_ncc_mode_validation(args, expect):
+    a = dict(image=FAKE, width=64, height=64, pitch=64, tmpl=FAKE, t_width=8, t_height=8, mode=1, workspace=FAKE,
+             workspace_bytes=1 << 20, sum_i=FAKE, coef=FAKE, variant=0)
+    a.update(args)
+    st = _lib.ncc_u8_run_mode(a["image"], a["width"], a["height"], a["pitch"], a["tmpl"], a["t_width"],
+                              a["t_height"], a["mode"], a["workspace"], a["workspace_bytes"], a["sum_i"], 0, 0,
+                              a["coef"], None, a["variant"])
+    assert st == expect, _lib.status_str(st)
+
+
+def test_ncc_mode_workspace_sizes():
+    """Workspace bytes: the padded image, rows of a 16-byte multiple pitch."""
+    for (w, h, tw, th, mode, expect) in ((64, 64, 8, 8, 0, 0),
+                                         (64, 64, 8, 8, 1, (64 + 7) * ((64 + 7 + 15) // 16 * 16)),
+                                         (64, 64, 8, 8, 2, (64 + 14) * ((64 + 14 + 15) // 16 * 16)),
+                                         (10, 12, 30, 20, 2, (12 + 38) * ((10 + 58 + 15) // 16 * 16))):
+        st, n = _lib.ncc_u8_mode_workspace(w, h, tw, th, mode)
+        assert st == 0 and n == expect, (w, h, tw, th, mode, n)
+    assert _lib.ncc_u8_mode_workspace(64, 64, 80, 8, 0)[0] == _lib.XC_ERR_SHAPE
+    assert _lib.ncc_u8_mode_workspace(64, 64, 80, 8, 1)[0] == 0  # same mode: larger templates allowed
+    assert _lib.ncc_u8_mode_workspace(64, 64, 8, 8, 5)[0] == _lib.XC_ERR_VARIANT
+    assert _lib.ncc_mode_shape(20, 10, 5, 3, _lib.XC_NCC_MODE_FULL) == (12, 24)
