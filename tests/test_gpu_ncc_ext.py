@@ -53,6 +53,24 @@ def test_ncc_any_template_width(shape):
         assert res["coef"][case.cut] == np.float32(1.0)
 
 
+# wide and tall templates on the matrix-core kernel: 3 and 4 template blocks
+# of 64 bytes (one workgroup per CU, up to 160 KiB of LDS) and template rows
+# in several chunks, so the column-sum waves slide from the saved head rows
+WIDE_TALL = [(300, 600, 250, 256), (280, 500, 200, 193), (120, 700, 100, 130), (200, 400, 150, 250)]
+
+
+@pytest.mark.parametrize("shape", WIDE_TALL, ids=[f"{s[0]}x{s[1]}_t{s[2]}x{s[3]}" for s in WIDE_TALL])
+def test_ncc_mfma_wide_tall_templates(shape):
+    h, w, th, tw = shape
+    case = ncc_case("t", 570 + tw, h, w, th, tw, cut=True)
+    ref = None
+    for name in ("mfma", "ilp", "auto"):
+        _gpu.log(f"ncc wide/tall {shape} variant {name}")
+        ref = _gpu.check_ncc(case, _gpu.run_ncc(case, variant=VARIANTS[name]), ref)
+    res = _gpu.run_ncc(case, variant=VARIANTS["mfma"], outputs=("coef",))
+    assert res["coef"][case.cut] == np.float32(1.0)
+
+
 def test_ncc_template_width_past_one_chunk():
     """3843 bytes: 961 packed words per row, so the packed-byte kernel's last
     template chunk holds the partial word alone."""
