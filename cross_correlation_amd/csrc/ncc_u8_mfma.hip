@@ -295,52 +295,10 @@ __device__ __forceinline__ void mf_col_walk(const uint32_t *img, int hcur, int j
             head[(j0 + rr) * nwd + wd] = p[rr * sw];
 }
 
-// The sliding pass of field F for word wd after the last chunk's walk: c holds
-// the column sums of absolute rows [0, th), i.e. output row 0's window.  Row
-// n's window adds absolute row n + th - 1 (tile row hcur + n - 1 of the last
-// chunk) and drops absolute row n - 1 (tile row n - 1 when the template came
-// in one chunk, else the saved head row).  Rows n = 0 .. MF_TY - 1 go to V
-// (row stride vs) when `keep`; reads are unconditional.
-template <int NKB, int F>
-__device__ __forceinline__ void mf_slide_word(const uint32_t *img, int hcur, bool one_chunk, const uint32_t *head,
-                                              int nwd, int wd, bool keep, uint32_t *V, int vs, uint32_t (&c)[4])
-{
-    constexpr int sw = mf_sw(NKB);
-    uint32_t in[MF_TY - 1], out[MF_TY - 1];
-#pragma unroll
-    for (int n = 1; n < MF_TY; ++n) {
-        in[n - 1] = img[(hcur + n - 1) * sw + wd];
-        out[n - 1] = one_chunk ? img[(n - 1) * sw + wd] : head[(n - 1) * nwd + wd];
-    }
-    if (keep)
-        *reinterpret_cast<uint4 *>(V + 4 * wd) = make_uint4(c[0], c[1], c[2], c[3]);
-#pragma unroll
-    for (int n = 1; n < MF_TY; ++n) {
-        uint32_t r[4] = {0u, 0u, 0u, 0u};
-        mf_col_add<F>(in[n - 1], c);
-        mf_col_add<F>(out[n - 1], r);
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            c[k] -= r[k];
-        if (keep)
-            *reinterpret_cast<uint4 *>(V + n * vs + 4 * wd) = make_uint4(c[0], c[1], c[2], c[3]);
-    }
-}
-
-// In-place inclusive prefix sums along the MF_TY rows of V (row stride vs)
-// over `ncols` columns, by one wave, half the rows at a time: lane l takes the
-// K contiguous columns [l*K, l*K + K) of a row (K odd, so the lanes' reads
-// fall in different banks; 64*K covers the widest half of NKB template
-// blocks).  Pass 1 sums each lane's columns for every row; one scan over the
-// lanes then serves all rows at once; pass 2 re-reads the columns,
-// scans them and adds the sum of the lanes before.  Reads are unconditional
-// (index clamped, value masked) so they are in flight together.  Each lane
-// writes only its own columns; the caller orders V's writers before and its
-// readers after.
 // Inclusive prefix sum over the 64 lanes of a wave in DPP moves: shifts by
 // 1, 2, 4 and 8 lanes within each row of 16 (lanes shifted in from outside
 // the row read 0), then lane 15's total added to rows 1 and 3 and lane 31's
-// to rows 2 and 3.
+// to rows 2 and 3.  Every lane of the wave must take part.
 __device__ __forceinline__ uint32_t mf_wave_scan(uint32_t v)
 {
     v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, true);   // row_shr:1
@@ -352,62 +310,57 @@ __device__ __forceinline__ uint32_t mf_wave_scan(uint32_t v)
     return v;
 }
 
-template <int NKB>
-__device__ __forceinline__ void mf_row_prefix_half(uint32_t *V, int vs, int ncols)
+// One row of a column-sum wave's prefix: lane l holds the column sums c of
+// word w0 + l, i.e. columns 4l .. 4l + 3 of the wave's half; the inclusive
+// prefix along the half at those columns is the sum over the lanes before
+// plus the running sum of c.  Lanes past the half (repeating its last word)
+// sit above every lane they could disturb.
+__device__ __forceinline__ uint4 mf_row_prefix4(const uint32_t (&c)[4])
 {
-    constexpr int K = ((4 * (32 + 8 * NKB) + 63) / 64) | 1;  // ncols <= 4 * ceil(nwd / 2)
-    constexpr int R = MF_TY / 2;
-    const int lane = threadIdx.x & 63;
-    const int c0 = lane * K;
-    uint32_t keep[K];  // all ones for the lane's columns inside the row
+    const uint32_t p1 = c[0] + c[1], p2 = p1 + c[2], t = p2 + c[3];
+    const uint32_t before = mf_wave_scan(t) - t;
+    return make_uint4(before + c[0], before + p1, before + p2, before + t);
+}
+
+// The sliding pass of field F for word wd after the last chunk's walk: c holds
+// the column sums of absolute rows [0, th), i.e. output row 0's window.  Row
+// n's window adds absolute row n + th - 1 (tile row hcur + n - 1 of the last
+// chunk) and drops absolute row n - 1 (tile row n - 1 when the template came
+// in one chunk, else the saved head row).  Each row's prefix along the wave's
+// half (mf_row_prefix4) goes to row n of V (row stride vs) when `keep`; reads
+// are unconditional and every lane takes part in the scans.
+template <int NKB, int F>
+__device__ __forceinline__ void mf_slide_word(const uint32_t *img, int hcur, bool one_chunk, const uint32_t *head,
+                                              int nwd, int wd, bool keep, uint32_t *V, int vs, uint32_t (&c)[4])
+{
+    constexpr int sw = mf_sw(NKB);
+    uint32_t in[MF_TY - 1], out[MF_TY - 1];
 #pragma unroll
-    for (int u = 0; u < K; ++u)
-        keep[u] = c0 + u < ncols ? 0xFFFFFFFFu : 0u;
-    uint32_t tot[R];
-#pragma unroll
-    for (int q = 0; q < R; ++q) {
-        uint32_t t = 0u;
-#pragma unroll
-        for (int u = 0; u < K; ++u)
-            t += V[q * vs + min(c0 + u, ncols - 1)] & keep[u];
-        tot[q] = t;
+    for (int n = 1; n < MF_TY; ++n) {
+        in[n - 1] = img[(hcur + n - 1) * sw + wd];
+        out[n - 1] = one_chunk ? img[(n - 1) * sw + wd] : head[(n - 1) * nwd + wd];
     }
-    uint32_t incl[R];
+    uint4 pre = mf_row_prefix4(c);
+    if (keep)
+        *reinterpret_cast<uint4 *>(V + 4 * wd) = pre;
 #pragma unroll
-    for (int q = 0; q < R; ++q)
-        incl[q] = tot[q];
+    for (int n = 1; n < MF_TY; ++n) {
+        uint32_t r[4] = {0u, 0u, 0u, 0u};
+        mf_col_add<F>(in[n - 1], c);
+        mf_col_add<F>(out[n - 1], r);
 #pragma unroll
-    for (int q = 0; q < R; ++q)
-        incl[q] = mf_wave_scan(incl[q]);
-#pragma unroll
-    for (int q = 0; q < R; ++q) {
-        uint32_t *r = V + q * vs;
-        uint32_t x[K];
-#pragma unroll
-        for (int u = 0; u < K; ++u)
-            x[u] = r[min(c0 + u, ncols - 1)] & keep[u];
-        uint32_t run = incl[q] - tot[q];  // sum of the lanes before this one
-#pragma unroll
-        for (int u = 0; u < K; ++u) {
-            run += x[u];
-            if (c0 + u < ncols)
-                r[c0 + u] = run;
-        }
+        for (int k = 0; k < 4; ++k)
+            c[k] -= r[k];
+        pre = mf_row_prefix4(c);
+        if (keep)
+            *reinterpret_cast<uint4 *>(V + n * vs + 4 * wd) = pre;
     }
 }
 
-template <int NKB>
-__device__ __forceinline__ void mf_row_prefix(uint32_t *V, int vs, int ncols)
-{
-#pragma nounroll
-    for (int h = 0; h < 2; ++h)
-        mf_row_prefix_half<NKB>(V + h * (MF_TY / 2) * vs, vs, ncols);
-}
-
-// Column walk, sliding pass and row prefix of field F over words
-// [w0, w0 + cnt) by one column-sum wave for one chunk (the last two after the
-// last chunk only).  The prefix runs over the wave's own columns
-// [4*w0, 4*(w0 + cnt)), starting from zero.
+// Column walk, then (after the last chunk only) the sliding pass with the row
+// prefix, of field F over words [w0, w0 + cnt) by one column-sum wave.  The
+// prefix runs over the wave's own columns [4*w0, 4*(w0 + cnt)), starting from
+// zero.
 template <int NKB, int F>
 __device__ __forceinline__ void mf_field_chunk(const uint32_t *img, int hcur, int j0, bool last, bool one_chunk,
                                                uint32_t *head, int nwd, int w0, int cnt, uint32_t *V, int vs,
@@ -417,13 +370,8 @@ __device__ __forceinline__ void mf_field_chunk(const uint32_t *img, int hcur, in
     const int wd = w0 + min(lane, cnt - 1);
     const bool keep = lane < cnt;
     mf_col_walk<NKB, F>(img, hcur, j0, !one_chunk, head, nwd, wd, keep, c);
-    if (!last)
-        return;
-    mf_slide_word<NKB, F>(img, hcur, one_chunk, head, nwd, wd, keep, V, vs, c);
-    // the slide's stores (other lanes' columns) before the scan's reads
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
-    __builtin_amdgcn_wave_barrier();
-    mf_row_prefix<NKB>(V + 4 * w0, vs, 4 * cnt);
+    if (last)
+        mf_slide_word<NKB, F>(img, hcur, one_chunk, head, nwd, wd, keep, V, vs, c);
 }
 
 // Workgroup roles (wave-uniform): waves 0 .. MF_MMA_WAVES - 1 run the matrix
