@@ -360,22 +360,24 @@ __host__ __device__ constexpr int bd_whole_w(int wp) { return (wp + 2 * BD_P) | 
 // Reduction area per wave (floats).
 __host__ __device__ constexpr int bd_red_floats(int S) { return 4 * BD_P * 65 + S * 3 * BD_P; }
 
-// The 4 rows of a row block at one column (zero outside the matrix).  The
-// four loads are issued unconditionally, from `safe` (any readable float)
-// where the element is outside the matrix, and the zeros are selected
-// afterwards: with no branch around them, the loads of several items stay
-// in flight together instead of waiting for each other.
-__device__ __forceinline__ float4 bd_load4(const float *src, const float *safe, int nrow_ok, int gc, int cols,
-                                           bool on)
+// Four zeros in device memory: the load source of staged elements outside
+// the matrix.
+__device__ float bd_zero4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+
+// The 4 rows of a row block at one column (zero outside the matrix).  Each
+// row is loaded from the matrix or, outside it, from bd_zero4, so the loaded
+// registers are the values themselves: nothing reads them before they are
+// stored to LDS, and a chunk's loads stay in flight during the walk over the
+// previous chunk instead of being waited for (and masked) up front.
+__device__ __forceinline__ float4 bd_load4(const float *src, int nrow_ok, int gc, int cols, bool on)
 {
-    const bool ok = on && nrow_ok > 0 && gc >= 0 && gc < cols;
-    const float *p = ok ? src + gc : safe;
-    const bool ok1 = ok && nrow_ok > 1, ok2 = ok && nrow_ok > 2, ok3 = ok && nrow_ok > 3;
-    const float x = p[0];
-    const float y = p[ok1 ? cols : 0];
-    const float z = p[ok2 ? 2 * cols : 0];
-    const float w = p[ok3 ? 3 * cols : 0];
-    return make_float4(ok ? x : 0.0f, ok1 ? y : 0.0f, ok2 ? z : 0.0f, ok3 ? w : 0.0f);
+    const bool ok = on && gc >= 0 && gc < cols;
+    const float *z = bd_zero4;
+    const float *p0 = ok && nrow_ok > 0 ? src + gc : z;
+    const float *p1 = ok && nrow_ok > 1 ? src + cols + gc : z;
+    const float *p2 = ok && nrow_ok > 2 ? src + 2 * cols + gc : z;
+    const float *p3 = ok && nrow_ok > 3 ? src + 3 * cols + gc : z;
+    return make_float4(*p0, *p1, *p2, *p3);
 }
 
 // ---- chunked staging: columns pass through LDS J walk steps at a time ----
@@ -434,10 +436,10 @@ __global__ __launch_bounds__(64 * NW) void xcorr_bd_chunk_kernel(BdArgs a)
             const int ua = u_first + t * J;
 #pragma unroll
             for (int k = 0; k < LPT; ++k)
-                vl[k] = bd_load4(st_l, a.x.left, nrow_ok, ua + cres + k * NW, cols, st_on);
+                vl[k] = bd_load4(st_l, nrow_ok, ua + cres + k * NW, cols, st_on);
 #pragma unroll
             for (int k = 0; k < RPT; ++k)
-                vr[k] = bd_load4(st_r, a.x.right, nrow_ok, ua + roff - (P - 1) + cres + k * NW, cols, st_on);
+                vr[k] = bd_load4(st_r, nrow_ok, ua + roff - (P - 1) + cres + k * NW, cols, st_on);
         };
         auto store_chunk = [&](float4 *buf, const float4 (&vl)[LPT], const float4 (&vr)[RPT]) {
             if (sb < S * nb) {
@@ -760,7 +762,7 @@ __global__ __launch_bounds__(64 * NW) void xcorr_bd_big_kernel(BdArgs a)
                     const int row0 = 4 * (is_l ? kb : rb);
                     const float *src = (is_l ? lmat : rmat) + (size_t)row0 * cols;
                     const int gc = is_l ? ua + cc : ua + roff - (P - 1) + cc;
-                    v[k] = bd_load4(src, is_l ? a.x.left : a.x.right, min(4, rows - row0), gc, cols, on);
+                    v[k] = bd_load4(src, min(4, rows - row0), gc, cols, on);
                 }
             };
             auto store_chunk = [&](float4 *buf, const float4 (&v)[IPT]) {
