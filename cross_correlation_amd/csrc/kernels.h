@@ -32,6 +32,23 @@ inline hipError_t allow_lds_once(K kernel, std::atomic<uint64_t> &done)
     return e;
 }
 
+// Compute units of the current device, queried once per device (256, the
+// gfx950 count, if the query fails).
+inline int device_cu_count()
+{
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n > 0)
+        return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        return 256;
+    cached[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
 // Arguments of every u8 normalized-correlation kernel (validated on the host).
 struct NccArgs {
     const uint8_t *image;

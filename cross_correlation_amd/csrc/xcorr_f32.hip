@@ -927,18 +927,33 @@ hipError_t xcorr_launch_blockdiag(const XcorrArgs &a, hipStream_t s)
     // split the two dx signs over workgroups when the grid would hold fewer
     // than 4096 waves (4 per SIMD)
     b.n_sides = pick(nw) * nw >= 4096 ? 1 : 2;
+    // Whole staging keeps every matrix of a pair group in LDS, so few of its
+    // workgroups fit on a CU.  Take it when those leave at least four waves
+    // per SIMD or the whole grid is resident at once; otherwise stream
+    // chunks, whose small LDS keeps the CUs full.  Below 32 columns the walks
+    // are too short to repay staging every column before the first step (the
+    // chunked kernel starts after its first J + P columns).
+    const int64_t cus = device_cu_count();
+    auto whole_ok = [&](int nw_, int sides) {
+        if (b.wp < 32) return false;
+        const size_t lds = bd_whole_lds(b, nw_);
+        if (lds > BD_LDS_MAX) return false;
+        const int64_t per_cu = (int64_t)(BD_LDS_MAX / lds);
+        const int64_t n_wg = per_side * ((b.nb + nw_ - 1) / nw_) * sides;
+        return per_cu * nw_ >= 16 || n_wg <= per_cu * cus;
+    };
     // Up to 8 diagonals: one 8-wave workgroup holds them all and shares one
     // staging; the dx signs go to separate workgroups.
-    if (b.nb <= 8 && bd_whole_lds(b, 8) <= BD_LDS_MAX) {
+    if (b.nb <= 8 && whole_ok(8, 2)) {
         b.n_sides = 2;
         return launch_whole<8>(b, s);
     }
-    if (nw == 16 && bd_whole_lds(b, 16) <= BD_LDS_MAX) return launch_whole<16>(b, s);
-    if (nw >= 8 && bd_whole_lds(b, 8) <= BD_LDS_MAX) {
+    if (nw == 16 && whole_ok(16, b.n_sides)) return launch_whole<16>(b, s);
+    if (nw >= 8 && whole_ok(8, nw == 16 ? 2 : b.n_sides)) {
         if (nw == 16) b.n_sides = 2;  // half the waves per workgroup: keep the wave count
         return launch_whole<8>(b, s);
     }
-    if (nw == 4 && bd_whole_lds(b, 4) <= BD_LDS_MAX) return launch_whole<4>(b, s);
+    if (nw == 4 && whole_ok(4, b.n_sides)) return launch_whole<4>(b, s);
     if (nw == 16) return launch_chunk<16, 16>(b, s);
     if (nw == 8) return launch_chunk<8, 8>(b, s);
     return launch_chunk<4, 8>(b, s);

@@ -62,6 +62,11 @@ def test_xcorr_edge_shapes(shape, algo):
                                    (1, 1, 35, 600), (2, 3, 41, 600), (2, 3, 65, 260),
                                    # 16 diagonals whose whole staging only fits at 8 waves
                                    (3, 3, 85, 72),
+                                   # whole staging would leave one wave per SIMD over several
+                                   # rounds, or the rows are narrower than 32 columns: chunked
+                                   (2, 3, 100, 70), (3, 5, 64, 64), (6, 6, 40, 24), (16, 16, 16, 16),
+                                   # whole staging, every workgroup resident at once
+                                   (32, 32, 32, 32),
                                    # more than 64 row blocks: passes of 64 blocks; 65 blocks
                                    # (the left window wraps onto itself), odd rows, 2-3 passes,
                                    # several pairs, wide rows
