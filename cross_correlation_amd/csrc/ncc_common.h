@@ -167,6 +167,38 @@ __device__ __forceinline__ void peak_commit_wg(unsigned long long *peak, unsigne
     }
 }
 
+// The coefficient num / sqrt(p), p = vI * vT (all exact integers in fp64,
+// p already rounded once), rounded to fp32: bit-identical to the IEEE fp64
+// square root and division followed by one rounding to fp32, at about half
+// their cost.  The reciprocal square root comes from the hardware estimate
+// (relative error at most 2^-23: 2^29 ulp of fp64) and one Newton step
+// (quadratic convergence: relative error below 2^-45), so c = num * y is
+// within |c| * 2^-45 of the IEEE quotient (itself within |c| * 2^-52 of the
+// real one).  Both round to the same fp32 value unless an fp32 rounding
+// boundary lies between them; those are the midpoints half an fp32 ulp either
+// side of f = fp32(c), or a quarter ulp below a power of two.  When c is
+// within |c| * 2^-42 of either distance (a few windows in a million) the IEEE
+// expression is evaluated instead.  |c| >= 2^-50 when num != 0 (num is a
+// nonzero integer, p < 2^100), so f is a normal number and its ulp is the
+// power of two read from its exponent field.
+__device__ __forceinline__ float ncc_coef_f32(double num, double p)
+{
+    double y = __builtin_amdgcn_rsq(p);
+    const double t = p * y;
+    const double e = fma(-t, y, 1.0);
+    y = fma(0.5 * y, e, y);
+    const double c = num * y;
+    const float f = (float)c;
+    if (c == 0.0)
+        return f;
+    const double r = fabs(c - (double)f);
+    const double ulp = (double)__uint_as_float((__float_as_uint(f) & 0x7F800000u) - (23u << 23));
+    const double margin = fabs(c) * 0x1p-42;
+    if (0.5 * ulp - r > margin && fabs(r - 0.25 * ulp) > margin)
+        return f;
+    return (float)(num / sqrt(p));
+}
+
 // Exact epilogue for one window; writes whichever outputs are requested and
 // folds the window into `best` when the best match is requested.
 __device__ __forceinline__ void ncc_store(const NccArgs &a, size_t o, uint32_t si, uint32_t sq, uint32_t st,
@@ -178,12 +210,12 @@ __device__ __forceinline__ void ncc_store(const NccArgs &a, size_t o, uint32_t s
     if (a.coef || a.peak) {
         const int64_t num = n * (int64_t)st - (int64_t)si * sum_t;
         const int64_t vi = n * (int64_t)sq - (int64_t)si * (int64_t)si;
-        double c = 0.0;
+        float c = 0.0f;
         if (vi != 0 && vt != 0)
-            c = (double)num / sqrt((double)vi * (double)vt);
-        if (a.coef) a.coef[o] = (float)c;
+            c = ncc_coef_f32((double)num, (double)vi * (double)vt);
+        if (a.coef) a.coef[o] = c;
         if (a.peak) {
-            const unsigned long long k = peak_key((float)c, (uint32_t)o);
+            const unsigned long long k = peak_key(c, (uint32_t)o);
             best = k > best ? k : best;
         }
     }

@@ -513,12 +513,12 @@ void ncc_u8_mfma_kernel(NccArgs a)
             const double sid = (double)si;
             const double num = fma(nd, (double)st, -(sid * std_));
             const double vi = fma(nd, (double)sq, -(sid * sid));
-            double cf = 0.0;
+            float cf = 0.0f;
             if (vi != 0.0 && vt != 0.0)
-                cf = num / sqrt(vi * vt);
-            if (a.coef) a.coef[o] = (float)cf;
+                cf = ncc_coef_f32(num, vi * vt);
+            if (a.coef) a.coef[o] = cf;
             if (a.peak) {
-                const unsigned long long k = peak_key((float)cf, (uint32_t)o);
+                const unsigned long long k = peak_key(cf, (uint32_t)o);
                 best = k > best ? k : best;
             }
         }
