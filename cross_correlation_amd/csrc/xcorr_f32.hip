@@ -279,6 +279,23 @@ __device__ __forceinline__ BdWho bd_who(const BdArgs &a)
     return w;
 }
 
+// Sum of col[lo .. hi) (a wave-uniform range) in a fixed order: four
+// interleaved partial sums, then ((0 + 1) + (2 + 3)).
+__device__ __forceinline__ float bd_col_sum(const float *col, int lo, int hi)
+{
+    float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
+    int b = lo;
+    for (; b + 4 <= hi; b += 4) {
+        a0 += col[b];
+        a1 += col[b + 1];
+        a2 += col[b + 2];
+        a3 += col[b + 3];
+    }
+    for (; b < hi; ++b)
+        a0 += col[b];
+    return (a0 + a1) + (a2 + a3);
+}
+
 // Cross-lane reduction of one side's partial sums, in a fixed order, then the
 // stores.  Each wave uses only its own LDS area, so a wave-level barrier
 // suffices.  comb = block-1 sums plus block-2 sums when both blocks share the
@@ -312,41 +329,32 @@ __device__ __forceinline__ void bd_reduce_store(const BdArgs &a, const BdWho &w,
     const int rows = a.x.rows, cols = a.x.cols, h4 = 4 * nb;
     const int oh = 2 * rows - 1, ow = 2 * cols - 1;
     const int64_t npairs = (int64_t)a.x.n_left * a.x.n_right;
-    const int per_slot = NV * 2;  // (r, wrapped, p), p fastest: 4 lanes store 16 contiguous bytes
-    for (int o = w.lane; o < S * per_slot; o += 64) {
-        const int sl = o / per_slot;
-        const int q = o - sl * per_slot;
+    // Lane (slot, r, p), p fastest (4 lanes store 16 contiguous bytes), sums
+    // its column of block partials in two wave-uniform ranges: blocks
+    // [0, split) for output row 4*delta + r and, wrapped, [split, nb) for row
+    // 4*delta + r - 4*nb (plus the wrap lane's block-2 sums).
+    const int split = nb - w.delta;
+    for (int o = w.lane; o < S * NV; o += 64) {
+        const int sl = o / NV;
+        const int q = o - sl * NV;
         const int p = q % P;
-        const int wr = (q / P) & 1;
-        const int r = q / (2 * P);
+        const int r = q / P;
         const int64_t pair = (int64_t)w.grp * S + sl;
-        const int dy = 4 * w.delta + r - (wr ? h4 : 0);
         const int c = w.c0 + p;
         const int dx = side ? c - a.wp : c;
-        const bool keep = pair < npairs && dy > -rows && dy < rows && dx > -cols && dx < cols;
-        const int blo = wr ? nb - w.delta : 0;
-        const int bhi = wr ? nb : nb - w.delta;
         const float *col = wred + (r * P + p) * RS + sl * nb;
-        // eight independent partial sums (block b into part[b % 8]),
-        // combined in a fixed tree order; the reads are unconditional (index
-        // clamped into the slot) so they are all in flight together
-        float part[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) part[i] = 0.0f;
-        for (int bb = blo & ~7; bb < bhi; bb += 8) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int b = bb + i;
-                const float v = col[min(b, nb - 1)];
-                const int keep_b = -(int)((b >= blo) & (b < bhi));  // all ones or zero
-                part[i] += __int_as_float(__float_as_int(v) & keep_b);
-            }
+        const float s_un = bd_col_sum(col, 0, split);
+        float s_wr = bd_col_sum(col, split, nb);
+        if (r >= 1)
+            s_wr += wextra[(sl * 3 + (r - 1)) * P + p];
+        if (pair < npairs && dx > -cols && dx < cols) {
+            const int dy0 = 4 * w.delta + r, dy1 = dy0 - h4;
+            float *const outp = a.x.out + (size_t)pair * oh * ow + (dx + cols - 1);
+            if (dy0 < rows)
+                outp[(size_t)(dy0 + rows - 1) * ow] = s_un;
+            if (dy1 > -rows)
+                outp[(size_t)(dy1 + rows - 1) * ow] = s_wr;
         }
-        float sum = ((part[0] + part[1]) + (part[2] + part[3])) + ((part[4] + part[5]) + (part[6] + part[7]));
-        if (wr && r >= 1)
-            sum += wextra[(sl * 3 + (r - 1)) * P + p];
-        if (keep)
-            a.x.out[((size_t)pair * oh + (dy + rows - 1)) * ow + (dx + cols - 1)] = sum;
     }
     // the next side's writes come after these reads in every lane's program
     // order and LDS serves one wave in order
