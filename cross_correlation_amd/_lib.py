@@ -30,6 +30,8 @@ XC_NCC_MFMA = 4
 XC_NCC_DOT4_ILP_Q1 = 5
 XC_NCC_DOT4_ILP_Q2 = 6
 XC_NCC_DOT4_ILP_Q4 = 7
+XC_NCC_MFMA_W4 = 8
+XC_NCC_MFMA_W2 = 9
 
 XC_NCC_MODE_VALID = 0
 XC_NCC_MODE_SAME = 1

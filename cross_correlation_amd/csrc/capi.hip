@@ -126,16 +126,18 @@ int ncc_dispatch(const xc::NccArgs &a, int variant, hipStream_t s)
     case XC_NCC_AUTO:
         // The matrix-core recast costs a nearly fixed time per output tile,
         // the packed-byte kernel a time that grows with the template; the
-        // recast wins from 512 template pixels at any image size, and from
-        // about 96 pixels once there are 400K outputs to spread its fixed
-        // cost over (measured on MI355X, packed-byte / recast: 1920x1080
-        // with 8x8 0.95, 10x10 1.15, 16x16 1.48, 64x64 8.3; 512x512 with
-        // 16x16 0.78, 24x24 1.18; 768x768 with 16x16 1.24; 256x256 with
-        // 16x16 0.71, 24x24 1.09).
+        // recast wins from 512 template pixels at any image size, from about
+        // 96 pixels once there are 400K outputs to spread its fixed cost
+        // over, and at any template size from about 1M outputs (measured on
+        // MI355X, packed-byte / recast time: 1920x1080 with 4x4 1.45, 8x8
+        // 1.59, 16x16 2.39, 32x32 5.1; 1024x1024 with 4x4 1.11, 8x8 1.31;
+        // 1280x720 with 4x4 0.93, 8x8 1.02, 10x10 1.37; 768x768 with 8x8
+        // 0.94, 10x10 1.40; 512x512 with 16x16 1.00, 24x24 1.65; 256x256 with
+        // 16x16 0.93, 24x24 1.55).
         {
             const int64_t npix = (int64_t)a.t_width * a.t_height;
             const int64_t nout = (int64_t)a.out_w * a.out_h;
-            if ((npix >= 512 || (npix >= 96 && nout >= 400000)) && xc::ncc_mfma_supported(a))
+            if ((npix >= 512 || (npix >= 96 && nout >= 400000) || nout >= 1000000) && xc::ncc_mfma_supported(a))
                 return hip_status(xc::ncc_launch_mfma(a, s));
             return hip_status(xc::ncc_launch_ilp(a, s));
         }
@@ -153,6 +155,10 @@ int ncc_dispatch(const xc::NccArgs &a, int variant, hipStream_t s)
         return hip_status(xc::ncc_launch_ilp(a, s, 2));
     case XC_NCC_DOT4_ILP_Q4:
         return hip_status(xc::ncc_launch_ilp(a, s, 4));
+    case XC_NCC_MFMA_W4:
+        return hip_status(xc::ncc_launch_mfma(a, s, 4));
+    case XC_NCC_MFMA_W2:
+        return hip_status(xc::ncc_launch_mfma(a, s, 2));
     default:
         return XC_ERR_VARIANT;
     }
@@ -161,9 +167,11 @@ int ncc_dispatch(const xc::NccArgs &a, int variant, hipStream_t s)
 // Variant check done before anything is enqueued.
 int ncc_variant_ok(const xc::NccArgs &a, int variant)
 {
-    if (variant < XC_NCC_AUTO || variant > XC_NCC_DOT4_ILP_Q4)
+    if (variant < XC_NCC_AUTO || variant > XC_NCC_MFMA_W2)
         return XC_ERR_VARIANT;
-    if (variant == XC_NCC_MFMA && !xc::ncc_mfma_supported(a))
+    if ((variant == XC_NCC_MFMA || variant == XC_NCC_MFMA_W4) && !xc::ncc_mfma_supported(a, 4))
+        return XC_ERR_SHAPE;
+    if (variant == XC_NCC_MFMA_W2 && !xc::ncc_mfma_supported(a, 2))
         return XC_ERR_SHAPE;
     return XC_OK;
 }

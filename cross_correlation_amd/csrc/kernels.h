@@ -71,8 +71,10 @@ struct NccArgs {
 hipError_t ncc_launch_ilp(NccArgs a, hipStream_t s, int force_q = 0);
 hipError_t ncc_launch_c1(NccArgs a, bool dot4, hipStream_t s);
 // SumIT on the i8 matrix cores; takes template rows up to 256 bytes.
-hipError_t ncc_launch_mfma(NccArgs a, hipStream_t s);
-bool ncc_mfma_supported(const NccArgs &a);
+// mw: matrix-core waves per workgroup (4: 256-column tiles, 2: 128-column
+// tiles, t_width <= 64 only); 0 lets the launcher pick from the grid.
+hipError_t ncc_launch_mfma(NccArgs a, hipStream_t s, int mw = 0);
+bool ncc_mfma_supported(const NccArgs &a, int mw = 0);
 // Best-match search around a correlation launch: set the key to 0 before it,
 // decode the key into (y, x, coefficient) after it.  `peak` points to an
 // xc_ncc_peak (include/xcorr.h).

@@ -21,22 +21,28 @@
 //     the window sum over every template row (B is the template placed
 //     Toeplitz-wise along the output rows); a fraction 15/(t_height + 15) of
 //     the products is against zero rows.
-//   * SumI and SumISq: while four waves of the workgroup run the matrix
-//     cores, four more walk the tile's image words (4 columns each) down the
-//     template's rows, keeping running sums per column of the biased pixels
-//     s = I - 128 (two waves, half of the words each) and of s^2 (two more),
-//     with signed v_dot4 on the staged bytes: the window of output row 0.  Each then slides its window down the 16 output rows (add the
-//     row entering, remove the row leaving; the tile's first 15 rows are kept
-//     for that when the template comes in several chunks) and takes prefix
-//     sums along each row of its half, so a window sum is the difference of
+//   * SumI and SumISq: while the matrix-core waves run, the column-sum waves
+//     walk the tile's image words (4 columns each) down the template's rows,
+//     keeping running sums per column of the biased pixels s = I - 128 and of
+//     s^2 (one field each; with four matrix-core waves, two waves per field,
+//     half of the words each), with signed v_dot4 on the staged bytes: the
+//     window of output row 0.  Each then slides its window down the 16
+//     output rows (add the row entering, remove the row leaving; the tile's
+//     first 15 rows are kept for that when the template comes in several
+//     chunks) and, as each row appears, takes its prefix along the wave's
+//     words in registers (a DPP scan), so a window sum is the difference of
 //     two entries (plus the first half's row total where a window spans both
 //     halves).  SumI = sum s + 128 N and SumISq = sum s^2 + 256 SumI -
 //     16384 N, all in wrapping 32-bit arithmetic, exact because every final
 //     sum is below 2^32.
+//   * Tiles: 16 output rows by 256 columns (four matrix-core waves, two
+//     workgroups per CU) or 128 columns (two, four workgroups per CU, for
+//     templates up to 64 bytes wide); the launcher takes the narrow tiles
+//     when they run the grid in fewer rounds of workgroups, or in as many
+//     with the template in one row chunk.
 //   * The coefficient follows the packed-byte kernels' exact formula: num, vI
 //     and vT are exact integers (held in fp64 here, formed with fused
-//     multiply-adds), then an IEEE fp64 divide and square root and one fp32
-//     rounding, so both paths return the same bits.
+//     multiply-adds), then ncc_coef_f32, so both paths return the same bits.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -48,18 +54,24 @@ namespace xc {
 typedef int mf_v4i __attribute__((ext_vector_type(4)));
 
 constexpr int MF_TY = 16;          // output rows per workgroup (MFMA N)
-constexpr int MF_TX = 256;         // output columns per workgroup (4 waves x 64)
-constexpr int MF_MMA_WAVES = 4;    // matrix-core waves
-constexpr int MF_THREADS = 64 * (MF_MMA_WAVES + 4);  // plus the four column-sum waves
 constexpr int MF_MAX_NKB = 4;      // template rows up to 256 bytes
 constexpr int MF_MAX_HC = 256;     // template rows per chunk
-constexpr int MF_ACC_STRIDE = 257; // i32 words per output row of the SumIT staging
+
+// A workgroup runs MW matrix-core waves of 64 output columns each, then its
+// column-sum waves: with MW = 4 one per field and half of the image words,
+// with MW = 2 (templates up to 64 bytes wide, whose 128 + t_width columns fit
+// one wave's 64 lanes of words) one per field for all of them.
+__host__ __device__ constexpr int mf_tx(int mw) { return 64 * mw; }
+__host__ __device__ constexpr int mf_walkers(int mw) { return mw == 4 ? 4 : 2; }
+__host__ __device__ constexpr int mf_threads(int mw) { return 64 * (mw + mf_walkers(mw)); }
+// i32 words per output row of the SumIT staging (odd: rows start in different banks)
+__host__ __device__ constexpr int mf_acc_stride(int mw) { return 64 * mw + 1; }
 
 // LDS plan of one workgroup (host and device agree through these helpers):
 //   V     2*MF_TY rows x vs u32: column sums of pixels (rows 0..15) and of
 //         squares (rows 16..31), then their row prefix (per half of the words)
 //   img   the staged image tile plus one spare row; after the walk, the
-//         SumIT' staging of MF_TY x MF_ACC_STRIDE i32
+//         SumIT' staging of MF_TY x mf_acc_stride(MW) i32
 //   tpl   template rows with zero rows around them (trows rows of tsb bytes)
 //   head  the tile's first MF_TY - 1 image rows (words 0..nwd-1), kept for
 //         the sliding pass when the template comes in several chunks
@@ -70,29 +82,30 @@ struct MfPlan {
     int sw;       // image LDS words per row
     int tsb;      // template LDS bytes per row
     int trows;    // template LDS rows
-    int nwd;      // image words covered by the column sums (64 .. 128)
+    int nwd;      // image words covered by the column sums (16 MW .. 16 MW + 64)
     int vs;       // u32 per row of V (a multiple of 4: 16-byte stores)
     int img_words;
     size_t bytes;
 };
 
-// LDS row strides for NKB 64-byte template blocks (compile-time in the
-// kernels, so consecutive rows are immediate offsets of one address)
-__host__ __device__ constexpr int mf_sw(int nkb) { return 64 + 16 * nkb + 4; }
+// LDS row strides for MW matrix waves and NKB 64-byte template blocks
+// (compile-time in the kernels, so consecutive rows are immediate offsets of
+// one address)
+__host__ __device__ constexpr int mf_sw(int mw, int nkb) { return 16 * mw + 16 * nkb + 4; }
 __host__ __device__ constexpr int mf_tsb(int nkb) { return 64 * nkb + 16; }
 
-__host__ __device__ inline MfPlan mf_plan(int t_width, int hc)
+__host__ __device__ inline MfPlan mf_plan(int mw, int t_width, int hc)
 {
     MfPlan p;
     p.nkb = (t_width + 63) / 64;
     p.hc = hc;
-    p.sw = mf_sw(p.nkb);
+    p.sw = mf_sw(mw, p.nkb);
     p.tsb = mf_tsb(p.nkb);
     p.trows = hc + 2 * MF_TY - 1;
-    p.nwd = 64 + (t_width + 2) / 4;  // words holding columns 0 .. 255 + t_width - 1
+    p.nwd = 16 * mw + (t_width + 2) / 4;  // words holding columns 0 .. 64 mw - 1 + t_width - 1
     p.vs = 4 * p.nwd + 4;
     int img = (MF_TY + hc) * p.sw;  // staged rows + one spare row
-    if (img < MF_TY * MF_ACC_STRIDE) img = MF_TY * MF_ACC_STRIDE;
+    if (img < MF_TY * mf_acc_stride(mw)) img = MF_TY * mf_acc_stride(mw);
     p.img_words = img;
     p.bytes = (size_t)2 * MF_TY * p.vs * 4 + (size_t)img * 4 + (size_t)p.trows * p.tsb +
               (size_t)(MF_TY - 1) * p.nwd * 4 + 8;
@@ -105,16 +118,17 @@ __host__ __device__ inline MfPlan mf_plan(int t_width, int hc)
 // Each thread takes its items in batches of 4, all loads of a batch issued
 // before any of its LDS stores (one memory round trip per batch); a chunk
 // outside the image loads from the image base and is zeroed afterwards.
+template <int NT>
 __device__ __forceinline__ void mf_stage_image(const uint8_t *__restrict__ image, int height, int pitch, int gy0,
                                                int gx0, int nrows, int nchunks, uint32_t *lds, int stride)
 {
     constexpr int SB = 4;
     const int total = nrows * nchunks;
-    for (int i0 = threadIdx.x; i0 < total; i0 += SB * MF_THREADS) {
+    for (int i0 = threadIdx.x; i0 < total; i0 += SB * NT) {
         uint4 v[SB];
 #pragma unroll
         for (int k = 0; k < SB; ++k) {
-            const int i = i0 + k * MF_THREADS;
+            const int i = i0 + k * NT;
             const int r = i / nchunks;
             const int b = i - r * nchunks;
             const int gy = gy0 + r;
@@ -126,7 +140,7 @@ __device__ __forceinline__ void mf_stage_image(const uint8_t *__restrict__ image
         }
 #pragma unroll
         for (int k = 0; k < SB; ++k) {
-            const int i = i0 + k * MF_THREADS;
+            const int i = i0 + k * NT;
             if (i < total) {
                 const int r = i / nchunks;
                 const int b = i - r * nchunks;
@@ -146,6 +160,7 @@ __device__ __forceinline__ void mf_stage_image(const uint8_t *__restrict__ image
 // after (the template rows that do not exist for some output row of the tile,
 // and the spare row the pipelined walk reads last) and zero bytes beyond
 // t_width up to the 64-byte block (a zero byte of T' adds nothing to sum I'T').
+template <int NT>
 __device__ __forceinline__ void mf_stage_template(const uint8_t *__restrict__ tmpl, int t_width, int j0, int hcur,
                                                   int kw, uint8_t *tpl, int tsb, int trows)
 {
@@ -155,11 +170,11 @@ __device__ __forceinline__ void mf_stage_template(const uint8_t *__restrict__ tm
     if (tmpl_word_rows(tmpl, t_width)) {
         // whole-word rows, in batches of 4 (loads first, then the LDS stores)
         constexpr int SB = 4;
-        for (int i0 = threadIdx.x; i0 < total; i0 += SB * MF_THREADS) {
+        for (int i0 = threadIdx.x; i0 < total; i0 += SB * NT) {
             uint32_t v[SB];
 #pragma unroll
             for (int q = 0; q < SB; ++q) {
-                const int i = i0 + q * MF_THREADS;
+                const int i = i0 + q * NT;
                 const int r = i / wpr;
                 const int k = i - r * wpr;
                 const int j = r - (MF_TY - 1);
@@ -169,7 +184,7 @@ __device__ __forceinline__ void mf_stage_template(const uint8_t *__restrict__ tm
             }
 #pragma unroll
             for (int q = 0; q < SB; ++q) {
-                const int i = i0 + q * MF_THREADS;
+                const int i = i0 + q * NT;
                 if (i < total) {
                     const int r = i / wpr;
                     const int k = i - r * wpr;
@@ -211,11 +226,11 @@ __device__ __forceinline__ void mf_col_add(uint32_t biased, uint32_t (&c)[4])
 // blocks per row; rows go in pairs through two register sets, the next row's
 // LDS words read while the current row's products issue (the read after the
 // last row lands in the spare row each LDS area keeps).
-template <int NKB>
+template <int MW, int NKB>
 __device__ __forceinline__ void mf_walk_chunk(const uint32_t *img, const uint8_t *tpl, int hcur, int wave,
                                               mf_v4i (&at)[4])
 {
-    constexpr int sw = mf_sw(NKB), tsb = mf_tsb(NKB);
+    constexpr int sw = mf_sw(MW, NKB), tsb = mf_tsb(NKB);
     const int lane = threadIdx.x & 63;
     const int m = lane & 15, g = lane >> 4;
     // A: output column x0 + 64*wave + 4m + t reads image words from 16*wave + m
@@ -271,11 +286,11 @@ __device__ __forceinline__ void mf_walk_chunk(const uint32_t *img, const uint8_t
 // save_head the raw words of the first MF_TY - 1 absolute rows go to `head`
 // for the sliding pass of the last chunk (only when `keep`: lanes past their
 // wave's words read a clamped word and store nothing).
-template <int NKB, int F>
+template <int MW, int NKB, int F>
 __device__ __forceinline__ void mf_col_walk(const uint32_t *img, int hcur, int j0, bool save_head, uint32_t *head,
                                             int nwd, int wd, bool keep, uint32_t (&c)[4])
 {
-    constexpr int sw = mf_sw(NKB);
+    constexpr int sw = mf_sw(MW, NKB);
     const uint32_t *p = img + wd;
     constexpr int U = 4;
     int rr = 0;
@@ -329,11 +344,11 @@ __device__ __forceinline__ uint4 mf_row_prefix4(const uint32_t (&c)[4])
 // in one chunk, else the saved head row).  Each row's prefix along the wave's
 // half (mf_row_prefix4) goes to row n of V (row stride vs) when `keep`; reads
 // are unconditional and every lane takes part in the scans.
-template <int NKB, int F>
+template <int MW, int NKB, int F>
 __device__ __forceinline__ void mf_slide_word(const uint32_t *img, int hcur, bool one_chunk, const uint32_t *head,
                                               int nwd, int wd, bool keep, uint32_t *V, int vs, uint32_t (&c)[4])
 {
-    constexpr int sw = mf_sw(NKB);
+    constexpr int sw = mf_sw(MW, NKB);
     uint32_t in[MF_TY - 1], out[MF_TY - 1];
 #pragma unroll
     for (int n = 1; n < MF_TY; ++n) {
@@ -361,7 +376,7 @@ __device__ __forceinline__ void mf_slide_word(const uint32_t *img, int hcur, boo
 // prefix, of field F over words [w0, w0 + cnt) by one column-sum wave.  The
 // prefix runs over the wave's own columns [4*w0, 4*(w0 + cnt)), starting from
 // zero.
-template <int NKB, int F>
+template <int MW, int NKB, int F>
 __device__ __forceinline__ void mf_field_chunk(const uint32_t *img, int hcur, int j0, bool last, bool one_chunk,
                                                uint32_t *head, int nwd, int w0, int cnt, uint32_t *V, int vs,
                                                uint32_t (&c)[4])
@@ -369,25 +384,27 @@ __device__ __forceinline__ void mf_field_chunk(const uint32_t *img, int hcur, in
     const int lane = threadIdx.x & 63;
     const int wd = w0 + min(lane, cnt - 1);
     const bool keep = lane < cnt;
-    mf_col_walk<NKB, F>(img, hcur, j0, !one_chunk, head, nwd, wd, keep, c);
+    mf_col_walk<MW, NKB, F>(img, hcur, j0, !one_chunk, head, nwd, wd, keep, c);
     if (last)
-        mf_slide_word<NKB, F>(img, hcur, one_chunk, head, nwd, wd, keep, V, vs, c);
+        mf_slide_word<MW, NKB, F>(img, hcur, one_chunk, head, nwd, wd, keep, V, vs, c);
 }
 
-// Workgroup roles (wave-uniform): waves 0 .. MF_MMA_WAVES - 1 run the matrix
-// cores, 64 output columns each; the next four keep the column sums, one wave
-// per field (pixels, squared pixels) and half of the image words (the first
-// pixel wave also sums the template), so the vector work of SumI and SumISq
-// runs beside the matrix products instead of inside their loop.  Every wave
-// takes part in the staging and in the epilogue.  The row prefix of each half
-// starts from zero; the epilogue adds the first half's row total where a
-// window reaches from the first half into the second.
-template <int NKB>
-__global__ __launch_bounds__(MF_THREADS) __attribute__((amdgpu_waves_per_eu(NKB == 1 ? 4 : 1)))
+// Workgroup roles (wave-uniform): waves 0 .. MW - 1 run the matrix cores, 64
+// output columns each; the next ones keep the column sums, one wave per field
+// (pixels, squared pixels) and, with MW = 4, half of the image words (the
+// first pixel wave also sums the template), so the vector work of SumI and
+// SumISq runs beside the matrix products instead of inside their loop.
+// Every wave takes part in the staging and in the epilogue.  The row prefix
+// of each half starts from zero; the epilogue adds the first half's row total
+// where a window reaches from the first half into the second (with one half,
+// never).
+template <int MW, int NKB>
+__global__ __launch_bounds__(mf_threads(MW)) __attribute__((amdgpu_waves_per_eu(NKB == 1 ? 4 : 1)))
 void ncc_u8_mfma_kernel(NccArgs a)
 {
+    constexpr int NT = mf_threads(MW), TX = mf_tx(MW), NWK = mf_walkers(MW), ACC = mf_acc_stride(MW);
     extern __shared__ uint4 mf_smem[];
-    const MfPlan P = mf_plan(a.t_width, a.hc);
+    const MfPlan P = mf_plan(MW, a.t_width, a.hc);
     uint32_t *const V1 = reinterpret_cast<uint32_t *>(mf_smem);
     uint32_t *const V2 = V1 + MF_TY * P.vs;
     uint32_t *const img = V2 + MF_TY * P.vs;
@@ -396,15 +413,15 @@ void ncc_u8_mfma_kernel(NccArgs a)
     uint32_t *const tsum = head + (MF_TY - 1) * P.nwd;
     int32_t *const acc_it = reinterpret_cast<int32_t *>(img);
 
-    const int x0 = blockIdx.x * MF_TX, y0 = blockIdx.y * MF_TY;
+    const int x0 = blockIdx.x * TX, y0 = blockIdx.y * MF_TY;
     const int tw = a.t_width, th = a.t_height;
     const int twords = (tw + 3) / 4;  // packed words per template row (the last one partial when tw % 4 != 0)
     const uint32_t tm = tail_mask(tw);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const bool one_chunk = th <= P.hc;
-    const int half = (P.nwd + 1) / 2;  // words of the first half (<= 64)
-    const int ce = 4 * half;           // first column of the second half
+    const int half = NWK == 4 ? (P.nwd + 1) / 2 : P.nwd;  // words of the first half (<= 64)
+    const int ce = 4 * half;                               // first column of the second half
 
     mf_v4i at[4];
 #pragma unroll
@@ -413,24 +430,25 @@ void ncc_u8_mfma_kernel(NccArgs a)
     uint32_t c[4] = {0u, 0u, 0u, 0u};
     uint32_t ts = 0u, tq = 0u;
 
-    const int nchunks16 = (64 + 16 * NKB) / 4;  // 16-byte chunks per staged image row
+    const int nchunks16 = 4 * (MW + NKB);  // 16-byte chunks per staged image row
     for (int j0 = 0; j0 < th; j0 += P.hc) {
         const int hcur = min(P.hc, th - j0);
         const bool last = j0 + hcur == th;
         __syncthreads();  // the previous chunk's readers are done
-        mf_stage_image(a.image, a.height, a.pitch, y0 + j0, x0, MF_TY - 1 + hcur, nchunks16, img, P.sw);
-        mf_stage_template(a.tmpl, tw, j0, hcur, 64 * NKB, tpl, P.tsb, P.trows);
+        mf_stage_image<NT>(a.image, a.height, a.pitch, y0 + j0, x0, MF_TY - 1 + hcur, nchunks16, img, P.sw);
+        mf_stage_template<NT>(a.tmpl, tw, j0, hcur, 64 * NKB, tpl, P.tsb, P.trows);
         __syncthreads();
-        if (wave < MF_MMA_WAVES) {
-            mf_walk_chunk<NKB>(img, tpl, hcur, wave, at);
+        if (wave < MW) {
+            mf_walk_chunk<MW, NKB>(img, tpl, hcur, wave, at);
         } else {
             // the column-sum waves issue first on their SIMD: the matrix
             // waves lose little (their products keep the matrix cores busy)
             // and the sums are ready when the products are
             __builtin_amdgcn_s_setprio(2);
-            const int h = (wave - MF_MMA_WAVES) & 1;
+            const int h = NWK == 4 ? (wave - MW) & 1 : 0;
+            const int field = NWK == 4 ? (wave - MW) >> 1 : wave - MW;
             const int w0 = h * half, cnt = h ? P.nwd - half : half;
-            if (wave < MF_MMA_WAVES + 2) {
+            if (field == 0) {
                 if (h == 0) {
                     // template sums from the staged (biased) rows of this
                     // chunk; the partial last word of a row (tm != ~0) is
@@ -446,14 +464,14 @@ void ncc_u8_mfma_kernel(NccArgs a)
                         tq = dot4u(w, w, tq);
                     }
                 }
-                mf_field_chunk<NKB, 0>(img, hcur, j0, last, one_chunk, head, P.nwd, w0, cnt, V1, P.vs, c);
+                mf_field_chunk<MW, NKB, 0>(img, hcur, j0, last, one_chunk, head, P.nwd, w0, cnt, V1, P.vs, c);
             } else {
-                mf_field_chunk<NKB, 1>(img, hcur, j0, last, one_chunk, head, P.nwd, w0, cnt, V2, P.vs, c);
+                mf_field_chunk<MW, NKB, 1>(img, hcur, j0, last, one_chunk, head, P.nwd, w0, cnt, V2, P.vs, c);
             }
             __builtin_amdgcn_s_setprio(0);
         }
     }
-    if (wave == MF_MMA_WAVES) {
+    if (wave == MW) {
         ts = wave_sum_u32(ts);
         tq = wave_sum_u32(tq);
         if (lane == 0) {
@@ -465,9 +483,9 @@ void ncc_u8_mfma_kernel(NccArgs a)
 
     // SumIT' to LDS (over the image tile): lane (g, n) holds columns
     // 64*wave + 16g + 4i + t of row n.
-    if (wave < MF_MMA_WAVES) {
+    if (wave < MW) {
         const int n = lane & 15, g = lane >> 4;
-        const int base = n * MF_ACC_STRIDE + 64 * wave + 16 * g;
+        const int base = n * ACC + 64 * wave + 16 * g;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -487,8 +505,8 @@ void ncc_u8_mfma_kernel(NccArgs a)
 
     // Each wave takes 64 consecutive columns of one output row at a time.
     unsigned long long best = 0ull;
-    for (int i = threadIdx.x; i < MF_TY * MF_TX; i += MF_THREADS) {
-        const int n = i / MF_TX, x = i % MF_TX;
+    for (int i = threadIdx.x; i < MF_TY * TX; i += NT) {
+        const int n = i / TX, x = i % TX;
         const int gx = x0 + x;
         if (gx >= a.out_w || y0 + n >= a.out_h)
             continue;
@@ -505,7 +523,7 @@ void ncc_u8_mfma_kernel(NccArgs a)
         // the column sums are of s = I - 128 and of s^2
         const uint32_t si = q1[hi] - (q1[xl] & left_keep) + (q1[ce - 1] & join_keep) + 128u * nn;
         const uint32_t sq = q2[hi] - (q2[xl] & left_keep) + (q2[ce - 1] & join_keep) + 256u * si - 16384u * nn;
-        const uint32_t st = (uint32_t)acc_it[n * MF_ACC_STRIDE + x] + 128u * si + bias;
+        const uint32_t st = (uint32_t)acc_it[n * ACC + x] + 128u * si + bias;
         if (a.sum_i) a.sum_i[o] = si;
         if (a.sum_isq) a.sum_isq[o] = sq;
         if (a.sum_it) a.sum_it[o] = st;
@@ -527,52 +545,86 @@ void ncc_u8_mfma_kernel(NccArgs a)
         peak_commit_wg(a.peak, best, reinterpret_cast<unsigned long long *>(tpl));
 }
 
-// Template rows per chunk: the most that fit two workgroups per CU (80 KiB
-// each); when that leaves fewer than 32 rows (wide template rows), the most
-// that fit one workgroup per CU.
-static int mf_fit_hc(const NccArgs &a, size_t budget)
+// Template rows per chunk: the most (up to MF_MAX_HC) whose plan fits `budget`
+// bytes of LDS, 0 if none does.
+static int mf_fit_hc(const NccArgs &a, size_t budget, int mw)
 {
     int hc = a.t_height < MF_MAX_HC ? a.t_height : MF_MAX_HC;
-    while (hc > 1 && mf_plan(a.t_width, hc).bytes > budget)
+    while (hc > 1 && mf_plan(mw, a.t_width, hc).bytes > budget)
         --hc;
-    return mf_plan(a.t_width, hc).bytes <= budget ? hc : 0;
+    return mf_plan(mw, a.t_width, hc).bytes <= budget ? hc : 0;
 }
 
-static int mf_pick_hc(const NccArgs &a)
+// 256-column tiles: the most rows that fit two workgroups per CU (80 KiB
+// each); when that leaves fewer than 32 rows (wide template rows), the most
+// that fit one workgroup per CU.
+static int mf_pick_hc4(const NccArgs &a)
 {
-    const int hc = mf_fit_hc(a, 80 * 1024);
+    const int hc = mf_fit_hc(a, 80 * 1024, 4);
     if (hc >= 32 || hc == a.t_height)
         return hc;
-    return mf_fit_hc(a, 160 * 1024);
+    return mf_fit_hc(a, 160 * 1024, 4);
 }
 
-bool ncc_mfma_supported(const NccArgs &a)
+// 128-column tiles: four 4-wave workgroups per CU (one wave per SIMD each),
+// so a quarter of the LDS; at least min(t_height, 16) rows per chunk.
+constexpr size_t MF2_LDS = 160 * 1024 / 4;
+static int mf_pick_hc2(const NccArgs &a)
 {
-    return (a.t_width + 63) / 64 <= MF_MAX_NKB && mf_pick_hc(a) > 0;
+    if ((a.t_width + 63) / 64 != 1)
+        return 0;
+    const int hc = mf_fit_hc(a, MF2_LDS, 2);
+    return hc >= (a.t_height < 16 ? a.t_height : 16) ? hc : 0;
 }
 
-template <int NKB>
+bool ncc_mfma_supported(const NccArgs &a, int mw)
+{
+    if (mw == 2)
+        return mf_pick_hc2(a) > 0;
+    return (a.t_width + 63) / 64 <= MF_MAX_NKB && mf_pick_hc4(a) > 0;
+}
+
+template <int MW, int NKB>
 static hipError_t mf_launch(const NccArgs &a, hipStream_t s)
 {
     // dynamic LDS above 64 KiB must be allowed explicitly
     static std::atomic<uint64_t> lds_allowed{0};
-    const hipError_t e = allow_lds_once(&ncc_u8_mfma_kernel<NKB>, lds_allowed);
+    const hipError_t e = allow_lds_once(&ncc_u8_mfma_kernel<MW, NKB>, lds_allowed);
     if (e != hipSuccess)
         return e;
-    const size_t lds = mf_plan(a.t_width, a.hc).bytes;
-    const dim3 grid((a.out_w + MF_TX - 1) / MF_TX, (a.out_h + MF_TY - 1) / MF_TY);
-    hipLaunchKernelGGL((ncc_u8_mfma_kernel<NKB>), grid, dim3(MF_THREADS), lds, s, a);
+    const size_t lds = mf_plan(MW, a.t_width, a.hc).bytes;
+    const dim3 grid((a.out_w + mf_tx(MW) - 1) / mf_tx(MW), (a.out_h + MF_TY - 1) / MF_TY);
+    hipLaunchKernelGGL((ncc_u8_mfma_kernel<MW, NKB>), grid, dim3(mf_threads(MW)), lds, s, a);
     return hipGetLastError();
 }
 
-hipError_t ncc_launch_mfma(NccArgs a, hipStream_t s)
+hipError_t ncc_launch_mfma(NccArgs a, hipStream_t s, int mw)
 {
-    a.hc = mf_pick_hc(a);
+    if (mw == 0 && mf_pick_hc2(a) > 0) {
+        // Two 8-wave workgroups of 256-column tiles fit per CU, four 4-wave
+        // ones of 128-column tiles: a grid a little over 2 wide tiles per CU
+        // runs a second round of them at nearly full cost (a workgroup's
+        // time is mostly its own chain of staging, walk and epilogue), where
+        // the narrow tiles may all fit at once.  Take them when they need
+        // fewer rounds, or as many when the template fits one row chunk (a
+        // narrow workgroup then stages and stores less and is no slower;
+        // with several chunks it restages the 15 overlap rows each time).
+        const int64_t cus = device_cu_count();
+        const int64_t ty = (a.out_h + MF_TY - 1) / MF_TY;
+        const int64_t t4 = (a.out_w + mf_tx(4) - 1) / mf_tx(4) * ty, t2 = (a.out_w + mf_tx(2) - 1) / mf_tx(2) * ty;
+        const int64_t r4 = (t4 + 2 * cus - 1) / (2 * cus), r2 = (t2 + 4 * cus - 1) / (4 * cus);
+        mw = r2 < r4 || (r2 == r4 && mf_pick_hc2(a) >= a.t_height) ? 2 : 4;
+    }
+    if (mw == 2) {
+        a.hc = mf_pick_hc2(a);
+        return mf_launch<2, 1>(a, s);
+    }
+    a.hc = mf_pick_hc4(a);
     switch ((a.t_width + 63) / 64) {
-    case 1: return mf_launch<1>(a, s);
-    case 2: return mf_launch<2>(a, s);
-    case 3: return mf_launch<3>(a, s);
-    default: return mf_launch<4>(a, s);
+    case 1: return mf_launch<4, 1>(a, s);
+    case 2: return mf_launch<4, 2>(a, s);
+    case 3: return mf_launch<4, 3>(a, s);
+    default: return mf_launch<4, 4>(a, s);
     }
 }
 

@@ -93,7 +93,8 @@ int ncc_u8_run(const uint8_t *image, int width, int height, int pitch_bytes,
  *   XC_NCC_AUTO          the library's choice (what ncc_u8_run uses): XC_NCC_MFMA
  *                        where it takes the template and the template has at
  *                        least 512 pixels, or at least 96 pixels with at least
- *                        400,000 outputs; else XC_NCC_DOT4_ILP
+ *                        400,000 outputs, or there are at least 1,000,000
+ *                        outputs; else XC_NCC_DOT4_ILP
  *   XC_NCC_DOT4_ILP      packed-byte dot products, 4 columns x several rows per lane
  *   XC_NCC_DOT4_C1       packed-byte dot products, one output per lane
  *   XC_NCC_SCALAR_C1     byte-at-a-time multiply-adds, one output per lane
@@ -108,6 +109,12 @@ int ncc_u8_run(const uint8_t *image, int width, int height, int pitch_bytes,
  *   XC_NCC_DOT4_ILP_Q4   each lane walking every template row itself (no split
  *                        of the template rows over waves, which
  *                        XC_NCC_DOT4_ILP adds for templates of 16 or more rows)
+ *   XC_NCC_MFMA_W4       XC_NCC_MFMA with its tile width fixed: 256 output
+ *   XC_NCC_MFMA_W2       columns per workgroup (4 matrix-core waves, two
+ *                        workgroups per CU) or 128 (2 matrix-core waves, four
+ *                        per CU; t_width <= 64 only, else XC_ERR_SHAPE).
+ *                        XC_NCC_MFMA picks the width that runs the output's
+ *                        tiles in fewer rounds of workgroups.
  */
 #define XC_NCC_AUTO 0
 #define XC_NCC_DOT4_ILP 1
@@ -117,6 +124,8 @@ int ncc_u8_run(const uint8_t *image, int width, int height, int pitch_bytes,
 #define XC_NCC_DOT4_ILP_Q1 5
 #define XC_NCC_DOT4_ILP_Q2 6
 #define XC_NCC_DOT4_ILP_Q4 7
+#define XC_NCC_MFMA_W4 8
+#define XC_NCC_MFMA_W2 9
 int ncc_u8_run_variant(const uint8_t *image, int width, int height, int pitch_bytes,
                        const uint8_t *tmpl, int t_width, int t_height,
                        uint32_t *sum_i, uint32_t *sum_isq, uint32_t *sum_it, float *coef,

@@ -14,9 +14,10 @@ import _gpu
 pytestmark = pytest.mark.gpu
 
 VARIANTS = [_lib.XC_NCC_AUTO, _lib.XC_NCC_DOT4_ILP, _lib.XC_NCC_DOT4_C1, _lib.XC_NCC_SCALAR_C1, _lib.XC_NCC_MFMA,
-            _lib.XC_NCC_DOT4_ILP_Q1, _lib.XC_NCC_DOT4_ILP_Q2, _lib.XC_NCC_DOT4_ILP_Q4]
-# template rows the matrix-core variant takes
-MFMA_MAX_T_WIDTH = 256
+            _lib.XC_NCC_DOT4_ILP_Q1, _lib.XC_NCC_DOT4_ILP_Q2, _lib.XC_NCC_DOT4_ILP_Q4, _lib.XC_NCC_MFMA_W4,
+            _lib.XC_NCC_MFMA_W2]
+# template rows the matrix-core variants take (256- and 128-column tiles)
+MFMA_MAX_T_WIDTH = {_lib.XC_NCC_MFMA: 256, _lib.XC_NCC_MFMA_W4: 256, _lib.XC_NCC_MFMA_W2: 64}
 
 
 def _case_from(img, tmpl, name="t", pitch=None):
@@ -48,7 +49,8 @@ def test_ncc_1080p_t64_full():
 
 
 @pytest.mark.parametrize("variant", [_lib.XC_NCC_DOT4_ILP, _lib.XC_NCC_DOT4_C1, _lib.XC_NCC_SCALAR_C1, _lib.XC_NCC_MFMA,
-                                     _lib.XC_NCC_DOT4_ILP_Q1, _lib.XC_NCC_DOT4_ILP_Q2, _lib.XC_NCC_DOT4_ILP_Q4])
+                                     _lib.XC_NCC_DOT4_ILP_Q1, _lib.XC_NCC_DOT4_ILP_Q2, _lib.XC_NCC_DOT4_ILP_Q4,
+                                     _lib.XC_NCC_MFMA_W4, _lib.XC_NCC_MFMA_W2])
 def test_ncc_1080p_variants_sampled(variant):
     """Ablation variants at full size: compare against the auto path bit for bit."""
     case = workload("ncc_1920x1080_t64")
@@ -152,7 +154,7 @@ def test_ncc_edge_shapes(shape, variant):
     tmpl = u8_uniform(rng, (th, tw))
     case = _case_from(img, tmpl, pitch=pitch_for(w) + extra)
     _gpu.log(f"ncc edge shape {shape} variant={variant}")
-    if variant == _lib.XC_NCC_MFMA and tw > MFMA_MAX_T_WIDTH:
+    if tw > MFMA_MAX_T_WIDTH.get(variant, tw):
         with pytest.raises(_lib.XcError) as e:
             _gpu.run_ncc(case, variant)
         assert e.value.status == _lib.XC_ERR_SHAPE
@@ -186,6 +188,33 @@ def test_ncc_mfma_shapes(shape):
     _gpu.check_ncc(case, _gpu.run_ncc(case, _lib.XC_NCC_MFMA))
 
 
+@pytest.mark.parametrize("shape", [
+    # (height, width, t_height, t_width): 128-column tiles (two matrix-core
+    # waves, one column-sum wave per field over all the words), template
+    # widths 1 .. 64 on both sides of a word, ragged column and row tiles, and
+    # templates taller than the rows one chunk holds (head rows kept)
+    (40, 200, 16, 4),
+    (31, 385, 9, 61),
+    (47, 577, 17, 64),
+    (33, 190, 5, 1),
+    (90, 450, 29, 63),        # two row chunks
+    (150, 400, 64, 64),       # three row chunks
+    (140, 250, 100, 7),       # many chunks of a narrow template
+    (1, 1024, 1, 64),         # one output row
+    (600, 64, 100, 64),       # one output column
+    (20, 129, 20, 2),         # one row, one column tile and one column over
+])
+@pytest.mark.parametrize("variant", [_lib.XC_NCC_MFMA_W2, _lib.XC_NCC_MFMA_W4])
+def test_ncc_mfma_tile_widths(shape, variant):
+    h, w, th, tw = shape
+    rng = np.random.default_rng(h * 137 + w * 11 + th)
+    img = u8_uniform(rng, (h, w))
+    tmpl = u8_uniform(rng, (th, tw))
+    case = _case_from(img, tmpl)
+    _gpu.log(f"ncc mfma tile width shape {shape} variant {variant}")
+    _gpu.check_ncc(case, _gpu.run_ncc(case, variant))
+
+
 def test_ncc_mfma_extreme_pixels():
     """All-255 and all-0 windows against 0/255 templates: the -128 bias and its
     exact correction at the ends of the byte range."""
@@ -195,8 +224,9 @@ def test_ncc_mfma_extreme_pixels():
         tmpl = np.full((12, 64), tv, np.uint8)
         tmpl[0, 0] = 255 - tv
         case = _case_from(img, tmpl)
-        _gpu.log(f"ncc mfma extremes image={iv} template={tv}")
-        _gpu.check_ncc(case, _gpu.run_ncc(case, _lib.XC_NCC_MFMA))
+        for v in (_lib.XC_NCC_MFMA_W4, _lib.XC_NCC_MFMA_W2):
+            _gpu.log(f"ncc mfma extremes image={iv} template={tv} variant {v}")
+            _gpu.check_ncc(case, _gpu.run_ncc(case, v))
 
 
 def test_ncc_output_subsets():

@@ -21,12 +21,16 @@ VARIANTS = {
     "ilp_q1": _lib.XC_NCC_DOT4_ILP_Q1,
     "ilp_q2": _lib.XC_NCC_DOT4_ILP_Q2,
     "ilp_q4": _lib.XC_NCC_DOT4_ILP_Q4,
+    "mfma_w4": _lib.XC_NCC_MFMA_W4,
+    "mfma_w2": _lib.XC_NCC_MFMA_W2,
 }
+# template rows the matrix-core variants take (256- and 128-column tiles)
+MAX_T_WIDTH = {"mfma": 256, "mfma_w4": 256, "mfma_w2": 64}
 
 
 def _variants(case):
-    """Every variant that takes the case (the matrix-core kernel takes rows up to 256 bytes)."""
-    return {k: v for k, v in VARIANTS.items() if k != "mfma" or case.t_width <= 256}
+    """Every variant that takes the case's template width."""
+    return {k: v for k, v in VARIANTS.items() if case.t_width <= MAX_T_WIDTH.get(k, case.t_width)}
 
 
 # (height, width, t_height, t_width): widths below four, odd and even

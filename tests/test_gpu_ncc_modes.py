@@ -16,7 +16,7 @@ pytestmark = pytest.mark.gpu
 
 MODES = {"same": _lib.XC_NCC_MODE_SAME, "full": _lib.XC_NCC_MODE_FULL}
 VARIANTS = {"auto": _lib.XC_NCC_AUTO, "ilp": _lib.XC_NCC_DOT4_ILP, "c1": _lib.XC_NCC_DOT4_C1,
-            "scalar": _lib.XC_NCC_SCALAR_C1, "mfma": _lib.XC_NCC_MFMA}
+            "scalar": _lib.XC_NCC_SCALAR_C1, "mfma": _lib.XC_NCC_MFMA, "mfma_w2": _lib.XC_NCC_MFMA_W2}
 WS_SENTINEL = 0xA5
 
 
@@ -78,7 +78,7 @@ def test_ncc_mode_matches_oracle(shape, mode):
     case = ncc_case("m", 600 + th * 13 + tw, h, w, th, tw, cut=False)
     ref = oracle.ncc_u8_mode(case.image, case.width, case.height, case.tmpl, MODES[mode])
     for vname, v in VARIANTS.items():
-        if vname == "mfma" and tw > 256:
+        if (vname == "mfma" and tw > 256) or (vname == "mfma_w2" and tw > 64):
             continue
         _gpu.log(f"ncc mode {mode} {shape} variant {vname}")
         _check(run_mode(case, MODES[mode], v), ref)
