@@ -6,6 +6,7 @@ prints the case it runs before touching the GPU.
 import numpy as np
 import pytest
 
+import oracle
 from cross_correlation_amd import _lib
 from cross_correlation_amd.inputs import ncc_case, u8_uniform, workload, pitch_for
 
@@ -46,6 +47,29 @@ def test_ncc_1080p_t64_full():
     _gpu.check_ncc(case, res)
     oy, ox = case.cut
     assert res["coef"][oy, ox] == np.float32(1.0)
+
+
+@pytest.mark.parametrize("th,tw", [(4, 4), (6, 6), (8, 8), (5, 13)])
+def test_ncc_1080p_small_templates_auto(th, tw):
+    """1920x1080 with small templates on the automatic path (the matrix-core
+    kernel from 1M outputs, on 128-column tiles here): 3,000 sampled windows
+    and the corners against the oracle, coefficient 1 at the cut, and every
+    output equal to the packed-byte kernel's bit for bit."""
+    case = ncc_case("s", 940 + th * tw, 1080, 1920, th, tw, cut=True)
+    _gpu.log(f"ncc 1080p small template {th}x{tw} auto")
+    res = _gpu.run_ncc(case)
+    oh, ow = res["sum_i"].shape
+    rng = np.random.default_rng(941)
+    ys = np.concatenate([[0, 0, oh - 1, oh - 1], rng.integers(0, oh, 3000)])
+    xs = np.concatenate([[0, ow - 1, 0, ow - 1], rng.integers(0, ow, 3000)])
+    ref = oracle.ncc_u8_points(case.image, case.width, case.height, case.tmpl, ys, xs)
+    for k in ("sum_i", "sum_isq", "sum_it"):
+        assert np.array_equal(res[k][ys, xs], ref[k]), k
+    assert np.array_equal(res["coef"][ys, xs].view(np.uint32), ref["coef"].view(np.uint32))
+    assert res["coef"][case.cut] == np.float32(1.0)
+    ilp = _gpu.run_ncc(case, _lib.XC_NCC_DOT4_ILP)
+    for k in res:
+        assert np.array_equal(res[k].view(np.uint32), ilp[k].view(np.uint32)), k
 
 
 @pytest.mark.parametrize("variant", [_lib.XC_NCC_DOT4_ILP, _lib.XC_NCC_DOT4_C1, _lib.XC_NCC_SCALAR_C1, _lib.XC_NCC_MFMA,
