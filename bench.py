@@ -187,9 +187,9 @@ def bench_ncc_ext(args, torch, lib, inputs):
     """The generalizations on the headline image: the best-match search
     (ncc_u8_peak, with and without the coefficient map), a template width
     that is not a multiple of four (63 x 63, the last packed word of each
-    template row masked), next to the 64 x 64 template, and the same and full
-    output modes (ncc_u8_run_mode: the zero-padded copy, then the automatic
-    variant; all four outputs)."""
+    template row masked), a 16 x 16 template (the matrix-core kernel's two
+    tile widths), and the same and full output modes (ncc_u8_run_mode: the
+    zero-padded copy, then the automatic variant; all four outputs)."""
     from cross_correlation_amd.inputs import ncc_case
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream().cuda_stream
@@ -210,24 +210,30 @@ def bench_ncc_ext(args, torch, lib, inputs):
         wall, per = timed_loop(launch, steps, warmup, torch)
         res[name] = {"ms_per_step": round(wall, 5), "launches_ms": round(per, 5),
                      "outputs_per_s": round(oh * ow / (per * 1e-3), 1)}
-    odd = ncc_case("ncc_1920x1080_t63", 2, 1080, 1920, 63, 63, image_kind="gradient", cut=True)
-    img63 = torch.from_numpy(odd.image).to(dev)
-    tm63 = torch.from_numpy(odd.tmpl).to(dev)
-    oh63, ow63 = odd.out_shape
-    outs = [torch.empty((oh63, ow63), dtype=torch.int32, device=dev) for _ in range(3)]
-    coef63 = torch.empty((oh63, ow63), dtype=torch.float32, device=dev)
-    for vname, v in (("dot4_ilp", lib.XC_NCC_DOT4_ILP), ("auto", lib.XC_NCC_AUTO)):
-        def launch():
-            st = lib.ncc_u8_run(img63.data_ptr(), odd.width, odd.height, odd.pitch, tm63.data_ptr(), odd.t_width,
-                                odd.t_height, outs[0].data_ptr(), outs[1].data_ptr(), outs[2].data_ptr(),
-                                coef63.data_ptr(), stream=stream, variant=v)
-            if st != 0:
-                raise RuntimeError(lib.status_str(st))
-        wall, per = timed_loop(launch, steps, warmup, torch)
-        # packed-byte work: 3 dot4 per packed word (16 per row, the last one masked) per output
-        dot4 = 3 * ((odd.t_width + 3) // 4) * odd.t_height * oh63 * ow63
-        res[f"t63x63_{vname}"] = {"kernel_ms": round(per, 5), "outputs_per_s": round(oh63 * ow63 / (per * 1e-3), 1),
-                                  "issued_Gdot4_per_s": round(dot4 / (per * 1e-3) / 1e9, 2)}
+    # A template width that is not a multiple of four (63 x 63), and a small
+    # template (16 x 16: 536 matrix-core tiles of 256 columns, two rounds of
+    # two workgroups per CU, against 1,005 of 128 columns, one round of four).
+    for tname, t, vlist in (("t63x63", 63, (("dot4_ilp", lib.XC_NCC_DOT4_ILP), ("auto", lib.XC_NCC_AUTO))),
+                            ("t16x16", 16, (("dot4_ilp", lib.XC_NCC_DOT4_ILP), ("mfma_w4", lib.XC_NCC_MFMA_W4),
+                                            ("auto", lib.XC_NCC_AUTO)))):
+        sc = ncc_case(f"ncc_1920x1080_{tname}", 2, 1080, 1920, t, t, image_kind="gradient", cut=True)
+        img_s = torch.from_numpy(sc.image).to(dev)
+        tm_s = torch.from_numpy(sc.tmpl).to(dev)
+        oh_s, ow_s = sc.out_shape
+        outs = [torch.empty((oh_s, ow_s), dtype=torch.int32, device=dev) for _ in range(3)]
+        coef_s = torch.empty((oh_s, ow_s), dtype=torch.float32, device=dev)
+        for vname, v in vlist:
+            def launch():
+                st = lib.ncc_u8_run(img_s.data_ptr(), sc.width, sc.height, sc.pitch, tm_s.data_ptr(), sc.t_width,
+                                    sc.t_height, outs[0].data_ptr(), outs[1].data_ptr(), outs[2].data_ptr(),
+                                    coef_s.data_ptr(), stream=stream, variant=v)
+                if st != 0:
+                    raise RuntimeError(lib.status_str(st))
+            wall, per = timed_loop(launch, steps, warmup, torch)
+            # packed-byte work: 3 dot4 per packed word (the last one masked when t % 4 != 0) per output
+            dot4 = 3 * ((sc.t_width + 3) // 4) * sc.t_height * oh_s * ow_s
+            res[f"{tname}_{vname}"] = {"kernel_ms": round(per, 5), "outputs_per_s": round(oh_s * ow_s / (per * 1e-3), 1),
+                                       "issued_Gdot4_per_s": round(dot4 / (per * 1e-3) / 1e9, 2)}
     for mname, mode in (("same_mode", lib.XC_NCC_MODE_SAME), ("full_mode", lib.XC_NCC_MODE_FULL)):
         st, nbytes = lib.ncc_u8_mode_workspace(case.width, case.height, case.t_width, case.t_height, mode)
         if st != 0:
