@@ -31,8 +31,9 @@
 //     doubles the waves per SIMD without a second copy of the tile.
 //   * Image tiles are staged into LDS with 16-byte loads (the page's uint4
 //     versus int finding: wide coalesced copies into on-chip memory).
-//   * The epilogue forms num, vI, vT exactly in 64-bit integers and divides in
-//     fp64, so the coefficient is the correctly rounded fp32 of the fp64 value.
+//   * The epilogue forms num, vI, vT exactly in 64-bit integers; the
+//     coefficient (ncc_coef_f32) is the fp32 rounding of the IEEE fp64
+//     quotient num / sqrt(vI * vT), bit for bit.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
