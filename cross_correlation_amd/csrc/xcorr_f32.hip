@@ -914,7 +914,10 @@ hipError_t xcorr_launch_blockdiag(const XcorrArgs &a, hipStream_t s)
         b.nls = 1;
         b.n_groups = (int)npairs;
         b.n_xtiles = b.wp / BD_P;
-        return launch_big<16, 8>(b, s);
+        // 16 walk steps per chunk: half the barriers of 8 (the prefetch of
+        // the next chunk overlaps the walk either way); five prologue values
+        // spill, reloaded once per pass
+        return launch_big<16, 16>(b, s);
     }
     b.S = 64 / b.nb;
     b.n_groups = (int)((npairs + b.S - 1) / b.S);
