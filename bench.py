@@ -345,7 +345,27 @@ def cpu_baseline(args, inputs, oracle_mod):
         "cores": oracle_mod.max_threads(),
         "kind": "oracle",
         "sample": f"{what} of the 1920x1080 image / 64x64 template workload ({dt:.1f} s)",
+        "host": host_info(),
     }
+
+
+def host_info() -> dict:
+    """The host the oracle ran on: CPU model, CPUs this process may use, and
+    OMP_NUM_THREADS as set."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count()
+    return {"cpu_model": model, "usable_cpus": usable, "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
 
 
 def main():
