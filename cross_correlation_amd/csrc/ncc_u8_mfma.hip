@@ -38,8 +38,11 @@
 //   * Tiles: 16 output rows by 256 columns (four matrix-core waves, two
 //     workgroups per CU) or 128 columns (two, four workgroups per CU, for
 //     templates up to 64 bytes wide); the launcher takes the narrow tiles
-//     when they run the grid in fewer rounds of workgroups, or in as many
-//     with the template in one row chunk.
+//     when they run the grid in fewer rounds of workgroups, or when the wide
+//     ones would cover at most half of the CUs.  On narrow tiles whose row
+//     prefixes would not let the template fit one row chunk, the column-sum
+//     waves store the window sums themselves (the prefix at x + t_width - 1
+//     less the one at x - 1, read across lanes), which take less LDS.
 //   * The coefficient follows the packed-byte kernels' exact formula: num, vI
 //     and vT are exact integers (held in fp64 here, formed with fused
 //     multiply-adds), then ncc_coef_f32, so both paths return the same bits.
@@ -85,6 +88,7 @@ struct MfPlan {
     int nwd;      // image words covered by the column sums (16 MW .. 16 MW + 64)
     int vs;       // u32 per row of V (a multiple of 4: 16-byte stores)
     int img_words;
+    int head_words;  // the first MF_TY - 1 rows' words, kept only when the template comes in several chunks
     size_t bytes;
 };
 
@@ -94,7 +98,7 @@ struct MfPlan {
 __host__ __device__ constexpr int mf_sw(int mw, int nkb) { return 16 * mw + 16 * nkb + 4; }
 __host__ __device__ constexpr int mf_tsb(int nkb) { return 64 * nkb + 16; }
 
-__host__ __device__ inline MfPlan mf_plan(int mw, int t_width, int hc)
+__host__ __device__ inline MfPlan mf_plan(int mw, int t_width, int hc, bool one_chunk, bool win)
 {
     MfPlan p;
     p.nkb = (t_width + 63) / 64;
@@ -103,12 +107,17 @@ __host__ __device__ inline MfPlan mf_plan(int mw, int t_width, int hc)
     p.tsb = mf_tsb(p.nkb);
     p.trows = hc + 2 * MF_TY - 1;
     p.nwd = 16 * mw + (t_width + 2) / 4;  // words holding columns 0 .. 64 mw - 1 + t_width - 1
-    p.vs = 4 * p.nwd + 4;
+    // each row's prefix over the words (in two halves when MW = 4), or with
+    // `win` (MW = 2) the window sums of the tile's 128 outputs themselves,
+    // which take less LDS (a row is stored and read by consecutive lanes, so
+    // it needs no padding)
+    p.vs = win ? 128 : 4 * p.nwd + 4;
     int img = (MF_TY + hc) * p.sw;  // staged rows + one spare row
     if (img < MF_TY * mf_acc_stride(mw)) img = MF_TY * mf_acc_stride(mw);
     p.img_words = img;
+    p.head_words = one_chunk ? 0 : (MF_TY - 1) * p.nwd;
     p.bytes = (size_t)2 * MF_TY * p.vs * 4 + (size_t)img * 4 + (size_t)p.trows * p.tsb +
-              (size_t)(MF_TY - 1) * p.nwd * 4 + 8;
+              (size_t)p.head_words * 4 + 8;
     return p;
 }
 
@@ -344,19 +353,55 @@ __device__ __forceinline__ uint4 mf_row_prefix4(const uint32_t (&c)[4])
 // in one chunk, else the saved head row).  Each row's prefix along the wave's
 // half (mf_row_prefix4) goes to row n of V (row stride vs) when `keep`; reads
 // are unconditional and every lane takes part in the scans.
-template <int MW, int NKB, int F>
+// One row of the window sums of a 128-column tile (MW = 2, one column-sum
+// wave per field over all the words, so lane l's prefix `pre` covers columns
+// 4l .. 4l + 3 from column 0): lane l < 32 stores the sums over columns
+// [x, x + tw) for its outputs x = 4l + k, the prefix at x + tw - 1 (lanes
+// l + d and l + d + 1, d = (tw - 1) / 4, read across the wave) less the
+// prefix at x - 1.  Every lane takes part in the cross-lane reads.
+__device__ __forceinline__ void mf_store_windows(const uint4 pre, int tw, uint32_t *row)
+{
+    const int lane = threadIdx.x & 63;
+    const int d = (tw - 1) >> 2, r = (tw - 1) & 3;  // wave-uniform
+    const int la = min(lane + d, 63), lb = min(lane + d + 1, 63);
+    const uint32_t a[4] = {(uint32_t)__shfl((int)pre.x, la, 64), (uint32_t)__shfl((int)pre.y, la, 64),
+                           (uint32_t)__shfl((int)pre.z, la, 64), (uint32_t)__shfl((int)pre.w, la, 64)};
+    const uint32_t b[3] = {(uint32_t)__shfl((int)pre.x, lb, 64), (uint32_t)__shfl((int)pre.y, lb, 64),
+                           (uint32_t)__shfl((int)pre.z, lb, 64)};
+    const uint32_t prev = (uint32_t)__shfl((int)pre.w, max(lane - 1, 0), 64);
+    // hi = prefix at columns 4l + k + tw - 1, k = 0..3: components k + r of
+    // lane l + d, continuing into lane l + d + 1
+    uint4 hi;
+    switch (r) {
+    case 0: hi = make_uint4(a[0], a[1], a[2], a[3]); break;
+    case 1: hi = make_uint4(a[1], a[2], a[3], b[0]); break;
+    case 2: hi = make_uint4(a[2], a[3], b[0], b[1]); break;
+    default: hi = make_uint4(a[3], b[0], b[1], b[2]); break;
+    }
+    if (lane < 32)
+        *reinterpret_cast<uint4 *>(row + 4 * lane) =
+            make_uint4(hi.x - (lane > 0 ? prev : 0u), hi.y - pre.x, hi.z - pre.y, hi.w - pre.z);
+}
+
+template <int MW, int NKB, int F, bool WIN>
 __device__ __forceinline__ void mf_slide_word(const uint32_t *img, int hcur, bool one_chunk, const uint32_t *head,
-                                              int nwd, int wd, bool keep, uint32_t *V, int vs, uint32_t (&c)[4])
+                                              int nwd, int wd, bool keep, uint32_t *V, int vs, int tw,
+                                              uint32_t (&c)[4])
 {
     constexpr int sw = mf_sw(MW, NKB);
     uint32_t in[MF_TY - 1], out[MF_TY - 1];
 #pragma unroll
     for (int n = 1; n < MF_TY; ++n) {
         in[n - 1] = img[(hcur + n - 1) * sw + wd];
-        out[n - 1] = one_chunk ? img[(n - 1) * sw + wd] : head[(n - 1) * nwd + wd];
+        // one address, then one read: the head rows exist only when the
+        // template came in several chunks
+        const uint32_t *src = one_chunk ? img + (n - 1) * sw + wd : head + (n - 1) * nwd + wd;
+        out[n - 1] = *src;
     }
     uint4 pre = mf_row_prefix4(c);
-    if (keep)
+    if (WIN)
+        mf_store_windows(pre, tw, V);
+    else if (keep)
         *reinterpret_cast<uint4 *>(V + 4 * wd) = pre;
 #pragma unroll
     for (int n = 1; n < MF_TY; ++n) {
@@ -367,7 +412,9 @@ __device__ __forceinline__ void mf_slide_word(const uint32_t *img, int hcur, boo
         for (int k = 0; k < 4; ++k)
             c[k] -= r[k];
         pre = mf_row_prefix4(c);
-        if (keep)
+        if (WIN)
+            mf_store_windows(pre, tw, V + n * vs);
+        else if (keep)
             *reinterpret_cast<uint4 *>(V + n * vs + 4 * wd) = pre;
     }
 }
@@ -376,9 +423,9 @@ __device__ __forceinline__ void mf_slide_word(const uint32_t *img, int hcur, boo
 // prefix, of field F over words [w0, w0 + cnt) by one column-sum wave.  The
 // prefix runs over the wave's own columns [4*w0, 4*(w0 + cnt)), starting from
 // zero.
-template <int MW, int NKB, int F>
+template <int MW, int NKB, int F, bool WIN>
 __device__ __forceinline__ void mf_field_chunk(const uint32_t *img, int hcur, int j0, bool last, bool one_chunk,
-                                               uint32_t *head, int nwd, int w0, int cnt, uint32_t *V, int vs,
+                                               uint32_t *head, int nwd, int w0, int cnt, uint32_t *V, int vs, int tw,
                                                uint32_t (&c)[4])
 {
     const int lane = threadIdx.x & 63;
@@ -386,7 +433,7 @@ __device__ __forceinline__ void mf_field_chunk(const uint32_t *img, int hcur, in
     const bool keep = lane < cnt;
     mf_col_walk<MW, NKB, F>(img, hcur, j0, !one_chunk, head, nwd, wd, keep, c);
     if (last)
-        mf_slide_word<MW, NKB, F>(img, hcur, one_chunk, head, nwd, wd, keep, V, vs, c);
+        mf_slide_word<MW, NKB, F, WIN>(img, hcur, one_chunk, head, nwd, wd, keep, V, vs, tw, c);
 }
 
 // Workgroup roles (wave-uniform): waves 0 .. MW - 1 run the matrix cores, 64
@@ -398,19 +445,20 @@ __device__ __forceinline__ void mf_field_chunk(const uint32_t *img, int hcur, in
 // of each half starts from zero; the epilogue adds the first half's row total
 // where a window reaches from the first half into the second (with one half,
 // never).
-template <int MW, int NKB>
+template <int MW, int NKB, bool WIN>
 __global__ __launch_bounds__(mf_threads(MW)) __attribute__((amdgpu_waves_per_eu(NKB == 1 ? 4 : 1)))
 void ncc_u8_mfma_kernel(NccArgs a)
 {
     constexpr int NT = mf_threads(MW), TX = mf_tx(MW), NWK = mf_walkers(MW), ACC = mf_acc_stride(MW);
     extern __shared__ uint4 mf_smem[];
-    const MfPlan P = mf_plan(MW, a.t_width, a.hc);
+    static_assert(!WIN || MW == 2, "window sums need one column-sum wave over all the words");
+    const MfPlan P = mf_plan(MW, a.t_width, a.hc, a.t_height <= a.hc, WIN);
     uint32_t *const V1 = reinterpret_cast<uint32_t *>(mf_smem);
     uint32_t *const V2 = V1 + MF_TY * P.vs;
     uint32_t *const img = V2 + MF_TY * P.vs;
     uint8_t *const tpl = reinterpret_cast<uint8_t *>(img + P.img_words);
     uint32_t *const head = reinterpret_cast<uint32_t *>(tpl + P.trows * P.tsb);
-    uint32_t *const tsum = head + (MF_TY - 1) * P.nwd;
+    uint32_t *const tsum = head + P.head_words;
     int32_t *const acc_it = reinterpret_cast<int32_t *>(img);
 
     const int x0 = blockIdx.x * TX, y0 = blockIdx.y * MF_TY;
@@ -464,9 +512,9 @@ void ncc_u8_mfma_kernel(NccArgs a)
                         tq = dot4u(w, w, tq);
                     }
                 }
-                mf_field_chunk<MW, NKB, 0>(img, hcur, j0, last, one_chunk, head, P.nwd, w0, cnt, V1, P.vs, c);
+                mf_field_chunk<MW, NKB, 0, WIN>(img, hcur, j0, last, one_chunk, head, P.nwd, w0, cnt, V1, P.vs, tw, c);
             } else {
-                mf_field_chunk<MW, NKB, 1>(img, hcur, j0, last, one_chunk, head, P.nwd, w0, cnt, V2, P.vs, c);
+                mf_field_chunk<MW, NKB, 1, WIN>(img, hcur, j0, last, one_chunk, head, P.nwd, w0, cnt, V2, P.vs, tw, c);
             }
             __builtin_amdgcn_s_setprio(0);
         }
@@ -520,9 +568,16 @@ void ncc_u8_mfma_kernel(NccArgs a)
         const uint32_t join_keep = hi >= ce && (x == 0 || x - 1 < ce) ? 0xFFFFFFFFu : 0u;
         const uint32_t *q1 = V1 + n * P.vs;
         const uint32_t *q2 = V2 + n * P.vs;
-        // the column sums are of s = I - 128 and of s^2
-        const uint32_t si = q1[hi] - (q1[xl] & left_keep) + (q1[ce - 1] & join_keep) + 128u * nn;
-        const uint32_t sq = q2[hi] - (q2[xl] & left_keep) + (q2[ce - 1] & join_keep) + 256u * si - 16384u * nn;
+        uint32_t si, sq;
+        if (WIN) {
+            // the column-sum waves stored the window sums themselves
+            si = q1[x] + 128u * nn;
+            sq = q2[x] + 256u * si - 16384u * nn;
+        } else {
+            // the column sums are of s = I - 128 and of s^2
+            si = q1[hi] - (q1[xl] & left_keep) + (q1[ce - 1] & join_keep) + 128u * nn;
+            sq = q2[hi] - (q2[xl] & left_keep) + (q2[ce - 1] & join_keep) + 256u * si - 16384u * nn;
+        }
         const uint32_t st = (uint32_t)acc_it[n * ACC + x] + 128u * si + bias;
         if (a.sum_i) a.sum_i[o] = si;
         if (a.sum_isq) a.sum_isq[o] = sq;
@@ -547,12 +602,12 @@ void ncc_u8_mfma_kernel(NccArgs a)
 
 // Template rows per chunk: the most (up to MF_MAX_HC) whose plan fits `budget`
 // bytes of LDS, 0 if none does.
-static int mf_fit_hc(const NccArgs &a, size_t budget, int mw)
+static int mf_fit_hc(const NccArgs &a, size_t budget, int mw, bool win)
 {
     int hc = a.t_height < MF_MAX_HC ? a.t_height : MF_MAX_HC;
-    while (hc > 1 && mf_plan(mw, a.t_width, hc).bytes > budget)
+    while (hc > 1 && mf_plan(mw, a.t_width, hc, hc >= a.t_height, win).bytes > budget)
         --hc;
-    return mf_plan(mw, a.t_width, hc).bytes <= budget ? hc : 0;
+    return mf_plan(mw, a.t_width, hc, hc >= a.t_height, win).bytes <= budget ? hc : 0;
 }
 
 // 256-column tiles: the most rows that fit two workgroups per CU (80 KiB
@@ -560,71 +615,83 @@ static int mf_fit_hc(const NccArgs &a, size_t budget, int mw)
 // that fit one workgroup per CU.
 static int mf_pick_hc4(const NccArgs &a)
 {
-    const int hc = mf_fit_hc(a, 80 * 1024, 4);
+    const int hc = mf_fit_hc(a, 80 * 1024, 4, false);
     if (hc >= 32 || hc == a.t_height)
         return hc;
-    return mf_fit_hc(a, 160 * 1024, 4);
+    return mf_fit_hc(a, 160 * 1024, 4, false);
 }
 
 // 128-column tiles: four 4-wave workgroups per CU (one wave per SIMD each),
-// so a quarter of the LDS; at least min(t_height, 16) rows per chunk.
+// so a quarter of the LDS.  The column-sum waves store row prefixes when the
+// template then fits one row chunk (the cheaper form for them), else window
+// sums when those let it fit one, else prefixes in chunks of at least
+// min(t_height, 16) rows.
 constexpr size_t MF2_LDS = 160 * 1024 / 4;
-static int mf_pick_hc2(const NccArgs &a)
+struct Mf2Pick {
+    int hc;
+    bool win;
+};
+static Mf2Pick mf_pick2(const NccArgs &a)
 {
     if ((a.t_width + 63) / 64 != 1)
-        return 0;
-    const int hc = mf_fit_hc(a, MF2_LDS, 2);
-    return hc >= (a.t_height < 16 ? a.t_height : 16) ? hc : 0;
+        return {0, false};
+    const int hp = mf_fit_hc(a, MF2_LDS, 2, false);
+    if (hp >= a.t_height)
+        return {hp, false};
+    if (mf_fit_hc(a, MF2_LDS, 2, true) >= a.t_height)
+        return {a.t_height, true};
+    return {hp >= (a.t_height < 16 ? a.t_height : 16) ? hp : 0, false};
 }
 
 bool ncc_mfma_supported(const NccArgs &a, int mw)
 {
     if (mw == 2)
-        return mf_pick_hc2(a) > 0;
+        return mf_pick2(a).hc > 0;
     return (a.t_width + 63) / 64 <= MF_MAX_NKB && mf_pick_hc4(a) > 0;
 }
 
-template <int MW, int NKB>
-static hipError_t mf_launch(const NccArgs &a, hipStream_t s)
+template <int MW, int NKB, bool WIN>
+static hipError_t mf_launch(NccArgs a, hipStream_t s)
 {
     // dynamic LDS above 64 KiB must be allowed explicitly
     static std::atomic<uint64_t> lds_allowed{0};
-    const hipError_t e = allow_lds_once(&ncc_u8_mfma_kernel<MW, NKB>, lds_allowed);
+    const hipError_t e = allow_lds_once(&ncc_u8_mfma_kernel<MW, NKB, WIN>, lds_allowed);
     if (e != hipSuccess)
         return e;
-    const size_t lds = mf_plan(MW, a.t_width, a.hc).bytes;
+    const size_t lds = mf_plan(MW, a.t_width, a.hc, a.hc >= a.t_height, WIN).bytes;
     const dim3 grid((a.out_w + mf_tx(MW) - 1) / mf_tx(MW), (a.out_h + MF_TY - 1) / MF_TY);
-    hipLaunchKernelGGL((ncc_u8_mfma_kernel<MW, NKB>), grid, dim3(mf_threads(MW)), lds, s, a);
+    hipLaunchKernelGGL((ncc_u8_mfma_kernel<MW, NKB, WIN>), grid, dim3(mf_threads(MW)), lds, s, a);
     return hipGetLastError();
 }
 
 hipError_t ncc_launch_mfma(NccArgs a, hipStream_t s, int mw)
 {
-    if (mw == 0 && mf_pick_hc2(a) > 0) {
+    const Mf2Pick p2 = mf_pick2(a);
+    if (mw == 0 && p2.hc >= a.t_height) {
         // Two 8-wave workgroups of 256-column tiles fit per CU, four 4-wave
         // ones of 128-column tiles: a grid a little over 2 wide tiles per CU
         // runs a second round of them at nearly full cost (a workgroup's
         // time is mostly its own chain of staging, walk and epilogue), where
-        // the narrow tiles may all fit at once.  Take them when they need
-        // fewer rounds, or as many when the template fits one row chunk (a
-        // narrow workgroup then stages and stores less and is no slower;
-        // with several chunks it restages the 15 overlap rows each time).
+        // the narrow tiles may all fit at once.  Take the narrow tiles (with
+        // the template in one row chunk) when they need fewer rounds, or
+        // when the wide ones would cover at most half of the CUs; on a full
+        // grid at equal rounds the wide ones are faster.
         const int64_t cus = device_cu_count();
         const int64_t ty = (a.out_h + MF_TY - 1) / MF_TY;
         const int64_t t4 = (a.out_w + mf_tx(4) - 1) / mf_tx(4) * ty, t2 = (a.out_w + mf_tx(2) - 1) / mf_tx(2) * ty;
         const int64_t r4 = (t4 + 2 * cus - 1) / (2 * cus), r2 = (t2 + 4 * cus - 1) / (4 * cus);
-        mw = r2 < r4 || (r2 == r4 && mf_pick_hc2(a) >= a.t_height) ? 2 : 4;
+        mw = r2 < r4 || 2 * t4 <= cus ? 2 : 4;
     }
     if (mw == 2) {
-        a.hc = mf_pick_hc2(a);
-        return mf_launch<2, 1>(a, s);
+        a.hc = p2.hc;
+        return p2.win ? mf_launch<2, 1, true>(a, s) : mf_launch<2, 1, false>(a, s);
     }
     a.hc = mf_pick_hc4(a);
     switch ((a.t_width + 63) / 64) {
-    case 1: return mf_launch<4, 1>(a, s);
-    case 2: return mf_launch<4, 2>(a, s);
-    case 3: return mf_launch<4, 3>(a, s);
-    default: return mf_launch<4, 4>(a, s);
+    case 1: return mf_launch<4, 1, false>(a, s);
+    case 2: return mf_launch<4, 2, false>(a, s);
+    case 3: return mf_launch<4, 3, false>(a, s);
+    default: return mf_launch<4, 4, false>(a, s);
     }
 }
 
