@@ -6,44 +6,53 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "kernels.h"
 #include "ncc_common.h"
 
 namespace xc {
 
 // Zero-padded copy for the same and full output modes (see ncc_pad_image).
-// A thread writes 16 bytes of one row; each 4-byte word is assembled from the
-// two aligned image words holding its bytes (v_alignbyte_b32), its bytes
-// outside the image (or past out_w) cleared.
+// A thread writes 16 bytes of one row.  Their image bytes start at column
+// s = c0 - pad_left, so all four output words take the same byte shift
+// (s mod 4) of five consecutive aligned image words; the five loads are
+// unconditional (addresses clamped into the row) and the bytes outside the
+// image, or past out_w, are cleared afterwards.
 __global__ __launch_bounds__(256) void ncc_pad_kernel(const uint8_t *__restrict__ image, int width, int height,
-                                                      int pitch, uint8_t *__restrict__ out, int out_w, int out_h,
-                                                      int out_pitch, int pad_top, int pad_left)
+                                                      int pitch, uint8_t *__restrict__ out, int out_w, int out_pitch,
+                                                      int pad_top, int pad_left, int row0, int nrows)
 {
     const int chunks = out_pitch / 16;
-    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (t >= (int64_t)out_h * chunks)
+    const int t = blockIdx.x * 256 + threadIdx.x;  // nrows * chunks <= 2^30: see ncc_pad_image
+    if (t >= nrows * chunks)
         return;
-    const int r = (int)(t / chunks);
-    const int c0 = (int)(t - (int64_t)r * chunks) * 16;
+    const int rl = t / chunks;
+    const int c0 = (t - rl * chunks) * 16;
+    const int r = row0 + rl;
     const int sr = r - pad_top;
-    uint32_t w[4] = {0u, 0u, 0u, 0u};
-    if (sr >= 0 && sr < height) {
-        const uint32_t *row = reinterpret_cast<const uint32_t *>(image + (size_t)sr * pitch);
-        const int nwords = pitch / 4;
+    const bool row_ok = sr >= 0 && sr < height;
+    const uint32_t *row = reinterpret_cast<const uint32_t *>(image + (size_t)(row_ok ? sr : 0) * pitch);
+    const int nwords = pitch / 4;
+    const int s = c0 - pad_left;   // image column of the chunk's first byte (may be negative)
+    const int sh = s & 3;          // two's complement: the remainder in 0..3
+    const int w0 = (s - sh) / 4;   // exact: floor(s / 4)
+    uint32_t v[5];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int s = c0 + 4 * q - pad_left;  // image column of the word's first byte (may be negative)
-            const int sh = s & 3;                 // two's complement: the remainder in 0..3
-            const int sw = (s - sh) / 4;          // exact: floor(s / 4)
-            const uint32_t lo = sw >= 0 && sw < nwords ? row[sw] : 0u;
-            const uint32_t hi = sw + 1 >= 0 && sw + 1 < nwords ? row[sw + 1] : 0u;
-            uint32_t m = 0u;
+    for (int k = 0; k < 5; ++k) {
+        const int wi = w0 + k;
+        v[k] = row[wi < 0 ? 0 : (wi < nwords ? wi : nwords - 1)];
+    }
+    // bytes [lo, hi) of the 16 are image pixels inside the output row
+    const int lo = max(0, -s);
+    const int hi = row_ok ? min(16, min(width - s, out_w - c0)) : 0;
+    uint32_t w[4];
 #pragma unroll
-            for (int b = 0; b < 4; ++b)
-                if (s + b >= 0 && s + b < width && c0 + 4 * q + b < out_w)
-                    m |= 0xFFu << (8 * b);
-            w[q] = shift_bytes(hi, lo, (uint32_t)sh) & m;
-        }
+    for (int q = 0; q < 4; ++q) {
+        // keep byte b of word q when lo <= 4q + b < hi
+        const int a = min(max(lo - 4 * q, 0), 4), e = min(max(hi - 4 * q, 0), 4);
+        const uint32_t keep = e > a ? ((e == 4 ? 0xFFFFFFFFu : (1u << (8 * e)) - 1u) & ~((1u << (8 * a)) - 1u)) : 0u;
+        w[q] = shift_bytes(v[q + 1], v[q], (uint32_t)sh) & keep;
     }
     *reinterpret_cast<uint4 *>(out + (size_t)r * out_pitch + c0) = make_uint4(w[0], w[1], w[2], w[3]);
 }
@@ -51,10 +60,20 @@ __global__ __launch_bounds__(256) void ncc_pad_kernel(const uint8_t *__restrict_
 hipError_t ncc_pad_image(const uint8_t *image, int width, int height, int pitch, uint8_t *out, int out_w, int out_h,
                          int out_pitch, int pad_top, int pad_left, hipStream_t s)
 {
-    const int64_t n = (int64_t)out_h * (out_pitch / 16);
-    hipLaunchKernelGGL(ncc_pad_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, image, width, height, pitch,
-                       out, out_w, out_h, out_pitch, pad_top, pad_left);
-    return hipGetLastError();
+    // 32-bit thread indexing: rows go in launches of at most 2^30 threads (one
+    // launch for any padded image under 16 GiB)
+    const int chunks = out_pitch / 16;
+    const int step = (int)std::max<int64_t>(1, ((int64_t)1 << 30) / chunks);
+    for (int64_t row0 = 0; row0 < out_h; row0 += step) {
+        const int nrows = (int)std::min<int64_t>(step, out_h - row0);
+        const int64_t n = (int64_t)nrows * chunks;
+        hipLaunchKernelGGL(ncc_pad_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, image, width, height,
+                           pitch, out, out_w, out_pitch, pad_top, pad_left, (int)row0, nrows);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
 }
 
 } // namespace xc
