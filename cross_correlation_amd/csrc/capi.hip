@@ -134,11 +134,37 @@ int ncc_dispatch(const xc::NccArgs &a, int variant, hipStream_t s)
         // 1280x720 with 4x4 0.93, 8x8 1.02, 10x10 1.37; 768x768 with 8x8
         // 0.94, 10x10 1.40; 512x512 with 16x16 1.00, 24x24 1.65; 256x256 with
         // 16x16 0.93, 24x24 1.55).
+        //
+        // Below that, on small images, the packed-byte kernel drops from
+        // 256 x 16 output tiles to 256 x 4 or 256 x 1 ones, which run few
+        // waves per SIMD, each a long chain.  When its 256 x 16 grid would be
+        // smaller than the chip, the one-output-per-thread dot4 kernel (64 x 4
+        // tiles, many more workgroups) is faster for word-aligned templates
+        // of up to 64 packed words while its grid times the template words
+        // stays within about 192 per CU; failing that, the matrix cores for
+        // templates over 16 words.  (That kernel is slower on widths that are
+        // not a multiple of 4.)  Measured on MI355X, HIP-event medians in us,
+        // packed-byte / this rule's choice: 256x256 with 8x8 5.3 / 4.2, 12x12
+        // 7.2 / 5.2, 16x16 7.7 / 6.7; 320x240 with 16x16 8.2 / 7.0; 640x480
+        // with 4x4 7.1 / 5.2, 8x8 9.1 / 6.3, 12x12 12.3 / 8.1, 16x16 15.2 /
+        // 9.0; 800x600 with 8x8 9.8 / 8.0; 1280x720 with 4x4 10.5 / 9.3;
+        // 400x300 with 10x10 10.2 / 9.0; 512x512 with 16x16 8.7 / 8.8.
         {
             const int64_t npix = (int64_t)a.t_width * a.t_height;
             const int64_t nout = (int64_t)a.out_w * a.out_h;
-            if ((npix >= 512 || (npix >= 96 && nout >= 400000) || nout >= 1000000) && xc::ncc_mfma_supported(a))
+            const bool mfma_ok = xc::ncc_mfma_supported(a);
+            if ((npix >= 512 || (npix >= 96 && nout >= 400000) || nout >= 1000000) && mfma_ok)
                 return hip_status(xc::ncc_launch_mfma(a, s));
+            const int64_t cus = xc::device_cu_count();
+            const int64_t n_ilp = (int64_t)((a.out_w + 255) / 256) * ((a.out_h + 15) / 16);
+            if (n_ilp < cus) {
+                const int64_t words = (int64_t)((a.t_width + 3) / 4) * a.t_height;
+                const int64_t n_c1 = (int64_t)((a.out_w + 63) / 64) * ((a.out_h + 3) / 4);
+                if (a.t_width % 4 == 0 && words <= 64 && n_c1 * words <= 192 * cus)
+                    return hip_status(xc::ncc_launch_c1(a, true, s));
+                if (words > 16 && mfma_ok)
+                    return hip_status(xc::ncc_launch_mfma(a, s));
+            }
             return hip_status(xc::ncc_launch_ilp(a, s));
         }
     case XC_NCC_DOT4_ILP:
