@@ -407,13 +407,15 @@ hipError_t ncc_launch_ilp(NccArgs a, hipStream_t s, int force_q)
     const int nw_whole = a.t_width / 4;
     int wc = 4;
     while (wc > 1 && nw_whole % wc) wc >>= 1;
-    // Tile shape: the big tile when the image yields enough work to fill
-    // 256 CUs, smaller ones for small images; the template-row split when
-    // the template is tall enough to give each slice several rows.
+    // Tile shape: the big tile (256 x 16 outputs) when the image yields
+    // enough of them to fill the CUs, else one-wave 256 x 1 tiles; the
+    // template-row split when the template is tall enough to give each slice
+    // several rows.  (A middle step, 256 x 4 tiles of two waves, was slower
+    // than the 256 x 1 tiles on every image small enough to take it:
+    // 640x480 with 16x16 15.3 against 10.5 us, with 8x8 9.2 against 7.1.)
     int q = 4, wv = 4;
     const long col_tiles = (a.out_w + 255) / 256;
-    if (col_tiles * ((a.out_h + 15) / 16) < 256) { q = 2; wv = 2; }
-    if (col_tiles * ((a.out_h + 3) / 4) < 256) { q = 1; wv = 1; }
+    if (col_tiles * ((a.out_h + 15) / 16) < device_cu_count()) { q = 1; wv = 1; }
     int ks = (q == 4 && a.t_height >= 16) ? 2 : 1;
     if (force_q) {  // the ablation series: Q rows per lane, no template-row split
         q = wv = force_q;
