@@ -188,8 +188,9 @@ def bench_ncc_ext(args, torch, lib, inputs):
     (ncc_u8_peak, with and without the coefficient map), a template width
     that is not a multiple of four (63 x 63, the last packed word of each
     template row masked), a 16 x 16 template (the matrix-core kernel's two
-    tile widths), and the same and full output modes (ncc_u8_run_mode: the
-    zero-padded copy, then the automatic variant; all four outputs)."""
+    tile widths), the same and full output modes (ncc_u8_run_mode: the
+    zero-padded copy, then the automatic variant; all four outputs), and
+    small images (each variant against the automatic choice)."""
     from cross_correlation_amd.inputs import ncc_case
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream().cuda_stream
@@ -252,6 +253,31 @@ def bench_ncc_ext(args, torch, lib, inputs):
         wall, per = timed_loop(launch, steps, warmup, torch)
         res[mname] = {"launches_ms": round(per, 5), "out_shape": [moh, mow],
                       "outputs_per_s": round(moh * mow / (per * 1e-3), 1)}
+    # Small images, where the packed-byte kernel's 256 x 16 tiles would not
+    # fill the chip: HIP-event microseconds per launch of each variant and of
+    # the automatic choice (uniform pixels, template cut from the image).
+    small = {}
+    vlist = (("dot4_ilp", lib.XC_NCC_DOT4_ILP), ("dot4_c1", lib.XC_NCC_DOT4_C1), ("mfma_w2", lib.XC_NCC_MFMA_W2),
+             ("auto", lib.XC_NCC_AUTO))
+    for (h, w, t) in ((256, 256, 16), (480, 640, 8), (480, 640, 16), (600, 800, 8)):
+        sc = ncc_case(f"ncc_{w}x{h}_t{t}", 3, h, w, t, t)
+        img_s = torch.from_numpy(sc.image).to(dev)
+        tm_s = torch.from_numpy(sc.tmpl).to(dev)
+        oh_s, ow_s = sc.out_shape
+        outs = [torch.empty((oh_s, ow_s), dtype=torch.int32, device=dev) for _ in range(3)]
+        coef_s = torch.empty((oh_s, ow_s), dtype=torch.float32, device=dev)
+        row = {}
+        for vname, v in vlist:
+            def launch():
+                st = lib.ncc_u8_run(img_s.data_ptr(), sc.width, sc.height, sc.pitch, tm_s.data_ptr(), sc.t_width,
+                                    sc.t_height, outs[0].data_ptr(), outs[1].data_ptr(), outs[2].data_ptr(),
+                                    coef_s.data_ptr(), stream=stream, variant=v)
+                if st != 0:
+                    raise RuntimeError(lib.status_str(st))
+            wall, per = timed_loop(launch, steps, warmup, torch)
+            row[vname + "_us"] = round(per * 1e3, 2)
+        small[f"{w}x{h}_t{t}x{t}"] = row
+    res["small_images"] = small
     return res
 
 
