@@ -68,7 +68,10 @@ def _check(res, ref):
 # (height, width, t_height, t_width): odd and even template sizes, widths not a
 # multiple of 4, ragged tiles, a template larger than the image, one row
 SHAPES = [(20, 37, 5, 7), (33, 70, 8, 12), (40, 300, 16, 16), (17, 29, 4, 6), (9, 11, 13, 15), (1, 50, 1, 9),
-          (70, 260, 9, 64), (25, 90, 31, 3)]
+          (70, 260, 9, 64), (25, 90, 31, 3),
+          # one image column; a 3-column image under a 40-wide template (the
+          # padding copy reads only clamped words around it)
+          (5, 1, 3, 1), (6, 3, 2, 40)]
 
 
 @pytest.mark.parametrize("mode", list(MODES))
