@@ -136,19 +136,23 @@ int ncc_dispatch(const xc::NccArgs &a, int variant, hipStream_t s)
         // 16x16 0.93, 24x24 1.55).
         //
         // Below that, on small images, the packed-byte kernel drops from
-        // 256 x 16 output tiles to 256 x 4 or 256 x 1 ones, which run few
-        // waves per SIMD, each a long chain.  When its 256 x 16 grid would be
-        // smaller than the chip, the one-output-per-thread dot4 kernel (64 x 4
-        // tiles, many more workgroups) is faster for word-aligned templates
-        // of up to 64 packed words while its grid times the template words
-        // stays within about 192 per CU; failing that, the matrix cores for
-        // templates over 16 words.  (That kernel is slower on widths that are
-        // not a multiple of 4.)  Measured on MI355X, HIP-event medians in us,
-        // packed-byte / this rule's choice: 256x256 with 8x8 5.3 / 4.2, 12x12
-        // 7.2 / 5.2, 16x16 7.7 / 6.7; 320x240 with 16x16 8.2 / 7.0; 640x480
-        // with 4x4 7.1 / 5.2, 8x8 9.1 / 6.3, 12x12 12.3 / 8.1, 16x16 15.2 /
-        // 9.0; 800x600 with 8x8 9.8 / 8.0; 1280x720 with 4x4 10.5 / 9.3;
-        // 400x300 with 10x10 10.2 / 9.0; 512x512 with 16x16 8.7 / 8.8.
+        // 256 x 16 output tiles to one-wave 256 x 1 ones, each a long chain.
+        // When its 256 x 16 grid would be smaller than the chip, the
+        // one-output-per-thread dot4 kernel (64 x 4 tiles, many more
+        // workgroups) is faster for word-aligned templates of up to 64 packed
+        // words while its grid times the template words stays within about
+        // 192 per CU; failing that, the matrix cores for templates over 16
+        // words.  Widths that are not a multiple of 4 cost both dot4 kernels
+        // a masked word per row: there the one-per-thread kernel takes
+        // templates of up to 16 words within 96 per CU, and the matrix cores
+        // the rest.  Measured on MI355X, HIP-event medians in us, packed-byte
+        // / this rule's choice: 256x256 with 7x7 7.7 / 6.6, 8x8 5.3 / 4.2,
+        // 12x12 7.2 / 5.2, 16x16 7.7 / 6.7; 320x240 with 11x11 10.8 / 8.7,
+        // 16x16 8.2 / 7.0; 640x480 with 4x4 7.1 / 5.2, 7x7 9.3 / 8.7, 8x8
+        // 9.1 / 6.3, 12x12 12.3 / 8.1, 16x16 15.2 / 9.0; 800x600 with 5x5
+        // 10.3 / 9.4, 8x8 9.8 / 8.0; 1280x720 with 4x4 10.5 / 9.3, 7x7 15.0
+        // / 11.5; 400x300 with 10x10 10.2 / 9.0; 512x512 with 16x16 8.7 /
+        // 8.8.
         {
             const int64_t npix = (int64_t)a.t_width * a.t_height;
             const int64_t nout = (int64_t)a.out_w * a.out_h;
@@ -160,9 +164,10 @@ int ncc_dispatch(const xc::NccArgs &a, int variant, hipStream_t s)
             if (n_ilp < cus) {
                 const int64_t words = (int64_t)((a.t_width + 3) / 4) * a.t_height;
                 const int64_t n_c1 = (int64_t)((a.out_w + 63) / 64) * ((a.out_h + 3) / 4);
-                if (a.t_width % 4 == 0 && words <= 64 && n_c1 * words <= 192 * cus)
+                const bool whole = a.t_width % 4 == 0;
+                if (words <= (whole ? 64 : 16) && n_c1 * words <= (whole ? 192 : 96) * cus)
                     return hip_status(xc::ncc_launch_c1(a, true, s));
-                if (words > 16 && mfma_ok)
+                if ((words > 16 || !whole) && mfma_ok)
                     return hip_status(xc::ncc_launch_mfma(a, s));
             }
             return hip_status(xc::ncc_launch_ilp(a, s));

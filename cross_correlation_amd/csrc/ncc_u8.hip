@@ -301,6 +301,16 @@ __global__ __launch_bounds__(256) void ncc_u8_c1_kernel(NccArgs a)
             // thread tx reads words tx/4 + k and tx/4 + k + 1, k < cw: 16 + cw words per row
             stage_tile(a.image, a.height, a.pitch, y0 + jc, x0 + 4 * ic, 4 + hc - 1, (16 + cw + 3) / 4,
                        lds, stride);
+            if (!WORD_ROWS) {
+                // rows that are not whole words: gather the chunk's template
+                // words once into LDS, after the image tile
+                uint32_t *tl = lds + (4 + a.hc - 1) * stride;
+                for (int t = threadIdx.x; t < hc * cw; t += 256) {
+                    const int r = t / cw;
+                    const int c = t - r * cw;
+                    tl[r * a.t_stride + c] = tmpl_word(a.tmpl, a.t_width, false, jc + r, ic + c);
+                }
+            }
             __syncthreads();
             for (int j = 0; j < hc; ++j) {
                 const uint32_t *rp = lds + (ty + j) * stride + (tx >> 2);
@@ -327,13 +337,14 @@ __global__ __launch_bounds__(256) void ncc_u8_c1_kernel(NccArgs a)
                     for (int k = 0; k < cw; ++k)
                         mac(shift_bytes(rp[k + 1], rp[k], sh), tw[k]);
                 } else {
-                    // gathered words, the row's partial last word with its image bytes masked
+                    // the staged words (wave-uniform LDS reads), the row's
+                    // partial last word with its image bytes masked
+                    const uint32_t *tw = lds + (4 + a.hc - 1) * stride + j * a.t_stride;
                     const int cw_main = cw - (ic + cw == nw && tm != 0xFFFFFFFFu ? 1 : 0);
                     for (int k = 0; k < cw_main; ++k)
-                        mac(shift_bytes(rp[k + 1], rp[k], sh), tmpl_row_word(trow, a.t_width, false, ic + k));
+                        mac(shift_bytes(rp[k + 1], rp[k], sh), tw[k]);
                     if (cw_main < cw)
-                        mac(shift_bytes(rp[cw_main + 1], rp[cw_main], sh) & tm,
-                            tmpl_row_word(trow, a.t_width, false, ic + cw_main));
+                        mac(shift_bytes(rp[cw_main + 1], rp[cw_main], sh) & tm, tw[cw_main]);
                 }
             }
         }
@@ -460,13 +471,16 @@ hipError_t ncc_launch_c1(NccArgs a, bool dot4, hipStream_t s)
     if (cw > 512) cw = 512;
     a.cw = cw;
     a.lds_stride = (16 + cw + 3) / 4 * 4;
-    int hc = (48 * 1024) / (a.lds_stride * 4) - 3;
+    const bool word_rows = a.t_width % 4 == 0 && (reinterpret_cast<uintptr_t>(a.tmpl) & 3) == 0;
+    // 48 KiB of LDS: the image tile, (4 + hc - 1) rows of lds_stride words,
+    // then (rows that are not whole words) hc rows of cw template words
+    a.t_stride = word_rows ? 0 : cw;
+    int hc = (12 * 1024 - 3 * a.lds_stride) / (a.lds_stride + a.t_stride);
     if (hc < 1) hc = 1;
     if (hc > a.t_height) hc = a.t_height;
     a.hc = hc;
     dim3 grid((a.out_w + 63) / 64, (a.out_h + 3) / 4);
-    const size_t lds = (size_t)(4 + hc - 1) * a.lds_stride * 4;
-    const bool word_rows = a.t_width % 4 == 0 && (reinterpret_cast<uintptr_t>(a.tmpl) & 3) == 0;
+    const size_t lds = ((size_t)(4 + hc - 1) * a.lds_stride + (size_t)hc * a.t_stride) * 4;
     if (dot4 && word_rows)
         hipLaunchKernelGGL((ncc_u8_c1_kernel<true, true>), grid, dim3(256), lds, s, a);
     else if (dot4)

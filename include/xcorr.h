@@ -97,11 +97,12 @@ int ncc_u8_run(const uint8_t *image, int width, int height, int pitch_bytes,
  *                        outputs.  Otherwise, on images too small for the
  *                        DOT4_ILP kernel's 256 x 16 output tiles to fill the
  *                        GPU's compute units: XC_NCC_DOT4_C1 for templates
- *                        of a width that is a multiple of 4 and at most 64
- *                        packed words, whose workgroups (64 x 4 outputs)
- *                        times template words are at most 192 per compute
- *                        unit; failing that, XC_NCC_MFMA for templates over
- *                        16 words.  Else XC_NCC_DOT4_ILP.
+ *                        of at most 64 packed words whose workgroups (64 x 4
+ *                        outputs) times template words are at most 192 per
+ *                        compute unit (widths not a multiple of 4: at most
+ *                        16 words and 96 per unit); failing that,
+ *                        XC_NCC_MFMA for templates over 16 words or of a
+ *                        width not a multiple of 4.  Else XC_NCC_DOT4_ILP.
  *   XC_NCC_DOT4_ILP      packed-byte dot products, 4 columns x several rows per lane
  *   XC_NCC_DOT4_C1       packed-byte dot products, one output per lane
  *   XC_NCC_SCALAR_C1     byte-at-a-time multiply-adds, one output per lane
