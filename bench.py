@@ -276,6 +276,9 @@ def bench_ncc_ext(args, torch, lib, inputs):
                     raise RuntimeError(lib.status_str(st))
             wall, per = timed_loop(launch, steps, warmup, torch)
             row[vname + "_us"] = round(per * 1e3, 2)
+        st, av = lib.ncc_u8_auto_variant(sc.width, sc.height, sc.t_width, sc.t_height)
+        row["auto_picks"] = {lib.XC_NCC_MFMA: "mfma", lib.XC_NCC_DOT4_C1: "dot4_c1",
+                             lib.XC_NCC_DOT4_ILP: "dot4_ilp"}.get(av, str(av)) if st == 0 else None
         small[f"{w}x{h}_t{t}x{t}"] = row
     res["small_images"] = small
     return res

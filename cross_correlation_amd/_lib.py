@@ -44,7 +44,8 @@ XC_XCORR_BLOCKDIAG = 2
 XC_NCC_MAX_TEMPLATE_PIXELS = 66051
 
 # Every symbol the public header declares.
-EXPORTED = ("ncc_u8_run", "ncc_u8_run_variant", "ncc_u8_peak", "ncc_u8_mode_workspace", "ncc_u8_run_mode",
+EXPORTED = ("ncc_u8_run", "ncc_u8_run_variant", "ncc_u8_peak", "ncc_u8_auto_variant", "ncc_u8_mode_workspace",
+            "ncc_u8_run_mode",
             "xcorr_f32_run", "xcorr_f32_run_algo", "xc_status_str")
 
 # xc_ncc_peak (include/xcorr.h): key u64, y i32, x i32, coef f32, reserved i32
@@ -81,6 +82,8 @@ def load(path: str = LIB_PATH):
     lib.ncc_u8_run_variant.argtypes = [_vp, _i, _i, _i, _vp, _i, _i, _vp, _vp, _vp, _vp, _i, _vp]
     lib.ncc_u8_peak.restype = _i
     lib.ncc_u8_peak.argtypes = [_vp, _i, _i, _i, _vp, _i, _i, _vp, _vp, _vp, _vp, _vp, _i, _vp]
+    lib.ncc_u8_auto_variant.restype = _i
+    lib.ncc_u8_auto_variant.argtypes = [_i, _i, _i, _i, ctypes.POINTER(ctypes.c_int)]
     lib.ncc_u8_mode_workspace.restype = _i
     lib.ncc_u8_mode_workspace.argtypes = [_i, _i, _i, _i, _i, ctypes.POINTER(ctypes.c_size_t)]
     lib.ncc_u8_run_mode.restype = _i
@@ -120,6 +123,13 @@ def ncc_u8_peak(image, width, height, pitch, tmpl, t_width, t_height, sum_i, sum
     return load().ncc_u8_peak(image, width, height, pitch, tmpl, t_width, t_height,
                               sum_i or None, sum_isq or None, sum_it or None, coef or None, peak or None,
                               variant, stream or None)
+
+
+def ncc_u8_auto_variant(width, height, t_width, t_height) -> tuple[int, int]:
+    """(status, variant) that ncc_u8_run picks for these shapes (host-only)."""
+    v = ctypes.c_int(-1)
+    st = load().ncc_u8_auto_variant(width, height, t_width, t_height, ctypes.byref(v))
+    return st, v.value
 
 
 def ncc_u8_mode_workspace(width, height, t_width, t_height, mode) -> tuple[int, int]:

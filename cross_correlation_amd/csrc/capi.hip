@@ -119,59 +119,66 @@ int xcorr_validate(const float *left, int n_left, const float *right, int n_righ
     return XC_OK;
 }
 
+// The kernel XC_NCC_AUTO runs for validated arguments (XC_NCC_MFMA,
+// XC_NCC_DOT4_C1 or XC_NCC_DOT4_ILP), from the shapes and the current
+// device's compute-unit count only.
+//
+// The matrix-core recast costs a nearly fixed time per output tile,
+// the packed-byte kernel a time that grows with the template; the
+// recast wins from 512 template pixels at any image size, from about
+// 96 pixels once there are 400K outputs to spread its fixed cost
+// over, and at any template size from about 1M outputs (measured on
+// MI355X, packed-byte / recast time: 1920x1080 with 4x4 1.45, 8x8
+// 1.59, 16x16 2.39, 32x32 5.1; 1024x1024 with 4x4 1.11, 8x8 1.31;
+// 1280x720 with 4x4 0.93, 8x8 1.02, 10x10 1.37; 768x768 with 8x8
+// 0.94, 10x10 1.40; 512x512 with 16x16 1.00, 24x24 1.65; 256x256 with
+// 16x16 0.93, 24x24 1.55).
+//
+// Below that, on small images, the packed-byte kernel drops from
+// 256 x 16 output tiles to one-wave 256 x 1 ones, each a long chain.
+// When its 256 x 16 grid would be smaller than the chip, the
+// one-output-per-thread dot4 kernel (64 x 4 tiles, many more
+// workgroups) is faster for word-aligned templates of up to 64 packed
+// words while its grid times the template words stays within about
+// 192 per CU; failing that, the matrix cores for templates over 16
+// words.  Widths that are not a multiple of 4 cost both dot4 kernels
+// a masked word per row: there the one-per-thread kernel takes
+// templates of up to 16 words within 96 per CU, and the matrix cores
+// the rest.  Measured on MI355X, HIP-event medians in us, packed-byte
+// / this rule's choice: 256x256 with 7x7 7.7 / 6.6, 8x8 5.3 / 4.2,
+// 12x12 7.2 / 5.2, 16x16 7.7 / 6.7; 320x240 with 11x11 10.8 / 8.7,
+// 16x16 8.2 / 7.0; 640x480 with 4x4 7.1 / 5.2, 7x7 9.3 / 8.7, 8x8
+// 9.1 / 6.3, 12x12 12.3 / 8.1, 16x16 15.2 / 9.0; 800x600 with 5x5
+// 10.3 / 9.4, 8x8 9.8 / 8.0; 1280x720 with 4x4 10.5 / 9.3, 7x7 15.0
+// / 11.5; 400x300 with 10x10 10.2 / 9.0; 512x512 with 16x16 8.7 /
+// 8.8.
+int ncc_auto_variant(const xc::NccArgs &a)
+{
+    const int64_t npix = (int64_t)a.t_width * a.t_height;
+    const int64_t nout = (int64_t)a.out_w * a.out_h;
+    const bool mfma_ok = xc::ncc_mfma_supported(a);
+    if ((npix >= 512 || (npix >= 96 && nout >= 400000) || nout >= 1000000) && mfma_ok)
+        return XC_NCC_MFMA;
+    const int64_t cus = xc::device_cu_count();
+    const int64_t n_ilp = (int64_t)((a.out_w + 255) / 256) * ((a.out_h + 15) / 16);
+    if (n_ilp < cus) {
+        const int64_t words = (int64_t)((a.t_width + 3) / 4) * a.t_height;
+        const int64_t n_c1 = (int64_t)((a.out_w + 63) / 64) * ((a.out_h + 3) / 4);
+        const bool whole = a.t_width % 4 == 0;
+        if (words <= (whole ? 64 : 16) && n_c1 * words <= (whole ? 192 : 96) * cus)
+            return XC_NCC_DOT4_C1;
+        if ((words > 16 || !whole) && mfma_ok)
+            return XC_NCC_MFMA;
+    }
+    return XC_NCC_DOT4_ILP;
+}
+
 // Launch the chosen variant on validated arguments.
 int ncc_dispatch(const xc::NccArgs &a, int variant, hipStream_t s)
 {
     switch (variant) {
     case XC_NCC_AUTO:
-        // The matrix-core recast costs a nearly fixed time per output tile,
-        // the packed-byte kernel a time that grows with the template; the
-        // recast wins from 512 template pixels at any image size, from about
-        // 96 pixels once there are 400K outputs to spread its fixed cost
-        // over, and at any template size from about 1M outputs (measured on
-        // MI355X, packed-byte / recast time: 1920x1080 with 4x4 1.45, 8x8
-        // 1.59, 16x16 2.39, 32x32 5.1; 1024x1024 with 4x4 1.11, 8x8 1.31;
-        // 1280x720 with 4x4 0.93, 8x8 1.02, 10x10 1.37; 768x768 with 8x8
-        // 0.94, 10x10 1.40; 512x512 with 16x16 1.00, 24x24 1.65; 256x256 with
-        // 16x16 0.93, 24x24 1.55).
-        //
-        // Below that, on small images, the packed-byte kernel drops from
-        // 256 x 16 output tiles to one-wave 256 x 1 ones, each a long chain.
-        // When its 256 x 16 grid would be smaller than the chip, the
-        // one-output-per-thread dot4 kernel (64 x 4 tiles, many more
-        // workgroups) is faster for word-aligned templates of up to 64 packed
-        // words while its grid times the template words stays within about
-        // 192 per CU; failing that, the matrix cores for templates over 16
-        // words.  Widths that are not a multiple of 4 cost both dot4 kernels
-        // a masked word per row: there the one-per-thread kernel takes
-        // templates of up to 16 words within 96 per CU, and the matrix cores
-        // the rest.  Measured on MI355X, HIP-event medians in us, packed-byte
-        // / this rule's choice: 256x256 with 7x7 7.7 / 6.6, 8x8 5.3 / 4.2,
-        // 12x12 7.2 / 5.2, 16x16 7.7 / 6.7; 320x240 with 11x11 10.8 / 8.7,
-        // 16x16 8.2 / 7.0; 640x480 with 4x4 7.1 / 5.2, 7x7 9.3 / 8.7, 8x8
-        // 9.1 / 6.3, 12x12 12.3 / 8.1, 16x16 15.2 / 9.0; 800x600 with 5x5
-        // 10.3 / 9.4, 8x8 9.8 / 8.0; 1280x720 with 4x4 10.5 / 9.3, 7x7 15.0
-        // / 11.5; 400x300 with 10x10 10.2 / 9.0; 512x512 with 16x16 8.7 /
-        // 8.8.
-        {
-            const int64_t npix = (int64_t)a.t_width * a.t_height;
-            const int64_t nout = (int64_t)a.out_w * a.out_h;
-            const bool mfma_ok = xc::ncc_mfma_supported(a);
-            if ((npix >= 512 || (npix >= 96 && nout >= 400000) || nout >= 1000000) && mfma_ok)
-                return hip_status(xc::ncc_launch_mfma(a, s));
-            const int64_t cus = xc::device_cu_count();
-            const int64_t n_ilp = (int64_t)((a.out_w + 255) / 256) * ((a.out_h + 15) / 16);
-            if (n_ilp < cus) {
-                const int64_t words = (int64_t)((a.t_width + 3) / 4) * a.t_height;
-                const int64_t n_c1 = (int64_t)((a.out_w + 63) / 64) * ((a.out_h + 3) / 4);
-                const bool whole = a.t_width % 4 == 0;
-                if (words <= (whole ? 64 : 16) && n_c1 * words <= (whole ? 192 : 96) * cus)
-                    return hip_status(xc::ncc_launch_c1(a, true, s));
-                if ((words > 16 || !whole) && mfma_ok)
-                    return hip_status(xc::ncc_launch_mfma(a, s));
-            }
-            return hip_status(xc::ncc_launch_ilp(a, s));
-        }
+        return ncc_dispatch(a, ncc_auto_variant(a), s);
     case XC_NCC_DOT4_ILP:
         return hip_status(xc::ncc_launch_ilp(a, s));
     case XC_NCC_DOT4_C1:
@@ -301,6 +308,25 @@ int ncc_u8_run(const uint8_t *image, int width, int height, int pitch_bytes, con
 {
     return ncc_u8_run_variant(image, width, height, pitch_bytes, tmpl, t_width, t_height, sum_i, sum_isq, sum_it,
                               coef, XC_NCC_AUTO, stream);
+}
+
+int ncc_u8_auto_variant(int width, int height, int t_width, int t_height, int *variant)
+{
+    if (!variant)
+        return XC_ERR_NULL;
+    // the shape checks of ncc_u8_run, with stand-in addresses (never read)
+    static const uint8_t probe[16] __attribute__((aligned(16))) = {};
+    uint32_t sum;
+    xc::NccArgs a;
+    const int64_t pitch = ((int64_t)width + 15) / 16 * 16;
+    if (pitch > INT32_MAX)
+        return XC_ERR_OVERFLOW;
+    const int st = ncc_validate(probe, width, height, (int)pitch, probe, t_width, t_height, &sum, nullptr, nullptr,
+                                nullptr, true, a);
+    if (st != XC_OK)
+        return st;
+    *variant = ncc_auto_variant(a);
+    return XC_OK;
 }
 
 int xcorr_f32_run_algo(const float *left, int n_left, const float *right, int n_right, int rows, int cols,

@@ -173,6 +173,18 @@ int ncc_u8_peak(const uint8_t *image, int width, int height, int pitch_bytes,
                 xc_ncc_peak *peak, int variant, void *stream);
 
 /*
+ * ncc_u8_auto_variant -- which kernel XC_NCC_AUTO (ncc_u8_run) runs for a
+ * valid-mode call on these shapes, written to *variant: XC_NCC_MFMA,
+ * XC_NCC_DOT4_C1 or XC_NCC_DOT4_ILP.  The choice depends only on the shapes
+ * and on the current device's compute-unit count (256, the MI355X count,
+ * when no device can be queried); the outputs are the same whichever kernel
+ * runs.  Host-only: nothing is launched.  Errors: XC_ERR_NULL if variant is
+ * NULL; XC_ERR_SHAPE or XC_ERR_OVERFLOW for shapes ncc_u8_run would reject.
+ * (Same and full modes run the valid-mode choice on the padded image.)
+ */
+int ncc_u8_auto_variant(int width, int height, int t_width, int t_height, int *variant);
+
+/*
  * ncc_u8_run_mode -- the 8-bit normalized correlation with a choice of output
  * domain.  The pages define only the windows inside the image (valid mode);
  * same and full modes follow the zero-padding convention of

@@ -149,3 +149,29 @@ def test_ncc_mode_workspace_sizes():
     assert _lib.ncc_u8_mode_workspace(64, 64, 80, 8, 1)[0] == 0  # same mode: larger templates allowed
     assert _lib.ncc_u8_mode_workspace(64, 64, 8, 8, 5)[0] == _lib.XC_ERR_VARIANT
     assert _lib.ncc_mode_shape(20, 10, 5, 3, _lib.XC_NCC_MODE_FULL) == (12, 24)
+
+
+def test_ncc_auto_variant_choice():
+    """The automatic kernel choice, queried without a launch (no device here,
+    so the rule uses the MI355X's 256 compute units)."""
+    M, C1, ILP = _lib.XC_NCC_MFMA, _lib.XC_NCC_DOT4_C1, _lib.XC_NCC_DOT4_ILP
+    for (w, h, tw, th, expect) in (
+            (1920, 1080, 64, 64, M),    # the headline workload: 512+ template pixels
+            (1920, 1080, 4, 4, M),      # a million outputs
+            (1280, 720, 16, 16, M),     # 96+ pixels and 400K+ outputs
+            (1280, 720, 8, 8, ILP),     # 225 big packed-byte tiles, too much work for one-per-thread
+            (1280, 720, 7, 7, M),       # the same with an unaligned width
+            (768, 768, 8, 8, C1),       # 144 big packed-byte tiles, 37K word-workgroups
+            (1600, 600, 4, 4, ILP),     # 266 big packed-byte tiles fill the chip
+            (256, 256, 16, 16, C1),     # small image, aligned template
+            (640, 480, 8, 8, C1),
+            (640, 480, 16, 16, M),      # one-per-thread grid x words over 192 per CU
+            (384, 384, 6, 6, C1),       # unaligned, 12 words
+            (400, 300, 10, 10, M),      # unaligned, 30 words
+            (64, 64, 64, 64, M),        # one output, 4096 pixels
+            (300, 40, 257, 7, ILP)):    # a template too wide for the matrix cores
+        st, v = _lib.ncc_u8_auto_variant(w, h, tw, th)
+        assert st == 0 and v == expect, (w, h, tw, th, v)
+    assert _lib.ncc_u8_auto_variant(10, 10, 20, 3)[0] == _lib.XC_ERR_SHAPE
+    assert _lib.ncc_u8_auto_variant(600, 600, 300, 300)[0] == _lib.XC_ERR_OVERFLOW
+    assert _lib.load().ncc_u8_auto_variant(64, 64, 8, 8, None) == _lib.XC_ERR_NULL
