@@ -132,6 +132,36 @@ def timed_loop(launch, steps, warmup, torch):
     return wall, per
 
 
+def trial_stats(launch, torch, min_ms=100.0, n_trials=5):
+    """Kernel time per launch as the median of `n_trials` trials, each a run
+    of back-to-back launches on the current stream lasting at least `min_ms`,
+    bracketed by two HIP events recorded on that stream (divided by the
+    launch count).  Returns the median, the spread and the trial size."""
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(3):
+        launch()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(3):
+        launch()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    est = e0.elapsed_time(e1) / 3
+    reps = max(1, int(-(-min_ms // max(est, 1e-4))))
+    times = []
+    for _ in range(n_trials):
+        e0.record(stream)
+        for _ in range(reps):
+            launch()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) / reps)
+    times.sort()
+    return {"median_ms": times[len(times) // 2], "min_ms": times[0], "max_ms": times[-1], "trials": n_trials,
+            "launches_per_trial": reps}
+
+
 def peak_probes():
     """Measured issue-rate ceilings of v_dot4_u32_u8, v_fmac_f32 (32
     independent chains per lane) and the two signed-byte MFMA shapes (8 or 4
@@ -158,10 +188,11 @@ def peak_probes():
     return res
 
 
-def bench_ncc(args, torch, lib, inputs, variant=0, steps=None, warmup=None):
+def bench_ncc(args, torch, lib, inputs, variant=0, steps=None, warmup=None, workload="ncc_1920x1080_t64",
+              min_ms=100.0, n_trials=5):
     steps = args.steps if steps is None else steps
     warmup = args.warmup if warmup is None else warmup
-    case = inputs.workload("ncc_1920x1080_t64")
+    case = inputs.workload(workload)
     dev = torch.device("cuda:0")
     img = torch.from_numpy(case.image).to(dev)
     tm = torch.from_numpy(case.tmpl).to(dev)
@@ -178,9 +209,11 @@ def bench_ncc(args, torch, lib, inputs, variant=0, steps=None, warmup=None):
             raise RuntimeError(lib.status_str(st))
 
     wall, per = timed_loop(launch, steps, warmup, torch)
+    tr = trial_stats(launch, torch, min_ms=min_ms, n_trials=n_trials)
     dot4 = 3 * (case.t_width // 4) * case.t_height * oh * ow
     bytes_alg = case.height * case.width + case.t_width * case.t_height + 16 * oh * ow
-    return case, dict(wall_ms=wall, kernel_ms=per, dot4=dot4, outputs=oh * ow, bytes=bytes_alg)
+    return case, dict(wall_ms=wall, loop_kernel_ms=per, kernel_ms=tr["median_ms"], trials=tr, dot4=dot4,
+                      outputs=oh * ow, bytes=bytes_alg)
 
 
 def bench_ncc_ext(args, torch, lib, inputs):
@@ -291,28 +324,30 @@ def bench_xcorr_large(args, torch, lib, inputs):
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream().cuda_stream
     res = {}
-    for n, seed, algos in ((512, 6, ("auto", "overlap")), (1024, 7, ("auto",))):
+    names = {"auto": lib.XC_XCORR_AUTO, "overlap": lib.XC_XCORR_OVERLAP, "wave": lib.XC_XCORR_WAVE}
+    for n, seed, algos in ((512, 6, ("auto", "overlap", "wave")), (1024, 7, ("auto", "wave"))):
         c = xcorr_case(f"xcorr_1to1_{n}", seed, 1, 1, n, n)
         L = torch.from_numpy(c.left).to(dev)
         R = torch.from_numpy(c.right).to(dev)
         out = torch.empty(c.out_shape, dtype=torch.float32, device=dev)
         flop = 2.0 * n ** 4
         for an in algos:
-            algo = lib.XC_XCORR_AUTO if an == "auto" else lib.XC_XCORR_OVERLAP
+            algo = names[an]
 
             def launch():
                 st = lib.xcorr_f32_run(L.data_ptr(), 1, R.data_ptr(), 1, n, n, out.data_ptr(), stream=stream, algo=algo)
                 if st != 0:
                     raise RuntimeError(lib.status_str(st))
 
-            steps = 5 if n >= 1024 or an == "overlap" else min(args.steps, 20)
-            _, per = timed_loop(launch, steps, 1, torch)
+            tr = trial_stats(launch, torch, min_ms=100.0, n_trials=5 if an == "auto" else 3)
+            per = tr["median_ms"]
             res[f"xcorr_1to1_{n}_{an}"] = {"kernel_ms": round(per, 4), "gflops": round(flop / (per * 1e-3) / 1e9, 1),
-                                           "frac_of_157.3T": round(flop / (per * 1e-3) / FP32_PEAK, 4)}
+                                           "frac_of_157.3T": round(flop / (per * 1e-3) / FP32_PEAK, 4),
+                                           "trials": f"median of {tr['trials']} x {tr['launches_per_trial']} launches"}
     return res
 
 
-def bench_xcorr(args, torch, lib, inputs):
+def bench_xcorr(args, torch, lib, inputs, oracle_mod=None):
     dev = torch.device("cuda:0")
     res = {}
     for name in ("xcorr_1to1_256", "xcorr_1to64_64", "xcorr_8to16_32"):
@@ -329,16 +364,22 @@ def bench_xcorr(args, torch, lib, inputs):
             if st != 0:
                 raise RuntimeError(lib.status_str(st))
 
-        wall, per = timed_loop(launch, args.steps, args.warmup, torch)
+        wall, _ = timed_loop(launch, args.steps, args.warmup, torch)
+        tr = trial_stats(launch, torch)
+        per = tr["median_ms"]
         flop = 2.0 * nl * nr * (c.rows * c.cols) ** 2
         res[name] = {
             "ms_per_step": round(wall, 5),
             "kernel_ms": round(per, 5),
+            "kernel_ms_min_max": [round(tr["min_ms"], 5), round(tr["max_ms"], 5)],
+            "trials": f"median of {tr['trials']} x {tr['launches_per_trial']} launches",
             "gflops": round(flop / (wall * 1e-3) / 1e9, 1),
             "kernel_gflops": round(flop / (per * 1e-3) / 1e9, 1),
             "frac_of_157.3T": round(flop / (per * 1e-3) / FP32_PEAK, 4),
             "flop_per_step": flop,
         }
+        if oracle_mod is not None:
+            res[name]["cpu_baseline"] = cpu_baseline_xcorr(args, c, oracle_mod)
     return res
 
 
@@ -376,6 +417,42 @@ def cpu_baseline(args, inputs, oracle_mod):
         "sample": f"{what} of the 1920x1080 image / 64x64 template workload ({dt:.1f} s)",
         "host": host_info(),
     }
+
+
+def cpu_baseline_xcorr(args, case, oracle_mod):
+    """The fp32 cross-correlation oracle (fp64 accumulation, the plain output
+    without the tolerance sums) on the whole workload, repeated to about
+    ``--cpu-seconds`` / 4 of host time; GFLOP/s at 2 * rows^2 * cols^2 per pair."""
+    nl, nr = case.left.shape[0], case.right.shape[0]
+    flop = 2.0 * nl * nr * (case.rows * case.cols) ** 2
+    t0 = time.perf_counter()
+    oracle_mod.xcorr_f32(case.left, case.right, with_abs=False)
+    dt1 = time.perf_counter() - t0
+    reps = max(1, int(round(args.cpu_seconds / 4 / max(dt1, 1e-6))))
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        oracle_mod.xcorr_f32(case.left, case.right, with_abs=False)
+    dt = time.perf_counter() - t0
+    return {"value": round(flop * reps / dt / 1e9, 3), "unit": "GFLOP/s", "cores": oracle_mod.max_threads(),
+            "kind": "oracle", "sample": f"the whole {case.name} workload, {reps} times ({dt:.1f} s)"}
+
+
+def cpu_baseline_ncc_small(args, case, oracle_mod):
+    """The u8 correlation oracle on the whole of a small workload, repeated to
+    about ``--cpu-seconds`` / 4 of host time."""
+    oh, ow = case.out_shape
+    per_out = 3 * ((case.t_width + 3) // 4) * case.t_height
+    t0 = time.perf_counter()
+    oracle_mod.ncc_u8(case.image, case.width, case.height, case.tmpl)
+    dt1 = time.perf_counter() - t0
+    reps = max(1, int(round(args.cpu_seconds / 4 / max(dt1, 1e-6))))
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        oracle_mod.ncc_u8(case.image, case.width, case.height, case.tmpl)
+    dt = time.perf_counter() - t0
+    return {"value": round(per_out * oh * ow * reps / dt / 1e9, 3), "unit": "Gdot4/s",
+            "cores": oracle_mod.max_threads(), "kind": "oracle",
+            "sample": f"the whole {case.name} workload ({oh}x{ow} outputs), {reps} times ({dt:.1f} s)"}
 
 
 def host_info() -> dict:
@@ -446,8 +523,26 @@ def main():
             "traffic": profiled_traffic("ncc_u8_1080p_t64.md", ["ncc_u8.hip", "ncc_common.h"]),
             "kernel": "ncc_u8_ilp_kernel",
             "kernel_ms": round(r["kernel_ms"], 5),
+            "kernel_ms_min_max": [round(r["trials"]["min_ms"], 5), round(r["trials"]["max_ms"], 5)],
+            "trials": f"median of {r['trials']['trials']} trials x {r['trials']['launches_per_trial']} "
+                      f"back-to-back launches (HIP events on the kernel's stream)",
             "outputs_per_s": round(r["outputs"] / (r["kernel_ms"] * 1e-3), 1),
         }
+        # The small u8 workload (256x256 image, 16x16 template): launch-bound,
+        # reported beside the headline with the oracle on the same input.
+        c1, r1 = bench_ncc(args, torch, _lib, inputs, variant=_lib.XC_NCC_AUTO, workload="ncc_256x256_t16")
+        out["ncc_256x256_t16"] = {
+            "kernel_ms": round(r1["kernel_ms"], 5),
+            "kernel_ms_min_max": [round(r1["trials"]["min_ms"], 5), round(r1["trials"]["max_ms"], 5)],
+            "nominal_Gdot4_per_s": round(r1["dot4"] / (r1["kernel_ms"] * 1e-3) / 1e9, 2),
+            "frac_of_dot4_peak": round(r1["dot4"] / (r1["kernel_ms"] * 1e-3) / DOT4_PEAK, 4),
+            "outputs_per_s": round(r1["outputs"] / (r1["kernel_ms"] * 1e-3), 1),
+            "auto_picks": {_lib.XC_NCC_MFMA: "mfma", _lib.XC_NCC_DOT4_C1: "dot4_c1", _lib.XC_NCC_DOT4_ILP: "dot4_ilp"}.get(
+                _lib.ncc_u8_auto_variant(c1.width, c1.height, c1.t_width, c1.t_height)[1]),
+        }
+        if not args.no_cpu_baseline:
+            import oracle
+            out["ncc_256x256_t16"]["cpu_baseline"] = cpu_baseline_ncc_small(args, c1, oracle)
         # The same workload through the other kernel variants (every variant
         # returns identical outputs): the page's ablation points (one output
         # per lane, byte-wise or packed-byte), the ILP series (4 columns x Q
@@ -455,11 +550,16 @@ def main():
         # SumIT.
         variants = {"dot4_c1": _lib.XC_NCC_DOT4_C1, "scalar_c1": _lib.XC_NCC_SCALAR_C1,
                     "dot4_ilp_q1": _lib.XC_NCC_DOT4_ILP_Q1, "dot4_ilp_q2": _lib.XC_NCC_DOT4_ILP_Q2,
-                    "dot4_ilp_q4": _lib.XC_NCC_DOT4_ILP_Q4, "mfma": _lib.XC_NCC_MFMA, "auto": _lib.XC_NCC_AUTO}
+                    "dot4_ilp_q4": _lib.XC_NCC_DOT4_ILP_Q4,
+                    "dot4_cols1": _lib.XC_NCC_DOT4_COLS1, "dot4_cols2": _lib.XC_NCC_DOT4_COLS2,
+                    "dot4_cols4": _lib.XC_NCC_DOT4_COLS4, "dot4_cols8": _lib.XC_NCC_DOT4_COLS8,
+                    "mfma": _lib.XC_NCC_MFMA, "auto": _lib.XC_NCC_AUTO}
         out["ncc_variants"] = {"dot4_ilp": {"kernel_ms": round(r["kernel_ms"], 5), "speedup_vs_dot4_ilp": 1.0}}
         for name, v in variants.items():
-            k = args.steps if name in ("mfma", "auto") else min(args.steps, 10)
-            _, rv = bench_ncc(args, torch, _lib, inputs, variant=v, steps=k, warmup=min(args.warmup, 3))
+            full = name in ("mfma", "auto")
+            k = args.steps if full else min(args.steps, 10)
+            _, rv = bench_ncc(args, torch, _lib, inputs, variant=v, steps=k, warmup=min(args.warmup, 3),
+                              min_ms=100.0 if full else 40.0, n_trials=5 if full else 3)
             out["ncc_variants"][name] = {
                 "kernel_ms": round(rv["kernel_ms"], 5),
                 "nominal_Gdot4_per_s": round(rv["dot4"] / (rv["kernel_ms"] * 1e-3) / 1e9, 2),
@@ -480,7 +580,10 @@ def main():
         if not args.no_ext:
             out["ncc_ext"] = bench_ncc_ext(args, torch, _lib, inputs)
     if args.only in ("xcorr", "all"):
-        out["xcorr"] = bench_xcorr(args, torch, _lib, inputs)
+        orc = None
+        if not args.no_cpu_baseline:
+            import oracle as orc
+        out["xcorr"] = bench_xcorr(args, torch, _lib, inputs, orc)
         if not args.no_ext:
             out["xcorr_large"] = bench_xcorr_large(args, torch, _lib, inputs)
     if not args.no_peak_probe:

@@ -32,6 +32,10 @@ XC_NCC_DOT4_ILP_Q2 = 6
 XC_NCC_DOT4_ILP_Q4 = 7
 XC_NCC_MFMA_W4 = 8
 XC_NCC_MFMA_W2 = 9
+XC_NCC_DOT4_COLS1 = 10
+XC_NCC_DOT4_COLS2 = 11
+XC_NCC_DOT4_COLS4 = 12
+XC_NCC_DOT4_COLS8 = 13
 
 XC_NCC_MODE_VALID = 0
 XC_NCC_MODE_SAME = 1
@@ -40,6 +44,7 @@ XC_NCC_MODE_FULL = 2
 XC_XCORR_AUTO = 0
 XC_XCORR_OVERLAP = 1
 XC_XCORR_BLOCKDIAG = 2
+XC_XCORR_WAVE = 3
 
 XC_NCC_MAX_TEMPLATE_PIXELS = 66051
 

@@ -197,6 +197,14 @@ int ncc_dispatch(const xc::NccArgs &a, int variant, hipStream_t s)
         return hip_status(xc::ncc_launch_mfma(a, s, 4));
     case XC_NCC_MFMA_W2:
         return hip_status(xc::ncc_launch_mfma(a, s, 2));
+    case XC_NCC_DOT4_COLS1:
+        return hip_status(xc::ncc_launch_cols(a, 1, s));
+    case XC_NCC_DOT4_COLS2:
+        return hip_status(xc::ncc_launch_cols(a, 2, s));
+    case XC_NCC_DOT4_COLS4:
+        return hip_status(xc::ncc_launch_cols(a, 4, s));
+    case XC_NCC_DOT4_COLS8:
+        return hip_status(xc::ncc_launch_cols(a, 8, s));
     default:
         return XC_ERR_VARIANT;
     }
@@ -205,7 +213,7 @@ int ncc_dispatch(const xc::NccArgs &a, int variant, hipStream_t s)
 // Variant check done before anything is enqueued.
 int ncc_variant_ok(const xc::NccArgs &a, int variant)
 {
-    if (variant < XC_NCC_AUTO || variant > XC_NCC_MFMA_W2)
+    if (variant < XC_NCC_AUTO || variant > XC_NCC_DOT4_COLS8)
         return XC_ERR_VARIANT;
     if ((variant == XC_NCC_MFMA || variant == XC_NCC_MFMA_W4) && !xc::ncc_mfma_supported(a, 4))
         return XC_ERR_SHAPE;
@@ -344,6 +352,8 @@ int xcorr_f32_run_algo(const float *left, int n_left, const float *right, int n_
         return hip_status(xc::xcorr_launch_overlap(a, s));
     case XC_XCORR_OVERLAP:
         return hip_status(xc::xcorr_launch_overlap(a, s));
+    case XC_XCORR_WAVE:
+        return hip_status(xc::xcorr_launch_wave(a, s));
     case XC_XCORR_BLOCKDIAG:
         if (!xc::xcorr_blockdiag_supported(a))
             return XC_ERR_SHAPE;

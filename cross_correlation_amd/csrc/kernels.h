@@ -70,6 +70,9 @@ struct NccArgs {
 // (and as many row waves), no template-row split.
 hipError_t ncc_launch_ilp(NccArgs a, hipStream_t s, int force_q = 0);
 hipError_t ncc_launch_c1(NccArgs a, bool dot4, hipStream_t s);
+// Column-ILP ablation: cols = 1, 2, 4 or 8 output columns per lane on
+// 256 x 4 output tiles.
+hipError_t ncc_launch_cols(NccArgs a, int cols, hipStream_t s);
 // SumIT on the i8 matrix cores; takes template rows up to 256 bytes.
 // mw: matrix-core waves per workgroup (4: 256-column tiles, 2: 128-column
 // tiles, t_width <= 64 only); 0 lets the launcher pick from the grid.
@@ -96,6 +99,7 @@ struct XcorrArgs {
 };
 
 hipError_t xcorr_launch_overlap(const XcorrArgs &a, hipStream_t s);
+hipError_t xcorr_launch_wave(const XcorrArgs &a, hipStream_t s);
 hipError_t xcorr_launch_blockdiag(const XcorrArgs &a, hipStream_t s);
 bool xcorr_blockdiag_supported(const XcorrArgs &a);
 

@@ -361,6 +361,129 @@ __global__ __launch_bounds__(256) void ncc_u8_c1_kernel(NccArgs a)
         peak_commit(a.peak, best);
 }
 
+// Ablation series of the page's ILP step: C adjacent output columns per lane
+// and one output row, on a fixed tile of 256 x 4 outputs per workgroup
+// (256 / C lanes per output row, 1024 / C threads), so that across
+// C = 1, 2, 4, 8 only the number of independent accumulator chains per lane
+// (3 * C) and the byte shifts a loaded image word is shared by change; the
+// tile, the staging and the template reads stay the same.  Lane tx owns
+// columns C*tx .. C*tx + C - 1 of the tile: they start in image word
+// (C*tx) / 4 at byte (C*tx) % 4, so C = 1 takes a per-lane shift of 0..3,
+// C = 2 the page's two columns (shifts s and s + 1, s = 0 or 2 from the
+// lane's column parity), C = 4 one aligned word group (shifts 0..3, the first
+// free) and C = 8 two word groups (three words per step).  Template words are
+// staged in LDS and read at a workgroup-uniform address (a broadcast).
+template <int C>
+__device__ __forceinline__ void ncc_cols_word(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t sh, uint32_t t,
+                                              uint32_t mask, uint32_t (&ai)[C], uint32_t (&aq)[C],
+                                              uint32_t (&at)[C])
+{
+    uint32_t v[C];
+    if (C == 1) {
+        v[0] = shift_bytes(w1, w0, sh);
+    } else if (C == 2) {
+        v[0] = shift_bytes(w1, w0, sh);
+        v[1 % C] = shift_bytes(w1, w0, sh + 1);
+    } else {
+#pragma unroll
+        for (int g = 0; g < C / 4; ++g) {
+            const uint32_t lo = g == 0 ? w0 : w1, hi = g == 0 ? w1 : w2;
+            v[(4 * g) % C] = lo;
+            v[(4 * g + 1) % C] = shift_bytes(hi, lo, 1);
+            v[(4 * g + 2) % C] = shift_bytes(hi, lo, 2);
+            v[(4 * g + 3) % C] = shift_bytes(hi, lo, 3);
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        const uint32_t x = v[c] & mask;
+        ai[c] = dot4u(x, 0x01010101u, ai[c]);
+        aq[c] = dot4u(x, x, aq[c]);
+        at[c] = dot4u(x, t, at[c]);
+    }
+}
+
+template <int C>
+__global__ __launch_bounds__(1024 / C) void ncc_u8_cols_kernel(NccArgs a)
+{
+    static_assert(C == 1 || C == 2 || C == 4 || C == 8, "columns per lane");
+    constexpr int TX = 256 / C;  // lanes per output row of the tile
+    extern __shared__ uint32_t lds[];
+    const int tx = threadIdx.x % TX;
+    const int ty = threadIdx.x / TX;
+    const int x0 = blockIdx.x * 256;
+    const int y0 = blockIdx.y * 4;
+    const int nw = (a.t_width + 3) >> 2;  // packed words per template row
+    const uint32_t tm = tail_mask(a.t_width);
+    const bool word_rows = tmpl_word_rows(a.tmpl, a.t_width);
+
+    uint32_t sum_t, sum_tsq;
+    template_sums(a.tmpl, a.t_width, a.t_height, sum_t, sum_tsq);
+
+    uint32_t ai[C], aq[C], at[C];
+#pragma unroll
+    for (int c = 0; c < C; ++c) ai[c] = aq[c] = at[c] = 0u;
+    const int wbase = (C * tx) >> 2;
+    const uint32_t sh = (uint32_t)((C * tx) & 3);
+    const int stride = a.lds_stride;
+    const int tstride = a.t_stride;
+    uint32_t *const tl = lds + (4 + a.hc - 1) * stride;
+    for (int jc = 0; jc < a.t_height; jc += a.hc) {
+        const int hc = min(a.hc, a.t_height - jc);
+        for (int ic = 0; ic < nw; ic += a.cw) {
+            const int cw = min(a.cw, nw - ic);
+            __syncthreads();
+            // the last lane reads words up to 63 + cw: 64 + cw words per row
+            stage_tile(a.image, a.height, a.pitch, y0 + jc, x0 + 4 * ic, 4 + hc - 1, (64 + cw + 3) / 4, lds,
+                       stride);
+            for (int t = threadIdx.x; t < hc * cw; t += 1024 / C) {
+                const int r = t / cw;
+                const int c = t - r * cw;
+                tl[r * tstride + c] = tmpl_word(a.tmpl, a.t_width, word_rows, jc + r, ic + c);
+            }
+            __syncthreads();
+            const uint32_t cm = ic + cw == nw ? tm : 0xFFFFFFFFu;
+            const int cw_main = cw - (cm != 0xFFFFFFFFu ? 1 : 0);
+            for (int j = 0; j < hc; ++j) {
+                const uint32_t *rp = lds + (ty + j) * stride + wbase;
+                const uint32_t *tw = tl + j * tstride;
+                uint32_t w0 = rp[0], w1 = rp[1], w2 = C == 8 ? rp[2] : 0u;
+                for (int k = 0; k < cw_main; ++k) {
+                    const uint32_t t = tw[k];
+                    uint32_t nx;
+                    if (C == 8) nx = rp[k + 3];
+                    else nx = rp[k + 2];
+                    ncc_cols_word<C>(w0, w1, w2, sh, t, 0xFFFFFFFFu, ai, aq, at);
+                    w0 = w1;
+                    if (C == 8) {
+                        w1 = w2;
+                        w2 = nx;
+                    } else {
+                        w1 = nx;
+                    }
+                }
+                if (cm != 0xFFFFFFFFu)
+                    ncc_cols_word<C>(w0, w1, w2, sh, tw[cw_main], cm, ai, aq, at);
+            }
+        }
+    }
+    const int y = y0 + ty;
+    const int64_t n = (int64_t)a.t_width * a.t_height;
+    const int64_t st64 = sum_t;
+    const int64_t vt = n * (int64_t)sum_tsq - st64 * st64;
+    unsigned long long best = 0ull;
+    if (y < a.out_h) {
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            const int x = x0 + C * tx + c;
+            if (x < a.out_w)
+                ncc_store(a, (size_t)y * a.out_w + x, ai[c], aq[c], at[c], n, st64, vt, best);
+        }
+    }
+    if (a.peak)
+        peak_commit(a.peak, best);
+}
+
 // Best match: clear the key before the correlation launch, decode it after.
 __global__ void ncc_peak_init_kernel(xc_ncc_peak *p)
 {
@@ -433,15 +556,19 @@ hipError_t ncc_launch_ilp(NccArgs a, hipStream_t s, int force_q)
         ks = 1;
     }
     const int lds_words = 64 * 1024 / 4;
-    // chunk of template words: a multiple of lcm(wc, 4) words (16-byte aligned chunk starts)
+    const int th = wv * q;
+    // Chunk of template words: a multiple of 4 words (16-byte aligned chunk
+    // starts), at most 960, and small enough that one template row fits
+    // beside the tile's th image rows in 64 KiB:
+    // th * (64 + cw) + cw <= lds_words (900 words for th = 16).
     const int unit = 4;
+    int max_cw = (lds_words - 64 * th) / (th + 1) / unit * unit;
+    if (max_cw > 960) max_cw = 960;
     int cw = nw;
-    const int max_cw = 960;
-    if (cw > max_cw) cw = max_cw / unit * unit;
+    if (cw > max_cw) cw = max_cw;
     a.cw = cw;
     a.lds_stride = (64 + cw + 3) / 4 * 4;
     a.t_stride = (cw + 3) / 4 * 4;
-    const int th = wv * q;
     // (th + hc - 1) * stride + hc * t_stride <= lds_words
     int hc = (lds_words - (th - 1) * a.lds_stride) / (a.lds_stride + a.t_stride);
     if (hc < 1) hc = 1;
@@ -462,6 +589,40 @@ hipError_t ncc_peak_finish(void *peak, int out_w, hipStream_t s)
 {
     hipLaunchKernelGGL(ncc_peak_finish_kernel, dim3(1), dim3(1), 0, s, static_cast<xc_ncc_peak *>(peak), out_w);
     return hipGetLastError();
+}
+
+template <int C>
+static hipError_t launch_cols(const NccArgs &a, hipStream_t s)
+{
+    dim3 grid((a.out_w + 255) / 256, (a.out_h + 3) / 4);
+    const size_t lds = ((size_t)(4 + a.hc - 1) * a.lds_stride + (size_t)a.hc * a.t_stride) * 4;
+    hipLaunchKernelGGL((ncc_u8_cols_kernel<C>), grid, dim3(1024 / C), lds, s, a);
+    return hipGetLastError();
+}
+
+// The column-ILP ablation series: `cols` (1, 2, 4 or 8) output columns per
+// lane on 256 x 4 tiles; template chunks of at most 512 words, the tile and
+// the chunk's template words within 64 KiB of LDS.
+hipError_t ncc_launch_cols(NccArgs a, int cols, hipStream_t s)
+{
+    const int nw = (a.t_width + 3) / 4;
+    int cw = nw;
+    if (cw > 512) cw = 512;
+    a.cw = cw;
+    a.lds_stride = (64 + cw + 3) / 4 * 4;
+    a.t_stride = (cw + 3) / 4 * 4;
+    // (4 + hc - 1) * lds_stride + hc * t_stride <= 16384 words (64 KiB)
+    int hc = (16 * 1024 - 3 * a.lds_stride) / (a.lds_stride + a.t_stride);
+    if (hc < 1) hc = 1;
+    if (hc > a.t_height) hc = a.t_height;
+    a.hc = hc;
+    switch (cols) {
+    case 1: return launch_cols<1>(a, s);
+    case 2: return launch_cols<2>(a, s);
+    case 4: return launch_cols<4>(a, s);
+    case 8: return launch_cols<8>(a, s);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t ncc_launch_c1(NccArgs a, bool dot4, hipStream_t s)

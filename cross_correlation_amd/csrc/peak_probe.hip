@@ -1,7 +1,8 @@
 // peak_probe.hip -- issue-rate probes for the two instructions the hot path
 // is bound by, so that "fraction of peak" can be quoted against a measured
 // ceiling as well as the spec sheet.  Not part of the correlation ABI; only
-// the bench harness loads this library.
+// the bench harness and one test (the fp64 reciprocal-square-root estimate's
+// error bound, xc_rsq_probe below) load this library.
 //
 // Each thread runs `iters` rounds of CH independent accumulation chains of
 // one instruction:
@@ -96,24 +97,53 @@ __global__ __launch_bounds__(64) void mfma32_probe(uint32_t *out, int iters)
     out[blockIdx.x * 64 + threadIdx.x] = (uint32_t)s;
 }
 
+// The hardware reciprocal-square-root estimate for fp64 (v_rsq_f64), the
+// first step of the u8 correlation coefficient's division: y[i] = rsq(p[i]).
+__global__ __launch_bounds__(256) void rsq_probe(const double *p, double *y, int n)
+{
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < n)
+        y[i] = __builtin_amdgcn_rsq(p[i]);
+}
+
 } // namespace
 
 extern "C" {
+
+// y[i] = the fp64 reciprocal-square-root estimate of p[i], i < n, for n
+// doubles in device memory (p and y caller-owned, not aliased); waits for the
+// result.  Returns 0, or -1 on a bad argument or a HIP error.  Lets a test
+// measure the estimate's relative error, which the coefficient's rounding
+// argument relies on.
+int xc_rsq_probe(const double *p, double *y, int n)
+{
+    if (!p || !y || n <= 0)
+        return -1;
+    hipLaunchKernelGGL(rsq_probe, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, 0, p, y, n);
+    if (hipGetLastError() != hipSuccess)
+        return -1;
+    return hipDeviceSynchronize() == hipSuccess ? 0 : -1;
+}
 
 // Runs the probe `reps` times after one warm-up launch; returns 0 and the mean
 // milliseconds per launch in *ms, or -1 on any HIP error or unknown kind.
 int xc_peak_probe(int kind, int waves_per_simd, int iters, int reps, double *ms, double *ops_per_launch)
 {
     constexpr int CH = 32;
+    if (kind < 0 || kind > 3 || waves_per_simd <= 0 || iters <= 0 || reps <= 0 || !ms || !ops_per_launch)
+        return -1;
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess) return -1;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
     const int blocks = cus * 4 * waves_per_simd;
     uint32_t *buf = nullptr;
     if (hipMalloc(&buf, (size_t)blocks * 64 * sizeof(uint32_t)) != hipSuccess) return -1;
-    hipEvent_t e0, e1;
-    if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) return -1;
-    if (kind < 0 || kind > 3) return -1;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+        if (e0) hipEventDestroy(e0);
+        (void)hipFree(buf);
+        return -1;
+    }
     auto launch = [&]() {
         if (kind == 0)
             hipLaunchKernelGGL(dot4_probe<CH>, dim3(blocks), dim3(64), 0, 0, buf, iters);

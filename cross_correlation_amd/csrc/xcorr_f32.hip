@@ -11,6 +11,10 @@
 // * xcorr_overlap_kernel -- the overlap-wise baseline the page compares
 //   against: one thread per output shift, no data reuse.
 //
+// * xcorr_wave_kernel -- the page's warp-per-overlap variant on a wave64:
+//   one wave per output shift, its lanes splitting the overlap, partial sums
+//   reduced across the wave in a fixed order.
+//
 // * xcorr_bd_whole_kernel / xcorr_bd_chunk_kernel / xcorr_bd_big_kernel --
 //   the register-blocked (block-diagonal) kernel, in two staging modes for up
 //   to 64 row blocks and in passes of 64 row blocks beyond.  The page's kernels give
@@ -99,6 +103,75 @@ hipError_t xcorr_launch_overlap(const XcorrArgs &a, hipStream_t s)
     const int64_t npairs = (int64_t)a.n_left * a.n_right;
     dim3 grid((per_pair + 255) / 256, (unsigned)(npairs < 65535 ? npairs : 65535));
     hipLaunchKernelGGL(xcorr_overlap_kernel, grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Wave-per-overlap: one wave64 computes one output shift.  The JPDC page's
+// warp-per-overlap variant gives a whole warp one overlap and reduces the
+// lanes' partial sums at the end; here the 64 lanes take the overlap's
+// elements in row-major order (lane l the elements l, l + 64, ...: adjacent
+// lanes read adjacent columns), each adds its products in that order, and a
+// butterfly of cross-lane exchanges (xor 32, 16, ..., 1) adds the 64 partial
+// sums in a fixed order, so every lane ends with the same total and the
+// result does not depend on scheduling.  Both matrices are read from global
+// memory (the caches serve the neighbouring shifts of a workgroup).  Waves
+// walk the outputs of all pairs in a grid-stride loop.
+
+__global__ __launch_bounds__(256) void xcorr_wave_kernel(XcorrArgs a)
+{
+    const int lane = threadIdx.x & 63;
+    const int rows = a.rows, cols = a.cols;
+    const int ow = 2 * cols - 1;
+    const int per_pair = (2 * rows - 1) * ow;
+    const int64_t total = (int64_t)a.n_left * a.n_right * per_pair;
+    const int64_t stride = (int64_t)gridDim.x * 4;
+    for (int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); w < total; w += stride) {
+        const int64_t pair = w / per_pair;
+        const int idx = (int)(w - pair * per_pair);
+        const int y = idx / ow;
+        const int x = idx - y * ow;
+        const int dy = y - (rows - 1);
+        const int dx = x - (cols - 1);
+        const int i0 = max(0, -dy), i1 = min(rows, rows - dy);
+        const int j0 = max(0, -dx), j1 = min(cols, cols - dx);
+        const int nw = j1 - j0;
+        const int n = (i1 - i0) * nw;
+        const int l = (int)(pair / a.n_right);
+        const int r = (int)(pair - (int64_t)l * a.n_right);
+        const float *L = a.left + (size_t)l * rows * cols;
+        const float *R = a.right + (size_t)r * rows * cols;
+        // element k of the overlap is (i0 + k / nw, j0 + k % nw): right
+        // matrix offset ro = i * cols + j, left offset ro + shift
+        const int shift = dy * cols + dx;
+        const int di = 64 / nw, dj = 64 - di * nw;
+        int i = i0 + lane / nw;
+        int j = j0 + (lane - (lane / nw) * nw);
+        float acc = 0.0f;
+        for (int k = lane; k < n; k += 64) {
+            const int ro = i * cols + j;
+            acc = fmaf(L[ro + shift], R[ro], acc);
+            i += di;
+            j += dj;
+            if (j >= j1) {
+                j -= nw;
+                ++i;
+            }
+        }
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1)
+            acc += __shfl_xor(acc, m, 64);
+        if (lane == 0)
+            a.out[(size_t)pair * per_pair + idx] = acc;
+    }
+}
+
+hipError_t xcorr_launch_wave(const XcorrArgs &a, hipStream_t s)
+{
+    const int64_t total = (int64_t)a.n_left * a.n_right * (2 * a.rows - 1) * (2 * a.cols - 1);
+    const int64_t blocks = (total + 3) / 4;
+    hipLaunchKernelGGL(xcorr_wave_kernel, dim3((unsigned)(blocks < (1 << 22) ? blocks : (1 << 22))), dim3(256), 0, s,
+                       a);
     return hipGetLastError();
 }
 

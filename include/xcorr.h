@@ -123,6 +123,13 @@ int ncc_u8_run(const uint8_t *image, int width, int height, int pitch_bytes,
  *                        per CU; t_width <= 64 only, else XC_ERR_SHAPE).
  *                        XC_NCC_MFMA picks the width that runs the output's
  *                        tiles in fewer rounds of workgroups.
+ *   XC_NCC_DOT4_COLS1    the column-ILP series of the ablation (the page's
+ *   XC_NCC_DOT4_COLS2    two-column step): packed-byte dot products with
+ *   XC_NCC_DOT4_COLS4    C = 1, 2, 4 or 8 adjacent output columns per lane
+ *   XC_NCC_DOT4_COLS8    and one output row, on the same 256 x 4 output tile
+ *                        per workgroup for every C, so only the independent
+ *                        accumulator chains per lane (3 * C) change.  C = 2
+ *                        is the page's two columns per thread.
  */
 #define XC_NCC_AUTO 0
 #define XC_NCC_DOT4_ILP 1
@@ -134,6 +141,10 @@ int ncc_u8_run(const uint8_t *image, int width, int height, int pitch_bytes,
 #define XC_NCC_DOT4_ILP_Q4 7
 #define XC_NCC_MFMA_W4 8
 #define XC_NCC_MFMA_W2 9
+#define XC_NCC_DOT4_COLS1 10
+#define XC_NCC_DOT4_COLS2 11
+#define XC_NCC_DOT4_COLS4 12
+#define XC_NCC_DOT4_COLS8 13
 int ncc_u8_run_variant(const uint8_t *image, int width, int height, int pitch_bytes,
                        const uint8_t *tmpl, int t_width, int t_height,
                        uint32_t *sum_i, uint32_t *sum_isq, uint32_t *sum_it, float *coef,
@@ -248,10 +259,16 @@ int xcorr_f32_run(const float *left, int n_left, const float *right, int n_right
  *                        overlap-wise baseline)
  *   XC_XCORR_BLOCKDIAG   register-blocked kernel: 4x4 row blocks along block
  *                        diagonals, a sliding column window per lane
+ *   XC_XCORR_WAVE        one 64-lane wave per output shift: the lanes split
+ *                        the overlap's elements and their partial sums are
+ *                        added across the wave in a fixed order (the JPDC
+ *                        README's warp-per-overlap variant, for large
+ *                        overlaps; no data reuse between shifts)
  */
 #define XC_XCORR_AUTO 0
 #define XC_XCORR_OVERLAP 1
 #define XC_XCORR_BLOCKDIAG 2
+#define XC_XCORR_WAVE 3
 int xcorr_f32_run_algo(const float *left, int n_left, const float *right, int n_right,
                        int rows, int cols, float *out, int algo, void *stream);
 

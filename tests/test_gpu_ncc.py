@@ -16,7 +16,8 @@ pytestmark = pytest.mark.gpu
 
 VARIANTS = [_lib.XC_NCC_AUTO, _lib.XC_NCC_DOT4_ILP, _lib.XC_NCC_DOT4_C1, _lib.XC_NCC_SCALAR_C1, _lib.XC_NCC_MFMA,
             _lib.XC_NCC_DOT4_ILP_Q1, _lib.XC_NCC_DOT4_ILP_Q2, _lib.XC_NCC_DOT4_ILP_Q4, _lib.XC_NCC_MFMA_W4,
-            _lib.XC_NCC_MFMA_W2]
+            _lib.XC_NCC_MFMA_W2, _lib.XC_NCC_DOT4_COLS1, _lib.XC_NCC_DOT4_COLS2, _lib.XC_NCC_DOT4_COLS4,
+            _lib.XC_NCC_DOT4_COLS8]
 # template rows the matrix-core variants take (256- and 128-column tiles)
 MFMA_MAX_T_WIDTH = {_lib.XC_NCC_MFMA: 256, _lib.XC_NCC_MFMA_W4: 256, _lib.XC_NCC_MFMA_W2: 64}
 
@@ -74,7 +75,8 @@ def test_ncc_1080p_small_templates_auto(th, tw):
 
 @pytest.mark.parametrize("variant", [_lib.XC_NCC_DOT4_ILP, _lib.XC_NCC_DOT4_C1, _lib.XC_NCC_SCALAR_C1, _lib.XC_NCC_MFMA,
                                      _lib.XC_NCC_DOT4_ILP_Q1, _lib.XC_NCC_DOT4_ILP_Q2, _lib.XC_NCC_DOT4_ILP_Q4,
-                                     _lib.XC_NCC_MFMA_W4, _lib.XC_NCC_MFMA_W2])
+                                     _lib.XC_NCC_MFMA_W4, _lib.XC_NCC_MFMA_W2, _lib.XC_NCC_DOT4_COLS1,
+                                     _lib.XC_NCC_DOT4_COLS2, _lib.XC_NCC_DOT4_COLS4, _lib.XC_NCC_DOT4_COLS8])
 def test_ncc_1080p_variants_sampled(variant):
     """Ablation variants at full size: compare against the auto path bit for bit."""
     case = workload("ncc_1920x1080_t64")
@@ -305,3 +307,29 @@ def test_ncc_largest_template_near_u32_limit(th, tw):
         res = _gpu.run_ncc(case, v)
         ref = _gpu.check_ncc(case, res, ref)
     assert int(ref["sum_isq"].max()) > 4_200_000_000  # far above 2^31: a signed 32-bit slip would show
+
+
+def test_api_rejects_mismatched_outputs():
+    """The torch wrappers check caller-supplied outputs against the output
+    shape before calling the library: a map one row short, a strided map, a
+    wrong dtype and a short best-match record are refused, and nothing is
+    written to them."""
+    import torch
+    from cross_correlation_amd import api
+    case = workload("ncc_256x256_t16")
+    _gpu.log("ncc wrappers: mismatched caller outputs")
+    img, tm = _gpu.to_dev(case.image), _gpu.to_dev(case.tmpl)
+    oh, ow = case.out_shape
+    short = torch.full((oh - 1, ow), 7, dtype=torch.int32, device="cuda")
+    wide = torch.full((oh, 2 * ow), 7, dtype=torch.int32, device="cuda")
+    for bad, msg in (({"sum_i": short}, "elements"), ({"sum_it": wide[:, ::2]}, "contiguous"),
+                     ({"coef": torch.empty((oh, ow), dtype=torch.float64, device="cuda")}, "dtype")):
+        with pytest.raises(ValueError, match=msg):
+            api.ncc_u8(img, tm, width=case.width, out=bad)
+    with pytest.raises(ValueError, match="bytes"):
+        api.ncc_u8_peak(img, tm, width=case.width, peak=torch.zeros(2, dtype=torch.int64, device="cuda"))
+    torch.cuda.synchronize()
+    assert bool((short == 7).all()) and bool((wide == 7).all())
+    L = torch.zeros((2, 16, 16), device="cuda")
+    with pytest.raises(ValueError, match="elements"):
+        api.xcorr_f32(L, L, out=torch.empty((2, 2, 31, 30), device="cuda"))

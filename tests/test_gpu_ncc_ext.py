@@ -23,6 +23,10 @@ VARIANTS = {
     "ilp_q4": _lib.XC_NCC_DOT4_ILP_Q4,
     "mfma_w4": _lib.XC_NCC_MFMA_W4,
     "mfma_w2": _lib.XC_NCC_MFMA_W2,
+    "cols1": _lib.XC_NCC_DOT4_COLS1,
+    "cols2": _lib.XC_NCC_DOT4_COLS2,
+    "cols4": _lib.XC_NCC_DOT4_COLS4,
+    "cols8": _lib.XC_NCC_DOT4_COLS8,
 }
 # template rows the matrix-core variants take (256- and 128-column tiles)
 MAX_T_WIDTH = {"mfma": 256, "mfma_w4": 256, "mfma_w2": 64}
@@ -83,6 +87,39 @@ def test_ncc_template_width_past_one_chunk():
     for name in ("auto", "ilp"):
         _gpu.log(f"ncc 40x4000 t17x3843 variant {name}")
         ref = _gpu.check_ncc(case, _gpu.run_ncc(case, variant=VARIANTS[name]), ref)
+
+
+def test_ncc_wide_template_q4_tiles():
+    """Template rows of 3,604 to 4,128 bytes on the 256 x 16 tiles (four row
+    waves of four rows): the template-word chunk is sized so that the tile's
+    16 image rows and one template row fit in 64 KiB of LDS.  Through the
+    Q = 4 ablation tile at a small size (every output against the oracle)."""
+    for tw in (3604, 3700, 4128):
+        case = ncc_case("t", 560 + tw % 97, 30, tw + 60, 16, tw, cut=True)
+        _gpu.log(f"ncc {case.height}x{case.width} t16x{tw} variant ilp_q4")
+        _gpu.check_ncc(case, _gpu.run_ncc(case, variant=VARIANTS["ilp_q4"]))
+
+
+def test_ncc_wide_template_auto_full_grid():
+    """A 3,700-byte template on an output of 1024 x 1024 (256 tiles of 256 x 16,
+    where the automatic choice takes the packed-byte kernel's big tiles and
+    splits the template rows over two waves): 3,000 sampled windows and the
+    corners against the oracle, coefficient 1 at the cut."""
+    tw, th = 3700, 17
+    case = ncc_case("t", 571, th + 1023, tw + 1023, th, tw, cut=True)
+    st, v = _lib.ncc_u8_auto_variant(case.width, case.height, tw, th)
+    assert st == 0 and v == _lib.XC_NCC_DOT4_ILP
+    _gpu.log(f"ncc {case.height}x{case.width} t{th}x{tw} auto (packed-byte, 256 x 16 tiles)")
+    res = _gpu.run_ncc(case)
+    oh, ow = case.out_shape
+    rng = np.random.default_rng(572)
+    ys = np.concatenate([[0, 0, oh - 1, oh - 1], rng.integers(0, oh, 3000)])
+    xs = np.concatenate([[0, ow - 1, 0, ow - 1], rng.integers(0, ow, 3000)])
+    ref = oracle.ncc_u8_points(case.image, case.width, case.height, case.tmpl, ys, xs)
+    for k in ("sum_i", "sum_isq", "sum_it"):
+        assert np.array_equal(res[k][ys, xs], ref[k]), k
+    assert np.max(np.abs(res["coef"][ys, xs].astype(np.float64) - ref["coef"])) <= 1e-5
+    assert res["coef"][case.cut] == np.float32(1.0)
 
 
 def test_ncc_unaligned_template_base():

@@ -16,7 +16,8 @@ pytestmark = pytest.mark.gpu
 
 MODES = {"same": _lib.XC_NCC_MODE_SAME, "full": _lib.XC_NCC_MODE_FULL}
 VARIANTS = {"auto": _lib.XC_NCC_AUTO, "ilp": _lib.XC_NCC_DOT4_ILP, "c1": _lib.XC_NCC_DOT4_C1,
-            "scalar": _lib.XC_NCC_SCALAR_C1, "mfma": _lib.XC_NCC_MFMA, "mfma_w2": _lib.XC_NCC_MFMA_W2}
+            "scalar": _lib.XC_NCC_SCALAR_C1, "mfma": _lib.XC_NCC_MFMA, "mfma_w2": _lib.XC_NCC_MFMA_W2,
+            "cols2": _lib.XC_NCC_DOT4_COLS2, "cols8": _lib.XC_NCC_DOT4_COLS8}
 WS_SENTINEL = 0xA5
 
 

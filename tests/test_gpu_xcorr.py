@@ -14,7 +14,7 @@ import _gpu
 
 pytestmark = pytest.mark.gpu
 
-ALGOS = [_lib.XC_XCORR_AUTO, _lib.XC_XCORR_OVERLAP, _lib.XC_XCORR_BLOCKDIAG]
+ALGOS = [_lib.XC_XCORR_AUTO, _lib.XC_XCORR_OVERLAP, _lib.XC_XCORR_BLOCKDIAG, _lib.XC_XCORR_WAVE]
 
 
 @pytest.mark.parametrize("name", ["xcorr_1to1_256", "xcorr_1to64_64", "xcorr_8to16_32"])
@@ -43,7 +43,7 @@ def test_xcorr_workloads_full(name, algo):
     (1, 2, 3, 2),
     (1, 1, 257, 19),
 ])
-@pytest.mark.parametrize("algo", [_lib.XC_XCORR_AUTO, _lib.XC_XCORR_OVERLAP])
+@pytest.mark.parametrize("algo", [_lib.XC_XCORR_AUTO, _lib.XC_XCORR_OVERLAP, _lib.XC_XCORR_WAVE])
 def test_xcorr_edge_shapes(shape, algo):
     nl, nr, rows, cols = shape
     rng = np.random.default_rng(rows * 131 + cols * 7 + nl + 17 * nr)
@@ -217,3 +217,40 @@ def test_xcorr_groupings(shape):
     _gpu.log(f"xcorr grouping {shape}")
     ref, ab = oracle.xcorr_f32(L, R)
     _gpu.check_xcorr(_gpu.run_xcorr(L, R, _lib.XC_XCORR_BLOCKDIAG), ref, ab)
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 3, 200), (1, 1, 200, 3), (2, 1, 70, 65), (1, 2, 9, 64), (1, 1, 128, 1)])
+def test_xcorr_wave_overlap_shapes(shape):
+    """Wave-per-overlap on overlaps narrower and wider than a wave: a lane's
+    next element wraps onto the next rows (64 // width of them) or stays in
+    the row."""
+    nl, nr, rows, cols = shape
+    rng = np.random.default_rng(1700 + rows * 3 + cols)
+    L = f32_uniform(rng, (nl, rows, cols))
+    R = f32_uniform(rng, (nr, rows, cols))
+    _gpu.log(f"xcorr wave-per-overlap {shape}")
+    ref, ab = oracle.xcorr_f32(L, R)
+    _gpu.check_xcorr(_gpu.run_xcorr(L, R, _lib.XC_XCORR_WAVE), ref, ab)
+
+
+def test_xcorr_wave_large_sampled():
+    """512x512 one-to-one through the wave-per-overlap kernel, sampled rows and
+    columns of the output against the oracle, and the whole output within
+    tolerance of the block-diagonal kernel's."""
+    rng = np.random.default_rng(1710)
+    rows = cols = 512
+    L = f32_uniform(rng, (1, rows, cols))
+    R = f32_uniform(rng, (1, rows, cols))
+    _gpu.log("xcorr 512x512 wave-per-overlap, sampled")
+    got = _gpu.run_xcorr(L, R, _lib.XC_XCORR_WAVE)
+    oh, ow = 2 * rows - 1, 2 * cols - 1
+    ys = np.concatenate([np.arange(oh), rng.integers(0, oh, 400)])
+    xs = np.concatenate([rng.integers(0, ow, oh), rng.integers(0, ow, 400)])
+    flat = ys * ow + xs
+    ref, ab = oracle.xcorr_f32_points(L, R, flat)
+    err = np.abs(got.reshape(-1)[flat].astype(np.float64) - ref)
+    assert np.all(err <= 1e-5 * ab + 1e-30)
+    bd = _gpu.run_xcorr(L, R, _lib.XC_XCORR_BLOCKDIAG)
+    # both within 1e-5 * sum|lr| of the exact value: within twice that of each other
+    sab = np.abs(L[0]).sum() * np.abs(R[0]).sum()
+    assert np.max(np.abs(got.astype(np.float64) - bd)) <= 2e-5 * sab
