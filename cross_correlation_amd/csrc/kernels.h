@@ -64,6 +64,13 @@ struct NccArgs {
     int cw;          // template words (4 bytes) per chunk
     int lds_stride;  // LDS words per staged image row
     int t_stride;    // LDS words per staged template row
+    // packed-byte (DOT4_ILP) tiles, set by its launcher: ncol_full x
+    // nrow_tiles ordinary tiles, then (tail_g > 1) the last column tile's
+    // narrow remainder as tail tiles whose lanes form tail_g groups of
+    // tail_nl lanes, each group taking its own rows
+    int ncol_full, nrow_tiles;
+    int tail_g, tail_nl;
+    uint32_t tail_m;  // ceil(2^16 / tail_nl): lane / tail_nl as a multiply
 };
 
 // force_q = 0: the tile picked for the shape; 1, 2 or 4: Q rows per lane

@@ -153,7 +153,7 @@ __device__ __forceinline__ void ncc_row_partial(const uint32_t *rp, const uint32
 // are added through LDS before the epilogue.
 // LDS: the image tile (WV*Q + hc - 1 rows of `lds_stride` words), then the
 // template chunk (hc rows of `t_stride` words).
-template <int Q, int WV, int KS, int WC>
+template <int Q, int WV, int KS, int WC, bool TAIL>
 __global__ __launch_bounds__(64 * WV * KS) void ncc_u8_ilp_kernel(NccArgs a)
 {
     extern __shared__ uint32_t lds[];
@@ -161,8 +161,31 @@ __global__ __launch_bounds__(64 * WV * KS) void ncc_u8_ilp_kernel(NccArgs a)
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int rw = wave % WV;  // output-row group of this wave
     const int kh = wave / WV;  // template-row slice of this wave
-    const int x0 = blockIdx.x * 256;
-    const int y0 = blockIdx.y * (WV * Q);
+    // Without TAIL, a 2D grid of 256 x WV*Q tiles.  With TAIL, a 1D grid:
+    // workgroups [0, ncol_full * nrow_tiles) are those tiles (column tile
+    // fastest), the rest tail tiles over the last column tile's remainder (at
+    // most 256 / tail_g columns): lane l is column lane l % tail_nl of group
+    // l / tail_nl, and the tail_g groups take tail_g consecutive bands of
+    // WV*Q rows, so the lanes past the remainder's width do useful work
+    // instead of idling (lanes of a last, incomplete group repeat group 0's
+    // work and store nothing).
+    int bx = blockIdx.x, by = blockIdx.y, G = 1, g = 0, cl = lane;
+    bool active = true;
+    if (TAIL) {
+        const int bid = blockIdx.x;
+        const int nfull = a.ncol_full * a.nrow_tiles;
+        const bool tail = bid >= nfull;  // workgroup-uniform
+        by = tail ? bid - nfull : bid / a.ncol_full;
+        bx = tail ? a.ncol_full : bid - by * a.ncol_full;
+        G = tail ? a.tail_g : 1;
+        g = tail ? (int)(((uint32_t)lane * a.tail_m) >> 16) : 0;  // lane / tail_nl
+        cl = tail ? lane - g * a.tail_nl : lane;                   // < tail_nl in a tail tile
+        active = g < G;
+        if (!active)
+            g = 0;
+    }
+    const int x0 = bx * 256;
+    const int y0 = by * (WV * Q * G);
     const int nw = (a.t_width + 3) >> 2;  // packed words per template row
     const uint32_t tm = tail_mask(a.t_width);
     const bool word_rows = tmpl_word_rows(a.tmpl, a.t_width);
@@ -179,7 +202,8 @@ __global__ __launch_bounds__(64 * WV * KS) void ncc_u8_ilp_kernel(NccArgs a)
 
     const int stride = a.lds_stride;
     const int tstride = a.t_stride;
-    uint32_t *const tl = lds + (WV * Q + a.hc - 1) * stride;
+    const int th = WV * Q * G;  // output rows of this tile
+    uint32_t *const tl = lds + (th + a.hc - 1) * stride;
     for (int jc = 0; jc < a.t_height; jc += a.hc) {
         const int hc = min(a.hc, a.t_height - jc);
         // this wave's template rows of the chunk: [j0, j1)
@@ -189,7 +213,7 @@ __global__ __launch_bounds__(64 * WV * KS) void ncc_u8_ilp_kernel(NccArgs a)
             const int cw = min(a.cw, nw - ic);
             __syncthreads();
             // lane l reads words l + k and l + k + 1, k < cw: 64 + cw words per row
-            stage_tile(a.image, a.height, a.pitch, y0 + jc, x0 + 4 * ic, WV * Q + hc - 1,
+            stage_tile(a.image, a.height, a.pitch, y0 + jc, x0 + 4 * ic, th + hc - 1,
                        (64 + cw + 3) / 4, lds, stride);
             for (int t = threadIdx.x; t < hc * cw; t += 64 * WV * KS) {
                 const int r = t / cw;
@@ -201,7 +225,7 @@ __global__ __launch_bounds__(64 * WV * KS) void ncc_u8_ilp_kernel(NccArgs a)
             const uint32_t cm = ic + cw == nw ? tm : 0xFFFFFFFFu;
             const int cw_main = cw - (cm != 0xFFFFFFFFu ? 1 : 0);
             if (j1 > j0) {
-                const uint32_t *wrow = lds + (rw * Q) * stride + lane;
+                const uint32_t *wrow = lds + (g * (WV * Q) + rw * Q) * stride + cl;
                 // Image rows rl (relative to the wave's first output row) meet
                 // template rows j = rl - q with j in [j0, j1).  Three straight
                 // loops -- ramp-up, steady (every q), ramp-down -- so the
@@ -258,12 +282,12 @@ __global__ __launch_bounds__(64 * WV * KS) void ncc_u8_ilp_kernel(NccArgs a)
     unsigned long long best = 0ull;
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
-        const int y = y0 + rw * Q + q;
-        if (y >= a.out_h)
+        const int y = y0 + g * (WV * Q) + rw * Q + q;
+        if (y >= a.out_h || !active)
             break;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            const int x = x0 + 4 * lane + c;
+            const int x = x0 + 4 * cl + c;
             if (x < a.out_w)
                 ncc_store(a, (size_t)y * a.out_w + x, ai[q][c], aq[q][c], at[q][c], n, st64, vt, best);
         }
@@ -510,13 +534,47 @@ __global__ void ncc_peak_finish_kernel(xc_ncc_peak *p, int out_w)
 // Host-side launch helpers (called by the C ABI after validation).
 
 template <int Q, int WV, int KS, int WC>
-static hipError_t launch_ilp(const NccArgs &a, hipStream_t s)
+static hipError_t launch_ilp(NccArgs a, hipStream_t s)
 {
-    dim3 grid((a.out_w + 255) / 256, (a.out_h + WV * Q - 1) / (WV * Q));
-    size_t lds = ((size_t)(WV * Q + a.hc - 1) * a.lds_stride + (size_t)a.hc * a.t_stride) * 4;
-    const size_t xchg = (size_t)WV * (KS - 1) * 3 * 4 * Q * 64 * 4;  // slice exchange, reuses the tile
-    if (xchg > lds) lds = xchg;
-    hipLaunchKernelGGL((ncc_u8_ilp_kernel<Q, WV, KS, WC>), grid, dim3(64 * WV * KS), lds, s, a);
+    auto kern_tail = ncc_u8_ilp_kernel<Q, WV, KS, WC, true>;
+    auto kern = ncc_u8_ilp_kernel<Q, WV, KS, WC, false>;
+    constexpr int NT = 64 * WV * KS;
+    auto lds_for = [&](int g) {  // LDS of tiles with g lane groups
+        size_t l = ((size_t)(WV * Q * g + a.hc - 1) * a.lds_stride + (size_t)a.hc * a.t_stride) * 4;
+        const size_t xchg = (size_t)WV * (KS - 1) * 3 * 4 * Q * 64 * 4;  // slice exchange, reuses the tile
+        return l > xchg ? l : xchg;
+    };
+    auto tails = [&](int g) { return g > 1 ? (a.out_h + WV * Q * g - 1) / (WV * Q * g) : 0; };
+    if (a.tail_g > 1) {
+        // Tail tiles pay only where they take the grid to fewer rounds of
+        // resident workgroups: every workgroup does the same work, so with
+        // the same number of rounds the kernel takes as long, and a tail
+        // tile's taller image tile makes it the last to finish (1920x1080
+        // with 64x64: 512 workgroups, two per CU either way, 221 against
+        // 226 us; with 16x16: 536 against 503, two rounds against one, 41
+        // against 31 us).
+        const int ncol = a.ncol_full + 1;
+        const int64_t w1 = (int64_t)ncol * a.nrow_tiles, wg = (int64_t)a.ncol_full * a.nrow_tiles + tails(a.tail_g);
+        int r1 = 0, rg = 0;
+        const bool known = hipOccupancyMaxActiveBlocksPerMultiprocessor(&r1, kern, NT, lds_for(1)) == hipSuccess &&
+                           hipOccupancyMaxActiveBlocksPerMultiprocessor(&rg, kern_tail, NT, lds_for(a.tail_g)) ==
+                               hipSuccess &&
+                           r1 > 0 && rg > 0;
+        const int64_t cus = device_cu_count();
+        if (!known || (wg + cus * rg - 1) / (cus * rg) >= (w1 + cus * r1 - 1) / (cus * r1)) {
+            a.tail_g = 1;
+            a.tail_nl = 64;
+            a.tail_m = 1024;  // ceil(2^16 / 64)
+            a.ncol_full = ncol;
+        }
+    }
+    if (a.tail_g > 1) {
+        const int64_t blocks = (int64_t)a.ncol_full * a.nrow_tiles + tails(a.tail_g);
+        if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL(kern_tail, dim3((unsigned)blocks), dim3(NT), lds_for(a.tail_g), s, a);
+    } else {
+        hipLaunchKernelGGL(kern, dim3(a.ncol_full, a.nrow_tiles), dim3(NT), lds_for(1), s, a);
+    }
     return hipGetLastError();
 }
 
@@ -574,6 +632,28 @@ hipError_t ncc_launch_ilp(NccArgs a, hipStream_t s, int force_q)
     if (hc < 1) hc = 1;
     if (hc > a.t_height) hc = a.t_height;
     a.hc = hc;
+    // Tiles: the column tiles, the last one holding rem = out_w - 256 * (n - 1)
+    // columns, i.e. nl = ceil(rem / 4) lanes.  When at least two groups of nl
+    // lanes fit in a wave, that last column may go to tail tiles of G = 64 / nl
+    // lane groups (G times the rows of a tile), as long as their taller
+    // image tile still holds the same template rows per chunk in 64 KiB
+    // (launch_ilp keeps them only where they save a round of workgroups).
+    const int ncol = (a.out_w + 255) / 256;
+    const int nl = ((a.out_w - 256 * (ncol - 1)) + 3) / 4;
+    int G = 64 / nl;
+    while (G >= 2 && ((G * th + hc - 1) * a.lds_stride + hc * a.t_stride > lds_words)) --G;
+    a.nrow_tiles = (a.out_h + th - 1) / th;
+    if (G >= 2) {
+        a.tail_g = G;
+        a.tail_nl = nl;
+        a.tail_m = (65536u + (uint32_t)nl - 1) / (uint32_t)nl;
+        a.ncol_full = ncol - 1;
+    } else {
+        a.tail_g = 1;
+        a.tail_nl = 64;
+        a.tail_m = 1024;  // ceil(2^16 / 64)
+        a.ncol_full = ncol;
+    }
     if (q == 4) return ks == 2 ? dispatch_wc<4, 4, 2>(a, wc, s) : dispatch_wc<4, 4, 1>(a, wc, s);
     if (q == 2) return dispatch_wc<2, 2, 1>(a, wc, s);
     return dispatch_wc<1, 1, 1>(a, wc, s);

@@ -190,9 +190,27 @@ struct BdArgs {
     int n_xtiles;    // wp / BD_P
     int n_dgroups;   // ceil(nb / waves per workgroup)
     int n_sides;     // 1: a workgroup walks both dx signs; 2: one sign each
+    int wg_sides;    // 1: both dx signs in one workgroup, one per half of its waves
     // multipliers for division by nb and by the whole-staging row widths
     uint32_t m_nb, m_nr;  // fast_div_m(nb), small_div_m16(n_right)
+    // exact division of any 32-bit value (div_m / div_exact) by n_sides,
+    // n_dgroups, n_xtiles and n_right (workgroup ids, pair indices)
+    uint32_t m_sides, m_dgroups, m_xtiles, m_right;
+    // whole staging: items per row (cols / 4 or cols), rows per slot (4 nb)
+    // and halo columns per unit
+    uint32_t m_c4, m_cols, m_rpb, m_nh;
 };
+
+// floor(x / d) for any 32-bit x and d >= 1, with m = div_m(d): the high
+// multiply gives floor(x / d) or one less (m = floor((2^32 - 1) / d) is at
+// most d / 2^32 below 2^32 / d), and one compare corrects it.
+__host__ __device__ constexpr uint32_t div_m(uint32_t d) { return 0xFFFFFFFFu / d; }
+__device__ __forceinline__ uint32_t div_exact(uint32_t x, uint32_t d, uint32_t m)
+{
+    uint32_t q = __umulhi(x, m);
+    q += (x - q * d >= d) ? 1u : 0u;
+    return q;
+}
 
 // floor(x / d) as one high multiply, with m = fast_div_m(d); exact whenever
 // x * d < 2^32 (m = (2^32 + e) / d with 0 < e <= d, so the product
@@ -231,19 +249,28 @@ __device__ __forceinline__ void bd_step(const float4 l1, const float4 l2, const 
 {
     const float la[4] = {l1.x, l1.y, l1.z, l1.w};
     const float lb[3] = {l2.x, l2.y, l2.z};
+    // right LDS column m + P - 1 - p lives in ring slot (m + P - 1 - p) mod (P + 1)
+    float re[P][4];
 #pragma unroll
     for (int p = 0; p < P; ++p) {
-        // right LDS column m + P - 1 - p lives in ring slot (m + P - 1 - p) mod (P + 1)
         const float4 rv = ring[(m + P - 1 - p) % (P + 1)];
-        const float re[4] = {rv.x, rv.y, rv.z, rv.w};
+        re[p][0] = rv.x;
+        re[p][1] = rv.y;
+        re[p][2] = rv.z;
+        re[p][3] = rv.w;
+    }
+    // e outermost: the 16 FMAs of one e go to 16 different accumulators, so
+    // an accumulator's successive FMAs are 16 instructions apart
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
+    for (int e = 0; e < 4; ++e) {
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
 #pragma unroll
             for (int ar = 0; ar < 4; ++ar) {
                 if (ar >= e)
-                    acc1[ar - e][p] = fmaf(la[ar], re[e], acc1[ar - e][p]);
+                    acc1[ar - e][p] = fmaf(la[ar], re[p][e], acc1[ar - e][p]);
                 else
-                    acc2[ar - e + 3][p] = fmaf(lb[ar], re[e], acc2[ar - e + 3][p]);
+                    acc2[ar - e + 3][p] = fmaf(lb[ar], re[p][e], acc2[ar - e + 3][p]);
             }
         }
     }
@@ -307,6 +334,7 @@ __device__ __forceinline__ int xcd_logical_id(int b, int n)
 // tile a workgroup / wave / lane works on.
 struct BdWho {
     int lane, wave, grp, c0, delta, s, b, kb1, kb2, ls, bstar, side_lo, side_hi;
+    int l_first, r_first;  // left and right matrix of the group's first pair
     bool wave_on;
 };
 
@@ -316,17 +344,30 @@ __device__ __forceinline__ BdWho bd_who(const BdArgs &a)
     BdWho w;
     w.lane = threadIdx.x & 63;
     w.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    int bid = xcd_logical_id(blockIdx.x, gridDim.x);
-    const int side = bid % a.n_sides;
-    bid /= a.n_sides;
-    const int dgrp = bid % a.n_dgroups;
-    bid /= a.n_dgroups;
-    const int xt = bid % a.n_xtiles;
-    w.grp = bid / a.n_xtiles;
+    uint32_t bid = (uint32_t)xcd_logical_id(blockIdx.x, gridDim.x);
+    uint32_t q = div_exact(bid, (uint32_t)a.n_sides, a.m_sides);
+    const int side = (int)(bid - q * (uint32_t)a.n_sides);
+    bid = q;
+    q = div_exact(bid, (uint32_t)a.n_dgroups, a.m_dgroups);
+    const int dgrp = (int)(bid - q * (uint32_t)a.n_dgroups);
+    bid = q;
+    q = div_exact(bid, (uint32_t)a.n_xtiles, a.m_xtiles);
+    const int xt = (int)(bid - q * (uint32_t)a.n_xtiles);
+    w.grp = (int)q;
     w.c0 = xt * BD_P;
     w.side_lo = a.n_sides == 2 ? side : 0;
     w.side_hi = a.n_sides == 2 ? side + 1 : 2;
     w.delta = dgrp * NW + w.wave;  // this wave's block diagonal
+    if (NW >= 2 && a.wg_sides) {
+        // waves h and h + NW/2 share a diagonal and take the two dx signs,
+        // whose walks (cols - c0 and c0 + P steps) add up to the same total
+        // for every column tile
+        constexpr int H = NW / 2;
+        const int hs = w.wave >= H ? 1 : 0;
+        w.side_lo = hs;
+        w.side_hi = hs + 1;
+        w.delta = dgrp * H + (w.wave - hs * H);
+    }
     w.wave_on = w.delta < a.nb;
     const int nb = a.nb;
     int sl = fast_div(w.lane, a.m_nb);
@@ -342,11 +383,15 @@ __device__ __forceinline__ BdWho bd_who(const BdArgs &a)
     w.kb2 = k2;
     // left-matrix slot: distinct left matrices of the group, in order.  The
     // group's first pair p0 is (l_first, r_first); pair p0 + d (d < 64) has
-    // left matrix l_first + (r_first + d) / n_right.
-    const int64_t p0 = (int64_t)w.grp * a.S;
-    const int64_t np = (int64_t)a.x.n_left * a.x.n_right;
-    const unsigned r_first = (unsigned)(p0 % a.x.n_right);
-    const unsigned d = (unsigned)min((int64_t)sl, np - 1 - p0);
+    // left matrix l_first + (r_first + d) / n_right.  (Pair indices are below
+    // 2^31: the block-diagonal kernels take at least 13 rows, so a pair has
+    // at least 625 outputs, and a call at most 2^40.)
+    const uint32_t p0 = (uint32_t)w.grp * (uint32_t)a.S;
+    const uint32_t np = (uint32_t)a.x.n_left * (uint32_t)a.x.n_right;
+    w.l_first = (int)div_exact(p0, (uint32_t)a.x.n_right, a.m_right);
+    const unsigned r_first = p0 - (uint32_t)w.l_first * (uint32_t)a.x.n_right;
+    w.r_first = (int)r_first;
+    const unsigned d = min((unsigned)sl, np - 1 - p0);
     w.ls = small_div((int)(r_first + d), a.x.n_right, a.m_nr);
     w.bstar = nb - dl - 1;  // the lane whose block 1 is unwrapped and block 2 wrapped
     return w;
@@ -370,17 +415,16 @@ __device__ __forceinline__ float bd_col_sum(const float *col, int lo, int hi)
 }
 
 // Cross-lane reduction of one side's partial sums, in a fixed order, then the
-// stores.  Each wave uses only its own LDS area, so a wave-level barrier
-// suffices.  comb = block-1 sums plus block-2 sums when both blocks share the
-// wrap status (every lane but bstar); bstar keeps its block-2 sums apart.
-__device__ __forceinline__ void bd_reduce_store(const BdArgs &a, const BdWho &w, int side, float *wred,
-                                                float *wextra, const float (&acc1)[4][BD_P],
-                                                const float (&acc2)[3][BD_P])
+// stores, in two parts.  bd_write_partials: each lane writes its 16 partials
+// to the wave's area (row (r, p) of 65 floats, one per lane); comb = block-1
+// sums plus block-2 sums when both blocks share the wrap status (every lane
+// but bstar); bstar keeps its block-2 sums apart in the area's extra part.
+__device__ __forceinline__ void bd_write_partials(const BdArgs &a, const BdWho &w, float *wred,
+                                                  const float (&acc1)[4][BD_P], const float (&acc2)[3][BD_P])
 {
     constexpr int P = BD_P;
-    constexpr int NV = 4 * P;
     constexpr int RS = 65;  // row stride: lanes reading different rows hit different banks
-    const int nb = a.nb, S = a.S;
+    float *const wextra = wred + 4 * P * RS;
 #pragma unroll
     for (int p = 0; p < P; ++p)
 #pragma unroll
@@ -389,23 +433,30 @@ __device__ __forceinline__ void bd_reduce_store(const BdArgs &a, const BdWho &w,
             if (r >= 1 && w.b != w.bstar) c += acc2[r - 1][p];
             wred[(r * P + p) * RS + w.lane] = c;
         }
-    if (w.b == w.bstar && w.lane < S * nb) {
+    if (w.b == w.bstar && w.lane < a.S * a.nb) {
 #pragma unroll
         for (int p = 0; p < P; ++p)
 #pragma unroll
             for (int r = 0; r < 3; ++r)
                 wextra[(w.s * 3 + r) * P + p] = acc2[r][p];
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// bd_sum_store: the outputs of one side from the wave's partial area, once
+// its writes are visible.  Lane (slot, r, p), p fastest (4 lanes store 16
+// contiguous bytes), sums its column of block partials over two
+// wave-uniform ranges: blocks [0, split) for output row 4*delta + r and,
+// wrapped, [split, nb) for row 4*delta + r - 4*nb (plus the wrap lane's
+// block-2 sums).
+__device__ __forceinline__ void bd_sum_store(const BdArgs &a, const BdWho &w, int side, const float *wred)
+{
+    constexpr int P = BD_P;
+    constexpr int NV = 4 * P;
+    constexpr int RS = 65;
+    const int nb = a.nb, S = a.S;
     const int rows = a.x.rows, cols = a.x.cols, h4 = 4 * nb;
     const int oh = 2 * rows - 1, ow = 2 * cols - 1;
     const int64_t npairs = (int64_t)a.x.n_left * a.x.n_right;
-    // Lane (slot, r, p), p fastest (4 lanes store 16 contiguous bytes), sums
-    // its column of block partials in two wave-uniform ranges: blocks
-    // [0, split) for output row 4*delta + r and, wrapped, [split, nb) for row
-    // 4*delta + r - 4*nb (plus the wrap lane's block-2 sums).
     const int split = nb - w.delta;
     for (int o = w.lane; o < S * NV; o += 64) {
         const int sl = o / NV;
@@ -419,7 +470,7 @@ __device__ __forceinline__ void bd_reduce_store(const BdArgs &a, const BdWho &w,
         const float s_un = bd_col_sum(col, 0, split);
         float s_wr = bd_col_sum(col, split, nb);
         if (r >= 1)
-            s_wr += wextra[(sl * 3 + (r - 1)) * P + p];
+            s_wr += wred[4 * P * RS + (sl * 3 + (r - 1)) * P + p];
         if (pair < npairs && dx > -cols && dx < cols) {
             const int dy0 = 4 * w.delta + r, dy1 = dy0 - h4;
             float *const outp = a.x.out + (size_t)pair * oh * ow + (dx + cols - 1);
@@ -429,6 +480,18 @@ __device__ __forceinline__ void bd_reduce_store(const BdArgs &a, const BdWho &w,
                 outp[(size_t)(dy1 + rows - 1) * ow] = s_wr;
         }
     }
+}
+
+// One side reduced within the wave: each wave uses only its own LDS area,
+// so a wave-level barrier suffices.
+__device__ __forceinline__ void bd_reduce_store(const BdArgs &a, const BdWho &w, int side, float *wred,
+                                                const float (&acc1)[4][BD_P], const float (&acc2)[3][BD_P])
+{
+    bd_write_partials(a, w, wred, acc1, acc2);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    bd_sum_store(a, w, side, wred);
     // the next side's writes come after these reads in every lane's program
     // order and LDS serves one wave in order
     __builtin_amdgcn_wave_barrier();
@@ -480,7 +543,6 @@ __global__ __launch_bounds__(64 * NW) void xcorr_bd_chunk_kernel(BdArgs a)
     const int buf_elems = l_elems + S * nb * G::NCR;
     float *const red = reinterpret_cast<float *>(smem);
     float *const wred = red + w.wave * bd_red_floats(S);
-    float *const wextra = wred + 4 * P * 65;
 
     // Staging: thread t owns row block sb = t / NW (slot * nb + block, all
     // S*nb <= 64 blocks) and the columns congruent to t mod NW.  One item is
@@ -562,8 +624,92 @@ __global__ __launch_bounds__(64 * NW) void xcorr_bd_chunk_kernel(BdArgs a)
             __syncthreads();
         }
         if (w.wave_on)
-            bd_reduce_store(a, w, side, wred, wextra, acc1, acc2);
+            bd_reduce_store(a, w, side, wred, acc1, acc2);
         __syncthreads();  // reduction reads done before the next side stages
+    }
+}
+
+// Whole staging of a pair group into LDS, layout [unit][W columns] of float4
+// (a unit is a block of 4 rows; its float4 at index g + P - 1 holds the 4
+// rows at source column g; zeros in the P - 1 columns before the data and
+// from index cols + P - 1 to W).  Units: nls left slots x nb blocks, then S
+// pair slots x nb blocks.  Staged as two regions of rows, left then right,
+// in one loop (the code is fetched once): region row R (of slots x 4 nb) is
+// row R mod 4nb of the region's slot R / 4nb, i.e. of matrix
+// (first + slot) mod n_mod, and lands in unit R / 4, row R mod 4.  The
+// workgroup's NT threads take a region's items in a flat loop, BK per batch
+// with all of a batch's loads issued before its LDS stores; an item is one
+// row's 4 consecutive columns (one 16-byte load into the 4 columns' float4
+// slots) when cols is a multiple of 4 (every row then starts 16-byte
+// aligned), else one element.  Rows past the matrix and empty slots load from
+// four zeros in device memory, so no value is selected after its load.
+template <int NT>
+__device__ __forceinline__ void bd_stage_whole(const BdArgs &a, float4 *smem, int W, const BdWho &w,
+                                               int64_t npairs)
+{
+    constexpr int P = BD_P;
+    constexpr int BK = 4;
+    float *const sf = reinterpret_cast<float *>(smem);
+    const int nb = a.nb, cols = a.x.cols, rows = a.x.rows, rpb = 4 * nb;
+    const bool vec4 = (cols & 3) == 0;  // workgroup-uniform
+    const int per_row = vec4 ? cols >> 2 : cols;
+    const uint32_t m_row = vec4 ? a.m_c4 : a.m_cols;
+    const int64_t p0 = (int64_t)w.grp * a.S;
+    const float *const left = a.x.left, *const right = a.x.right;
+    const uint32_t mat_elems = (uint32_t)rows * (uint32_t)cols;
+    for (int reg = 0; reg < 2; ++reg) {
+        // left slots: matrices l_first + sl (never wrap), present below
+        // n_left; pair slots: right matrices (r_first + sl) mod n_right,
+        // present while the pair exists
+        const float *const base = reg ? right : left;
+        const int nslots = reg ? a.S : a.nls;
+        const int first = reg ? w.r_first : w.l_first;
+        const uint32_t n_mod = reg ? (uint32_t)a.x.n_right : 0x40000000u;
+        const uint32_t m_mod = reg ? a.m_right : 3u;  // div_m(2^30) = 3
+        const int n_on = reg ? (int)min((int64_t)a.S, npairs - p0) : a.x.n_left - w.l_first;
+        const int unit0 = reg ? a.nls * nb : 0;
+        const int total = nslots * rpb * per_row;
+        for (int i0 = threadIdx.x; i0 < total; i0 += BK * NT) {
+            float4 v[BK];
+            int dst[BK];
+#pragma unroll
+            for (int k = 0; k < BK; ++k) {
+                const int i = i0 + k * NT;
+                const int R = fast_div(i, m_row);     // region row
+                const int c = i - R * per_row;        // column group (vec4) or column
+                const int sl = fast_div(R, a.m_rpb);  // slot
+                const int rr = R - sl * rpb;          // row within the matrix
+                const uint32_t t = (uint32_t)(first + sl);
+                const uint32_t mi = t - div_exact(t, n_mod, m_mod) * n_mod;  // t mod n_mod
+                const bool ok = i < total && rr < rows && sl < n_on;
+                const int cc = vec4 ? 4 * c : c;
+                const float *src = base + ((uint64_t)mi * mat_elems + (uint32_t)(rr * cols + cc));
+                const float *zs = bd_zero4;
+                if (vec4)
+                    v[k] = *reinterpret_cast<const float4 *>(ok ? src : zs);
+                else
+                    v[k].x = *(ok ? src : zs);
+                dst[k] = i < total ? (((unit0 + (R >> 2)) * W + (P - 1) + cc) * 4 + (R & 3)) : -1;
+            }
+#pragma unroll
+            for (int k = 0; k < BK; ++k)
+                if (dst[k] >= 0) {
+                    sf[dst[k]] = v[k].x;
+                    if (vec4) {
+                        sf[dst[k] + 4] = v[k].y;
+                        sf[dst[k] + 8] = v[k].z;
+                        sf[dst[k] + 12] = v[k].w;
+                    }
+                }
+        }
+    }
+    // zero halos: columns [0, P - 1) and [cols + P - 1, W) of every unit
+    const int n_units = (a.nls + a.S) * nb;
+    const int nh = W - cols;
+    for (int i = threadIdx.x; i < n_units * nh; i += NT) {
+        const int u = fast_div(i, a.m_nh);
+        const int h = i - u * nh;
+        smem[u * W + (h < P - 1 ? h : cols + h)] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     }
 }
 
@@ -590,85 +736,8 @@ __global__ __launch_bounds__(64 * NW) void xcorr_bd_whole_kernel(BdArgs a)
     float4 *const Rs = smem + l_elems;
     float *const red = reinterpret_cast<float *>(smem + l_elems + S * nb * W);
     float *const wred = red + w.wave * bd_red_floats(S);
-    float *const wextra = wred + 4 * P * 65;
 
-    const int64_t p0 = (int64_t)w.grp * S;
-    const int l_first = (int)(p0 / a.x.n_right);
-    const int r_first = (int)(p0 % a.x.n_right);  // right matrix of the group's first pair
-    // Staging, in two steps.  (1) The first threads build a table in the
-    // (still unused) reduction area: for each unit, the offset of its first
-    // source row in the left or right array and the number of source rows
-    // (0: an empty slot, all zeros).  (2) Waves then take whole units, wave-uniform: the table entry
-    // goes to scalar registers and a lane only adds its own column, so a
-    // unit costs a lane a handful of instructions; the loads of KB units are
-    // issued before any of their LDS stores, so they are in flight together.
-    // Lanes below W - cols also write the unit's zero halo columns.
-    const int n_units = n_lu + S * nb;
-    uint4 *const table = reinterpret_cast<uint4 *>(red);
-    if ((int)threadIdx.x < n_units) {
-        const int u = threadIdx.x;
-        const bool is_l = u < n_lu;
-        const int ur = is_l ? u : u - n_lu;
-        const int sl = fast_div(ur, a.m_nb);
-        const int row0 = 4 * (ur - sl * nb);
-        int mat;
-        bool on;
-        if (is_l) {
-            // left slot sl: matrix l_first + sl
-            mat = l_first + sl;
-            on = mat < a.x.n_left;
-        } else {
-            // pair slot sl: pair p0 + sl, right matrix (r_first + sl) mod n_right
-            const int rq = r_first + sl;
-            mat = rq - small_div(rq, a.x.n_right, a.m_nr) * a.x.n_right;
-            on = p0 + sl < npairs;
-        }
-        const uint64_t off = (uint64_t)(on ? mat : 0) * rows * cols + (uint64_t)row0 * cols;  // elements
-        table[u] = make_uint4((uint32_t)off, (uint32_t)(off >> 32), on ? (uint32_t)min(4, rows - row0) : 0u,
-                              is_l ? 1u : 0u);
-    }
-    __syncthreads();
-    {
-        constexpr int KB = 8;
-        const int n_halo = W - cols;  // P - 1 columns left of the data, the rest right of it
-        const int halo_c = w.lane < P - 1 ? w.lane : cols + w.lane;
-        for (int cp = 0; cp * 64 < cols; ++cp) {
-            const int gc = cp * 64 + w.lane;  // source column
-            const bool col_ok = gc < cols;
-            for (int u0 = w.wave; u0 < n_units; u0 += NW * KB) {
-                float4 v[KB];
-#pragma unroll
-                for (int k = 0; k < KB; ++k) {
-                    const int u = u0 + k * NW;  // wave-uniform
-                    v[k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-                    if (u < n_units) {
-                        const uint4 e = table[u];
-                        const uint32_t lo = __builtin_amdgcn_readfirstlane(e.x);
-                        const uint32_t hi = __builtin_amdgcn_readfirstlane(e.y);
-                        const int nrow = (int)__builtin_amdgcn_readfirstlane(e.z);
-                        const bool t_l = __builtin_amdgcn_readfirstlane(e.w) != 0;
-                        const float *src = (t_l ? a.x.left : a.x.right) + (((uint64_t)hi << 32) | lo);
-                        if (col_ok && nrow > 0) {
-                            v[k].x = src[gc];
-                            if (nrow > 1) v[k].y = src[cols + gc];
-                            if (nrow > 2) v[k].z = src[2 * cols + gc];
-                            if (nrow > 3) v[k].w = src[3 * cols + gc];
-                        }
-                    }
-                }
-#pragma unroll
-                for (int k = 0; k < KB; ++k) {
-                    const int u = u0 + k * NW;
-                    if (u < n_units) {
-                        if (col_ok)
-                            smem[u * W + (P - 1) + gc] = v[k];
-                        if (cp == 0 && w.lane < n_halo)
-                            smem[u * W + halo_c] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-                    }
-                }
-            }
-        }
-    }
+    bd_stage_whole<64 * NW>(a, smem, W, w, npairs);
     __syncthreads();
     if (!w.wave_on)
         return;
@@ -689,7 +758,7 @@ __global__ __launch_bounds__(64 * NW) void xcorr_bd_whole_kernel(BdArgs a)
         bd_compute<16>(Ls + (w.ls * nb + w.kb1) * W + (P - 1) + u_first,
                        Ls + (w.ls * nb + w.kb2) * W + (P - 1) + u_first,
                        Rs + (w.s * nb + w.b) * W + u_first + roff, u_end - u_first, acc1, acc2);
-        bd_reduce_store(a, w, side, wred, wextra, acc1, acc2);
+        bd_reduce_store(a, w, side, wred, acc1, acc2);
     }
 }
 
@@ -903,6 +972,7 @@ bool xcorr_blockdiag_supported(const XcorrArgs &a)
 
 constexpr size_t BD_LDS_MAX = 160 * 1024;
 
+// Whole staging LDS: the staged units, then one partial-sum area per wave.
 static size_t bd_whole_lds(const BdArgs &b, int nw)
 {
     return (size_t)(b.nls + b.S) * b.nb * bd_whole_w(b.wp) * sizeof(float4) +
@@ -918,6 +988,22 @@ static size_t bd_chunk_lds(const BdArgs &b)
     return stage > red ? stage : red;
 }
 
+// Multipliers for the kernels' divisions by this launch's grid factors and
+// staging widths (set once the launcher has fixed them).
+static void bd_set_magic(BdArgs &b)
+{
+    b.m_sides = div_m((uint32_t)b.n_sides);
+    b.m_dgroups = div_m((uint32_t)b.n_dgroups);
+    b.m_xtiles = div_m((uint32_t)b.n_xtiles);
+    // whole staging only (rows of at least 29 columns, so every divisor
+    // below is at least 2, as fast_div needs); unused by the other kernels
+    const uint32_t nc4 = (uint32_t)(b.x.cols / 4), nh = (uint32_t)(bd_whole_w(b.wp) - b.x.cols);
+    b.m_c4 = nc4 >= 2 ? fast_div_m(nc4) : 0u;
+    b.m_cols = b.x.cols >= 2 ? fast_div_m((uint32_t)b.x.cols) : 0u;
+    b.m_nh = nh >= 2 ? fast_div_m(nh) : 0u;
+    b.m_rpb = fast_div_m((uint32_t)(4 * b.nb));
+}
+
 template <int NW>
 static hipError_t launch_whole(BdArgs b, hipStream_t s)
 {
@@ -925,7 +1011,9 @@ static hipError_t launch_whole(BdArgs b, hipStream_t s)
     static std::atomic<uint64_t> lds_allowed{0};
     const hipError_t e = allow_lds_once(&xcorr_bd_whole_kernel<NW>, lds_allowed);
     if (e != hipSuccess) return e;
-    b.n_dgroups = (b.nb + NW - 1) / NW;
+    const int dpw = b.wg_sides ? NW / 2 : NW;  // diagonals per workgroup
+    b.n_dgroups = (b.nb + dpw - 1) / dpw;
+    bd_set_magic(b);
     const unsigned blocks = (unsigned)((int64_t)b.n_groups * b.n_xtiles * b.n_dgroups * b.n_sides);
     const size_t lds = bd_whole_lds(b, NW);
     hipLaunchKernelGGL((xcorr_bd_whole_kernel<NW>), dim3(blocks), dim3(64 * NW), lds, s, b);
@@ -940,6 +1028,7 @@ static hipError_t launch_chunk(BdArgs b, hipStream_t s)
     const hipError_t e = allow_lds_once(&xcorr_bd_chunk_kernel<NW, J>, lds_allowed);
     if (e != hipSuccess) return e;
     b.n_dgroups = (b.nb + NW - 1) / NW;
+    bd_set_magic(b);
     const unsigned blocks = (unsigned)((int64_t)b.n_groups * b.n_xtiles * b.n_dgroups * b.n_sides);
     const size_t lds = bd_chunk_lds<NW, J>(b);
     hipLaunchKernelGGL((xcorr_bd_chunk_kernel<NW, J>), dim3(blocks), dim3(64 * NW), lds, s, b);
@@ -979,6 +1068,8 @@ hipError_t xcorr_launch_blockdiag(const XcorrArgs &a, hipStream_t s)
     b.wp = (a.cols + BD_P - 1) / BD_P * BD_P;
     b.m_nb = fast_div_m((uint32_t)b.nb);
     b.m_nr = small_div_m16((uint32_t)a.n_right);
+    b.m_right = div_m((uint32_t)a.n_right);
+    b.wg_sides = 0;
 
     const int64_t npairs = (int64_t)a.n_left * a.n_right;
     if (b.nb > 64) {
@@ -1026,10 +1117,12 @@ hipError_t xcorr_launch_blockdiag(const XcorrArgs &a, hipStream_t s)
         const int64_t n_wg = per_side * ((b.nb + nw_ - 1) / nw_) * sides;
         return per_cu * nw_ >= 16 || n_wg <= per_cu * cus;
     };
-    // Up to 8 diagonals: one 8-wave workgroup holds them all and shares one
-    // staging; the dx signs go to separate workgroups.
+    // Up to 8 diagonals: 8-wave workgroups, each half walking one dx sign of
+    // the same 4 diagonals (the two signs' walks add up to the same length
+    // for every column tile, so every SIMD gets the same work).
     if (b.nb <= 8 && whole_ok(8, 2)) {
-        b.n_sides = 2;
+        b.n_sides = 1;
+        b.wg_sides = 1;
         return launch_whole<8>(b, s);
     }
     if (nw == 16 && whole_ok(16, b.n_sides)) return launch_whole<16>(b, s);

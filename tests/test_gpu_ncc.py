@@ -333,3 +333,21 @@ def test_api_rejects_mismatched_outputs():
     L = torch.zeros((2, 16, 16), device="cuda")
     with pytest.raises(ValueError, match="elements"):
         api.xcorr_f32(L, L, out=torch.empty((2, 2, 31, 30), device="cuda"))
+
+
+# Output widths whose last 256-column tile is narrow: the packed-byte kernel
+# may give that remainder to tail tiles of several lane groups (64 // lanes
+# needed), each group taking its own band of rows, where that saves a round
+# of resident workgroups.  The 3200-row outputs with 16 x 16 templates do on
+# a 256-CU MI355X (600 tiles of 256 x 16, two per CU, against 500 or fewer
+# with tail tiles) with 4, 44 and 128 columns left over (up to 16, 5 and 2
+# groups, fewer where the taller tile would not fit in LDS); the other shapes
+# keep ordinary tiles (and one-row tiles on the short image).
+@pytest.mark.parametrize("out_w,out_h,t", [(516, 3200, 16), (556, 3200, 16), (640, 3200, 16), (257, 690, 9),
+                                           (385, 690, 64), (300, 36, 5)])
+def test_ncc_ilp_tail_tiles(out_w, out_h, t):
+    case = ncc_case("tail", 77 + out_w + t, out_h + t - 1, out_w + t - 1, t, t, cut=True)
+    _gpu.log(f"ncc packed-byte tail tiles: {case.height}x{case.width} t{t}x{t} (out {out_h}x{out_w})")
+    res = _gpu.run_ncc(case, _lib.XC_NCC_DOT4_ILP)
+    _gpu.check_ncc(case, res)
+    assert res["coef"][case.cut] == np.float32(1.0)
