@@ -21,6 +21,7 @@ XC_ERR_OVERFLOW = -4
 XC_ERR_ALIGN = -5
 XC_ERR_HIP = -6
 XC_ERR_VARIANT = -7
+XC_ERR_SCRATCH = -8
 
 XC_NCC_AUTO = 0
 XC_NCC_DOT4_ILP = 1
@@ -50,7 +51,7 @@ XC_NCC_MAX_TEMPLATE_PIXELS = 66051
 
 # Every symbol the public header declares.
 EXPORTED = ("ncc_u8_run", "ncc_u8_run_variant", "ncc_u8_peak", "ncc_u8_auto_variant", "ncc_u8_mode_workspace",
-            "ncc_u8_run_mode",
+            "ncc_u8_run_mode", "ncc_u8_run_mode_noalloc",
             "xcorr_f32_run", "xcorr_f32_run_algo", "xc_status_str")
 
 # xc_ncc_peak (include/xcorr.h): key u64, y i32, x i32, coef f32, reserved i32
@@ -94,6 +95,8 @@ def load(path: str = LIB_PATH):
     lib.ncc_u8_run_mode.restype = _i
     lib.ncc_u8_run_mode.argtypes = [_vp, _i, _i, _i, _vp, _i, _i, _i, _vp, ctypes.c_size_t, _vp, _vp, _vp, _vp, _i,
                                     _vp]
+    lib.ncc_u8_run_mode_noalloc.restype = _i
+    lib.ncc_u8_run_mode_noalloc.argtypes = [_vp, _i, _i, _i, _vp, _i, _i, _i, _vp, _vp, _vp, _vp, _i, _vp]
     lib.xcorr_f32_run.restype = _i
     lib.xcorr_f32_run.argtypes = [_vp, _i, _vp, _i, _i, _i, _vp, _vp]
     lib.xcorr_f32_run_algo.restype = _i
@@ -159,6 +162,17 @@ def ncc_u8_run_mode(image, width, height, pitch, tmpl, t_width, t_height, mode, 
     return load().ncc_u8_run_mode(image, width, height, pitch, tmpl, t_width, t_height, mode, workspace or None,
                                   workspace_bytes, sum_i or None, sum_isq or None, sum_it or None, coef or None,
                                   variant, stream or None)
+
+
+XC_NCC_MODE_SCRATCH_BYTES = 16 << 20
+
+
+def ncc_u8_run_mode_noalloc(image, width, height, pitch, tmpl, t_width, t_height, mode, sum_i, sum_isq, sum_it,
+                            coef, stream=None, variant=XC_NCC_AUTO) -> int:
+    """Raw call with integer device addresses (0 for NULL); returns the status."""
+    return load().ncc_u8_run_mode_noalloc(image, width, height, pitch, tmpl, t_width, t_height, mode,
+                                          sum_i or None, sum_isq or None, sum_it or None, coef or None, variant,
+                                          stream or None)
 
 
 def decode_peak(raw: bytes) -> tuple[int, int, float]:

@@ -4,8 +4,19 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "kernels.h"
 #include "xcorr.h"
+
+// Device scratch of ncc_u8_run_mode_noalloc: the padded image lives here
+// instead of in a caller-owned workspace.  Each GPU the library runs on holds
+// its own copy (XC_NCC_MODE_SCRATCH_BYTES) until the process ends; calls on
+// one GPU share it, so overlapping calls on one GPU race.  Host code never
+// names the array directly (on the host its name is only a stand-in for the
+// symbol): it uses the device address hipGetSymbolAddress returns, kept per
+// device.
+static __device__ __align__(256) uint8_t scratch[XC_NCC_MODE_SCRATCH_BYTES];
 
 namespace {
 
@@ -222,6 +233,61 @@ int ncc_variant_ok(const xc::NccArgs &a, int variant)
     return XC_OK;
 }
 
+// Same or full mode over a padded-image buffer of `padded_bytes` bytes at
+// the device address `padded` (16-byte aligned, or NULL): validation, then
+// the zero-padded copy and the valid-mode variant on it, both on `stream`.
+// `padded` may be NULL only to ask for the validation of everything else
+// (the caller reports the missing buffer).
+int ncc_mode_run(const uint8_t *image, int width, int height, int pitch_bytes, const uint8_t *tmpl, int t_width,
+                 int t_height, const NccModeGeom &g, uint8_t *padded, size_t padded_bytes, uint32_t *sum_i,
+                 uint32_t *sum_isq, uint32_t *sum_it, float *coef, int variant, void *stream)
+{
+    if (!image || !tmpl || !padded)
+        return XC_ERR_NULL;
+    if (pitch_bytes < width || (int64_t)height * pitch_bytes > ((int64_t)1 << 40))
+        return XC_ERR_SHAPE;
+    if (!aligned(image, 16) || pitch_bytes % 16 != 0 || !aligned(padded, 16))
+        return XC_ERR_ALIGN;
+    if (padded_bytes < g.bytes)
+        return XC_ERR_SHAPE;
+    // the valid-mode computation on the padded image
+    xc::NccArgs a;
+    int st = ncc_validate(padded, g.pw, g.ph, g.ppitch, tmpl, t_width, t_height, sum_i, sum_isq, sum_it, coef, true,
+                          a);
+    if (st != XC_OK)
+        return st;
+    if ((st = ncc_variant_ok(a, variant)) != XC_OK)
+        return st;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if ((st = hip_status(xc::ncc_pad_image(image, width, height, pitch_bytes, padded, g.pw, g.ph, g.ppitch, g.pad_top,
+                                           g.pad_left, s))) != XC_OK)
+        return st;
+    return ncc_dispatch(a, variant, s);
+}
+
+// Device address of `scratch` on the current device, looked up on the first
+// call on each device (ids below 64; higher ids look it up every time), or
+// NULL if the lookup fails.  Thread-safe: concurrent first calls store the
+// same address.
+uint8_t *scratch_ptr()
+{
+    static std::atomic<uint8_t *> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        return nullptr;
+    if (dev < 64) {
+        uint8_t *p = cached[dev].load(std::memory_order_acquire);
+        if (p)
+            return p;
+    }
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+        return nullptr;
+    if (dev < 64)
+        cached[dev].store(static_cast<uint8_t *>(p), std::memory_order_release);
+    return static_cast<uint8_t *>(p);
+}
+
 } // namespace
 
 extern "C" {
@@ -277,6 +343,7 @@ int ncc_u8_mode_workspace(int width, int height, int t_width, int t_height, int 
     return XC_OK;
 }
 
+
 int ncc_u8_run_mode(const uint8_t *image, int width, int height, int pitch_bytes, const uint8_t *tmpl, int t_width,
                     int t_height, int mode, void *workspace, size_t workspace_bytes, uint32_t *sum_i,
                     uint32_t *sum_isq, uint32_t *sum_it, float *coef, int variant, void *stream)
@@ -285,30 +352,32 @@ int ncc_u8_run_mode(const uint8_t *image, int width, int height, int pitch_bytes
         return ncc_u8_run_variant(image, width, height, pitch_bytes, tmpl, t_width, t_height, sum_i, sum_isq, sum_it,
                                   coef, variant, stream);
     NccModeGeom g;
-    int st = ncc_mode_geom(width, height, t_width, t_height, mode, g);
+    const int st = ncc_mode_geom(width, height, t_width, t_height, mode, g);
     if (st != XC_OK)
         return st;
-    if (!image || !tmpl || !workspace)
-        return XC_ERR_NULL;
-    if (pitch_bytes < width || (int64_t)height * pitch_bytes > ((int64_t)1 << 40))
-        return XC_ERR_SHAPE;
-    if (!aligned(image, 16) || pitch_bytes % 16 != 0 || !aligned(workspace, 16))
-        return XC_ERR_ALIGN;
-    if (workspace_bytes < g.bytes)
-        return XC_ERR_SHAPE;
-    // the valid-mode computation on the padded image, which lives in the workspace
-    uint8_t *const padded = static_cast<uint8_t *>(workspace);
-    xc::NccArgs a;
-    st = ncc_validate(padded, g.pw, g.ph, g.ppitch, tmpl, t_width, t_height, sum_i, sum_isq, sum_it, coef, true, a);
+    return ncc_mode_run(image, width, height, pitch_bytes, tmpl, t_width, t_height, g,
+                        static_cast<uint8_t *>(workspace), workspace_bytes, sum_i, sum_isq, sum_it, coef, variant,
+                        stream);
+}
+
+int ncc_u8_run_mode_noalloc(const uint8_t *image, int width, int height, int pitch_bytes, const uint8_t *tmpl,
+                            int t_width, int t_height, int mode, uint32_t *sum_i, uint32_t *sum_isq, uint32_t *sum_it,
+                            float *coef, int variant, void *stream)
+{
+    if (mode == XC_NCC_MODE_VALID)
+        return ncc_u8_run_variant(image, width, height, pitch_bytes, tmpl, t_width, t_height, sum_i, sum_isq, sum_it,
+                                  coef, variant, stream);
+    NccModeGeom g;
+    const int st = ncc_mode_geom(width, height, t_width, t_height, mode, g);
     if (st != XC_OK)
         return st;
-    if ((st = ncc_variant_ok(a, variant)) != XC_OK)
-        return st;
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    if ((st = hip_status(xc::ncc_pad_image(image, width, height, pitch_bytes, padded, g.pw, g.ph, g.ppitch, g.pad_top,
-                                           g.pad_left, s))) != XC_OK)
-        return st;
-    return ncc_dispatch(a, variant, s);
+    if (g.bytes > (size_t)XC_NCC_MODE_SCRATCH_BYTES)
+        return XC_ERR_SCRATCH;
+    uint8_t *const p = scratch_ptr();
+    if (!p)
+        return XC_ERR_HIP;
+    return ncc_mode_run(image, width, height, pitch_bytes, tmpl, t_width, t_height, g, p,
+                        (size_t)XC_NCC_MODE_SCRATCH_BYTES, sum_i, sum_isq, sum_it, coef, variant, stream);
 }
 
 int ncc_u8_run(const uint8_t *image, int width, int height, int pitch_bytes, const uint8_t *tmpl, int t_width,
@@ -380,6 +449,7 @@ const char *xc_status_str(int status)
     case XC_ERR_ALIGN: return "a base pointer or the row pitch is not suitably aligned (16 bytes for images and matrices)";
     case XC_ERR_HIP: return "HIP launch or runtime error (or no device)";
     case XC_ERR_VARIANT: return "unknown variant or algorithm selector";
+    case XC_ERR_SCRATCH: return "the call needs a larger padded image than the library's static device scratch holds (XC_NCC_MODE_SCRATCH_BYTES)";
     default: return "unknown status";
     }
 }

@@ -53,6 +53,7 @@ extern "C" {
 #define XC_ERR_ALIGN (-5)          /* a base pointer or the pitch is not 16-byte aligned        */
 #define XC_ERR_HIP (-6)            /* HIP launch or runtime error (including: no device)        */
 #define XC_ERR_VARIANT (-7)        /* unknown variant / algorithm / output-mode selector        */
+#define XC_ERR_SCRATCH (-8)        /* the call needs more than the static device scratch holds  */
 
 /* Largest template area for which the u32 sums cannot wrap: N * 255^2 < 2^32. */
 #define XC_NCC_MAX_TEMPLATE_PIXELS 66051
@@ -232,6 +233,28 @@ int ncc_u8_run_mode(const uint8_t *image, int width, int height, int pitch_bytes
                     void *workspace, size_t workspace_bytes,
                     uint32_t *sum_i, uint32_t *sum_isq, uint32_t *sum_it, float *coef,
                     int variant, void *stream);
+
+/*
+ * ncc_u8_run_mode_noalloc -- ncc_u8_run_mode for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same arguments without the workspace, the same
+ * outputs.  The zero-padded image of same and full modes goes to a static
+ * device buffer of XC_NCC_MODE_SCRATCH_BYTES (16 MiB) that the library holds
+ * on each GPU it runs on until the process ends; the call allocates nothing
+ * (no hipMalloc, no allocating library routine).  Every call on one GPU
+ * shares that GPU's buffer and leaves its contents behind (the padded copy of
+ * its image; each call overwrites all of the bytes it reads), so calls that
+ * overlap on one GPU -- on different streams, or from several threads without
+ * ordering -- race: serialize them, e.g. on one stream.  Valid mode uses no
+ * buffer.  Errors: as ncc_u8_run_mode, plus XC_ERR_SCRATCH when the padded
+ * image (ncc_u8_mode_workspace's byte count) exceeds XC_NCC_MODE_SCRATCH_BYTES,
+ * and XC_ERR_HIP if the buffer's device address cannot be obtained.
+ */
+#define XC_NCC_MODE_SCRATCH_BYTES 16777216u /* 16 MiB */
+int ncc_u8_run_mode_noalloc(const uint8_t *image, int width, int height, int pitch_bytes,
+                            const uint8_t *tmpl, int t_width, int t_height, int mode,
+                            uint32_t *sum_i, uint32_t *sum_isq, uint32_t *sum_it, float *coef,
+                            int variant, void *stream);
 
 /*
  * xcorr_f32_run -- fp32 full 2D cross-correlation of every (left, right) pair.

@@ -35,7 +35,7 @@ def test_header_constants_match_binding():
 
 
 def test_status_strings():
-    for code in range(0, -8, -1):
+    for code in range(0, -9, -1):
         assert _lib.status_str(code) and _lib.status_str(code) != "unknown status"
     assert _lib.status_str(-99) == "unknown status"
 
