@@ -347,6 +347,35 @@ def bench_xcorr_large(args, torch, lib, inputs):
     return res
 
 
+def bench_xcorr_small(args, torch, lib, inputs):
+    """Groupings of small matrices (rows <= 12, below the block-diagonal
+    kernel's 13): the small-matrix kernel (what the automatic choice runs)
+    against the overlap-wise baseline."""
+    from cross_correlation_amd.inputs import xcorr_case
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream().cuda_stream
+    res = {}
+    for nl, nr, rows, cols in ((64, 64, 8, 8), (1, 512, 4, 4), (16, 16, 12, 12), (4, 4, 6, 200)):
+        c = xcorr_case("small", 8, nl, nr, rows, cols)
+        L = torch.from_numpy(c.left).to(dev)
+        R = torch.from_numpy(c.right).to(dev)
+        out = torch.empty(c.out_shape, dtype=torch.float32, device=dev)
+        flop = 2.0 * nl * nr * (rows * cols) ** 2
+        row = {}
+        for an, algo in (("small", lib.XC_XCORR_SMALL), ("overlap", lib.XC_XCORR_OVERLAP)):
+            def launch():
+                st = lib.xcorr_f32_run(L.data_ptr(), nl, R.data_ptr(), nr, rows, cols, out.data_ptr(), stream=stream,
+                                       algo=algo)
+                if st != 0:
+                    raise RuntimeError(lib.status_str(st))
+            tr = trial_stats(launch, torch, min_ms=40.0, n_trials=3)
+            row[f"{an}_us"] = round(tr["median_ms"] * 1e3, 2)
+            row[f"{an}_gflops"] = round(flop / (tr["median_ms"] * 1e-3) / 1e9, 1)
+        row["speedup"] = round(row["overlap_us"] / row["small_us"], 2)
+        res[f"{nl}x{nr}_of_{rows}x{cols}"] = row
+    return res
+
+
 def bench_xcorr(args, torch, lib, inputs, oracle_mod=None):
     dev = torch.device("cuda:0")
     res = {}
@@ -586,6 +615,7 @@ def main():
         out["xcorr"] = bench_xcorr(args, torch, _lib, inputs, orc)
         if not args.no_ext:
             out["xcorr_large"] = bench_xcorr_large(args, torch, _lib, inputs)
+            out["xcorr_small"] = bench_xcorr_small(args, torch, _lib, inputs)
     if not args.no_peak_probe:
         out["measured_ceilings"] = peak_probes()
         if "ncc_variants" in out:

@@ -418,11 +418,17 @@ int xcorr_f32_run_algo(const float *left, int n_left, const float *right, int n_
     case XC_XCORR_AUTO:
         if (xc::xcorr_blockdiag_supported(a))
             return hip_status(xc::xcorr_launch_blockdiag(a, s));
+        if (xc::xcorr_small_supported(a))
+            return hip_status(xc::xcorr_launch_small(a, s));
         return hip_status(xc::xcorr_launch_overlap(a, s));
     case XC_XCORR_OVERLAP:
         return hip_status(xc::xcorr_launch_overlap(a, s));
     case XC_XCORR_WAVE:
         return hip_status(xc::xcorr_launch_wave(a, s));
+    case XC_XCORR_SMALL:
+        if (!xc::xcorr_small_supported(a))
+            return XC_ERR_SHAPE;
+        return hip_status(xc::xcorr_launch_small(a, s));
     case XC_XCORR_BLOCKDIAG:
         if (!xc::xcorr_blockdiag_supported(a))
             return XC_ERR_SHAPE;

@@ -107,6 +107,9 @@ struct XcorrArgs {
 
 hipError_t xcorr_launch_overlap(const XcorrArgs &a, hipStream_t s);
 hipError_t xcorr_launch_wave(const XcorrArgs &a, hipStream_t s);
+// Matrices with a dimension of at most 16 (rows or cols).
+hipError_t xcorr_launch_small(const XcorrArgs &a, hipStream_t s);
+bool xcorr_small_supported(const XcorrArgs &a);
 hipError_t xcorr_launch_blockdiag(const XcorrArgs &a, hipStream_t s);
 bool xcorr_blockdiag_supported(const XcorrArgs &a);
 

@@ -287,11 +287,19 @@ int xcorr_f32_run(const float *left, int n_left, const float *right, int n_right
  *                        added across the wave in a fixed order (the JPDC
  *                        README's warp-per-overlap variant, for large
  *                        overlaps; no data reuse between shifts)
+ *   XC_XCORR_SMALL       matrices with rows <= 16 or cols <= 16: a thread
+ *                        owns one pair, one shift along the other dimension
+ *                        and 8 shifts along the small one, and keeps two
+ *                        lines (rows, or columns) in registers, each value
+ *                        serving up to 8 products; XC_ERR_SHAPE for larger
+ *                        matrices.  XC_XCORR_AUTO takes BLOCKDIAG from 13
+ *                        rows, this below.
  */
 #define XC_XCORR_AUTO 0
 #define XC_XCORR_OVERLAP 1
 #define XC_XCORR_BLOCKDIAG 2
 #define XC_XCORR_WAVE 3
+#define XC_XCORR_SMALL 4
 int xcorr_f32_run_algo(const float *left, int n_left, const float *right, int n_right,
                        int rows, int cols, float *out, int algo, void *stream);
 

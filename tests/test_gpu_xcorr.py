@@ -254,3 +254,52 @@ def test_xcorr_wave_large_sampled():
     # both within 1e-5 * sum|lr| of the exact value: within twice that of each other
     sab = np.abs(L[0]).sum() * np.abs(R[0]).sum()
     assert np.max(np.abs(got.astype(np.float64) - bd)) <= 2e-5 * sab
+
+
+# Matrices with a dimension of at most 16: rows 1 .. 12 (which the automatic
+# choice gives to this kernel) with narrow and wide rows (the wide ones walk
+# columns and keep the rows in registers), and narrow columns under tall rows.
+SMALL_SHAPES = [(1, 1, 1, 1), (2, 3, 1, 9), (1, 2, 3, 2), (3, 5, 4, 4), (64, 64, 8, 8), (1, 512, 4, 4),
+                (2, 2, 5, 7), (4, 3, 7, 13), (16, 16, 12, 12), (3, 2, 12, 16), (2, 2, 9, 17), (1, 3, 12, 100),
+                (2, 1, 3, 300), (2, 2, 40, 6), (1, 2, 200, 16), (3, 3, 16, 40)]
+
+
+@pytest.mark.parametrize("shape", SMALL_SHAPES, ids=["x".join(map(str, s)) for s in SMALL_SHAPES])
+@pytest.mark.parametrize("algo", [_lib.XC_XCORR_SMALL, _lib.XC_XCORR_AUTO])
+def test_xcorr_small_matrices(shape, algo):
+    nl, nr, rows, cols = shape
+    if algo == _lib.XC_XCORR_AUTO and rows > 12:
+        pytest.skip("the automatic choice takes the block-diagonal kernel from 13 rows")
+    rng = np.random.default_rng(2000 + rows * 37 + cols * 3 + nl + nr)
+    L = f32_uniform(rng, (nl, rows, cols))
+    R = f32_uniform(rng, (nr, rows, cols))
+    _gpu.log(f"xcorr small matrices {shape} algo={algo}")
+    ref, ab = oracle.xcorr_f32(L, R)
+    _gpu.check_xcorr(_gpu.run_xcorr(L, R, algo), ref, ab)
+
+
+def test_xcorr_small_exact_and_orientation():
+    """Small-integer inputs exactly, and delta matrices land on their shift, in
+    both walking directions (rows in registers or columns in registers)."""
+    rng = np.random.default_rng(2100)
+    for rows, cols in ((6, 10), (10, 40)):
+        L = rng.integers(-2, 3, size=(2, rows, cols)).astype(np.float32)
+        R = rng.integers(-2, 3, size=(3, rows, cols)).astype(np.float32)
+        _gpu.log(f"xcorr small exact {rows}x{cols}")
+        ref, _ = oracle.xcorr_f32(L, R)
+        assert np.array_equal(_gpu.run_xcorr(L, R, _lib.XC_XCORR_SMALL).astype(np.float64), ref)
+        for (a, b, c, d) in ((0, 0, rows - 1, cols - 1), (rows - 1, cols - 1, 0, 0), (1, 3, rows - 2, 2)):
+            Ld = np.zeros((1, rows, cols), np.float32)
+            Rd = np.zeros((1, rows, cols), np.float32)
+            Ld[0, a, b] = 1.0
+            Rd[0, c, d] = 1.0
+            got = _gpu.run_xcorr(Ld, Rd, _lib.XC_XCORR_SMALL)
+            expect = np.zeros((2 * rows - 1, 2 * cols - 1), np.float32)
+            expect[a - c + rows - 1, b - d + cols - 1] = 1.0
+            assert np.array_equal(got[0, 0], expect)
+    L = np.zeros((1, 20, 20), np.float32)
+    with pytest.raises(_lib.XcError) as e:
+        from cross_correlation_amd import api
+        import torch
+        api.xcorr_f32(torch.from_numpy(L).cuda(), torch.from_numpy(L).cuda(), algo=_lib.XC_XCORR_SMALL)
+    assert e.value.status == _lib.XC_ERR_SHAPE
