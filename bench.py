@@ -88,6 +88,9 @@ def parse():
     ap.add_argument("--no-peak-probe", action="store_true", help="skip the measured issue-rate ceilings")
     ap.add_argument("--no-ext", action="store_true",
                     help="skip the ncc_ext timings (profiling runs: each kernel then sees one workload)")
+    ap.add_argument("--trial-ms", type=float, default=100.0,
+                    help="minimum length of each timed trial of the headline and the workloads (ms)")
+    ap.add_argument("--trials", type=int, default=5, help="timed trials per workload (the median is reported)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (a known-size kernel that "
                          "calibrates the FETCH_SIZE / WRITE_SIZE counters), then exit")
@@ -189,9 +192,11 @@ def peak_probes():
 
 
 def bench_ncc(args, torch, lib, inputs, variant=0, steps=None, warmup=None, workload="ncc_1920x1080_t64",
-              min_ms=100.0, n_trials=5):
+              min_ms=None, n_trials=None):
     steps = args.steps if steps is None else steps
     warmup = args.warmup if warmup is None else warmup
+    min_ms = args.trial_ms if min_ms is None else min(min_ms, args.trial_ms)
+    n_trials = args.trials if n_trials is None else min(n_trials, args.trials)
     case = inputs.workload(workload)
     dev = torch.device("cuda:0")
     img = torch.from_numpy(case.image).to(dev)
@@ -339,7 +344,7 @@ def bench_xcorr_large(args, torch, lib, inputs):
                 if st != 0:
                     raise RuntimeError(lib.status_str(st))
 
-            tr = trial_stats(launch, torch, min_ms=100.0, n_trials=5 if an == "auto" else 3)
+            tr = trial_stats(launch, torch, min_ms=args.trial_ms, n_trials=min(args.trials, 5 if an == "auto" else 3))
             per = tr["median_ms"]
             res[f"xcorr_1to1_{n}_{an}"] = {"kernel_ms": round(per, 4), "gflops": round(flop / (per * 1e-3) / 1e9, 1),
                                            "frac_of_157.3T": round(flop / (per * 1e-3) / FP32_PEAK, 4),
@@ -368,7 +373,7 @@ def bench_xcorr_small(args, torch, lib, inputs):
                                        algo=algo)
                 if st != 0:
                     raise RuntimeError(lib.status_str(st))
-            tr = trial_stats(launch, torch, min_ms=40.0, n_trials=3)
+            tr = trial_stats(launch, torch, min_ms=min(40.0, args.trial_ms), n_trials=min(3, args.trials))
             row[f"{an}_us"] = round(tr["median_ms"] * 1e3, 2)
             row[f"{an}_gflops"] = round(flop / (tr["median_ms"] * 1e-3) / 1e9, 1)
         row["speedup"] = round(row["overlap_us"] / row["small_us"], 2)
@@ -394,7 +399,7 @@ def bench_xcorr(args, torch, lib, inputs, oracle_mod=None):
                 raise RuntimeError(lib.status_str(st))
 
         wall, _ = timed_loop(launch, args.steps, args.warmup, torch)
-        tr = trial_stats(launch, torch)
+        tr = trial_stats(launch, torch, min_ms=args.trial_ms, n_trials=args.trials)
         per = tr["median_ms"]
         flop = 2.0 * nl * nr * (c.rows * c.cols) ** 2
         res[name] = {

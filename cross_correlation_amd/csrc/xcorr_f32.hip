@@ -872,7 +872,12 @@ __global__ __launch_bounds__(64 * NW) void xcorr_bd_whole_kernel(BdArgs a)
     __syncthreads();
     if (!w.wave_on)
         return;
-    for (int side = w.side_lo; side < w.side_hi; ++side) {
+    // When a wave walks both dx signs, odd waves take them in the other
+    // order, so that the waves of a SIMD do not all reach their reductions
+    // (LDS round trips) at once.
+    const int flip = (w.side_hi - w.side_lo == 2) ? (w.wave & 1) : 0;
+    for (int sd = w.side_lo; sd < w.side_hi; ++sd) {
+        const int side = sd ^ flip;
         const int u_first = side ? 0 : w.c0;
         const int u_end = side ? w.c0 + P : wp;
         const int roff = side ? wp - w.c0 : -w.c0;
