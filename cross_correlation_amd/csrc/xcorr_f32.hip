@@ -319,39 +319,47 @@ __device__ __forceinline__ void bd_compute(const float4 *Lb1, const float4 *Lb2,
 
 // ---------------------------------------------------------------------------
 // Small matrices: one dimension of at most 16 (the "register" dimension, of
-// size m <= M), the other any (the "loop" dimension, of size n).  A thread
-// owns one pair, one shift d along the loop dimension and SP = 8 consecutive
-// shifts s along the register dimension (KC threads cover the 2M - 1 of
-// them), and walks the lines of the loop dimension where both matrices
-// exist: at line i it holds line i + d of the left matrix and line i of the
-// right one in registers (m values each, zero past the matrix) and adds, for
-// each of its shifts, the products left[j + s] * right[j].  Each loaded value
-// serves up to SP products, where the overlap-wise kernel loads two values
-// per product.  Lines are rows (TR = false: the register dimension is cols)
-// or columns (TR = true: it is rows).  Sums are in line order, then element
-// order.  With one value per lane and only a few lines per thread, these
-// launches are latency-bound: splitting the shifts over KC threads puts more
-// waves on the chip (16x16 pairs of 12x12: 9.1 us, against 14.7 with one
-// thread per (pair, d) and 11.8 for the overlap-wise kernel).
+// size m <= M), the other any (the "loop" dimension, of size n).  A group of
+// LC adjacent lanes owns one pair, one shift d along the loop dimension and
+// SP = 8 consecutive shifts s along the register dimension (KC groups cover
+// the 2M - 1 of them); lane lc of the group walks the lines i = i0 + lc,
+// i0 + lc + LC, ... of the loop dimension where both matrices exist: at line
+// i it holds line i + d of the left matrix and line i of the right one in
+// registers (m values each, zero past the matrix) and adds, for each of its
+// shifts, the products left[j + s] * right[j].  Each loaded value serves up
+// to SP products, where the overlap-wise kernel loads two values per
+// product.  Lines are rows (TR = false: the register dimension is cols) or
+// columns (TR = true: it is rows).  A lane sums its lines in order, then the
+// group adds its LC partial sums in a fixed butterfly of cross-lane
+// exchanges, and its first min(LC, SP) lanes store the SP results
+// round-robin.  LC (a power of two up to 64, chosen on the host from the
+// shape alone) spreads long loops over lanes: these launches are
+// latency-bound, and a short chain per lane with more waves on the chip
+// finishes sooner (4x4 pairs of 6x200: 70.4 us with one lane per group,
+// 10.4 with 16; 3x1 of 3x300: 49.7, 4.4 with 64).
 struct SmallArgs {
     XcorrArgs x;
+    int lc_log2;  // LC = 1 << lc_log2 lanes per group
 };
 
 template <int M, bool TR>
 __global__ __launch_bounds__(256) void xcorr_small_kernel(SmallArgs sa)
 {
-    constexpr int SP = 8;                          // register-dimension shifts per thread
-    constexpr int KC = (2 * M - 1 + SP - 1) / SP;  // threads per (pair, d)
+    constexpr int SP = 8;                          // register-dimension shifts per group
+    constexpr int KC = (2 * M - 1 + SP - 1) / SP;  // groups per (pair, d)
     const XcorrArgs &a = sa.x;
     const int rows = a.rows, cols = a.cols;
     const int m = TR ? rows : cols, n = TR ? cols : rows;
     const int nd = 2 * n - 1;
-    const int64_t total = (int64_t)a.n_left * a.n_right * nd * KC;
+    const int lcs = sa.lc_log2, LC = 1 << lcs;
+    const int64_t total = ((int64_t)a.n_left * a.n_right * nd * KC) << lcs;
     const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (t >= total)
+    if (t >= total)  // whole groups only: total is a multiple of LC, LC divides 64
         return;
-    const int kc = (int)(t % KC);
-    const int64_t u = t / KC;
+    const int lc = (int)(t & (LC - 1));
+    const int64_t g = t >> lcs;
+    const int kc = (int)(g % KC);
+    const int64_t u = g / KC;
     const int64_t pair = u / nd;
     const int d = (int)(u - pair * nd) - (n - 1);
     const int l = (int)(pair / a.n_right);
@@ -360,13 +368,13 @@ __global__ __launch_bounds__(256) void xcorr_small_kernel(SmallArgs sa)
     const float *R = a.right + (size_t)r * rows * cols;
     // element q of line i: (row i, col q) or (row q, col i)
     const int qs = TR ? cols : 1, is = TR ? 1 : cols;
-    const int s0 = kc * SP - (M - 1);  // this thread's first shift
+    const int s0 = kc * SP - (M - 1);  // this group's first shift
     float acc[SP];
 #pragma unroll
     for (int k = 0; k < SP; ++k)
         acc[k] = 0.0f;
     const int i0 = max(0, -d), i1 = min(n, n - d);  // lines where both exist
-    for (int i = i0; i < i1; ++i) {
+    for (int i = i0 + lc; i < i1; i += LC) {
         float lv[M], rv[M];
 #pragma unroll
         for (int q = 0; q < M; ++q) {
@@ -383,7 +391,7 @@ __global__ __launch_bounds__(256) void xcorr_small_kernel(SmallArgs sa)
 #pragma unroll
             for (int k = 0; k < SP; ++k) {
                 // left element j + s0 + k (zero outside the line), picked
-                // from registers by this thread's chunk kc
+                // from registers by this group's chunk kc
                 float lq = 0.0f;
 #pragma unroll
                 for (int c = 0; c < KC; ++c) {
@@ -395,12 +403,19 @@ __global__ __launch_bounds__(256) void xcorr_small_kernel(SmallArgs sa)
             }
         }
     }
+    // butterfly over the group's lanes (xor 1, 2, ..., LC / 2): every lane
+    // ends with the same sums, added in the same order
+    for (int off = 1; off < LC; off <<= 1) {
+#pragma unroll
+        for (int k = 0; k < SP; ++k)
+            acc[k] += __shfl_xor(acc[k], off);
+    }
     const int oh = 2 * rows - 1, ow = 2 * cols - 1;
     float *const o = a.out + (size_t)pair * oh * ow;
 #pragma unroll
     for (int k = 0; k < SP; ++k) {
         const int sft = s0 + k;
-        if (sft > -m && sft < m) {
+        if ((k & (LC - 1)) == lc && sft > -m && sft < m) {  // lanes past SP store nothing
             const int dy = TR ? sft : d, dx = TR ? d : sft;
             o[(size_t)(dy + rows - 1) * ow + (dx + cols - 1)] = acc[k];
         }
@@ -429,11 +444,18 @@ hipError_t xcorr_launch_small(const XcorrArgs &a, hipStream_t s)
     bool tr;
     const int M = small_m(a, tr);
     const int n = tr ? a.cols : a.rows;
-    const int64_t total = (int64_t)a.n_left * a.n_right * (2 * n - 1) * ((2 * M - 1 + 7) / 8);
-    const int64_t blocks = (total + 255) / 256;
+    const int64_t groups = (int64_t)a.n_left * a.n_right * (2 * n - 1) * ((2 * M - 1 + 7) / 8);
+    // Lanes per group: double while each lane keeps at least two lines and
+    // the launch stays within 2^19 threads (8 waves per SIMD); a cap of 16
+    // lanes or of 2^18 threads was slower on long loops (1x2 pairs of
+    // 200x16: 47.4 and 23.8 us against 24.0; 1x1 of 12x4000: 187 and 280
+    // against 183)
+    int lcs = 0;
+    while (lcs < 6 && (2 << (lcs + 1)) <= n && (groups << (lcs + 1)) <= (int64_t)1 << 19) ++lcs;
+    const int64_t blocks = ((groups << lcs) + 255) / 256;
     if (M == 0 || blocks > INT32_MAX)
         return hipErrorInvalidValue;
-    const SmallArgs sa{a};
+    const SmallArgs sa{a, lcs};
     const dim3 g((unsigned)blocks), b(256);
     switch (M * 2 + (tr ? 1 : 0)) {
     case 8: hipLaunchKernelGGL((xcorr_small_kernel<4, false>), g, b, 0, s, sa); break;

@@ -261,7 +261,8 @@ def test_xcorr_wave_large_sampled():
 # columns and keep the rows in registers), and narrow columns under tall rows.
 SMALL_SHAPES = [(1, 1, 1, 1), (2, 3, 1, 9), (1, 2, 3, 2), (3, 5, 4, 4), (64, 64, 8, 8), (1, 512, 4, 4),
                 (2, 2, 5, 7), (4, 3, 7, 13), (16, 16, 12, 12), (3, 2, 12, 16), (2, 2, 9, 17), (1, 3, 12, 100),
-                (2, 1, 3, 300), (2, 2, 40, 6), (1, 2, 200, 16), (3, 3, 16, 40)]
+                (2, 1, 3, 300), (2, 2, 40, 6), (1, 2, 200, 16), (3, 3, 16, 40), (4, 4, 6, 200), (3, 1, 3, 300),
+                (1, 1, 2, 1000)]
 
 
 @pytest.mark.parametrize("shape", SMALL_SHAPES, ids=["x".join(map(str, s)) for s in SMALL_SHAPES])
@@ -282,7 +283,7 @@ def test_xcorr_small_exact_and_orientation():
     """Small-integer inputs exactly, and delta matrices land on their shift, in
     both walking directions (rows in registers or columns in registers)."""
     rng = np.random.default_rng(2100)
-    for rows, cols in ((6, 10), (10, 40)):
+    for rows, cols in ((6, 10), (10, 40), (3, 300), (200, 5)):
         L = rng.integers(-2, 3, size=(2, rows, cols)).astype(np.float32)
         R = rng.integers(-2, 3, size=(3, rows, cols)).astype(np.float32)
         _gpu.log(f"xcorr small exact {rows}x{cols}")
