@@ -786,74 +786,101 @@ __global__ __launch_bounds__(64 * NW) void xcorr_bd_chunk_kernel(BdArgs a)
 // (a unit is a block of 4 rows; its float4 at index g + P - 1 holds the 4
 // rows at source column g; zeros in the P - 1 columns before the data and
 // from index cols + P - 1 to W).  Units: nls left slots x nb blocks, then S
-// pair slots x nb blocks.  Staged as two regions of rows, left then right,
-// in one loop (the code is fetched once): region row R (of slots x 4 nb) is
-// row R mod 4nb of the region's slot R / 4nb, i.e. of matrix
-// (first + slot) mod n_mod, and lands in unit R / 4, row R mod 4.  The
-// workgroup's NT threads take a region's items in a flat loop, BK per batch
-// with all of a batch's loads issued before its LDS stores; an item is one
-// row's 4 consecutive columns (one 16-byte load into the 4 columns' float4
-// slots) when cols is a multiple of 4 (every row then starts 16-byte
-// aligned), else one element.  Rows past the matrix and empty slots load from
-// four zeros in device memory, so no value is selected after its load.
+// pair slots x nb blocks; a left slot sl holds matrix l_first + sl (present
+// below n_left), a pair slot the right matrix (r_first + sl) mod n_right
+// (present while the pair exists).  Rows past the matrix and empty slots
+// load from four zeros in device memory, so no value is selected after its
+// load.  When cols is a multiple of 4 (every row then starts 16-byte
+// aligned) an item is one unit's 4 x 4 block at a column group: four 16-byte
+// row loads, transposed in registers into four float4 columns, four 16-byte
+// LDS stores; the workgroup's NT threads take BK items per batch, all loads
+// of a batch issued before its stores (one batch covers the groupings that
+// stage whole).  Otherwise an item is one element of a region row (the left
+// slots' rows, then the pair slots', in one loop): region row R (of slots x
+// 4 nb) is row R mod 4nb of slot R / 4nb and lands in unit R / 4, row R mod 4.
 template <int NT>
 __device__ __forceinline__ void bd_stage_whole(const BdArgs &a, float4 *smem, int W, const BdWho &w,
                                                int64_t npairs)
 {
     constexpr int P = BD_P;
-    constexpr int BK = 4;
-    float *const sf = reinterpret_cast<float *>(smem);
-    const int nb = a.nb, cols = a.x.cols, rows = a.x.rows, rpb = 4 * nb;
-    const bool vec4 = (cols & 3) == 0;  // workgroup-uniform
-    const int per_row = vec4 ? cols >> 2 : cols;
-    const uint32_t m_row = vec4 ? a.m_c4 : a.m_cols;
+    const int nb = a.nb, cols = a.x.cols, rows = a.x.rows;
     const int64_t p0 = (int64_t)w.grp * a.S;
-    const float *const left = a.x.left, *const right = a.x.right;
     const uint32_t mat_elems = (uint32_t)rows * (uint32_t)cols;
-    for (int reg = 0; reg < 2; ++reg) {
-        // left slots: matrices l_first + sl (never wrap), present below
-        // n_left; pair slots: right matrices (r_first + sl) mod n_right,
-        // present while the pair exists
-        const float *const base = reg ? right : left;
-        const int nslots = reg ? a.S : a.nls;
-        const int first = reg ? w.r_first : w.l_first;
-        const uint32_t n_mod = reg ? (uint32_t)a.x.n_right : 0x40000000u;
-        const uint32_t m_mod = reg ? a.m_right : 3u;  // div_m(2^30) = 3
-        const int n_on = reg ? (int)min((int64_t)a.S, npairs - p0) : a.x.n_left - w.l_first;
-        const int unit0 = reg ? a.nls * nb : 0;
-        const int total = nslots * rpb * per_row;
+    const int n_on_l = a.x.n_left - w.l_first;
+    const int n_on_r = (int)min((int64_t)a.S, npairs - p0);
+    // the matrix of slot sl of a region: left slots never wrap (n_mod 2^30)
+    auto matrix = [&](bool rg, int sl) {
+        const uint32_t t = (uint32_t)((rg ? w.r_first : w.l_first) + sl);
+        const uint32_t n_mod = rg ? (uint32_t)a.x.n_right : 0x40000000u;
+        const uint32_t m_mod = rg ? a.m_right : 3u;  // div_m(2^30) = 3
+        const uint32_t mi = t - div_exact(t, n_mod, m_mod) * n_mod;  // t mod n_mod
+        return (rg ? a.x.right : a.x.left) + (uint64_t)mi * mat_elems;
+    };
+    if ((cols & 3) == 0) {  // workgroup-uniform
+        constexpr int BK = 2;
+        const int nc4 = cols >> 2;
+        const int n_lu = a.nls * nb;
+        const int total = (a.nls + a.S) * nb * nc4;
         for (int i0 = threadIdx.x; i0 < total; i0 += BK * NT) {
-            float4 v[BK];
+            float4 v[BK][4];
             int dst[BK];
 #pragma unroll
             for (int k = 0; k < BK; ++k) {
                 const int i = i0 + k * NT;
-                const int R = fast_div(i, m_row);     // region row
-                const int c = i - R * per_row;        // column group (vec4) or column
-                const int sl = fast_div(R, a.m_rpb);  // slot
-                const int rr = R - sl * rpb;          // row within the matrix
-                const uint32_t t = (uint32_t)(first + sl);
-                const uint32_t mi = t - div_exact(t, n_mod, m_mod) * n_mod;  // t mod n_mod
-                const bool ok = i < total && rr < rows && sl < n_on;
-                const int cc = vec4 ? 4 * c : c;
-                const float *src = base + ((uint64_t)mi * mat_elems + (uint32_t)(rr * cols + cc));
-                const float *zs = bd_zero4;
-                if (vec4)
-                    v[k] = *reinterpret_cast<const float4 *>(ok ? src : zs);
-                else
-                    v[k].x = *(ok ? src : zs);
-                dst[k] = i < total ? (((unit0 + (R >> 2)) * W + (P - 1) + cc) * 4 + (R & 3)) : -1;
+                const int U = fast_div(i, a.m_c4);  // unit
+                const int cg = i - U * nc4;         // column group
+                const bool rg = U >= n_lu;          // right region
+                const int Ur = rg ? U - n_lu : U;
+                const int sl = fast_div(Ur, a.m_nb);  // slot
+                const int blk = Ur - sl * nb;
+                const bool on = i < total && sl < (rg ? n_on_r : n_on_l);
+                const float *src = matrix(rg, sl) + (uint32_t)(4 * blk * cols + 4 * cg);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const bool ok = on && 4 * blk + j < rows;
+                    v[k][j] = *reinterpret_cast<const float4 *>(ok ? src + j * cols : bd_zero4);
+                }
+                dst[k] = i < total ? U * W + (P - 1) + 4 * cg : -1;
             }
 #pragma unroll
             for (int k = 0; k < BK; ++k)
                 if (dst[k] >= 0) {
-                    sf[dst[k]] = v[k].x;
-                    if (vec4) {
-                        sf[dst[k] + 4] = v[k].y;
-                        sf[dst[k] + 8] = v[k].z;
-                        sf[dst[k] + 12] = v[k].w;
-                    }
+                    smem[dst[k]] = make_float4(v[k][0].x, v[k][1].x, v[k][2].x, v[k][3].x);
+                    smem[dst[k] + 1] = make_float4(v[k][0].y, v[k][1].y, v[k][2].y, v[k][3].y);
+                    smem[dst[k] + 2] = make_float4(v[k][0].z, v[k][1].z, v[k][2].z, v[k][3].z);
+                    smem[dst[k] + 3] = make_float4(v[k][0].w, v[k][1].w, v[k][2].w, v[k][3].w);
                 }
+        }
+    } else {
+        constexpr int BK = 4;
+        float *const sf = reinterpret_cast<float *>(smem);
+        const int rpb = 4 * nb;
+        for (int reg = 0; reg < 2; ++reg) {
+            const bool rg = reg != 0;
+            const int nslots = rg ? a.S : a.nls;
+            const int n_on = rg ? n_on_r : n_on_l;
+            const int unit0 = rg ? a.nls * nb : 0;
+            const int total = nslots * rpb * cols;
+            for (int i0 = threadIdx.x; i0 < total; i0 += BK * NT) {
+                float v[BK];
+                int dst[BK];
+#pragma unroll
+                for (int k = 0; k < BK; ++k) {
+                    const int i = i0 + k * NT;
+                    const int R = fast_div(i, a.m_cols);  // region row
+                    const int c = i - R * cols;           // column
+                    const int sl = fast_div(R, a.m_rpb);  // slot
+                    const int rr = R - sl * rpb;          // row within the matrix
+                    const bool ok = i < total && rr < rows && sl < n_on;
+                    const float *src = matrix(rg, sl) + (uint32_t)(rr * cols + c);
+                    v[k] = *(ok ? src : bd_zero4);
+                    dst[k] = i < total ? (((unit0 + (R >> 2)) * W + (P - 1) + c) * 4 + (R & 3)) : -1;
+                }
+#pragma unroll
+                for (int k = 0; k < BK; ++k)
+                    if (dst[k] >= 0)
+                        sf[dst[k]] = v[k];
+            }
         }
     }
     // zero halos: columns [0, P - 1) and [cols + P - 1, W) of every unit
