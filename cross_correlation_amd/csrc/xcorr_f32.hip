@@ -851,6 +851,19 @@ __device__ __forceinline__ void bd_stage_whole(const BdArgs &a, float4 *smem, in
                     smem[dst[k] + 3] = make_float4(v[k][0].w, v[k][1].w, v[k][2].w, v[k][3].w);
                 }
         }
+        // zero halos, one thread per unit: its P - 1 columns before the data
+        // and the W - cols - P + 1 after it
+        const float4 z4 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        const int nhr = W - cols - (P - 1);
+        for (int i = threadIdx.x; i < (a.nls + a.S) * nb; i += NT) {
+            float4 *const u = smem + i * W;
+#pragma unroll
+            for (int h = 0; h < P - 1; ++h)
+                u[h] = z4;
+            for (int h = 0; h < nhr; ++h)
+                u[cols + P - 1 + h] = z4;
+        }
+        return;
     } else {
         constexpr int BK = 4;
         float *const sf = reinterpret_cast<float *>(smem);
