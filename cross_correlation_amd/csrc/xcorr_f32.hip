@@ -596,11 +596,15 @@ __device__ __forceinline__ void bd_write_partials(const BdArgs &a, const BdWho &
 }
 
 // bd_sum_store: the outputs of one side from the wave's partial area, once
-// its writes are visible.  Lane (slot, r, p), p fastest (4 lanes store 16
+// its writes are visible (PAIRS: two outputs per lane per pass, their LDS
+// reads issued together -- the whole-staging kernels, whose reduction is a
+// larger share of the launch; the chunked kernel keeps one, as the pairs
+// cost it registers).  Lane (slot, r, p), p fastest (4 lanes store 16
 // contiguous bytes), sums its column of block partials over two
 // wave-uniform ranges: blocks [0, split) for output row 4*delta + r and,
 // wrapped, [split, nb) for row 4*delta + r - 4*nb (plus the wrap lane's
 // block-2 sums).
+template <bool PAIRS>
 __device__ __forceinline__ void bd_sum_store(const BdArgs &a, const BdWho &w, int side, const float *wred)
 {
     constexpr int P = BD_P;
@@ -611,32 +615,94 @@ __device__ __forceinline__ void bd_sum_store(const BdArgs &a, const BdWho &w, in
     const int oh = 2 * rows - 1, ow = 2 * cols - 1;
     const int64_t npairs = (int64_t)a.x.n_left * a.x.n_right;
     const int split = nb - w.delta;
-    for (int o = w.lane; o < S * NV; o += 64) {
-        const int sl = o / NV;
-        const int q = o - sl * NV;
-        const int p = q % P;
-        const int r = q / P;
-        const int64_t pair = (int64_t)w.grp * S + sl;
-        const int c = w.c0 + p;
-        const int dx = side ? c - a.wp : c;
-        const float *col = wred + (r * P + p) * RS + sl * nb;
-        const float s_un = bd_col_sum(col, 0, split);
-        float s_wr = bd_col_sum(col, split, nb);
-        if (r >= 1)
-            s_wr += wred[4 * P * RS + (sl * 3 + (r - 1)) * P + p];
-        if (pair < npairs && dx > -cols && dx < cols) {
-            const int dy0 = 4 * w.delta + r, dy1 = dy0 - h4;
-            float *const outp = a.x.out + (size_t)pair * oh * ow + (dx + cols - 1);
-            if (dy0 < rows)
-                outp[(size_t)(dy0 + rows - 1) * ow] = s_un;
-            if (dy1 > -rows)
-                outp[(size_t)(dy1 + rows - 1) * ow] = s_wr;
+    if constexpr (PAIRS) {
+        // two outputs per lane per pass (o and o + 64), their LDS reads together
+        for (int o0 = w.lane; o0 < S * NV; o0 += 128) {
+            const bool has1 = o0 + 64 < S * NV;
+            int sl[2], r[2], p[2];
+            const float *col[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int o = h && has1 ? o0 + 64 : o0;
+                sl[h] = o / NV;
+                const int q = o - sl[h] * NV;
+                p[h] = q % P;
+                r[h] = q / P;
+                col[h] = wred + (r[h] * P + p[h]) * RS + sl[h] * nb;
+            }
+            float un[2][4] = {}, wr[2][4] = {};
+            int b = 0;
+            for (; b + 4 <= split; b += 4)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int k = 0; k < 4; ++k)
+                        un[h][k] += col[h][b + k];
+            for (; b < split; ++b)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    un[h][0] += col[h][b];
+            b = split;
+            for (; b + 4 <= nb; b += 4)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int k = 0; k < 4; ++k)
+                        wr[h][k] += col[h][b + k];
+            for (; b < nb; ++b)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    wr[h][0] += col[h][b];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                if (h && !has1)
+                    break;
+                const float s_un = (un[h][0] + un[h][1]) + (un[h][2] + un[h][3]);
+                float s_wr = (wr[h][0] + wr[h][1]) + (wr[h][2] + wr[h][3]);
+                if (r[h] >= 1)
+                    s_wr += wred[4 * P * RS + (sl[h] * 3 + (r[h] - 1)) * P + p[h]];
+                const int64_t pair = (int64_t)w.grp * S + sl[h];
+                const int c = w.c0 + p[h];
+                const int dx = side ? c - a.wp : c;
+                if (pair < npairs && dx > -cols && dx < cols) {
+                    const int dy0 = 4 * w.delta + r[h], dy1 = dy0 - h4;
+                    float *const outp = a.x.out + (size_t)pair * oh * ow + (dx + cols - 1);
+                    if (dy0 < rows)
+                        outp[(size_t)(dy0 + rows - 1) * ow] = s_un;
+                    if (dy1 > -rows)
+                        outp[(size_t)(dy1 + rows - 1) * ow] = s_wr;
+                }
+            }
+        }
+    } else {
+        for (int o = w.lane; o < S * NV; o += 64) {
+            const int sl = o / NV;
+            const int q = o - sl * NV;
+            const int p = q % P;
+            const int r = q / P;
+            const int64_t pair = (int64_t)w.grp * S + sl;
+            const int c = w.c0 + p;
+            const int dx = side ? c - a.wp : c;
+            const float *col = wred + (r * P + p) * RS + sl * nb;
+            const float s_un = bd_col_sum(col, 0, split);
+            float s_wr = bd_col_sum(col, split, nb);
+            if (r >= 1)
+                s_wr += wred[4 * P * RS + (sl * 3 + (r - 1)) * P + p];
+            if (pair < npairs && dx > -cols && dx < cols) {
+                const int dy0 = 4 * w.delta + r, dy1 = dy0 - h4;
+                float *const outp = a.x.out + (size_t)pair * oh * ow + (dx + cols - 1);
+                if (dy0 < rows)
+                    outp[(size_t)(dy0 + rows - 1) * ow] = s_un;
+                if (dy1 > -rows)
+                    outp[(size_t)(dy1 + rows - 1) * ow] = s_wr;
+            }
         }
     }
 }
 
 // One side reduced within the wave: each wave uses only its own LDS area,
 // so a wave-level barrier suffices.
+template <bool PAIRS = false>
 __device__ __forceinline__ void bd_reduce_store(const BdArgs &a, const BdWho &w, int side, float *wred,
                                                 const float (&acc1)[4][BD_P], const float (&acc2)[3][BD_P])
 {
@@ -644,7 +710,7 @@ __device__ __forceinline__ void bd_reduce_store(const BdArgs &a, const BdWho &w,
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    bd_sum_store(a, w, side, wred);
+    bd_sum_store<PAIRS>(a, w, side, wred);
     // the next side's writes come after these reads in every lane's program
     // order and LDS serves one wave in order
     __builtin_amdgcn_wave_barrier();
@@ -956,7 +1022,7 @@ __global__ __launch_bounds__(64 * NW) void xcorr_bd_whole_kernel(BdArgs a)
         bd_compute<16>(Ls + (w.ls * nb + w.kb1) * W + (P - 1) + u_first,
                        Ls + (w.ls * nb + w.kb2) * W + (P - 1) + u_first,
                        Rs + (w.s * nb + w.b) * W + u_first + roff, u_end - u_first, acc1, acc2);
-        bd_reduce_store(a, w, side, wred, acc1, acc2);
+        bd_reduce_store<true>(a, w, side, wred, acc1, acc2);
     }
 }
 
