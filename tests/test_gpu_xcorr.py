@@ -67,6 +67,10 @@ def test_xcorr_edge_shapes(shape, algo):
                                    (2, 3, 100, 70), (3, 5, 64, 64), (6, 6, 40, 24), (16, 16, 16, 16),
                                    # whole staging, every workgroup resident at once
                                    (32, 32, 32, 32),
+                                   # whole staging of 4 x 4 blocks (rows a multiple of 4 columns
+                                   # wide) with a ragged last row block, in both modes: one dx
+                                   # sign per half of the workgroup (up to 8 blocks) and both
+                                   (8, 16, 30, 32), (5, 9, 29, 36), (1, 64, 61, 64), (2, 40, 18, 44),
                                    # more than 64 row blocks: passes of 64 blocks; 65 blocks
                                    # (the left window wraps onto itself), odd rows, 2-3 passes,
                                    # several pairs, wide rows
