@@ -336,7 +336,7 @@ __device__ __forceinline__ void bd_compute(const float4 *Lb1, const float4 *Lb2,
 // shape alone) spreads long loops over lanes: these launches are
 // latency-bound, and a short chain per lane with more waves on the chip
 // finishes sooner (4x4 pairs of 6x200: 70.4 us with one lane per group,
-// 10.4 with 16; 3x1 of 3x300: 49.7, 4.4 with 64).
+// 10.4 with 32; 3x1 of 3x300: 49.7, 4.4 with 64).
 struct SmallArgs {
     XcorrArgs x;
     int lc_log2;  // LC = 1 << lc_log2 lanes per group
