@@ -96,7 +96,13 @@ struct MfPlan {
 // (compile-time in the kernels, so consecutive rows are immediate offsets of
 // one address)
 __host__ __device__ constexpr int mf_sw(int mw, int nkb) { return 16 * mw + 16 * nkb + 4; }
-__host__ __device__ constexpr int mf_tsb(int nkb) { return 64 * nkb + 16; }
+// Template rows: 64-byte blocks plus 16 bytes of padding, or 32 for the
+// 256-column tiles of one block, whose 16-byte B-fragment reads (lane m at row
+// 15 - m) then meet no LDS bank conflicts: SQ_LDS_BANK_CONFLICT of the 1080p /
+// 64x64 launch 707,584 -> 60,416 cycles (a 48-byte pad conflicts as 16 does;
+// the 128-column tiles keep 16, as 32 would push a 64x64 template out of one
+// row chunk of their 40 KiB)
+__host__ __device__ constexpr int mf_tsb(int mw, int nkb) { return 64 * nkb + (mw == 4 && nkb == 1 ? 32 : 16); }
 
 __host__ __device__ inline MfPlan mf_plan(int mw, int t_width, int hc, bool one_chunk, bool win)
 {
@@ -104,7 +110,7 @@ __host__ __device__ inline MfPlan mf_plan(int mw, int t_width, int hc, bool one_
     p.nkb = (t_width + 63) / 64;
     p.hc = hc;
     p.sw = mf_sw(mw, p.nkb);
-    p.tsb = mf_tsb(p.nkb);
+    p.tsb = mf_tsb(mw, p.nkb);
     p.trows = hc + 2 * MF_TY - 1;
     p.nwd = 16 * mw + (t_width + 2) / 4;  // words holding columns 0 .. 64 mw - 1 + t_width - 1
     // each row's prefix over the words (in two halves when MW = 4), or with
@@ -239,7 +245,7 @@ template <int MW, int NKB>
 __device__ __forceinline__ void mf_walk_chunk(const uint32_t *img, const uint8_t *tpl, int hcur, int wave,
                                               mf_v4i (&at)[4])
 {
-    constexpr int sw = mf_sw(MW, NKB), tsb = mf_tsb(NKB);
+    constexpr int sw = mf_sw(MW, NKB), tsb = mf_tsb(MW, NKB);
     const int lane = threadIdx.x & 63;
     const int m = lane & 15, g = lane >> 4;
     // A: output column x0 + 64*wave + 4m + t reads image words from 16*wave + m
