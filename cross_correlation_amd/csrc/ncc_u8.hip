@@ -299,13 +299,17 @@ __global__ __launch_bounds__(64 * WV * KS) void ncc_u8_ilp_kernel(NccArgs a)
 // Ablation kernels: one output per thread, a 64 x 4 tile per workgroup, the
 // image tile in LDS.  DOT4 selects packed-byte dot products; otherwise the
 // bytes are multiplied and added one at a time.  Each thread runs one
-// dependent chain per sum, as the page's baseline kernels do.
-template <bool DOT4, bool WORD_ROWS>
-__global__ __launch_bounds__(256) void ncc_u8_c1_kernel(NccArgs a)
+// dependent chain per sum, as the page's baseline kernels do.  With KS > 1
+// (small grids only, the launcher's choice) KS waves share each output row,
+// each taking a slice of every template chunk's rows; the slices' partial
+// sums are added through LDS before the epilogue.
+template <bool DOT4, bool WORD_ROWS, int KS>
+__global__ __launch_bounds__(256 * KS) void ncc_u8_c1_kernel(NccArgs a)
 {
     extern __shared__ uint32_t lds[];
     const int tx = threadIdx.x & 63;
-    const int ty = threadIdx.x >> 6;
+    const int ty = (threadIdx.x >> 6) & 3;  // output row of the tile
+    const int ks = threadIdx.x >> 8;        // template-row slice of this wave
     const int x0 = blockIdx.x * 64;
     const int y0 = blockIdx.y * 4;
     const int nw = (a.t_width + 3) >> 2;  // packed words per template row
@@ -329,14 +333,14 @@ __global__ __launch_bounds__(256) void ncc_u8_c1_kernel(NccArgs a)
                 // rows that are not whole words: gather the chunk's template
                 // words once into LDS, after the image tile
                 uint32_t *tl = lds + (4 + a.hc - 1) * stride;
-                for (int t = threadIdx.x; t < hc * cw; t += 256) {
+                for (int t = threadIdx.x; t < hc * cw; t += blockDim.x) {
                     const int r = t / cw;
                     const int c = t - r * cw;
                     tl[r * a.t_stride + c] = tmpl_word(a.tmpl, a.t_width, false, jc + r, ic + c);
                 }
             }
             __syncthreads();
-            for (int j = 0; j < hc; ++j) {
+            for (int j = hc * ks / KS; j < hc * (ks + 1) / KS; ++j) {
                 const uint32_t *rp = lds + (ty + j) * stride + (tx >> 2);
                 const uint8_t *trow = a.tmpl + (size_t)(jc + j) * a.t_width;
                 auto mac = [&](uint32_t i4, uint32_t t4) {
@@ -371,6 +375,25 @@ __global__ __launch_bounds__(256) void ncc_u8_c1_kernel(NccArgs a)
                         mac(shift_bytes(rp[cw_main + 1], rp[cw_main], sh) & tm, tw[cw_main]);
                 }
             }
+        }
+    }
+    if (KS > 1) {
+        // the slices' partial sums, added through LDS by the first slice's waves
+        __syncthreads();
+        uint32_t *xb = lds + (size_t)(threadIdx.x & 255);
+        if (ks > 0) {
+            xb[((ks - 1) * 3 + 0) * 256] = si;
+            xb[((ks - 1) * 3 + 1) * 256] = sq;
+            xb[((ks - 1) * 3 + 2) * 256] = st;
+        }
+        __syncthreads();
+        if (ks > 0)
+            return;
+#pragma unroll
+        for (int o = 0; o < KS - 1; ++o) {
+            si += xb[(o * 3 + 0) * 256];
+            sq += xb[(o * 3 + 1) * 256];
+            st += xb[(o * 3 + 2) * 256];
         }
     }
     const int y = y0 + ty;
@@ -721,15 +744,40 @@ hipError_t ncc_launch_c1(NccArgs a, bool dot4, hipStream_t s)
     if (hc > a.t_height) hc = a.t_height;
     a.hc = hc;
     dim3 grid((a.out_w + 63) / 64, (a.out_h + 3) / 4);
-    const size_t lds = ((size_t)(4 + hc - 1) * a.lds_stride + (size_t)hc * a.t_stride) * 4;
-    if (dot4 && word_rows)
-        hipLaunchKernelGGL((ncc_u8_c1_kernel<true, true>), grid, dim3(256), lds, s, a);
-    else if (dot4)
-        hipLaunchKernelGGL((ncc_u8_c1_kernel<true, false>), grid, dim3(256), lds, s, a);
-    else if (word_rows)
-        hipLaunchKernelGGL((ncc_u8_c1_kernel<false, true>), grid, dim3(256), lds, s, a);
-    else
-        hipLaunchKernelGGL((ncc_u8_c1_kernel<false, false>), grid, dim3(256), lds, s, a);
+    size_t lds = ((size_t)(4 + hc - 1) * a.lds_stride + (size_t)hc * a.t_stride) * 4;
+    // The dot4 form splits the template rows over KS = 2 or 4 waves per
+    // output row when the grid would otherwise leave the SIMDs with about
+    // one wave each (a long dependent chain per lane, its LDS and scalar
+    // loads exposed): the most waves that stay within 4 per SIMD.
+    // 256x256 with 16x16: 7.7 -> 5.3 us at KS = 4; 400x300 with 12x12:
+    // 6.3 -> 5.6 at KS = 2; grids of over 1,000 workgroups (640x480 with
+    // 8x8: 6.7 against 7.8 at KS = 2) keep KS = 1, and the scalar form
+    // always does.
+    const int64_t wgs = (int64_t)grid.x * grid.y, slots = 4 * (int64_t)device_cu_count();
+    int ks = 1;
+    if (dot4 && a.t_height >= 2)
+        ks = wgs * 4 <= slots && a.t_height >= 4 ? 4 : wgs * 2 <= slots ? 2 : 1;
+    if (ks > 1 && lds < (size_t)3 * (ks - 1) * 256 * 4)
+        lds = (size_t)3 * (ks - 1) * 256 * 4;  // the slices' partial sums
+    if (dot4 && word_rows) {
+        if (ks == 4)
+            hipLaunchKernelGGL((ncc_u8_c1_kernel<true, true, 4>), grid, dim3(1024), lds, s, a);
+        else if (ks == 2)
+            hipLaunchKernelGGL((ncc_u8_c1_kernel<true, true, 2>), grid, dim3(512), lds, s, a);
+        else
+            hipLaunchKernelGGL((ncc_u8_c1_kernel<true, true, 1>), grid, dim3(256), lds, s, a);
+    } else if (dot4) {
+        if (ks == 4)
+            hipLaunchKernelGGL((ncc_u8_c1_kernel<true, false, 4>), grid, dim3(1024), lds, s, a);
+        else if (ks == 2)
+            hipLaunchKernelGGL((ncc_u8_c1_kernel<true, false, 2>), grid, dim3(512), lds, s, a);
+        else
+            hipLaunchKernelGGL((ncc_u8_c1_kernel<true, false, 1>), grid, dim3(256), lds, s, a);
+    } else if (word_rows) {
+        hipLaunchKernelGGL((ncc_u8_c1_kernel<false, true, 1>), grid, dim3(256), lds, s, a);
+    } else {
+        hipLaunchKernelGGL((ncc_u8_c1_kernel<false, false, 1>), grid, dim3(256), lds, s, a);
+    }
     return hipGetLastError();
 }
 

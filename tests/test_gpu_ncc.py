@@ -351,3 +351,19 @@ def test_ncc_ilp_tail_tiles(out_w, out_h, t):
     res = _gpu.run_ncc(case, _lib.XC_NCC_DOT4_ILP)
     _gpu.check_ncc(case, res)
     assert res["coef"][case.cut] == np.float32(1.0)
+
+
+# The one-output-per-thread dot4 kernel splits the template rows over 4 or 2
+# waves per output row on grids of at most one or two workgroups per SIMD
+# (256x256 with 16x16: 244 workgroups, 4 waves; 400x300 with 12x12: 511, 2),
+# a template row each at least; widths that are not a multiple of 4 take the
+# gathered-word form; a 700-row template comes in two row chunks.
+@pytest.mark.gpu
+@pytest.mark.parametrize("h,w,th,tw", [(256, 256, 16, 16), (300, 400, 12, 12), (300, 300, 10, 10),
+                                       (64, 200, 3, 8), (64, 200, 2, 5), (800, 200, 700, 8), (70, 70, 65, 6)])
+def test_ncc_c1_template_row_slices(h, w, th, tw):
+    case = ncc_case("c1ks", 91 + h + th, h, w, th, tw, cut=True)
+    _gpu.log(f"ncc dot4 c1 row slices: {h}x{w} t{th}x{tw}")
+    res = _gpu.run_ncc(case, _lib.XC_NCC_DOT4_C1)
+    _gpu.check_ncc(case, res)
+    assert res["coef"][case.cut] == np.float32(1.0)
