@@ -166,6 +166,9 @@ def test_ncc_auto_variant_choice():
             (256, 256, 16, 16, C1),     # small image, aligned template
             (640, 480, 8, 8, C1),
             (640, 480, 16, 16, M),      # one-per-thread grid x words over 192 per CU
+            (256, 256, 24, 24, C1),     # 144 words, grid x words within 180 per CU
+            (300, 300, 24, 24, M),      # 144 words over 180 per CU
+            (256, 256, 32, 32, M),      # 256 words
             (384, 384, 6, 6, C1),       # unaligned, 12 words
             (400, 300, 10, 10, M),      # unaligned, 30 words
             (64, 64, 64, 64, M),        # one output, 4096 pixels
