@@ -167,11 +167,14 @@ int xcorr_validate(const float *left, int n_left, const float *right, int n_righ
 // Since the one-per-thread kernel splits the template rows over several
 // waves on small grids, it is taken first there (ahead of the matrix cores'
 // template-size rule) for word-aligned templates of up to 200 words while
-// its grid times the words stays within about 180 per CU, where it beats
-// the matrix cores (one-per-thread / matrix cores, us: 256x256 with 20x20
+// its grid times the words stays within about 180 per CU (145 when the grid
+// holds more workgroups than CUs, so the rows split over two waves, not
+// four), where it beats the matrix cores (one-per-thread / matrix cores,
+// us: 256x256 with 20x20
 // 6.1 / 8.5, 24x24 7.0 / 8.7, 28x28 8.1 / 8.9; 256x192 with 24x24 6.8 /
 // 8.7; 300x300 with 20x20 7.8 / 8.6; 320x240 with 20x20 7.7 / 8.6), and
-// not beyond (300x300 with 24x24 9.5 / 8.9, 400x400 with 20x20 11.0 /
+// not beyond (320x240 with 24x24 9.4 / 8.7, 300x300 with 24x24 9.5 / 8.9,
+// 400x400 with 20x20 11.0 /
 // 8.8, 512x256 with 24x24 9.9 / 8.8, 256x256 with 40x40 12.2 / 9.9).
 int ncc_auto_variant(const xc::NccArgs &a)
 {
@@ -183,7 +186,7 @@ int ncc_auto_variant(const xc::NccArgs &a)
     const int64_t words = (int64_t)((a.t_width + 3) / 4) * a.t_height;
     const int64_t n_c1 = (int64_t)((a.out_w + 63) / 64) * ((a.out_h + 3) / 4);
     const bool whole = a.t_width % 4 == 0;
-    if (n_ilp < cus && whole && words <= 200 && n_c1 * words <= 180 * cus)
+    if (n_ilp < cus && whole && words <= 200 && n_c1 * words <= (n_c1 <= cus ? 180 : 145) * cus)
         return XC_NCC_DOT4_C1;
     if ((npix >= 512 || (npix >= 96 && nout >= 400000) || nout >= 1000000) && mfma_ok)
         return XC_NCC_MFMA;
