@@ -1278,9 +1278,11 @@ static hipError_t launch_whole(BdArgs b, hipStream_t s)
     const int dpw = b.wg_sides ? NW / 2 : NW;  // diagonals per workgroup
     b.n_dgroups = (b.nb + dpw - 1) / dpw;
     bd_set_magic(b);
-    const unsigned blocks = (unsigned)((int64_t)b.n_groups * b.n_xtiles * b.n_dgroups * b.n_sides);
+    const int64_t blocks = (int64_t)b.n_groups * b.n_xtiles * b.n_dgroups * b.n_sides;
+    if (blocks > INT32_MAX)  // the kernels number workgroups with 32-bit signed ids
+        return hipErrorInvalidConfiguration;
     const size_t lds = bd_whole_lds(b, NW);
-    hipLaunchKernelGGL((xcorr_bd_whole_kernel<NW>), dim3(blocks), dim3(64 * NW), lds, s, b);
+    hipLaunchKernelGGL((xcorr_bd_whole_kernel<NW>), dim3((unsigned)blocks), dim3(64 * NW), lds, s, b);
     return hipGetLastError();
 }
 
@@ -1293,9 +1295,11 @@ static hipError_t launch_chunk(BdArgs b, hipStream_t s)
     if (e != hipSuccess) return e;
     b.n_dgroups = (b.nb + NW - 1) / NW;
     bd_set_magic(b);
-    const unsigned blocks = (unsigned)((int64_t)b.n_groups * b.n_xtiles * b.n_dgroups * b.n_sides);
+    const int64_t blocks = (int64_t)b.n_groups * b.n_xtiles * b.n_dgroups * b.n_sides;
+    if (blocks > INT32_MAX)  // the kernels number workgroups with 32-bit signed ids
+        return hipErrorInvalidConfiguration;
     const size_t lds = bd_chunk_lds<NW, J>(b);
-    hipLaunchKernelGGL((xcorr_bd_chunk_kernel<NW, J>), dim3(blocks), dim3(64 * NW), lds, s, b);
+    hipLaunchKernelGGL((xcorr_bd_chunk_kernel<NW, J>), dim3((unsigned)blocks), dim3(64 * NW), lds, s, b);
     return hipGetLastError();
 }
 
@@ -1318,9 +1322,11 @@ static hipError_t launch_big(BdArgs b, hipStream_t s)
     b.n_dgroups = (b.nb + NW - 1) / NW;
     const int64_t per = (int64_t)b.n_groups * b.n_xtiles * b.n_dgroups;
     b.n_sides = per >= 1024 ? 1 : 2;
-    const unsigned blocks = (unsigned)(per * b.n_sides);
+    const int64_t blocks = per * b.n_sides;
+    if (blocks > INT32_MAX)
+        return hipErrorInvalidConfiguration;
     const size_t lds = bd_big_lds<NW, J>();
-    hipLaunchKernelGGL((xcorr_bd_big_kernel<NW, J>), dim3(blocks), dim3(64 * NW), lds, s, b);
+    hipLaunchKernelGGL((xcorr_bd_big_kernel<NW, J>), dim3((unsigned)blocks), dim3(64 * NW), lds, s, b);
     return hipGetLastError();
 }
 

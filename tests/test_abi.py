@@ -177,4 +177,7 @@ def test_ncc_auto_variant_choice():
         assert st == 0 and v == expect, (w, h, tw, th, v)
     assert _lib.ncc_u8_auto_variant(10, 10, 20, 3)[0] == _lib.XC_ERR_SHAPE
     assert _lib.ncc_u8_auto_variant(600, 600, 300, 300)[0] == _lib.XC_ERR_OVERFLOW
+    # the output-count limit, 2^31 - 1 windows: 2045 x 1,050,114 passes, one more row does not
+    assert _lib.ncc_u8_auto_variant(2048, 1050117, 4, 4)[0] == 0
+    assert _lib.ncc_u8_auto_variant(2048, 1050118, 4, 4)[0] == _lib.XC_ERR_OVERFLOW
     assert _lib.load().ncc_u8_auto_variant(64, 64, 8, 8, None) == _lib.XC_ERR_NULL
