@@ -173,14 +173,12 @@ __device__ __forceinline__ void peak_commit_wg(unsigned long long *peak, unsigne
 // their cost.  The reciprocal square root comes from the hardware estimate
 // (relative error at most 2^-23: 2^29 ulp of fp64) and one Newton step
 // (quadratic convergence: relative error below 2^-45), so c = num * y is
-// within |c| * 2^-45 of the IEEE quotient (itself within |c| * 2^-52 of the
-// real one).  Both round to the same fp32 value unless an fp32 rounding
-// boundary lies between them; those are the midpoints half an fp32 ulp either
-// side of f = fp32(c), or a quarter ulp below a power of two.  When c is
-// within |c| * 2^-42 of either distance (a few windows in a million) the IEEE
-// expression is evaluated instead.  |c| >= 2^-50 when num != 0 (num is a
-// nonzero integer, p < 2^100), so f is a normal number and its ulp is the
-// power of two read from its exponent field.
+// within |c| * 2^-44 of the IEEE quotient d (itself within |c| * 2^-52 of the
+// real one).  With m = |c| * 2^-42, c - m <= d <= c + m even after rounding
+// both ends to fp64, and rounding to fp32 is monotonic, so when both ends
+// round to the same fp32 value d does too.  They differ only when an fp32
+// rounding boundary lies within about |c| * 2^-42 of c (a few windows in a
+// million); the IEEE expression is evaluated then.  c = 0 gives m = 0.
 __device__ __forceinline__ float ncc_coef_f32(double num, double p)
 {
     double y = __builtin_amdgcn_rsq(p);
@@ -188,14 +186,10 @@ __device__ __forceinline__ float ncc_coef_f32(double num, double p)
     const double e = fma(-t, y, 1.0);
     y = fma(0.5 * y, e, y);
     const double c = num * y;
-    const float f = (float)c;
-    if (c == 0.0)
-        return f;
-    const double r = fabs(c - (double)f);
-    const double ulp = (double)__uint_as_float((__float_as_uint(f) & 0x7F800000u) - (23u << 23));
-    const double margin = fabs(c) * 0x1p-42;
-    if (0.5 * ulp - r > margin && fabs(r - 0.25 * ulp) > margin)
-        return f;
+    const double m = fabs(c) * 0x1p-42;
+    const float lo = (float)(c - m);
+    if (lo == (float)(c + m))
+        return lo;
     return (float)(num / sqrt(p));
 }
 

@@ -24,25 +24,33 @@
 //   * SumI and SumISq: while the matrix-core waves run, the column-sum waves
 //     walk the tile's image words (4 columns each) down the template's rows,
 //     keeping running sums per column of the biased pixels s = I - 128 and of
-//     s^2 (one field each; with four matrix-core waves, two waves per field,
-//     half of the words each), with signed v_dot4 on the staged bytes: the
-//     window of output row 0.  Each then slides its window down the 16
-//     output rows (add the row entering, remove the row leaving; the tile's
-//     first 15 rows are kept for that when the template comes in several
-//     chunks) and, as each row appears, takes its prefix along the wave's
-//     words in registers (a DPP scan), so a window sum is the difference of
-//     two entries (plus the first half's row total where a window spans both
-//     halves).  SumI = sum s + 128 N and SumISq = sum s^2 + 256 SumI -
-//     16384 N, all in wrapping 32-bit arithmetic, exact because every final
-//     sum is below 2^32.
+//     the squares (one field each; with four matrix-core waves, two waves per
+//     field, one per half of the tile's outputs), four rows at a time through
+//     a byte transpose and one dot4 per column: the window of output row 0.
+//     Each then slides its window down the 16 output rows (add the row
+//     entering, remove the row leaving; the tile's first 15 rows are kept
+//     for that when the template comes in several chunks) and, as each row
+//     appears, takes its prefix along the wave's words in registers (a DPP
+//     scan), from which a window sum is the difference of two entries.
+//   * Window sums or prefixes.  For templates up to 128 bytes wide a
+//     column-sum wave takes every word its 128 outputs read (the two halves
+//     of a 256-column tile overlap by the template's width), so it forms the
+//     window sums itself (the prefix at x + t_width - 1 less the one at x - 1,
+//     read across lanes), SumI = sum s + 128 N and SumISq = sum I^2 (the
+//     squares of the unbiased pixels), keeps them in LDS for the epilogue and
+//     stores them to the outputs while the matrix-core waves still walk, so
+//     only SumIT and the coefficient are written at the end.  Wider templates
+//     (and narrow tiles whose window sums would not take less LDS) keep the
+//     row prefixes of s and s^2 over disjoint halves; the epilogue then forms
+//     every sum, adding the first half's row total where a window spans both
+//     halves, and SumISq = sum s^2 + 256 SumI - 16384 N.  All in wrapping
+//     32-bit arithmetic, exact because every final sum is below 2^32.
 //   * Tiles: 16 output rows by 256 columns (four matrix-core waves, two
 //     workgroups per CU) or 128 columns (two, four workgroups per CU, for
 //     templates up to 64 bytes wide); the launcher takes the narrow tiles
 //     when they run the grid in fewer rounds of workgroups, or when the wide
-//     ones would cover at most half of the CUs.  On narrow tiles whose row
-//     prefixes would not let the template fit one row chunk, the column-sum
-//     waves store the window sums themselves (the prefix at x + t_width - 1
-//     less the one at x - 1, read across lanes), which take less LDS.
+//     ones would cover at most half of the CUs.  Narrow tiles store row
+//     prefixes when the template then fits one row chunk, else window sums.
 //   * The coefficient follows the packed-byte kernels' exact formula: num, vI
 //     and vT are exact integers (held in fp64 here, formed with fused
 //     multiply-adds), then ncc_coef_f32, so both paths return the same bits.
@@ -117,7 +125,7 @@ __host__ __device__ inline MfPlan mf_plan(int mw, int t_width, int hc, bool one_
     // `win` (MW = 2) the window sums of the tile's 128 outputs themselves,
     // which take less LDS (a row is stored and read by consecutive lanes, so
     // it needs no padding)
-    p.vs = win ? 128 : 4 * p.nwd + 4;
+    p.vs = win ? 64 * mw : 4 * p.nwd + 4;
     int img = (MF_TY + hc) * p.sw;  // staged rows + one spare row
     if (img < MF_TY * mf_acc_stride(mw)) img = MF_TY * mf_acc_stride(mw);
     p.img_words = img;
@@ -224,16 +232,53 @@ __device__ __forceinline__ void mf_stage_template(const uint8_t *__restrict__ tm
 
 // Column sums of field F over one staged image word (4 columns of biased
 // pixels s = I - 128, signed bytes), into c[0..3]: F = 0 adds s, F = 1 adds
-// s^2 (v_dot4_i32_i8, wrapping 32-bit sums).  The epilogue recovers
-// SumI = sum s + 128 N and SumISq = sum s^2 + 256 SumI - 16384 N exactly.
+// s^2 (v_dot4_i32_i8), F = 2 adds I^2 (v_dot4_u32_u8 on the unbiased bytes);
+// wrapping 32-bit sums.  SumI = sum s + 128 N and SumISq = sum s^2 + 256 SumI
+// - 16384 N, or sum I^2 itself, exactly.
 template <int F>
 __device__ __forceinline__ void mf_col_add(uint32_t biased, uint32_t (&c)[4])
 {
+    if (F == 2) {
+        const uint32_t u = biased ^ 0x80808080u;  // the pixels themselves
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            c[k] = __builtin_amdgcn_udot4(u & (0xFFu << (8 * k)), u, c[k], false);
+        return;
+    }
 #pragma unroll
     for (int k = 0; k < 4; ++k)
         c[k] = (uint32_t)__builtin_amdgcn_sdot4(
             F == 0 ? (int)biased : (int)(biased & (0xFFu << (8 * k))), F == 0 ? (int)(1u << (8 * k)) : (int)biased,
             (int)c[k], false);
+}
+
+// Column sums of field F over the same word of four consecutive rows u[0..3]:
+// a 4x4 byte transpose (eight v_perm_b32) gives each column's four bytes in
+// one word, which one dot4 then sums, against ones (F = 0) or against itself
+// (F = 1 on the biased bytes, F = 2 on the pixels themselves).  The same
+// sums as four calls of mf_col_add, in fewer instructions (12 or 16 per four
+// rows instead of 16, 32 or 36).
+template <int F>
+__device__ __forceinline__ void mf_col_add4(const uint32_t (&u)[4], uint32_t (&c)[4])
+{
+    // perm(hi, lo, sel): byte i of the result is byte sel_i of hi:lo (lo in bytes 0..3)
+    const uint32_t a_lo = __builtin_amdgcn_perm(u[1], u[0], 0x05010400u);  // u0.b0 u1.b0 u0.b1 u1.b1
+    const uint32_t a_hi = __builtin_amdgcn_perm(u[1], u[0], 0x07030602u);  // u0.b2 u1.b2 u0.b3 u1.b3
+    const uint32_t b_lo = __builtin_amdgcn_perm(u[3], u[2], 0x05010400u);
+    const uint32_t b_hi = __builtin_amdgcn_perm(u[3], u[2], 0x07030602u);
+    uint32_t col[4] = {__builtin_amdgcn_perm(b_lo, a_lo, 0x05040100u), __builtin_amdgcn_perm(b_lo, a_lo, 0x07060302u),
+                       __builtin_amdgcn_perm(b_hi, a_hi, 0x05040100u), __builtin_amdgcn_perm(b_hi, a_hi, 0x07060302u)};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        if (F == 0)
+            c[k] = (uint32_t)__builtin_amdgcn_sdot4((int)col[k], 0x01010101, (int)c[k], false);
+        else if (F == 1)
+            c[k] = (uint32_t)__builtin_amdgcn_sdot4((int)col[k], (int)col[k], (int)c[k], false);
+        else {
+            const uint32_t px = col[k] ^ 0x80808080u;
+            c[k] = __builtin_amdgcn_udot4(px, px, c[k], false);
+        }
+    }
 }
 
 // The matrix-core walk of one template-row chunk for one wave: every image
@@ -314,9 +359,7 @@ __device__ __forceinline__ void mf_col_walk(const uint32_t *img, int hcur, int j
 #pragma unroll
         for (int q = 0; q < U; ++q)
             u[q] = p[(rr + q) * sw];
-#pragma unroll
-        for (int q = 0; q < U; ++q)
-            mf_col_add<F>(u[q], c);
+        mf_col_add4<F>(u, c);
     }
     for (; rr < hcur; ++rr)
         mf_col_add<F>(p[rr * sw], c);
@@ -444,20 +487,27 @@ __device__ __forceinline__ void mf_field_chunk(const uint32_t *img, int hcur, in
 
 // Workgroup roles (wave-uniform): waves 0 .. MW - 1 run the matrix cores, 64
 // output columns each; the next ones keep the column sums, one wave per field
-// (pixels, squared pixels) and, with MW = 4, half of the image words (the
+// (pixels, squared pixels) and, with MW = 4, half of the tile's outputs (the
 // first pixel wave also sums the template), so the vector work of SumI and
 // SumISq runs beside the matrix products instead of inside their loop.
-// Every wave takes part in the staging and in the epilogue.  The row prefix
-// of each half starts from zero; the epilogue adds the first half's row total
-// where a window reaches from the first half into the second (with one half,
-// never).
+// Every wave takes part in the staging and in the epilogue.  With WIN the
+// column-sum waves store window sums (and SumI, SumISq themselves); without,
+// row prefixes over disjoint halves, each starting from zero, and the
+// epilogue adds the first half's row total where a window reaches from the
+// first half into the second (with one half, never).
+// Wave priorities, measured on 1920x1080 with 64x64 (HIP-event medians of
+// one run, us): staging 3, column-sum waves 3 and matrix-core waves 1 during
+// the walk, 21.5; column-sum waves 2 or 1 and matrix-core waves 2 or 1,
+// 22.9 - 23.8; column-sum waves 0, 24.4.  On a SIMD the matrix waves' byte
+// shifts mostly hide under their products, the column-sum waves' vector
+// work does not (without it the launch took 18.4 us against 23.4).
 template <int MW, int NKB, bool WIN>
 __global__ __launch_bounds__(mf_threads(MW)) __attribute__((amdgpu_waves_per_eu(NKB == 1 ? 4 : 1)))
 void ncc_u8_mfma_kernel(NccArgs a)
 {
     constexpr int NT = mf_threads(MW), TX = mf_tx(MW), NWK = mf_walkers(MW), ACC = mf_acc_stride(MW);
     extern __shared__ uint4 mf_smem[];
-    static_assert(!WIN || MW == 2, "window sums need one column-sum wave over all the words");
+    static_assert(!WIN || NKB <= 2, "a column-sum wave's 64 lanes hold the words of 128 outputs");
     const MfPlan P = mf_plan(MW, a.t_width, a.hc, a.t_height <= a.hc, WIN);
     uint32_t *const V1 = reinterpret_cast<uint32_t *>(mf_smem);
     uint32_t *const V2 = V1 + MF_TY * P.vs;
@@ -489,19 +539,26 @@ void ncc_u8_mfma_kernel(NccArgs a)
         const int hcur = min(P.hc, th - j0);
         const bool last = j0 + hcur == th;
         __syncthreads();  // the previous chunk's readers are done
+        __builtin_amdgcn_s_setprio(3);  // staging first on a shared CU: it starts this workgroup's chain
         mf_stage_image<NT>(a.image, a.height, a.pitch, y0 + j0, x0, MF_TY - 1 + hcur, nchunks16, img, P.sw);
         mf_stage_template<NT>(a.tmpl, tw, j0, hcur, 64 * NKB, tpl, P.tsb, P.trows);
         __syncthreads();
         if (wave < MW) {
+            __builtin_amdgcn_s_setprio(1);
             mf_walk_chunk<MW, NKB>(img, tpl, hcur, wave, at);
+            __builtin_amdgcn_s_setprio(0);
         } else {
-            // the column-sum waves issue first on their SIMD: the matrix
-            // waves lose little (their products keep the matrix cores busy)
-            // and the sums are ready when the products are
-            __builtin_amdgcn_s_setprio(2);
+            // the column-sum waves issue first on their SIMD, so their sums
+            // (and, with WIN, their stores) are done when the products are
+            __builtin_amdgcn_s_setprio(3);
             const int h = NWK == 4 ? (wave - MW) & 1 : 0;
             const int field = NWK == 4 ? (wave - MW) >> 1 : wave - MW;
-            const int w0 = h * half, cnt = h ? P.nwd - half : half;
+            // window sums: each wave takes every word its 128 outputs read
+            // (the two halves overlap by the template's width), so its sums
+            // need nothing from the other half; prefixes: disjoint halves
+            const int w0 = WIN ? 32 * h : h * half;
+            const int cnt = WIN ? 32 + (tw + 2) / 4 : h ? P.nwd - half : half;
+            uint32_t *const vf = (field == 0 ? V1 : V2) + (WIN ? 128 * h : 0);
             if (field == 0) {
                 if (h == 0) {
                     // template sums from the staged (biased) rows of this
@@ -518,11 +575,44 @@ void ncc_u8_mfma_kernel(NccArgs a)
                         tq = dot4u(w, w, tq);
                     }
                 }
-                mf_field_chunk<MW, NKB, 0, WIN>(img, hcur, j0, last, one_chunk, head, P.nwd, w0, cnt, V1, P.vs, tw, c);
+                mf_field_chunk<MW, NKB, 0, WIN>(img, hcur, j0, last, one_chunk, head, P.nwd, w0, cnt, vf, P.vs, tw, c);
             } else {
-                mf_field_chunk<MW, NKB, 1, WIN>(img, hcur, j0, last, one_chunk, head, P.nwd, w0, cnt, V2, P.vs, tw, c);
+                mf_field_chunk<MW, NKB, WIN ? 2 : 1, WIN>(img, hcur, j0, last, one_chunk, head, P.nwd, w0, cnt, vf,
+                                                         P.vs, tw, c);
             }
             __builtin_amdgcn_s_setprio(0);
+        }
+    }
+    const uint32_t nn = (uint32_t)(tw * th);
+    if (WIN && wave >= MW) {
+        // Window sums are final as soon as a column-sum wave has its rows:
+        // it stores its 128 outputs of each row now (one per lane, from the
+        // rows it wrote to V), SumI = sum s + 128 N or SumISq = sum I^2,
+        // while the matrix-core waves still walk.
+        const int h = NWK == 4 ? (wave - MW) & 1 : 0;
+        const int field = NWK == 4 ? (wave - MW) >> 1 : wave - MW;
+        uint32_t *const out = field == 0 ? a.sum_i : a.sum_isq;
+        const int xh = x0 + 128 * h;
+        if (out && xh < a.out_w) {
+            const uint32_t *const vf = (field == 0 ? V1 : V2) + 128 * h;
+            const uint32_t add = field == 0 ? 128u * nn : 0u;
+            uint32_t *const ob = out + ((size_t)y0 * a.out_w + xh);  // 32-bit offsets from here
+            // every LDS read first (one wait, not one per row), then the stores
+            uint32_t v[MF_TY][2];
+#pragma unroll
+            for (int n = 0; n < MF_TY; ++n)
+#pragma unroll
+                for (int k = 0; k < 2; ++k)
+                    v[n][k] = vf[n * P.vs + 64 * k + lane] + add;
+            const int nrows = min(MF_TY, a.out_h - y0);
+#pragma unroll
+            for (int n = 0; n < MF_TY; ++n)
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    const int col = 64 * k + lane;
+                    if (n < nrows && xh + col < a.out_w)
+                        ob[(uint32_t)n * (uint32_t)a.out_w + (uint32_t)col] = v[n][k];
+                }
         }
     }
     if (wave == MW) {
@@ -549,7 +639,6 @@ void ncc_u8_mfma_kernel(NccArgs a)
     __syncthreads();
 
     const uint32_t sum_t = tsum[0], sum_tsq = tsum[1];
-    const uint32_t nn = (uint32_t)(tw * th);
     const uint32_t bias = 128u * sum_t - 16384u * nn;
     // num, vI, vT are integers below 2^50 (N <= 66,051 and every sum below
     // 2^32), so fp64 fused multiply-adds form them exactly: the same doubles,
@@ -557,48 +646,60 @@ void ncc_u8_mfma_kernel(NccArgs a)
     const double nd = (double)nn, std_ = (double)sum_t;
     const double vt = fma(nd, (double)sum_tsq, -(std_ * std_));
 
-    // Each wave takes 64 consecutive columns of one output row at a time.
+    // Each wave takes 64 consecutive columns of one output row at a time (one
+    // column per lane: whole cache lines per store, no LDS bank conflicts).
+    // NT is a multiple of TX, so a thread keeps its column and its terms
+    // (the prefix entries it reads, whether its window needs the first
+    // half's row total) while its rows advance by NT / TX.  A window needs
+    // that total when it starts in the first half and ends in the second,
+    // i.e. when x lies in [ce - tw + 1, ce].  Outputs are addressed from the
+    // tile's first one with 32-bit offsets (n * out_w + x < 2^32).
+    constexpr int RS = NT / TX;  // rows per pass
+    static_assert(NT % TX == 0, "a thread keeps one column");
+    const int x = threadIdx.x % TX, gx = x0 + x;
+    const int hi = x + tw - 1, xl = x > 0 ? x - 1 : 0;
+    const uint32_t left_keep = x > 0 ? 0xFFFFFFFFu : 0u;
+    const uint32_t join_keep = (uint32_t)(x - (ce - tw + 1)) <= (uint32_t)(tw - 1) ? 0xFFFFFFFFu : 0u;
+    const size_t o0 = (size_t)y0 * a.out_w + x0;
+    uint32_t *const out_i = a.sum_i ? a.sum_i + o0 : nullptr;
+    uint32_t *const out_isq = a.sum_isq ? a.sum_isq + o0 : nullptr;
+    uint32_t *const out_it = a.sum_it ? a.sum_it + o0 : nullptr;
+    float *const out_c = a.coef ? a.coef + o0 : nullptr;
     unsigned long long best = 0ull;
-    for (int i = threadIdx.x; i < MF_TY * TX; i += NT) {
-        const int n = i / TX, x = i % TX;
-        const int gx = x0 + x;
-        if (gx >= a.out_w || y0 + n >= a.out_h)
-            continue;
-        const size_t o = (size_t)(y0 + n) * a.out_w + gx;
-        // window sums as differences of the row prefix at columns hi and lo:
-        // the entry left of column 0 is read from column 0 and masked to
-        // zero, and the first half's row total (at ce - 1) is added when hi
-        // is in the second half and lo is not; every read is unconditional
-        const int hi = x + tw - 1, xl = x > 0 ? x - 1 : 0;
-        const uint32_t left_keep = x > 0 ? 0xFFFFFFFFu : 0u;
-        const uint32_t join_keep = hi >= ce && (x == 0 || x - 1 < ce) ? 0xFFFFFFFFu : 0u;
-        const uint32_t *q1 = V1 + n * P.vs;
-        const uint32_t *q2 = V2 + n * P.vs;
-        uint32_t si, sq;
-        if (WIN) {
-            // the column-sum waves stored the window sums themselves
-            si = q1[x] + 128u * nn;
-            sq = q2[x] + 256u * si - 16384u * nn;
-        } else {
-            // the column sums are of s = I - 128 and of s^2
-            si = q1[hi] - (q1[xl] & left_keep) + (q1[ce - 1] & join_keep) + 128u * nn;
-            sq = q2[hi] - (q2[xl] & left_keep) + (q2[ce - 1] & join_keep) + 256u * si - 16384u * nn;
-        }
-        const uint32_t st = (uint32_t)acc_it[n * ACC + x] + 128u * si + bias;
-        if (a.sum_i) a.sum_i[o] = si;
-        if (a.sum_isq) a.sum_isq[o] = sq;
-        if (a.sum_it) a.sum_it[o] = st;
-        if (a.coef || a.peak) {
-            const double sid = (double)si;
-            const double num = fma(nd, (double)st, -(sid * std_));
-            const double vi = fma(nd, (double)sq, -(sid * sid));
-            float cf = 0.0f;
-            if (vi != 0.0 && vt != 0.0)
-                cf = ncc_coef_f32(num, vi * vt);
-            if (a.coef) a.coef[o] = cf;
-            if (a.peak) {
-                const unsigned long long k = peak_key(cf, (uint32_t)o);
-                best = k > best ? k : best;
+    if (gx < a.out_w) {
+        for (int n = threadIdx.x / TX; n < MF_TY && y0 + n < a.out_h; n += RS) {
+            const uint32_t off = (uint32_t)n * (uint32_t)a.out_w + (uint32_t)x;
+            const uint32_t *q1 = V1 + n * P.vs;
+            const uint32_t *q2 = V2 + n * P.vs;
+            uint32_t si, sq;
+            if (WIN) {
+                // the column-sum waves stored the window sums themselves (of
+                // s and of I^2), and SumI and SumISq already
+                si = q1[x] + 128u * nn;
+                sq = q2[x];
+            } else {
+                // window sums as differences of the row prefix (of s = I -
+                // 128 and of s^2) at columns hi and x - 1; the entry left of
+                // column 0 is read from column 0 and masked to zero
+                si = q1[hi] - (q1[xl] & left_keep) + (q1[ce - 1] & join_keep) + 128u * nn;
+                sq = q2[hi] - (q2[xl] & left_keep) + (q2[ce - 1] & join_keep) + 256u * si - 16384u * nn;
+            }
+            const uint32_t st = (uint32_t)acc_it[n * ACC + x] + 128u * si + bias;
+            if (!WIN && out_i) out_i[off] = si;
+            if (!WIN && out_isq) out_isq[off] = sq;
+            if (out_it) out_it[off] = st;
+            if (out_c || a.peak) {
+                const double sid = (double)si;
+                const double num = fma(nd, (double)st, -(sid * std_));
+                const double vi = fma(nd, (double)sq, -(sid * sid));
+                float cf = 0.0f;
+                if (vi != 0.0 && vt != 0.0)
+                    cf = ncc_coef_f32(num, vi * vt);
+                if (out_c) out_c[off] = cf;
+                if (a.peak) {
+                    const unsigned long long k = peak_key(cf, (uint32_t)(o0 + off));
+                    best = k > best ? k : best;
+                }
             }
         }
     }
@@ -621,10 +722,11 @@ static int mf_fit_hc(const NccArgs &a, size_t budget, int mw, bool win)
 // that fit one workgroup per CU.
 static int mf_pick_hc4(const NccArgs &a)
 {
-    const int hc = mf_fit_hc(a, 80 * 1024, 4, false);
+    const bool win = (a.t_width + 63) / 64 <= 2;
+    const int hc = mf_fit_hc(a, 80 * 1024, 4, win);
     if (hc >= 32 || hc == a.t_height)
         return hc;
-    return mf_fit_hc(a, 160 * 1024, 4, false);
+    return mf_fit_hc(a, 160 * 1024, 4, win);
 }
 
 // 128-column tiles: four 4-wave workgroups per CU (one wave per SIMD each),
@@ -695,8 +797,8 @@ hipError_t ncc_launch_mfma(NccArgs a, hipStream_t s, int mw)
     }
     a.hc = mf_pick_hc4(a);
     switch ((a.t_width + 63) / 64) {
-    case 1: return mf_launch<4, 1, false>(a, s);
-    case 2: return mf_launch<4, 2, false>(a, s);
+    case 1: return mf_launch<4, 1, true>(a, s);
+    case 2: return mf_launch<4, 2, true>(a, s);
     case 3: return mf_launch<4, 3, false>(a, s);
     default: return mf_launch<4, 4, false>(a, s);
     }
