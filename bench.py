@@ -608,9 +608,9 @@ def main():
         m["roofline"] = {"bound": "mfma", "achieved": round(mf_achieved / 1e12, 2), "peak": I8_MFMA_PEAK / 1e12,
                          "unit": "TOP/s", "frac": round(mf_achieved / I8_MFMA_PEAK, 4),
                          "kernel": "ncc_u8_mfma_kernel",
-                         "note": "matrix-core and vector instructions of a SIMD take turns: the byte "
-                                 "alignment of the A operand, the column sums and the fp64 epilogue "
-                                 "lengthen the product walk"}
+                         "note": "the column-sum waves' vector work does not hide under the products "
+                                 "of its SIMD and lengthens the walk; staging before and the SumIT and "
+                                 "coefficient writes after it do not overlap the walk"}
         if not args.no_ext:
             out["ncc_ext"] = bench_ncc_ext(args, torch, _lib, inputs)
     if args.only in ("xcorr", "all"):
