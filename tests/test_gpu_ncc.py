@@ -241,6 +241,43 @@ def test_ncc_mfma_tile_widths(shape, variant):
     _gpu.check_ncc(case, _gpu.run_ncc(case, variant))
 
 
+@pytest.mark.parametrize("shape", [
+    # (height, width, t_height, t_width): 256-column tiles whose column-sum
+    # waves store window sums, with the template in several row chunks (the
+    # head rows kept for the slide), widths on both sides of 64 bytes
+    (140, 400, 100, 64),      # two chunks
+    (170, 600, 150, 100),     # two 64-byte blocks, three chunks
+    (160, 530, 120, 33),      # an odd width, two chunks
+    (230, 300, 200, 128),     # the widest window-sum template, four chunks
+])
+def test_ncc_mfma_window_sums_row_chunks(shape):
+    h, w, th, tw = shape
+    rng = np.random.default_rng(h * 151 + w * 13 + th)
+    img = u8_uniform(rng, (h, w))
+    tmpl = u8_uniform(rng, (th, tw))
+    case = _case_from(img, tmpl)
+    _gpu.log(f"ncc mfma window sums in row chunks {shape}")
+    _gpu.check_ncc(case, _gpu.run_ncc(case, _lib.XC_NCC_MFMA_W4))
+
+
+@pytest.mark.parametrize("shape", [(120, 700, 20, 40), (200, 700, 64, 64)])
+@pytest.mark.parametrize("variant", [_lib.XC_NCC_MFMA_W4, _lib.XC_NCC_MFMA_W2])
+def test_ncc_mfma_output_subsets(variant, shape):
+    """Subsets of the outputs through the matrix-core kernels (window sums
+    on 256-column tiles; on 128-column tiles row prefixes for the 20-row
+    template, window sums for the 64-row one), whose column-sum waves store
+    SumI and SumISq during the walk when they form window sums and whose
+    epilogue writes the rest: each requested map is right, none other is
+    touched (the helper's guard bands and sentinels)."""
+    h, w, th, tw = shape
+    case = ncc_case("t", 330 + th, h, w, th, tw, cut=True)
+    ref = None
+    for outs in (("coef",), ("sum_it",), ("sum_i",), ("sum_isq",), ("sum_i", "coef"), ("sum_isq", "sum_it"),
+                 ("sum_i", "sum_isq", "sum_it", "coef")):
+        _gpu.log(f"ncc mfma outputs {outs} variant {variant}")
+        ref = _gpu.check_ncc(case, _gpu.run_ncc(case, variant, outputs=outs), ref)
+
+
 def test_ncc_mfma_extreme_pixels():
     """All-255 and all-0 windows against 0/255 templates: the -128 bias and its
     exact correction at the ends of the byte range."""
