@@ -720,13 +720,31 @@ static int mf_fit_hc(const NccArgs &a, size_t budget, int mw, bool win)
 // 256-column tiles: the most rows that fit two workgroups per CU (80 KiB
 // each); when that leaves fewer than 32 rows (wide template rows), the most
 // that fit one workgroup per CU.
-static int mf_pick_hc4(const NccArgs &a)
+static int mf_pick_hc4(const NccArgs &a, bool win)
 {
-    const bool win = (a.t_width + 63) / 64 <= 2;
     const int hc = mf_fit_hc(a, 80 * 1024, 4, win);
     if (hc >= 32 || hc == a.t_height)
         return hc;
     return mf_fit_hc(a, 160 * 1024, 4, win);
+}
+
+// Whether 256-column tiles take window sums (stored during the walk) rather
+// than row prefixes: only where the walk is long enough to hide the
+// column-sum waves' extra work and stores, templates of at least 48 rows
+// (and at most two 64-byte blocks), and not where the prefixes need fewer
+// row chunks.  A/B on 1920x1080, prefixes / window sums (us): 64x64 25.8 /
+// 23.6, 16 wide x 64 tall 25.0 / 22.8, 32x64 25.6 / 23.3, 96x96 58.6 /
+// 52.6 (three chunks / two), 48x48 29.4 / 29.6; but 40x40 28.6 / 29.7,
+// 32x32 27.4 / 28.5, 64 wide x 16 tall 24.2 / 26.8, 8x8 22.9 / 25.6, and
+// 128x128 58.8 / 70.9 (one chunk at one workgroup per CU / three).
+static bool mf_win4(const NccArgs &a)
+{
+    if ((a.t_width + 63) / 64 > 2 || a.t_height < 48)
+        return false;
+    const int hw = mf_pick_hc4(a, true), hp = mf_pick_hc4(a, false);
+    if (hw == 0 || hp == 0)
+        return hw > 0;
+    return (a.t_height + hw - 1) / hw <= (a.t_height + hp - 1) / hp;
 }
 
 // 128-column tiles: four 4-wave workgroups per CU (one wave per SIMD each),
@@ -755,7 +773,7 @@ bool ncc_mfma_supported(const NccArgs &a, int mw)
 {
     if (mw == 2)
         return mf_pick2(a).hc > 0;
-    return (a.t_width + 63) / 64 <= MF_MAX_NKB && mf_pick_hc4(a) > 0;
+    return (a.t_width + 63) / 64 <= MF_MAX_NKB && mf_pick_hc4(a, mf_win4(a)) > 0;
 }
 
 template <int MW, int NKB, bool WIN>
@@ -795,10 +813,11 @@ hipError_t ncc_launch_mfma(NccArgs a, hipStream_t s, int mw)
         a.hc = p2.hc;
         return p2.win ? mf_launch<2, 1, true>(a, s) : mf_launch<2, 1, false>(a, s);
     }
-    a.hc = mf_pick_hc4(a);
+    const bool win = mf_win4(a);
+    a.hc = mf_pick_hc4(a, win);
     switch ((a.t_width + 63) / 64) {
-    case 1: return mf_launch<4, 1, true>(a, s);
-    case 2: return mf_launch<4, 2, true>(a, s);
+    case 1: return win ? mf_launch<4, 1, true>(a, s) : mf_launch<4, 1, false>(a, s);
+    case 2: return win ? mf_launch<4, 2, true>(a, s) : mf_launch<4, 2, false>(a, s);
     case 3: return mf_launch<4, 3, false>(a, s);
     default: return mf_launch<4, 4, false>(a, s);
     }

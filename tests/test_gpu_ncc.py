@@ -243,12 +243,14 @@ def test_ncc_mfma_tile_widths(shape, variant):
 
 @pytest.mark.parametrize("shape", [
     # (height, width, t_height, t_width): 256-column tiles whose column-sum
-    # waves store window sums, with the template in several row chunks (the
-    # head rows kept for the slide), widths on both sides of 64 bytes
+    # waves store window sums (templates of 48 rows and more), mostly with
+    # the template in several row chunks (the head rows kept for the slide),
+    # widths on both sides of 64 bytes
     (140, 400, 100, 64),      # two chunks
     (170, 600, 150, 100),     # two 64-byte blocks, three chunks
     (160, 530, 120, 33),      # an odd width, two chunks
-    (230, 300, 200, 128),     # the widest window-sum template, four chunks
+    (100, 500, 64, 128),      # the widest window-sum template, one chunk
+    (230, 300, 200, 128),     # row prefixes: two chunks at one workgroup per CU
 ])
 def test_ncc_mfma_window_sums_row_chunks(shape):
     h, w, th, tw = shape
