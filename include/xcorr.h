@@ -91,28 +91,36 @@ int ncc_u8_run(const uint8_t *image, int width, int height, int pitch_bytes,
 /*
  * ncc_u8_run_variant -- the same computation through a chosen kernel variant,
  * for ablation studies.  Every variant returns identical outputs.
- *   XC_NCC_AUTO          the library's choice (what ncc_u8_run uses): XC_NCC_MFMA
- *                        where it takes the template and the template has at
- *                        least 512 pixels, or at least 96 pixels with at least
+ *   XC_NCC_AUTO          the library's choice (what ncc_u8_run uses).  On
+ *                        images too small for the DOT4_ILP kernel's 256 x 16
+ *                        output tiles to fill the GPU's compute units, first
+ *                        XC_NCC_DOT4_C1 for templates whose width is a
+ *                        multiple of 4, of at most 200 packed words, whose
+ *                        workgroups (64 x 4 outputs) times template words are
+ *                        at most 180 per compute unit (145 when there are
+ *                        more workgroups than units).  Then XC_NCC_MFMA where
+ *                        it takes the template and the template has at least
+ *                        512 pixels, or at least 96 pixels with at least
  *                        400,000 outputs, or there are at least 1,000,000
- *                        outputs.  Otherwise, on images too small for the
- *                        DOT4_ILP kernel's 256 x 16 output tiles to fill the
- *                        GPU's compute units: XC_NCC_DOT4_C1 for templates
- *                        of at most 64 packed words whose workgroups (64 x 4
- *                        outputs) times template words are at most 192 per
- *                        compute unit (widths not a multiple of 4: at most
- *                        16 words and 96 per unit); failing that,
+ *                        outputs.  Then, on those small images again,
+ *                        XC_NCC_DOT4_C1 for templates of at most 64 packed
+ *                        words and at most 192 per unit (widths not a
+ *                        multiple of 4: 16 words, 96 per unit), failing that
  *                        XC_NCC_MFMA for templates over 16 words or of a
  *                        width not a multiple of 4.  Else XC_NCC_DOT4_ILP.
+ *                        ncc_u8_auto_variant reports the choice.
  *   XC_NCC_DOT4_ILP      packed-byte dot products, 4 columns x several rows per lane
  *   XC_NCC_DOT4_C1       packed-byte dot products, one output per lane
  *   XC_NCC_SCALAR_C1     byte-at-a-time multiply-adds, one output per lane
  *   XC_NCC_MFMA          SumIT as a signed-byte matrix product on the matrix
  *                        cores (pixels and template biased by -128, corrected
  *                        exactly with SumI and SumT), SumI and SumISq as
- *                        separable box sums; t_width <= 256 only, else
- *                        XC_ERR_SHAPE.  A recast of the page's computation,
- *                        not its DP4A method.
+ *                        separable box sums in waves of their own (which,
+ *                        for templates of 48 rows or more up to 128 bytes
+ *                        wide, store those two outputs while the products
+ *                        run); t_width <= 256 only, else XC_ERR_SHAPE.  A
+ *                        recast of the page's computation, not its DP4A
+ *                        method.
  *   XC_NCC_DOT4_ILP_Q1   the ILP series of the ablation: packed-byte dot
  *   XC_NCC_DOT4_ILP_Q2   products, 4 columns x Q = 1, 2 or 4 rows per lane,
  *   XC_NCC_DOT4_ILP_Q4   each lane walking every template row itself (no split
