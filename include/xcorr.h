@@ -131,7 +131,8 @@ int ncc_u8_run(const uint8_t *image, int width, int height, int pitch_bytes,
  *                        workgroups per CU) or 128 (2 matrix-core waves, four
  *                        per CU; t_width <= 64 only, else XC_ERR_SHAPE).
  *                        XC_NCC_MFMA picks the width that runs the output's
- *                        tiles in fewer rounds of workgroups.
+ *                        tiles in fewer rounds of workgroups, and the narrow
+ *                        one where wide tiles would leave compute units idle.
  *   XC_NCC_DOT4_COLS1    the column-ILP series of the ablation (the page's
  *   XC_NCC_DOT4_COLS2    two-column step): packed-byte dot products with
  *   XC_NCC_DOT4_COLS4    C = 1, 2, 4 or 8 adjacent output columns per lane
