@@ -498,9 +498,10 @@ __device__ __forceinline__ void mf_field_chunk(const uint32_t *img, int hcur, in
 // Wave priorities, measured on 1920x1080 with 64x64 (HIP-event medians of
 // one run, us): staging 3, column-sum waves 3 and matrix-core waves 1 during
 // the walk, 21.5; column-sum waves 2 or 1 and matrix-core waves 2 or 1,
-// 22.9 - 23.8; column-sum waves 0, 24.4.  On a SIMD the matrix waves' byte
-// shifts mostly hide under their products, the column-sum waves' vector
-// work does not (without it the launch took 18.4 us against 23.4).
+// 22.9 - 23.8; column-sum waves 0, 24.4.  On a SIMD the vector instructions
+// and the matrix products largely take turns (without the column-sum waves'
+// work the launch took 18.4 us against 23.4), so every vector instruction in
+// the walk lengthens it.
 template <int MW, int NKB, bool WIN>
 __global__ __launch_bounds__(mf_threads(MW)) __attribute__((amdgpu_waves_per_eu(NKB == 1 ? 4 : 1)))
 void ncc_u8_mfma_kernel(NccArgs a)
