@@ -87,3 +87,60 @@ def test_xcorr_random_shape_all_algorithms(seed):
             assert e.value.status == _lib.XC_ERR_SHAPE
             continue
         _gpu.check_xcorr(_gpu.run_xcorr(L, R, algo), ref, ab)
+
+
+MODE_VARIANTS = [_lib.XC_NCC_AUTO, _lib.XC_NCC_DOT4_ILP, _lib.XC_NCC_DOT4_C1, _lib.XC_NCC_MFMA,
+                 _lib.XC_NCC_MFMA_W2, _lib.XC_NCC_DOT4_COLS2]
+
+
+@pytest.mark.parametrize("seed", range(9000, 9012))
+def test_ncc_modes_random_shape(seed):
+    """Same and full output modes on random shapes (templates larger than the
+    image included), through the automatic choice and one other variant drawn
+    per case, against the mode oracle; canary bands around the outputs and the
+    workspace."""
+    from test_gpu_ncc_modes import _check, run_mode
+    rng = np.random.default_rng(seed)
+    h, w = int(rng.integers(1, 121)), int(rng.integers(1, 201))
+    th, tw = int(rng.integers(1, 90)), int(rng.integers(1, 140))
+    while th * tw > 8000:
+        th = max(1, th // 2)
+    img = u8_uniform(rng, (h, w))
+    buf = np.zeros((h, pitch_for(w)), np.uint8)
+    buf[:, :w] = img
+    case = NccCase("m", buf, w, h, u8_uniform(rng, (th, tw)), None)
+    other = MODE_VARIANTS[1 + int(rng.integers(0, len(MODE_VARIANTS) - 1))]
+    for mode in (_lib.XC_NCC_MODE_SAME, _lib.XC_NCC_MODE_FULL):
+        ref = oracle.ncc_u8_mode(case.image, case.width, case.height, case.tmpl, mode)
+        for v in (_lib.XC_NCC_AUTO, other):
+            if tw > MFMA_MAX_T_WIDTH.get(v, tw):
+                continue
+            _gpu.log(f"ncc mode {mode} random seed {seed}: image {h}x{w}, template {th}x{tw}, variant {v}")
+            _check(run_mode(case, mode, v), ref)
+
+
+@pytest.mark.parametrize("seed", range(9100, 9112))
+def test_ncc_peak_random_shape(seed):
+    """The best match on random shapes (a cut template for most), through the
+    automatic choice and one other variant per case, against the oracle's
+    first maximum of its own coefficient map."""
+    from test_gpu_ncc_ext import _check_peak, _run_peak
+    rng, h, w, th, tw, extra = _ncc_shape(seed)
+    img = u8_uniform(rng, (h, w))
+    cut = None
+    if rng.integers(0, 4) > 0:
+        cut = (int(rng.integers(0, h - th + 1)), int(rng.integers(0, w - tw + 1)))
+        tmpl = np.ascontiguousarray(img[cut[0]:cut[0] + th, cut[1]:cut[1] + tw])
+    else:
+        tmpl = u8_uniform(rng, (th, tw))
+    buf = np.zeros((h, pitch_for(w) + extra), np.uint8)
+    buf[:, :w] = img
+    case = NccCase("p", buf, w, h, tmpl, cut)
+    ref = oracle.ncc_u8(case.image, case.width, case.height, case.tmpl)
+    other = NCC_VARIANTS[1 + int(rng.integers(0, len(NCC_VARIANTS) - 1))]
+    for v in (_lib.XC_NCC_AUTO, other):
+        if tw > MFMA_MAX_T_WIDTH.get(v, tw):
+            continue
+        _gpu.log(f"ncc peak random seed {seed}: image {h}x{w}, template {th}x{tw}, variant {v}")
+        got, maps = _run_peak(case, v, outputs=("coef",))
+        _check_peak(case, got, maps["coef"], ref["coef"])
