@@ -48,7 +48,9 @@
 //     - whole: when every matrix a workgroup touches fits in LDS with zero
 //       column halos, it is staged once (left matrices shared by consecutive
 //       pairs only once) and the waves walk both dx signs from LDS with no
-//       further workgroup barrier;
+//       further workgroup barrier (xcorr_bd_whole_pair_kernel, for up to 8
+//       diagonals: the two signs of a diagonal on two waves that share
+//       their walks evenly, with one barrier to hand partial sums over);
 //     - chunk: otherwise columns pass through two LDS buffers J walk steps at
 //       a time, the next chunk prefetched into registers during the FMAs.
 //   The host picks waves per workgroup (16, 8 or 4 diagonals sharing one
@@ -190,7 +192,7 @@ struct BdArgs {
     int n_xtiles;    // wp / BD_P
     int n_dgroups;   // ceil(nb / waves per workgroup)
     int n_sides;     // 1: a workgroup walks both dx signs; 2: one sign each
-    int wg_sides;    // 1: both dx signs in one workgroup, one per half of its waves
+    int wg_sides;    // 1: the pair kernel (a diagonal's two dx signs on two waves of a workgroup)
     // multipliers for division by nb and by the whole-staging row widths
     uint32_t m_nb, m_nr;  // fast_div_m(nb), small_div_m16(n_right)
     // exact division of any 32-bit value (div_m / div_exact) by n_sides,
@@ -982,7 +984,6 @@ __global__ __launch_bounds__(64 * NW) void xcorr_bd_whole_kernel(BdArgs a)
     extern __shared__ float4 smem[];
     const BdWho w = bd_who<NW>(a);
     const int nb = a.nb, S = a.S, wp = a.wp;
-    const int rows = a.x.rows, cols = a.x.cols;
     const int64_t npairs = (int64_t)a.x.n_left * a.x.n_right;
     // Every staged row block ("unit") is W LDS columns wide, left and right
     // alike: source column g at index g + P - 1, zero halos on both sides
@@ -1024,6 +1025,121 @@ __global__ __launch_bounds__(64 * NW) void xcorr_bd_whole_kernel(BdArgs a)
                        Rs + (w.s * nb + w.b) * W + u_first + roff, u_end - u_first, acc1, acc2);
         bd_reduce_store<true>(a, w, side, wred, acc1, acc2);
     }
+}
+
+// Whole staging with the two dx signs of a diagonal on two waves of one
+// workgroup (waves h and h + NW/2, which the hardware places on the same
+// SIMD: a workgroup's waves go round-robin over the CU's four, so with NW = 8
+// each SIMD holds one diagonal's pair).  The signs' walks, wp - c0 and c0 + P
+// steps, add up to wp + P for every column tile but are far apart at the
+// edge tiles (32 and 4 steps at c0 = 0 for 32 columns), where the longer
+// one would run mostly alone on its SIMD.  So the wave of the shorter sign
+// also walks the last `tail` steps of the longer one, leaving each wave at
+// most `half` = (wp + P) / 2 rounded up to P steps.  Both waves walk `tail`
+// steps first (the longer sign's first and last), the second wave parks its
+// partial sums in LDS, and a workgroup barrier (reached by every wave after
+// the same number of steps, as all share the column tile) hands them over;
+// then the first wave walks the rest of its share and adds them, and the
+// second walks its own sign whole.  The longer sign's sums are thus formed
+// in two parts added once, a fixed order.
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void xcorr_bd_whole_pair_kernel(BdArgs a)
+{
+    constexpr int P = BD_P, H = NW / 2;
+    static_assert(NW >= 2 && NW % 2 == 0, "waves come in pairs");
+    extern __shared__ float4 smem[];
+    const BdWho w = bd_who<NW>(a);  // a.wg_sides is set: side_lo is this wave's sign
+    const int nb = a.nb, S = a.S, wp = a.wp;
+    const int64_t npairs = (int64_t)a.x.n_left * a.x.n_right;
+    const int W = bd_whole_w(wp);
+    const int l_elems = a.nls * nb * W;
+    float4 *const Ls = smem;
+    float4 *const Rs = smem + l_elems;
+    float *const red = reinterpret_cast<float *>(smem + l_elems + S * nb * W);
+    float *const wred = red + w.wave * bd_red_floats(S);
+    // handover area: per diagonal of the workgroup, 7 float4s of partial
+    // sums per lane, lane-fastest
+    const int own = w.side_lo;
+    float4 *const part = reinterpret_cast<float4 *>(red + NW * bd_red_floats(S)) + (w.wave - own * H) * 7 * 64;
+
+    bd_stage_whole<64 * NW>(a, smem, W, w, npairs);
+    __syncthreads();
+
+    const int len0 = wp - w.c0, len1 = w.c0 + P;
+    const int g = len0 >= len1 ? 0 : 1;  // the longer sign
+    const int lg = g ? len1 : len0;
+    const int half = ((wp + P) / 2 + P - 1) / P * P;
+    const int tail = lg > half ? lg - half : 0;  // uniform over the workgroup, a multiple of P
+    const bool head = own == g;
+    const float4 *const Lb1 = Ls + (w.ls * nb + w.kb1) * W + (P - 1);
+    const float4 *const Lb2 = Ls + (w.ls * nb + w.kb2) * W + (P - 1);
+    const float4 *const Rb = Rs + (w.s * nb + w.b) * W;
+    float acc1[4][P], acc2[3][P];
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc1[r][p] = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 3; ++r) acc2[r][p] = 0.0f;
+    }
+#pragma unroll 1
+    for (int ph = tail > 0 ? 0 : 1; ph < 2; ++ph) {
+        // phase 0: `tail` steps of the longer sign, from its start (head
+        // wave) or up to its end (the other); phase 1: the rest of the head
+        // wave's share, or the other wave's own sign whole
+        const int side = head || ph == 0 ? g : own;
+        const int u_first = side ? 0 : w.c0;
+        const int roff = side ? wp - w.c0 : -w.c0;
+        int u0, n;
+        if (head) {
+            u0 = u_first + (ph ? tail : 0);
+            n = ph ? lg - 2 * tail : tail;
+        } else {
+            u0 = ph ? u_first : u_first + lg - tail;
+            n = ph ? (side ? len1 : len0) : tail;
+        }
+        // ring preload reads right indices u0 + roff .. + P - 1 (>= 0: roff >= -c0, u0 >= c0 on side 0)
+        if (w.wave_on && n > 0)
+            bd_compute<16>(Lb1 + u0, Lb2 + u0, Rb + u0 + roff, n, acc1, acc2);
+        if (ph == 0) {
+            if (w.wave_on && !head) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    part[r * 64 + w.lane] = make_float4(acc1[r][0], acc1[r][1], acc1[r][2], acc1[r][3]);
+#pragma unroll
+                    for (int p = 0; p < P; ++p) acc1[r][p] = 0.0f;
+                }
+#pragma unroll
+                for (int r = 0; r < 3; ++r) {
+                    part[(4 + r) * 64 + w.lane] = make_float4(acc2[r][0], acc2[r][1], acc2[r][2], acc2[r][3]);
+#pragma unroll
+                    for (int p = 0; p < P; ++p) acc2[r][p] = 0.0f;
+                }
+            }
+            __syncthreads();
+        }
+    }
+    if (!w.wave_on)
+        return;
+    if (head && tail > 0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float4 v = part[r * 64 + w.lane];
+            acc1[r][0] += v.x;
+            acc1[r][1] += v.y;
+            acc1[r][2] += v.z;
+            acc1[r][3] += v.w;
+        }
+#pragma unroll
+        for (int r = 0; r < 3; ++r) {
+            const float4 v = part[(4 + r) * 64 + w.lane];
+            acc2[r][0] += v.x;
+            acc2[r][1] += v.y;
+            acc2[r][2] += v.z;
+            acc2[r][3] += v.w;
+        }
+    }
+    bd_reduce_store<true>(a, w, own, wred, acc1, acc2);
 }
 
 // ---- more than 64 row blocks: passes over 64-block ranges ----
@@ -1237,10 +1353,11 @@ bool xcorr_blockdiag_supported(const XcorrArgs &a)
 constexpr size_t BD_LDS_MAX = 160 * 1024;
 
 // Whole staging LDS: the staged units, then one partial-sum area per wave.
-static size_t bd_whole_lds(const BdArgs &b, int nw)
+static size_t bd_whole_lds(const BdArgs &b, int nw, bool pairs)
 {
     return (size_t)(b.nls + b.S) * b.nb * bd_whole_w(b.wp) * sizeof(float4) +
-           (size_t)nw * bd_red_floats(b.S) * sizeof(float);
+           (size_t)nw * bd_red_floats(b.S) * sizeof(float) +
+           (pairs ? (size_t)(nw / 2) * 7 * 64 * sizeof(float4) : 0);  // the pair kernel's handover area
 }
 
 template <int NW, int J>
@@ -1275,14 +1392,33 @@ static hipError_t launch_whole(BdArgs b, hipStream_t s)
     static std::atomic<uint64_t> lds_allowed{0};
     const hipError_t e = allow_lds_once(&xcorr_bd_whole_kernel<NW>, lds_allowed);
     if (e != hipSuccess) return e;
-    const int dpw = b.wg_sides ? NW / 2 : NW;  // diagonals per workgroup
-    b.n_dgroups = (b.nb + dpw - 1) / dpw;
+    b.wg_sides = 0;
+    b.n_dgroups = (b.nb + NW - 1) / NW;
     bd_set_magic(b);
     const int64_t blocks = (int64_t)b.n_groups * b.n_xtiles * b.n_dgroups * b.n_sides;
     if (blocks > INT32_MAX)  // the kernels number workgroups with 32-bit signed ids
         return hipErrorInvalidConfiguration;
-    const size_t lds = bd_whole_lds(b, NW);
+    const size_t lds = bd_whole_lds(b, NW, false);
     hipLaunchKernelGGL((xcorr_bd_whole_kernel<NW>), dim3((unsigned)blocks), dim3(64 * NW), lds, s, b);
+    return hipGetLastError();
+}
+
+// NW / 2 diagonals per workgroup, each on a pair of waves
+template <int NW>
+static hipError_t launch_whole_pairs(BdArgs b, hipStream_t s)
+{
+    static std::atomic<uint64_t> lds_allowed{0};
+    const hipError_t e = allow_lds_once(&xcorr_bd_whole_pair_kernel<NW>, lds_allowed);
+    if (e != hipSuccess) return e;
+    b.wg_sides = 1;
+    b.n_sides = 1;
+    b.n_dgroups = (b.nb + NW / 2 - 1) / (NW / 2);
+    bd_set_magic(b);
+    const int64_t blocks = (int64_t)b.n_groups * b.n_xtiles * b.n_dgroups;
+    if (blocks > INT32_MAX)
+        return hipErrorInvalidConfiguration;
+    const size_t lds = bd_whole_lds(b, NW, true);
+    hipLaunchKernelGGL((xcorr_bd_whole_pair_kernel<NW>), dim3((unsigned)blocks), dim3(64 * NW), lds, s, b);
     return hipGetLastError();
 }
 
@@ -1379,22 +1515,19 @@ hipError_t xcorr_launch_blockdiag(const XcorrArgs &a, hipStream_t s)
     // are too short to repay staging every column before the first step (the
     // chunked kernel starts after its first J + P columns).
     const int64_t cus = device_cu_count();
-    auto whole_ok = [&](int nw_, int sides) {
+    auto whole_ok = [&](int nw_, int sides, bool pairs = false) {
         if (b.wp < 32) return false;
-        const size_t lds = bd_whole_lds(b, nw_);
+        const size_t lds = bd_whole_lds(b, nw_, pairs);
         if (lds > BD_LDS_MAX) return false;
         const int64_t per_cu = (int64_t)(BD_LDS_MAX / lds);
         const int64_t n_wg = per_side * ((b.nb + nw_ - 1) / nw_) * sides;
         return per_cu * nw_ >= 16 || n_wg <= per_cu * cus;
     };
     // Up to 8 diagonals: 8-wave workgroups, each half walking one dx sign of
-    // the same 4 diagonals (the two signs' walks add up to the same length
-    // for every column tile, so every SIMD gets the same work).
-    if (b.nb <= 8 && whole_ok(8, 2)) {
-        b.n_sides = 1;
-        b.wg_sides = 1;
-        return launch_whole<8>(b, s);
-    }
+    // the same 4 diagonals, the pair of waves of a diagonal sharing its two
+    // walks evenly (at most (wp + P) / 2, rounded up to P, steps each).
+    if (b.nb <= 8 && whole_ok(8, 2, true))
+        return launch_whole_pairs<8>(b, s);
     if (nw == 16 && whole_ok(16, b.n_sides)) return launch_whole<16>(b, s);
     if (nw >= 8 && whole_ok(8, nw == 16 ? 2 : b.n_sides)) {
         if (nw == 16) b.n_sides = 2;  // half the waves per workgroup: keep the wave count
