@@ -3,7 +3,7 @@
 The normalized correlation runs on a 2048-column image (2304-byte pitch) with
 a 4x4 template and the most output rows a 2045-column map may have: 2045 x
 1,050,114 windows, 517 short of the 2^31 - 1 limit, read from an image of
-2.42 GB (rows past the 2^31st byte).  The all-shift correlation runs three
+2.42 GB (rows past the 2^31st byte).  The all-shift correlation runs four
 pair sets whose outputs pass 2^31 elements.  The oracle cannot produce maps of
 this size, so every run is checked on sampled outputs against it (the first
 and last output rows or pairs whole, plus random ones) and on the device over
@@ -127,8 +127,12 @@ def test_ncc_largest_output_peak(ncc_big):
 
 
 @pytest.mark.parametrize("shape,algos", [
-    # (n_left, n_right, rows, cols): 9.9 G, 8.7 G and 8.7 G bytes of output
+    # (n_left, n_right, rows, cols): 9.9 G, 8.6 G, 8.7 G and 8.7 G bytes of
+    # output; the automatic choice runs the chunked block-diagonal kernel on
+    # the first, the whole-staging one (16 waves, every matrix of a pair
+    # group in LDS) on the second, the small-matrix kernel on the others
     ((512, 300, 64, 64), (_lib.XC_XCORR_AUTO,)),
+    ((512, 525, 64, 32), (_lib.XC_XCORR_AUTO,)),
     ((2048, 1100, 16, 16), (_lib.XC_XCORR_AUTO, _lib.XC_XCORR_SMALL)),
     ((8192, 5400, 4, 4), (_lib.XC_XCORR_AUTO, _lib.XC_XCORR_OVERLAP, _lib.XC_XCORR_WAVE)),
 ])
