@@ -68,8 +68,9 @@ def test_xcorr_edge_shapes(shape, algo):
                                    # whole staging, every workgroup resident at once
                                    (32, 32, 32, 32),
                                    # whole staging of 4 x 4 blocks (rows a multiple of 4 columns
-                                   # wide) with a ragged last row block, in both modes: one dx
-                                   # sign per half of the workgroup (up to 8 blocks) and both
+                                   # wide) with a ragged last row block, in both modes: the pair
+                                   # kernel (up to 8 blocks, a diagonal's two dx signs shared by
+                                   # two waves) and one wave walking both signs
                                    (8, 16, 30, 32), (5, 9, 29, 36), (1, 64, 61, 64), (2, 40, 18, 44),
                                    # more than 64 row blocks: passes of 64 blocks; 65 blocks
                                    # (the left window wraps onto itself), odd rows, 2-3 passes,
@@ -84,6 +85,37 @@ def test_xcorr_blockdiag_edge_shapes(shape):
     _gpu.log(f"xcorr blockdiag edge {shape}")
     ref, ab = oracle.xcorr_f32(L, R)
     _gpu.check_xcorr(_gpu.run_xcorr(L, R, _lib.XC_XCORR_BLOCKDIAG), ref, ab)
+
+
+# Shapes the pair kernel takes (up to 8 row blocks, rows of at least 32
+# padded columns, every workgroup resident at once); its two waves of a
+# diagonal share the walks, so the longer dx sign's sums come in two parts.
+PAIR_SHAPES = [(4, 6, 30, 40), (3, 5, 18, 33), (1, 1, 32, 32), (2, 3, 13, 64)]
+
+
+@pytest.mark.parametrize("shape", PAIR_SHAPES, ids=["x".join(map(str, s)) for s in PAIR_SHAPES])
+def test_xcorr_pair_kernel_exact(shape):
+    """Small integers (every partial sum an integer below 2^24, so exact in
+    any order) bit for bit through the block-diagonal and automatic choices,
+    and single ones at opposite corners and inside (orientation) in the last
+    pair of the group."""
+    nl, nr, rows, cols = shape
+    rng = np.random.default_rng(rows * 7 + cols)
+    L = rng.integers(-2, 3, size=(nl, rows, cols)).astype(np.float32)
+    R = rng.integers(-2, 3, size=(nr, rows, cols)).astype(np.float32)
+    ref, _ = oracle.xcorr_f32(L, R)
+    for algo in (_lib.XC_XCORR_BLOCKDIAG, _lib.XC_XCORR_AUTO):
+        _gpu.log(f"xcorr pair kernel {shape} small integers algo={algo}")
+        assert np.array_equal(_gpu.run_xcorr(L, R, algo).astype(np.float64), ref)
+    for (a, b, c, d) in ((0, 0, rows - 1, cols - 1), (rows - 1, cols - 1, 0, 0), (rows // 2, 1, 2, cols - 2)):
+        Ld = np.zeros((nl, rows, cols), np.float32)
+        Rd = np.zeros((nr, rows, cols), np.float32)
+        Ld[-1, a, b] = 1.0
+        Rd[-1, c, d] = 1.0
+        _gpu.log(f"xcorr pair kernel {shape} delta ({a},{b}) ({c},{d})")
+        expect = np.zeros((nl, nr, 2 * rows - 1, 2 * cols - 1), np.float32)
+        expect[-1, -1, a - c + rows - 1, b - d + cols - 1] = 1.0
+        assert np.array_equal(_gpu.run_xcorr(Ld, Rd, _lib.XC_XCORR_BLOCKDIAG), expect)
 
 
 @pytest.mark.parametrize("algo", ALGOS)
