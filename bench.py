@@ -167,9 +167,11 @@ def trial_stats(launch, torch, min_ms=100.0, n_trials=5):
 
 def peak_probes():
     """Measured issue-rate ceilings of v_dot4_u32_u8, v_fmac_f32 (32
-    independent chains per lane) and the two signed-byte MFMA shapes (8 or 4
-    independent accumulators per wave), 2..16 waves per SIMD; the best rate is
-    the measured ceiling."""
+    independent chains per lane; with a literal and one fixed register as the
+    factors, and with both factors drawn from two 4-register vectors, the
+    operand form of the fp32 walks) and the two signed-byte MFMA shapes (8 or
+    4 independent accumulators per wave), 2..16 waves per SIMD; the best rate
+    is the measured ceiling."""
     import ctypes
     from cross_correlation_amd import build as b
 
@@ -179,6 +181,7 @@ def peak_probes():
                                   ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
     res = {}
     for kind, name, per_op in ((0, "dot4_T_per_s", 1.0), (1, "fp32_TFLOP_per_s", 2.0),
+                               (4, "fp32_register_operands_TFLOP_per_s", 2.0),
                                (2, "mfma_i8_16x16x64_TOP_per_s", 1.0), (3, "mfma_i8_32x32x32_TOP_per_s", 1.0)):
         rates = {}
         for w in (2, 4, 8, 16):
@@ -632,8 +635,10 @@ def main():
             out["roofline"]["frac_of_measured_ceiling"] = round(out["roofline"]["achieved"] / ceil, 4)
         if "xcorr" in out:
             ceil = out["measured_ceilings"]["fp32_TFLOP_per_s"]["max"]
+            ceil_r = out["measured_ceilings"]["fp32_register_operands_TFLOP_per_s"]["max"]
             for v in out["xcorr"].values():
                 v["frac_of_measured_ceiling"] = round(v["kernel_gflops"] / 1e3 / ceil, 4)
+                v["frac_of_register_operand_ceiling"] = round(v["kernel_gflops"] / 1e3 / ceil_r, 4)
     if not args.no_cpu_baseline and args.only in ("ncc", "all"):
         import oracle
 

@@ -10,6 +10,11 @@
 //   kind 1: v_fmac_f32    (fp32 fused multiply-add, 2 flops)
 //   kind 2: v_mfma_i32_16x16x64_i8 (16x16x64 signed-byte MACs per wave)
 //   kind 3: v_mfma_i32_32x32x32_i8 (32x32x32 signed-byte MACs per wave)
+//   kind 4: v_fmac_f32 with all three operands in registers: every pairing
+//           of four per-lane left values with four per-lane right values
+//           (all combinations of their register banks), the operand form of
+//           an outer-product walk; kind 1 takes one operand as a literal and
+//           the same register for another, which issues faster
 // (the matrix-core kinds run 8 and 4 independent accumulators per wave).
 // A launch has 64-thread workgroups, `waves_per_simd` per SIMD of every CU.
 #include <hip/hip_runtime.h>
@@ -46,6 +51,32 @@ __global__ __launch_bounds__(64) void fma_probe(uint32_t *out, int iters)
 #pragma unroll
         for (int c = 0; c < CH; ++c) acc[c] = fmaf(a, b, acc[c]);
         a += 1.0f;
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) s += acc[c];
+    out[blockIdx.x * 64 + threadIdx.x] = __float_as_uint(s);
+}
+
+typedef float probe_v4f __attribute__((ext_vector_type(4)));
+
+template <int CH>
+__global__ __launch_bounds__(64) void fma3_probe(uint32_t *out, int iters)
+{
+    probe_v4f x, y;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        x[k] = (float)(threadIdx.x + k);
+        y[k] = 1.0f + (float)(threadIdx.x * 4 + k) * 0x1p-20f;
+    }
+    // each vector in four consecutive registers, as a 16-byte load leaves it
+    asm volatile("" : "+v"(x), "+v"(y));
+    float acc[CH];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) acc[c] = (float)c;
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+        for (int c = 0; c < CH; ++c) acc[c] = fmaf(x[c & 3], y[(c >> 2) & 3], acc[c]);
     }
     float s = 0.0f;
 #pragma unroll
@@ -130,7 +161,7 @@ int xc_rsq_probe(const double *p, double *y, int n)
 int xc_peak_probe(int kind, int waves_per_simd, int iters, int reps, double *ms, double *ops_per_launch)
 {
     constexpr int CH = 32;
-    if (kind < 0 || kind > 3 || waves_per_simd <= 0 || iters <= 0 || reps <= 0 || !ms || !ops_per_launch)
+    if (kind < 0 || kind > 4 || waves_per_simd <= 0 || iters <= 0 || reps <= 0 || !ms || !ops_per_launch)
         return -1;
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess) return -1;
@@ -140,7 +171,7 @@ int xc_peak_probe(int kind, int waves_per_simd, int iters, int reps, double *ms,
     if (hipMalloc(&buf, (size_t)blocks * 64 * sizeof(uint32_t)) != hipSuccess) return -1;
     hipEvent_t e0 = nullptr, e1 = nullptr;
     if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
-        if (e0) hipEventDestroy(e0);
+        if (e0) (void)hipEventDestroy(e0);
         (void)hipFree(buf);
         return -1;
     }
@@ -149,6 +180,8 @@ int xc_peak_probe(int kind, int waves_per_simd, int iters, int reps, double *ms,
             hipLaunchKernelGGL(dot4_probe<CH>, dim3(blocks), dim3(64), 0, 0, buf, iters);
         else if (kind == 1)
             hipLaunchKernelGGL(fma_probe<CH>, dim3(blocks), dim3(64), 0, 0, buf, iters);
+        else if (kind == 4)
+            hipLaunchKernelGGL(fma3_probe<CH>, dim3(blocks), dim3(64), 0, 0, buf, iters);
         else if (kind == 2)
             hipLaunchKernelGGL(mfma16_probe, dim3(blocks), dim3(64), 0, 0, buf, iters);
         else
@@ -158,22 +191,23 @@ int xc_peak_probe(int kind, int waves_per_simd, int iters, int reps, double *ms,
     int st = hipDeviceSynchronize() == hipSuccess ? 0 : -1;
     float t = 0.0f;
     if (st == 0) {
-        hipEventRecord(e0, 0);
+        st = hipEventRecord(e0, 0) == hipSuccess ? 0 : -1;
         for (int r = 0; r < reps; ++r) launch();
-        hipEventRecord(e1, 0);
-        st = (hipEventSynchronize(e1) == hipSuccess && hipEventElapsedTime(&t, e0, e1) == hipSuccess) ? 0 : -1;
+        if (st == 0 && hipEventRecord(e1, 0) != hipSuccess) st = -1;
+        if (st == 0)
+            st = (hipEventSynchronize(e1) == hipSuccess && hipEventElapsedTime(&t, e0, e1) == hipSuccess) ? 0 : -1;
     }
     *ms = (double)t / reps;
-    // lane-operations for kinds 0 and 1; int8 operations (2 per MAC) for the
-    // matrix-core kinds
-    if (kind <= 1)
+    // lane-operations for kinds 0, 1 and 4; int8 operations (2 per MAC) for
+    // the matrix-core kinds
+    if (kind <= 1 || kind == 4)
         *ops_per_launch = (double)blocks * 64 * iters * CH;
     else if (kind == 2)
         *ops_per_launch = (double)blocks * iters * 8 * (16.0 * 16 * 64) * 2;
     else
         *ops_per_launch = (double)blocks * iters * 4 * (32.0 * 32 * 32) * 2;
-    hipEventDestroy(e0);
-    hipEventDestroy(e1);
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
     if (hipFree(buf) != hipSuccess) st = -1;
     return st;
 }
