@@ -590,10 +590,10 @@ def main():
                     "dot4_ilp_q4": _lib.XC_NCC_DOT4_ILP_Q4,
                     "dot4_cols1": _lib.XC_NCC_DOT4_COLS1, "dot4_cols2": _lib.XC_NCC_DOT4_COLS2,
                     "dot4_cols4": _lib.XC_NCC_DOT4_COLS4, "dot4_cols8": _lib.XC_NCC_DOT4_COLS8,
-                    "mfma": _lib.XC_NCC_MFMA, "auto": _lib.XC_NCC_AUTO}
+                    "mfma": _lib.XC_NCC_MFMA, "mfma32": _lib.XC_NCC_MFMA32, "auto": _lib.XC_NCC_AUTO}
         out["ncc_variants"] = {"dot4_ilp": {"kernel_ms": round(r["kernel_ms"], 5), "speedup_vs_dot4_ilp": 1.0}}
         for name, v in variants.items():
-            full = name in ("mfma", "auto")
+            full = name in ("mfma", "mfma32", "auto")
             k = args.steps if full else min(args.steps, 10)
             _, rv = bench_ncc(args, torch, _lib, inputs, variant=v, steps=k, warmup=min(args.warmup, 3),
                               min_ms=100.0 if full else 40.0, n_trials=5 if full else 3)

@@ -37,6 +37,7 @@ XC_NCC_DOT4_COLS1 = 10
 XC_NCC_DOT4_COLS2 = 11
 XC_NCC_DOT4_COLS4 = 12
 XC_NCC_DOT4_COLS8 = 13
+XC_NCC_MFMA32 = 14
 
 XC_NCC_MODE_VALID = 0
 XC_NCC_MODE_SAME = 1

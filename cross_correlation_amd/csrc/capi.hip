@@ -231,6 +231,8 @@ int ncc_dispatch(const xc::NccArgs &a, int variant, hipStream_t s)
         return hip_status(xc::ncc_launch_cols(a, 4, s));
     case XC_NCC_DOT4_COLS8:
         return hip_status(xc::ncc_launch_cols(a, 8, s));
+    case XC_NCC_MFMA32:
+        return hip_status(xc::ncc_launch_mfma32(a, s));
     default:
         return XC_ERR_VARIANT;
     }
@@ -239,8 +241,10 @@ int ncc_dispatch(const xc::NccArgs &a, int variant, hipStream_t s)
 // Variant check done before anything is enqueued.
 int ncc_variant_ok(const xc::NccArgs &a, int variant)
 {
-    if (variant < XC_NCC_AUTO || variant > XC_NCC_DOT4_COLS8)
+    if (variant < XC_NCC_AUTO || variant > XC_NCC_MFMA32)
         return XC_ERR_VARIANT;
+    if (variant == XC_NCC_MFMA32 && !xc::ncc_mfma32_supported(a))
+        return XC_ERR_SHAPE;
     if ((variant == XC_NCC_MFMA || variant == XC_NCC_MFMA_W4) && !xc::ncc_mfma_supported(a, 4))
         return XC_ERR_SHAPE;
     if (variant == XC_NCC_MFMA_W2 && !xc::ncc_mfma_supported(a, 2))

@@ -85,6 +85,10 @@ hipError_t ncc_launch_cols(NccArgs a, int cols, hipStream_t s);
 // tiles, t_width <= 64 only); 0 lets the launcher pick from the grid.
 hipError_t ncc_launch_mfma(NccArgs a, hipStream_t s, int mw = 0);
 bool ncc_mfma_supported(const NccArgs &a, int mw = 0);
+// SumIT on the 32x32x32 i8 matrix cores with the template as the Toeplitz
+// operand; t_width <= 65 and a tile plan within 160 KiB of LDS.
+hipError_t ncc_launch_mfma32(NccArgs a, hipStream_t s);
+bool ncc_mfma32_supported(const NccArgs &a);
 // Best-match search around a correlation launch: set the key to 0 before it,
 // decode the key into (y, x, coefficient) after it.  `peak` points to an
 // xc_ncc_peak (include/xcorr.h).

@@ -140,6 +140,17 @@ int ncc_u8_run(const uint8_t *image, int width, int height, int pitch_bytes,
  *                        per workgroup for every C, so only the independent
  *                        accumulator chains per lane (3 * C) change.  C = 2
  *                        is the page's two columns per thread.
+ *   XC_NCC_MFMA32        SumIT on the 32x32x32 signed-byte matrix cores with
+ *                        the operands turned round: the image rows as they
+ *                        are staged (no byte shifts) against the template
+ *                        row shifted by each output column (the Toeplitz
+ *                        operand), 32 x 256 outputs per workgroup, template
+ *                        rows split over four waves; SumI and SumISq as
+ *                        sliding sums in four waves beside them.  An
+ *                        ablation point (slower than XC_NCC_MFMA on the
+ *                        shapes measured).  t_width <= 65 and templates
+ *                        short enough for the tile's LDS plan (136 rows at
+ *                        width 64), else XC_ERR_SHAPE.
  */
 #define XC_NCC_AUTO 0
 #define XC_NCC_DOT4_ILP 1
@@ -155,6 +166,7 @@ int ncc_u8_run(const uint8_t *image, int width, int height, int pitch_bytes,
 #define XC_NCC_DOT4_COLS2 11
 #define XC_NCC_DOT4_COLS4 12
 #define XC_NCC_DOT4_COLS8 13
+#define XC_NCC_MFMA32 14
 int ncc_u8_run_variant(const uint8_t *image, int width, int height, int pitch_bytes,
                        const uint8_t *tmpl, int t_width, int t_height,
                        uint32_t *sum_i, uint32_t *sum_isq, uint32_t *sum_it, float *coef,

@@ -19,6 +19,31 @@ GUARD = 4096  # elements of canary band on each side
 U32_SENTINEL = np.uint32(0xDEADBEEF)
 
 
+# Template widths the matrix-core variants take (their LDS limits on tall
+# templates are not reached by the shapes the tests use).
+MFMA_MAX_T_WIDTH = {_lib.XC_NCC_MFMA: 256, _lib.XC_NCC_MFMA_W4: 256, _lib.XC_NCC_MFMA_W2: 64}
+
+
+def mfma32_fits(th: int, tw: int) -> bool:
+    """Whether XC_NCC_MFMA32 takes a th x tw template: t_width <= 65 and its
+    tile plan (staged image rows, padded template rows, helper batches, window
+    sums) within 160 KiB of LDS, as the library computes it."""
+    if tw > 65:
+        return False
+    nkb = 2 if tw < 2 else (tw + 62) // 32
+    s = 32 * (8 + nkb - 1) + 16
+    img = -(-max((32 + th) * s, 32 * 264 * 4) // 16) * 16
+    tpl = (th + 1) * (32 * nkb + 48)
+    return img + tpl + 4 * 4 * 324 * 4 + 2 * 32 * 260 * 4 + 16 <= 160 * 1024
+
+
+def ncc_takes(variant: int, th: int, tw: int) -> bool:
+    """Whether a u8 variant takes the template shape (else XC_ERR_SHAPE)."""
+    if variant == _lib.XC_NCC_MFMA32:
+        return mfma32_fits(th, tw)
+    return tw <= MFMA_MAX_T_WIDTH.get(variant, tw)
+
+
 def log(msg: str) -> None:
     print(msg, flush=True)
     sys.stdout.flush()

@@ -57,7 +57,7 @@ FAKE = 1 << 20  # a 16-byte aligned non-null address; never dereferenced (valida
     (dict(pitch=72), _lib.XC_ERR_ALIGN),
     (dict(coef=FAKE + 2), _lib.XC_ERR_ALIGN),
     (dict(variant=42), _lib.XC_ERR_VARIANT),
-    (dict(variant=_lib.XC_NCC_DOT4_COLS8 + 1), _lib.XC_ERR_VARIANT),
+    (dict(variant=_lib.XC_NCC_MFMA32 + 1), _lib.XC_ERR_VARIANT),
     # the matrix-core tile widths: 128 columns only for templates up to 64 wide
     (dict(t_width=68, width=200, pitch=208, variant=_lib.XC_NCC_MFMA_W2), _lib.XC_ERR_SHAPE),
     (dict(t_width=300, width=400, pitch=400, variant=_lib.XC_NCC_MFMA_W4), _lib.XC_ERR_SHAPE),

@@ -17,9 +17,7 @@ pytestmark = pytest.mark.gpu
 VARIANTS = [_lib.XC_NCC_AUTO, _lib.XC_NCC_DOT4_ILP, _lib.XC_NCC_DOT4_C1, _lib.XC_NCC_SCALAR_C1, _lib.XC_NCC_MFMA,
             _lib.XC_NCC_DOT4_ILP_Q1, _lib.XC_NCC_DOT4_ILP_Q2, _lib.XC_NCC_DOT4_ILP_Q4, _lib.XC_NCC_MFMA_W4,
             _lib.XC_NCC_MFMA_W2, _lib.XC_NCC_DOT4_COLS1, _lib.XC_NCC_DOT4_COLS2, _lib.XC_NCC_DOT4_COLS4,
-            _lib.XC_NCC_DOT4_COLS8]
-# template rows the matrix-core variants take (256- and 128-column tiles)
-MFMA_MAX_T_WIDTH = {_lib.XC_NCC_MFMA: 256, _lib.XC_NCC_MFMA_W4: 256, _lib.XC_NCC_MFMA_W2: 64}
+            _lib.XC_NCC_DOT4_COLS8, _lib.XC_NCC_MFMA32]
 
 
 def _case_from(img, tmpl, name="t", pitch=None):
@@ -76,7 +74,8 @@ def test_ncc_1080p_small_templates_auto(th, tw):
 @pytest.mark.parametrize("variant", [_lib.XC_NCC_DOT4_ILP, _lib.XC_NCC_DOT4_C1, _lib.XC_NCC_SCALAR_C1, _lib.XC_NCC_MFMA,
                                      _lib.XC_NCC_DOT4_ILP_Q1, _lib.XC_NCC_DOT4_ILP_Q2, _lib.XC_NCC_DOT4_ILP_Q4,
                                      _lib.XC_NCC_MFMA_W4, _lib.XC_NCC_MFMA_W2, _lib.XC_NCC_DOT4_COLS1,
-                                     _lib.XC_NCC_DOT4_COLS2, _lib.XC_NCC_DOT4_COLS4, _lib.XC_NCC_DOT4_COLS8])
+                                     _lib.XC_NCC_DOT4_COLS2, _lib.XC_NCC_DOT4_COLS4, _lib.XC_NCC_DOT4_COLS8,
+                                     _lib.XC_NCC_MFMA32])
 def test_ncc_1080p_variants_sampled(variant):
     """Ablation variants at full size: compare against the auto path bit for bit."""
     case = workload("ncc_1920x1080_t64")
@@ -180,7 +179,7 @@ def test_ncc_edge_shapes(shape, variant):
     tmpl = u8_uniform(rng, (th, tw))
     case = _case_from(img, tmpl, pitch=pitch_for(w) + extra)
     _gpu.log(f"ncc edge shape {shape} variant={variant}")
-    if tw > MFMA_MAX_T_WIDTH.get(variant, tw):
+    if not _gpu.ncc_takes(variant, th, tw):
         with pytest.raises(_lib.XcError) as e:
             _gpu.run_ncc(case, variant)
         assert e.value.status == _lib.XC_ERR_SHAPE

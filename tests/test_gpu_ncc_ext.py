@@ -27,14 +27,16 @@ VARIANTS = {
     "cols2": _lib.XC_NCC_DOT4_COLS2,
     "cols4": _lib.XC_NCC_DOT4_COLS4,
     "cols8": _lib.XC_NCC_DOT4_COLS8,
+    "mfma32": _lib.XC_NCC_MFMA32,
 }
 # template rows the matrix-core variants take (256- and 128-column tiles)
 MAX_T_WIDTH = {"mfma": 256, "mfma_w4": 256, "mfma_w2": 64}
 
 
 def _variants(case):
-    """Every variant that takes the case's template width."""
-    return {k: v for k, v in VARIANTS.items() if case.t_width <= MAX_T_WIDTH.get(k, case.t_width)}
+    """Every variant that takes the case's template shape."""
+    return {k: v for k, v in VARIANTS.items()
+            if case.t_width <= MAX_T_WIDTH.get(k, case.t_width) and _gpu.ncc_takes(v, case.t_height, case.t_width)}
 
 
 # (height, width, t_height, t_width): widths below four, odd and even

@@ -19,8 +19,7 @@ pytestmark = pytest.mark.gpu
 NCC_VARIANTS = [_lib.XC_NCC_AUTO, _lib.XC_NCC_DOT4_ILP, _lib.XC_NCC_DOT4_C1, _lib.XC_NCC_SCALAR_C1,
                 _lib.XC_NCC_MFMA, _lib.XC_NCC_MFMA_W4, _lib.XC_NCC_MFMA_W2, _lib.XC_NCC_DOT4_ILP_Q1,
                 _lib.XC_NCC_DOT4_ILP_Q2, _lib.XC_NCC_DOT4_ILP_Q4, _lib.XC_NCC_DOT4_COLS1, _lib.XC_NCC_DOT4_COLS2,
-                _lib.XC_NCC_DOT4_COLS4, _lib.XC_NCC_DOT4_COLS8]
-MFMA_MAX_T_WIDTH = {_lib.XC_NCC_MFMA: 256, _lib.XC_NCC_MFMA_W4: 256, _lib.XC_NCC_MFMA_W2: 64}
+                _lib.XC_NCC_DOT4_COLS4, _lib.XC_NCC_DOT4_COLS8, _lib.XC_NCC_MFMA32]
 XCORR_ALGOS = [_lib.XC_XCORR_AUTO, _lib.XC_XCORR_OVERLAP, _lib.XC_XCORR_BLOCKDIAG, _lib.XC_XCORR_WAVE,
                _lib.XC_XCORR_SMALL]
 
@@ -54,7 +53,7 @@ def test_ncc_random_shape_all_variants(seed):
     ref = None
     for v in NCC_VARIANTS:
         _gpu.log(f"ncc random seed {seed}: image {h}x{w} (pitch {pitch}), template {th}x{tw}, variant {v}")
-        if tw > MFMA_MAX_T_WIDTH.get(v, tw):
+        if not _gpu.ncc_takes(v, th, tw):
             with pytest.raises(_lib.XcError) as e:
                 _gpu.run_ncc(case, v)
             assert e.value.status == _lib.XC_ERR_SHAPE
@@ -113,7 +112,7 @@ def test_ncc_modes_random_shape(seed):
     for mode in (_lib.XC_NCC_MODE_SAME, _lib.XC_NCC_MODE_FULL):
         ref = oracle.ncc_u8_mode(case.image, case.width, case.height, case.tmpl, mode)
         for v in (_lib.XC_NCC_AUTO, other):
-            if tw > MFMA_MAX_T_WIDTH.get(v, tw):
+            if not _gpu.ncc_takes(v, th, tw):
                 continue
             _gpu.log(f"ncc mode {mode} random seed {seed}: image {h}x{w}, template {th}x{tw}, variant {v}")
             _check(run_mode(case, mode, v), ref)
@@ -139,7 +138,7 @@ def test_ncc_peak_random_shape(seed):
     ref = oracle.ncc_u8(case.image, case.width, case.height, case.tmpl)
     other = NCC_VARIANTS[1 + int(rng.integers(0, len(NCC_VARIANTS) - 1))]
     for v in (_lib.XC_NCC_AUTO, other):
-        if tw > MFMA_MAX_T_WIDTH.get(v, tw):
+        if not _gpu.ncc_takes(v, th, tw):
             continue
         _gpu.log(f"ncc peak random seed {seed}: image {h}x{w}, template {th}x{tw}, variant {v}")
         got, maps = _run_peak(case, v, outputs=("coef",))
