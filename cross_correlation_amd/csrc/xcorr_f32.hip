@@ -431,6 +431,119 @@ __global__ __launch_bounds__(256) void xcorr_small_kernel(SmallArgs sa)
     }
 }
 
+// Tiny matrices: both dimensions at most 16 (the many-pair groupings of
+// small matrices).  A group of LC = 1 << LCS adjacent lanes owns one pair and
+// one row shift dy and computes the whole output row: all 2 cols - 1 column
+// shifts.  Lane c of the group takes the rows i = i0 + c, i0 + c + LC, ...
+// where both matrices exist (at most RM of them), loads every one of those
+// rows of both matrices before any product (left row i + dy, right row i; M
+// values each, zero past the matrix, 16-byte loads when rows are whole
+// float4s), then adds left[j + dx] * right[j] for every j and shift dx, each
+// product at a compile-time register (M^2 per row pair, none against the
+// padding when cols == M).  The group's lanes add their sums in a fixed
+// butterfly.  Consecutive groups are consecutive output rows (pair-major,
+// then dy), so a wave's output is one contiguous span: lane c puts the shifts
+// k = c, c + LC, ... of its group's row into the wave's LDS area, and the
+// wave stores the span with consecutive lanes on consecutive floats.  Index
+// math in 32 bits (the launcher checks the range).
+struct TinyArgs {
+    XcorrArgs x;
+    uint32_t ngroups;  // pairs * (2 rows - 1)
+};
+
+template <int M, bool VEC>
+__device__ __forceinline__ void tiny_row(const float *__restrict__ p, int cols, bool ok, float (&v)[M])
+{
+    if (VEC) {
+#pragma unroll
+        for (int q = 0; q < M / 4; ++q) {
+            const float4 f = reinterpret_cast<const float4 *>(p)[q];
+            v[4 * q] = ok ? f.x : 0.0f;
+            v[4 * q + 1] = ok ? f.y : 0.0f;
+            v[4 * q + 2] = ok ? f.z : 0.0f;
+            v[4 * q + 3] = ok ? f.w : 0.0f;
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < M; ++q) {
+            const float f = p[q < cols ? q : 0];
+            v[q] = ok && q < cols ? f : 0.0f;
+        }
+    }
+}
+
+template <int M, int LCS, int RM, bool VEC>
+__global__ __launch_bounds__(256) void xcorr_tiny_kernel(TinyArgs ta)
+{
+    constexpr int LC = 1 << LCS, NS = 2 * M - 1, GW = 64 / LC;  // groups per wave
+    __shared__ float stage[4][GW * NS];  // each wave's output rows, as stored
+    const XcorrArgs &a = ta.x;
+    const int rows = a.rows, cols = a.cols;
+    const uint32_t t = blockIdx.x * 256u + threadIdx.x;
+    const uint32_t grp = t >> LCS;
+    const int lane = threadIdx.x & 63;
+    const uint32_t g0 = (t - lane) >> LCS;  // the wave's first group
+    if (g0 >= ta.ngroups)  // the whole wave is past the last group
+        return;
+    const bool live = grp < ta.ngroups;  // whole groups: LC divides 64
+    const int c = (int)(t & (LC - 1));
+    const uint32_t nd = 2u * rows - 1u;
+    const uint32_t pair = (live ? grp : g0) / nd;  // dead lanes compute a live group's row, never stored
+    const int dy = (int)((live ? grp : g0) - pair * nd) - (rows - 1);
+    const uint32_t l = pair / (uint32_t)a.n_right;
+    const uint32_t r = pair - l * (uint32_t)a.n_right;
+    const float *L = a.left + (size_t)l * rows * cols;
+    const float *R = a.right + (size_t)r * rows * cols;
+    const int i0 = max(0, -dy), i1 = min(rows, rows - dy);  // rows where both exist
+    float lv[RM][M], rv[RM][M];
+#pragma unroll
+    for (int q = 0; q < RM; ++q) {
+        const int i = i0 + c + q * LC;
+        const bool ok = i < i1;
+        const int ii = ok ? i : i0;  // a row that exists; zeroed below
+        tiny_row<M, VEC>(L + (size_t)(ii + dy) * cols, cols, ok, lv[q]);
+        tiny_row<M, VEC>(R + (size_t)ii * cols, cols, ok, rv[q]);
+    }
+    float acc[NS];
+#pragma unroll
+    for (int k = 0; k < NS; ++k)
+        acc[k] = 0.0f;
+#pragma unroll
+    for (int q = 0; q < RM; ++q)
+#pragma unroll
+        for (int j = 0; j < M; ++j)
+#pragma unroll
+            for (int k = 0; k < NS; ++k) {
+                const int e = j + k - (M - 1);  // left element j + dx, dx = k - (M - 1)
+                if (e >= 0 && e < M)
+                    acc[k] = fmaf(lv[q][e], rv[q][j], acc[k]);
+            }
+#pragma unroll
+    for (int off = 1; off < LC; off <<= 1)
+#pragma unroll
+        for (int k = 0; k < NS; ++k)
+            acc[k] += __shfl_xor(acc[k], off);
+    // the wave's groups are consecutive output rows, i.e. one contiguous
+    // span: each group's row goes to the wave's LDS area, then the wave
+    // stores the span with consecutive lanes on consecutive floats
+    const int ow = 2 * cols - 1, k0 = M - cols;  // acc[k0 + x] is output column x
+    float *const st = stage[threadIdx.x >> 6];
+    const int gl = lane >> LCS;
+#pragma unroll
+    for (int k = 0; k < NS; ++k) {
+        const int x = k - k0;
+        if ((k & (LC - 1)) == c && x >= 0 && x < ow)
+            st[gl * ow + x] = acc[k];
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): one wave's LDS requests complete in order
+    __builtin_amdgcn_wave_barrier();
+    const uint32_t nv = min((uint32_t)GW, ta.ngroups - g0);
+    const int span = (int)nv * ow;
+    float *const o = a.out + (size_t)g0 * ow;
+    for (int e = lane; e < span; e += 64)
+        o[e] = st[e];
+}
+
 // Template size of the register dimension for a shape (0 when neither
 // dimension is at most 16) and whether lines are columns.
 static int small_m(const XcorrArgs &a, bool &tr)
@@ -448,8 +561,57 @@ bool xcorr_small_supported(const XcorrArgs &a)
     return small_m(a, tr) > 0;
 }
 
+// Launch of the tiny kernel for lcs (lanes per group 1 << lcs) and rm row
+// slots per lane.
+template <int M, bool VEC>
+static hipError_t tiny_launch_m(const TinyArgs &ta, int lcs, int rm, hipStream_t s)
+{
+    const uint64_t threads = (uint64_t)ta.ngroups << lcs;
+    const dim3 g((unsigned)((threads + 255) / 256)), b(256);
+    switch (lcs * 8 + rm) {
+    case 0 * 8 + 1: hipLaunchKernelGGL((xcorr_tiny_kernel<M, 0, 1, VEC>), g, b, 0, s, ta); break;
+    case 1 * 8 + 1: hipLaunchKernelGGL((xcorr_tiny_kernel<M, 1, 1, VEC>), g, b, 0, s, ta); break;
+    case 1 * 8 + 2: hipLaunchKernelGGL((xcorr_tiny_kernel<M, 1, 2, VEC>), g, b, 0, s, ta); break;
+    case 2 * 8 + 1: hipLaunchKernelGGL((xcorr_tiny_kernel<M, 2, 1, VEC>), g, b, 0, s, ta); break;
+    case 2 * 8 + 2: hipLaunchKernelGGL((xcorr_tiny_kernel<M, 2, 2, VEC>), g, b, 0, s, ta); break;
+    case 2 * 8 + 3: hipLaunchKernelGGL((xcorr_tiny_kernel<M, 2, 3, VEC>), g, b, 0, s, ta); break;
+    case 3 * 8 + 2: hipLaunchKernelGGL((xcorr_tiny_kernel<M, 3, 2, VEC>), g, b, 0, s, ta); break;
+    default: hipLaunchKernelGGL((xcorr_tiny_kernel<M, 2, 4, VEC>), g, b, 0, s, ta); break;
+    }
+    return hipGetLastError();
+}
+
+static hipError_t xcorr_launch_tiny(const XcorrArgs &a, hipStream_t s)
+{
+    const int rows = a.rows, cols = a.cols;
+    const int M = cols <= 4 ? 4 : cols <= 8 ? 8 : cols <= 12 ? 12 : 16;
+    const bool vec = cols == M;  // rows of whole float4s (bases are 16-byte aligned)
+    // lanes per group: 1 for one row, 2 up to 3 rows, else 4, and 8 from 9
+    // rows when four lanes per group would give fewer than 64K threads (short
+    // chains on more waves); row slots per lane
+    const uint64_t ngroups = (uint64_t)a.n_left * a.n_right * (2 * rows - 1);
+    const int lcs = rows == 1 ? 0 : rows <= 3 ? 1 : (rows >= 9 && (ngroups << 2) < 65536) ? 3 : 2;
+    const int rm = (rows + (1 << lcs) - 1) >> lcs;
+    const TinyArgs ta{a, (uint32_t)ngroups};
+    switch (M * 2 + (vec ? 1 : 0)) {
+    case 8: return tiny_launch_m<4, false>(ta, lcs, rm, s);
+    case 9: return tiny_launch_m<4, true>(ta, lcs, rm, s);
+    case 16: return tiny_launch_m<8, false>(ta, lcs, rm, s);
+    case 17: return tiny_launch_m<8, true>(ta, lcs, rm, s);
+    case 24: return tiny_launch_m<12, false>(ta, lcs, rm, s);
+    case 25: return tiny_launch_m<12, true>(ta, lcs, rm, s);
+    case 32: return tiny_launch_m<16, false>(ta, lcs, rm, s);
+    default: return tiny_launch_m<16, true>(ta, lcs, rm, s);
+    }
+}
+
 hipError_t xcorr_launch_small(const XcorrArgs &a, hipStream_t s)
 {
+    // both dimensions at most 16, groups and threads within 32-bit indices:
+    // the tiny kernel
+    if (a.rows <= 16 && a.cols <= 16 &&
+        ((uint64_t)a.n_left * a.n_right * (2 * a.rows - 1) << 3) < ((uint64_t)1 << 31))
+        return xcorr_launch_tiny(a, s);
     bool tr;
     const int M = small_m(a, tr);
     const int n = tr ? a.cols : a.rows;

@@ -308,15 +308,20 @@ int xcorr_f32_run(const float *left, int n_left, const float *right, int n_right
  *                        added across the wave in a fixed order (the JPDC
  *                        README's warp-per-overlap variant, for large
  *                        overlaps; no data reuse between shifts)
- *   XC_XCORR_SMALL       matrices with rows <= 16 or cols <= 16: a group of
- *                        1 to 64 lanes (more for longer loops) owns one pair,
- *                        one shift along the other dimension and 8 shifts
- *                        along the small one; each lane keeps two lines
- *                        (rows, or columns) in registers, each value serving
- *                        up to 8 products, over its share of the lines, and
- *                        the group adds its partial sums in a fixed order;
- *                        XC_ERR_SHAPE for larger matrices.  XC_XCORR_AUTO
- *                        takes BLOCKDIAG from 13 rows, this below.
+ *   XC_XCORR_SMALL       matrices with rows <= 16 or cols <= 16.  When both
+ *                        are: a group of 1 to 8 lanes owns one pair and one
+ *                        row shift and computes the whole output row, each
+ *                        lane loading its share of the rows of both matrices
+ *                        before any product; a wave's output rows are stored
+ *                        as one contiguous span.  Otherwise a group of 1 to
+ *                        64 lanes (more for longer loops) owns one pair, one
+ *                        shift along the long dimension and 8 shifts along
+ *                        the short one, each lane keeping two lines (rows or
+ *                        columns) in registers, each value serving up to 8
+ *                        products.  Either way the group adds its partial
+ *                        sums in a fixed order; XC_ERR_SHAPE for larger
+ *                        matrices.  XC_XCORR_AUTO takes BLOCKDIAG from 13
+ *                        rows, this below.
  */
 #define XC_XCORR_AUTO 0
 #define XC_XCORR_OVERLAP 1

@@ -342,3 +342,29 @@ def test_xcorr_small_exact_and_orientation():
         import torch
         api.xcorr_f32(torch.from_numpy(L).cuda(), torch.from_numpy(L).cuda(), algo=_lib.XC_XCORR_SMALL)
     assert e.value.status == _lib.XC_ERR_SHAPE
+
+
+# Both dimensions at most 16 take the tiny-matrix kernel; these shapes reach
+# each of its launched instances: lanes per group 1, 2, 4 or 8 with 1 to 4 row
+# slots per lane, register widths 4, 8, 12 and 16, rows of whole float4s or
+# not (cols below the register width).
+TINY_SHAPES = [  # (rows, cols, n_left, n_right)
+    (1, 16, 5, 7), (2, 8, 3, 4), (3, 4, 2, 2), (4, 4, 3, 5), (6, 16, 8, 8), (7, 13, 4, 3),
+    (9, 12, 40, 30), (11, 5, 40, 30), (13, 3, 40, 30), (16, 16, 40, 30), (10, 8, 4, 4), (15, 14, 2, 3),
+]
+
+
+@pytest.mark.parametrize("shape", TINY_SHAPES, ids=["x".join(map(str, s)) for s in TINY_SHAPES])
+def test_xcorr_tiny_instances(shape):
+    rows, cols, nl, nr = shape
+    rng = np.random.default_rng(2200 + rows * 17 + cols)
+    L = f32_uniform(rng, (nl, rows, cols))
+    R = f32_uniform(rng, (nr, rows, cols))
+    _gpu.log(f"xcorr tiny {nl}x{nr} pairs of {rows}x{cols}")
+    ref, ab = oracle.xcorr_f32(L, R)
+    _gpu.check_xcorr(_gpu.run_xcorr(L, R, _lib.XC_XCORR_SMALL), ref, ab)
+    # small integers: every product and sum exact, in any order
+    Li = rng.integers(-3, 4, size=(nl, rows, cols)).astype(np.float32)
+    Ri = rng.integers(-3, 4, size=(nr, rows, cols)).astype(np.float32)
+    refi, _ = oracle.xcorr_f32(Li, Ri)
+    assert np.array_equal(_gpu.run_xcorr(Li, Ri, _lib.XC_XCORR_SMALL).astype(np.float64), refi)
