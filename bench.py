@@ -415,6 +415,19 @@ def bench_xcorr(args, torch, lib, inputs, oracle_mod=None):
             "frac_of_157.3T": round(flop / (per * 1e-3) / FP32_PEAK, 4),
             "flop_per_step": flop,
         }
+        # the same workload through each algorithm that takes it
+        algos = {"blockdiag": lib.XC_XCORR_BLOCKDIAG, "mfma": lib.XC_XCORR_MFMA}
+        res[name]["algos"] = {}
+        for an, av in algos.items():
+            def launch_a(av=av):
+                st = lib.xcorr_f32_run(*p, stream=stream, algo=av)
+                if st != 0:
+                    raise RuntimeError(lib.status_str(st))
+            if lib.xcorr_f32_run(*p, stream=stream, algo=av) != 0:
+                continue
+            tra = trial_stats(launch_a, torch, min_ms=min(args.trial_ms, 40.0), n_trials=3)
+            res[name]["algos"][an] = {"kernel_ms": round(tra["median_ms"], 5),
+                                      "frac_of_157.3T": round(flop / (tra["median_ms"] * 1e-3) / FP32_PEAK, 4)}
         if oracle_mod is not None:
             res[name]["cpu_baseline"] = cpu_baseline_xcorr(args, c, oracle_mod)
     return res

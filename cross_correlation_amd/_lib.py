@@ -48,6 +48,7 @@ XC_XCORR_OVERLAP = 1
 XC_XCORR_BLOCKDIAG = 2
 XC_XCORR_WAVE = 3
 XC_XCORR_SMALL = 4
+XC_XCORR_MFMA = 5
 
 XC_NCC_MAX_TEMPLATE_PIXELS = 66051
 

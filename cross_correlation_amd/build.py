@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libxcorr_hip.so")
-SOURCES = ["capi.hip", "ncc_u8.hip", "ncc_u8_mfma.hip", "ncc_u8_mfma32.hip", "ncc_pad.hip", "xcorr_f32.hip"]
+SOURCES = ["capi.hip", "ncc_u8.hip", "ncc_u8_mfma.hip", "ncc_u8_mfma32.hip", "ncc_pad.hip", "xcorr_f32.hip", "xcorr_mfma.hip"]
 # Issue-rate probes used only by the bench harness (not part of the ABI).
 PEAK_LIB = os.path.join(HERE, "libxcorr_peak.so")
 PEAK_SOURCES = ["peak_probe.hip"]

@@ -452,6 +452,10 @@ int xcorr_f32_run_algo(const float *left, int n_left, const float *right, int n_
         if (!xc::xcorr_blockdiag_supported(a))
             return XC_ERR_SHAPE;
         return hip_status(xc::xcorr_launch_blockdiag(a, s));
+    case XC_XCORR_MFMA:
+        if (!xc::xcorr_mfma_supported(a))
+            return XC_ERR_SHAPE;
+        return hip_status(xc::xcorr_launch_mfma(a, s));
     default:
         return XC_ERR_VARIANT;
     }

@@ -116,5 +116,10 @@ hipError_t xcorr_launch_small(const XcorrArgs &a, hipStream_t s);
 bool xcorr_small_supported(const XcorrArgs &a);
 hipError_t xcorr_launch_blockdiag(const XcorrArgs &a, hipStream_t s);
 bool xcorr_blockdiag_supported(const XcorrArgs &a);
+// fp32 matrix cores (v_mfma_f32_16x16x4f32), one 16 x 16 tile of shifts per
+// workgroup; cols % 4 == 0 and a staging plan within its per-thread items
+// and the LDS.
+hipError_t xcorr_launch_mfma(const XcorrArgs &a, hipStream_t s);
+bool xcorr_mfma_supported(const XcorrArgs &a);
 
 } // namespace xc

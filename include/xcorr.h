@@ -322,12 +322,22 @@ int xcorr_f32_run(const float *left, int n_left, const float *right, int n_right
  *                        sums in a fixed order; XC_ERR_SHAPE for larger
  *                        matrices.  XC_XCORR_AUTO takes BLOCKDIAG from 13
  *                        rows, this below.
+ *   XC_XCORR_MFMA        the fp32 matrix cores (v_mfma_f32_16x16x4f32): for
+ *                        each left row u, the contribution to all shifts is a
+ *                        matrix product of the right rows u - dy and the left
+ *                        row u shifted by dx; one 16 x 16 tile of shifts per
+ *                        workgroup, its left rows split over four waves and
+ *                        added in a fixed order.  An ablation point (slower
+ *                        than BLOCKDIAG on the groupings measured).
+ *                        XC_ERR_SHAPE unless cols is a multiple of 4 and the
+ *                        tile's staging fits (cols up to about 340).
  */
 #define XC_XCORR_AUTO 0
 #define XC_XCORR_OVERLAP 1
 #define XC_XCORR_BLOCKDIAG 2
 #define XC_XCORR_WAVE 3
 #define XC_XCORR_SMALL 4
+#define XC_XCORR_MFMA 5
 int xcorr_f32_run_algo(const float *left, int n_left, const float *right, int n_right,
                        int rows, int cols, float *out, int algo, void *stream);
 

@@ -21,7 +21,7 @@ NCC_VARIANTS = [_lib.XC_NCC_AUTO, _lib.XC_NCC_DOT4_ILP, _lib.XC_NCC_DOT4_C1, _li
                 _lib.XC_NCC_DOT4_ILP_Q2, _lib.XC_NCC_DOT4_ILP_Q4, _lib.XC_NCC_DOT4_COLS1, _lib.XC_NCC_DOT4_COLS2,
                 _lib.XC_NCC_DOT4_COLS4, _lib.XC_NCC_DOT4_COLS8, _lib.XC_NCC_MFMA32]
 XCORR_ALGOS = [_lib.XC_XCORR_AUTO, _lib.XC_XCORR_OVERLAP, _lib.XC_XCORR_BLOCKDIAG, _lib.XC_XCORR_WAVE,
-               _lib.XC_XCORR_SMALL]
+               _lib.XC_XCORR_SMALL, _lib.XC_XCORR_MFMA]
 
 
 def _ncc_shape(seed):
@@ -79,7 +79,8 @@ def test_xcorr_random_shape_all_algorithms(seed):
     for algo in XCORR_ALGOS:
         _gpu.log(f"xcorr random seed {seed}: {nl}x{nr} pairs of {rows}x{cols}, algorithm {algo}")
         supported = {_lib.XC_XCORR_BLOCKDIAG: (rows + 3) // 4 >= 4,
-                     _lib.XC_XCORR_SMALL: _small_supported(rows, cols)}.get(algo, True)
+                     _lib.XC_XCORR_SMALL: _small_supported(rows, cols),
+                     _lib.XC_XCORR_MFMA: cols % 4 == 0}.get(algo, True)
         if not supported:
             with pytest.raises(_lib.XcError) as e:
                 _gpu.run_xcorr(L, R, algo)
