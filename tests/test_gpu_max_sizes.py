@@ -95,7 +95,8 @@ def _check_ncc_maps(b):
 
 
 @pytest.mark.parametrize("variant", [_lib.XC_NCC_AUTO, _lib.XC_NCC_DOT4_ILP, _lib.XC_NCC_DOT4_C1,
-                                     _lib.XC_NCC_SCALAR_C1, _lib.XC_NCC_MFMA_W4, _lib.XC_NCC_MFMA_W2])
+                                     _lib.XC_NCC_SCALAR_C1, _lib.XC_NCC_MFMA_W4, _lib.XC_NCC_MFMA_W2,
+                                     _lib.XC_NCC_MFMA32])
 def test_ncc_largest_output(ncc_big, variant):
     """2,147,483,130 windows: the 64-bit image and output offsets, the grids
     of over 65,535 row tiles, and the last rows of the image."""
@@ -129,9 +130,10 @@ def test_ncc_largest_output_peak(ncc_big):
 @pytest.mark.parametrize("shape,algos", [
     # (n_left, n_right, rows, cols): 9.9 G, 8.6 G, 8.7 G and 8.7 G bytes of
     # output; the automatic choice runs the chunked block-diagonal kernel on
-    # the first, the whole-staging one (16 waves, every matrix of a pair
-    # group in LDS) on the second, the small-matrix kernel on the others
-    ((512, 300, 64, 64), (_lib.XC_XCORR_AUTO,)),
+    # the first (also run on the fp32 matrix cores), the whole-staging one (16
+    # waves, every matrix of a pair group in LDS) on the second, the
+    # tiny-matrix kernel on the third and the small-matrix kernel on the last
+    ((512, 300, 64, 64), (_lib.XC_XCORR_AUTO, _lib.XC_XCORR_MFMA)),
     ((512, 525, 64, 32), (_lib.XC_XCORR_AUTO,)),
     ((2048, 1100, 16, 16), (_lib.XC_XCORR_AUTO, _lib.XC_XCORR_SMALL)),
     ((8192, 5400, 4, 4), (_lib.XC_XCORR_AUTO, _lib.XC_XCORR_OVERLAP, _lib.XC_XCORR_WAVE)),
