@@ -61,6 +61,10 @@ FAKE = 1 << 20  # a 16-byte aligned non-null address; never dereferenced (valida
     # the matrix-core tile widths: 128 columns only for templates up to 64 wide
     (dict(t_width=68, width=200, pitch=208, variant=_lib.XC_NCC_MFMA_W2), _lib.XC_ERR_SHAPE),
     (dict(t_width=300, width=400, pitch=400, variant=_lib.XC_NCC_MFMA_W4), _lib.XC_ERR_SHAPE),
+    # the 32x32x32 recast: rows up to 65 bytes, templates short enough for its LDS plan
+    (dict(t_width=66, width=200, pitch=208, variant=_lib.XC_NCC_MFMA32), _lib.XC_ERR_SHAPE),
+    (dict(t_width=64, t_height=137, width=200, height=200, pitch=208, variant=_lib.XC_NCC_MFMA32),
+     _lib.XC_ERR_SHAPE),
     (dict(variant=-1), _lib.XC_ERR_VARIANT),
 ])
 def test_ncc_validation(args, expect):
@@ -104,7 +108,11 @@ def test_decode_peak_layout():
     (dict(left=FAKE + 8), _lib.XC_ERR_ALIGN),
     (dict(out=FAKE + 2), _lib.XC_ERR_ALIGN),
     (dict(algo=9), _lib.XC_ERR_VARIANT),
+    (dict(algo=_lib.XC_XCORR_MFMA + 1), _lib.XC_ERR_VARIANT),
     (dict(rows=8, algo=_lib.XC_XCORR_BLOCKDIAG), _lib.XC_ERR_SHAPE),
+    # the fp32 matrix cores: cols a multiple of 4, staging within the plan
+    (dict(cols=30, algo=_lib.XC_XCORR_MFMA), _lib.XC_ERR_SHAPE),
+    (dict(cols=1000, algo=_lib.XC_XCORR_MFMA), _lib.XC_ERR_SHAPE),
 ])
 def test_xcorr_validation(args, expect):
     a = dict(left=FAKE, n_left=1, right=FAKE, n_right=1, rows=32, cols=32, out=FAKE, algo=0)
