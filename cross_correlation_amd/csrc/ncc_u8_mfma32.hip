@@ -9,8 +9,8 @@
 // SumIT = sum I'T' + 128 SumI + 128 SumT - 16384 N exactly, mod 2^32), but
 // with the roles of the operands turned round:
 //
-//   * Product: for one workgroup tile of 32 output rows m and 256 output
-//     columns (eight 32-column tiles j), and each template row rt,
+//   * Product: for one workgroup tile of 32 output rows m and 128 output
+//     columns (four 32-column tiles j), and each template row rt,
 //       D_j[m][n] += sum_k A_{j+kb}[m][k] * B_kb[k][n]
 //         A_a[m][k]  = I'[y0 + m + rt][x0 + 32a + k]   (image bytes as staged:
 //                                                     aligned 16-byte reads)
@@ -21,17 +21,19 @@
 //     window sum of output (y0 + m, x0 + 32j + n) over template row rt.  No
 //     operand needs a byte shift per output column: the shift is in B, built
 //     once per template row (four v_alignbyte_b32 per fragment) and used by
-//     all eight column tiles.  A fraction 1 - t_width / (32 NKB) of the
+//     all four column tiles.  A fraction 1 - t_width / (32 NKB) of the
 //     products is against the zero bytes around the template row.
 //   * Template rows are split over the four matrix-core waves; their partial
 //     sums are added in LDS (exact integer adds, so the order does not matter).
-//   * SumI, SumISq: four helper waves (pixels or squares, times the upper or
-//     lower 16 output rows) run beside the products.  Each keeps exact
-//     column sums over the template's rows for 4 image columns per lane and
-//     slides them down its rows, writing each row's column sums to LDS in
-//     batches of 4 rows; lanes then take 16 consecutive outputs of one of
-//     those rows each and slide the window along the row (one add and one
-//     subtract per output), writing SumI or SumISq to LDS.
+//   * SumI, SumISq: two helper waves (pixels, squares) run beside the
+//     products.  Each keeps exact column sums over the template's rows for 4
+//     image columns per lane (every image word of the tile's windows, one
+//     per lane) and slides them down the 32 output rows; for each row it
+//     takes the prefix along the row (in the lane, then a DPP scan across
+//     lanes) and forms the window sums as differences of two prefix entries
+//     read across lanes, writing SumI or SumISq to LDS.
+//   * Two workgroups per CU (six waves each, at most 168 VGPRs), so each
+//     SIMD holds two matrix-core waves.
 //   * Epilogue: one output column per lane, so every store writes whole cache
 //     lines; the coefficient with the exact formula of the other kernels
 //     (ncc_coef_f32), so all kernels return the same bits.
@@ -47,16 +49,14 @@ typedef int m32_v4i __attribute__((ext_vector_type(4)));
 typedef int m32_v16i __attribute__((ext_vector_type(16)));
 
 constexpr int M32_TY = 32;     // output rows per workgroup (the MFMA's M)
-constexpr int M32_TX = 256;    // output columns per workgroup
-constexpr int M32_NT = 8;      // 32-column tiles per matrix-core wave
+constexpr int M32_TX = 128;    // output columns per workgroup
+constexpr int M32_NT = 4;      // 32-column tiles per matrix-core wave
 constexpr int M32_MW = 4;      // matrix-core waves (template rows split four ways)
-constexpr int M32_HW = 4;      // helper waves: (field, row half)
+constexpr int M32_HW = 2;      // helper waves: one per field
 constexpr int M32_THREADS = 64 * (M32_MW + M32_HW);
-constexpr int M32_ACCS = 264;  // i32 per row of the merged SumIT' (the two row groups of a
+constexpr int M32_ACCS = 136;  // i32 per row of the merged SumIT' (the two row groups of a
                                // write sit 32 banks apart)
-constexpr int M32_VB = 4;      // rows per batch of a helper wave's column sums
-constexpr int M32_RSV = 324;   // u32 per row of a helper batch (up to 80 words of 4 columns)
-constexpr int M32_SRS = 260;   // u32 per row of the window sums
+constexpr int M32_SRS = 132;   // u32 per row of the window sums
 
 // 32-byte blocks of K a template row of t_width bytes needs: the output
 // columns n = 0..31 of a tile read template bytes c = 32 kb + k - n, which
@@ -69,12 +69,11 @@ __host__ __device__ constexpr int m32_nkb(int tw) { return tw < 2 ? 2 : (tw + 62
 //         s bytes; after the walk the merged SumIT' (M32_TY x M32_ACCS i32)
 //   tpl   template rows (biased) with 32 zero bytes before and zeros after,
 //         t_height + 1 rows of ptw bytes
-//   vb    per helper wave, M32_VB rows of column sums
 //   sb    SumI and SumISq of the tile, M32_TY rows of M32_SRS each
 //   tsum  SumT, SumTSq
 struct M32Plan {
     int nkb, na, s, ptw, nwd;
-    size_t img, tpl, vb, sb, bytes;
+    size_t img, tpl, sb, bytes;
 };
 
 __host__ __device__ inline M32Plan m32_plan(int tw, int th)
@@ -84,13 +83,12 @@ __host__ __device__ inline M32Plan m32_plan(int tw, int th)
     p.na = M32_NT + p.nkb - 1;       // 32-byte image blocks a tile row reads
     p.s = 32 * p.na + 16;            // 8 NA + 4 words: 16 consecutive rows start in 16 bank groups
     p.ptw = 32 * p.nkb + 48;         // covers the five words read from byte 32 NKB + 16
-    p.nwd = (M32_TX + tw - 1 + 3) / 4;  // image words under the tile's windows
+    p.nwd = (M32_TX + tw - 1 + 3) / 4;  // image words under the tile's windows (at most 48)
     const size_t img = (size_t)(M32_TY + th) * p.s, sit = (size_t)M32_TY * M32_ACCS * 4;
     p.img = ((img > sit ? img : sit) + 15) & ~(size_t)15;
     p.tpl = (size_t)(th + 1) * p.ptw;
-    p.vb = (size_t)M32_HW * M32_VB * M32_RSV * 4;
     p.sb = (size_t)2 * M32_TY * M32_SRS * 4;
-    p.bytes = p.img + p.tpl + p.vb + p.sb + 16;
+    p.bytes = p.img + p.tpl + p.sb + 16;
     return p;
 }
 
@@ -284,111 +282,103 @@ __device__ __forceinline__ void m32_slide1(uint32_t in, uint32_t out, uint32_t (
     }
 }
 
-// A helper wave: field F over output rows [16h, 16h + 16) of the tile.
-// Lanes hold image words w = lane and lane + 64 (the second only while below
-// nwd; idle lanes read a valid word and store nothing).  Column sums of the
-// first output row's window, then for each batch of M32_VB rows: each row's
-// column sums (unbiased: SumI's adds 128 t_height back) to the wave's batch
-// rows, the slide to the next row, and the window sums of the batch along the
-// rows: lane (r, s) = (lane >> 4, lane & 15) takes outputs 16s .. 16s + 15 of
-// batch row r, the first as a sum over t_width column sums, each next one by
-// adding the column entering and removing the one leaving.
+// Inclusive prefix sum over the 64 lanes of a wave in DPP moves: shifts by
+// 1, 2, 4 and 8 lanes within each row of 16 (lanes shifted in from outside
+// the row read 0), then lane 15's total added to rows 1 and 3 and lane 31's
+// to rows 2 and 3.  Every lane of the wave must take part.
+__device__ __forceinline__ uint32_t m32_wave_scan(uint32_t v)
+{
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, true);   // row_shr:1
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, true);   // row_shr:2
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, true);   // row_shr:4
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, true);   // row_shr:8
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+    return v;
+}
+
+// A helper wave: field F (0: pixels, 1: squared pixels) over the tile's 32
+// output rows.  Lane l holds image word l (columns 4l .. 4l + 3 of the tile;
+// lanes past the last word repeat it, which changes no prefix below them).
+// The column sums of the first output row's window, then for each output
+// row: the prefix along the row at the lane's four columns (a running sum in
+// the lane plus an exclusive scan of the lane totals), the window sums of
+// outputs x = 4l + k as the prefix at x + t_width - 1 less the one at x - 1
+// (read from lanes l + d and l + d + 1, d = (t_width - 1) / 4, and l - 1),
+// stored by the lanes of the 128 outputs, and the slide to the next row.
+// All u32, exact (every window sum is below 2^32).
 template <int F>
-__device__ __forceinline__ void m32_helper(const uint8_t *img, int S, int th, int tw, int h, int nwd, uint32_t *vb,
-                                           uint32_t *sf)
+__device__ __forceinline__ void m32_helper(const uint8_t *img, int S, int th, int tw, int nwd, uint32_t *srow)
 {
     const int lane = threadIdx.x & 63;
-    const bool k1 = lane + 64 < nwd;
-    const int w0 = lane < nwd ? lane : nwd - 1, w1 = k1 ? lane + 64 : nwd - 1;
-    const uint8_t *base = img + (16 * h) * S;
-    uint32_t c0[4] = {0u, 0u, 0u, 0u}, c1[4] = {0u, 0u, 0u, 0u};
+    const int wd = lane < nwd ? lane : nwd - 1;
+    uint32_t c[4] = {0u, 0u, 0u, 0u};
     int r = 0;
 #pragma unroll 2
     for (; r + 4 <= th; r += 4) {
-        uint32_t u[4], v[4];
+        uint32_t u[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            u[q] = *reinterpret_cast<const uint32_t *>(base + (r + q) * S + 4 * w0);
-            v[q] = *reinterpret_cast<const uint32_t *>(base + (r + q) * S + 4 * w1);
-        }
-        m32_col4<F>(u, c0);
-        m32_col4<F>(v, c1);
+        for (int q = 0; q < 4; ++q)
+            u[q] = *reinterpret_cast<const uint32_t *>(img + (r + q) * S + 4 * wd);
+        m32_col4<F>(u, c);
     }
-    for (; r < th; ++r) {
-        m32_col1<F>(*reinterpret_cast<const uint32_t *>(base + r * S + 4 * w0), c0);
-        m32_col1<F>(*reinterpret_cast<const uint32_t *>(base + r * S + 4 * w1), c1);
-    }
+    for (; r < th; ++r)
+        m32_col1<F>(*reinterpret_cast<const uint32_t *>(img + r * S + 4 * wd), c);
     const uint32_t add = F == 0 ? 128u * (uint32_t)th : 0u;
-    const int hr = lane >> 4, hs = lane & 15;
-    for (int b = 0; b < 16 / M32_VB; ++b) {
-#pragma unroll
-        for (int rr = 0; rr < M32_VB; ++rr) {
-            const int ml = M32_VB * b + rr;  // output row within the half
-            uint32_t *row = vb + rr * M32_RSV;
-            if (lane < nwd)
-                *reinterpret_cast<uint4 *>(row + 4 * w0) = make_uint4(c0[0] + add, c0[1] + add, c0[2] + add, c0[3] + add);
-            if (k1)
-                *reinterpret_cast<uint4 *>(row + 4 * w1) = make_uint4(c1[0] + add, c1[1] + add, c1[2] + add, c1[3] + add);
-            if (ml < 15) {
-                const uint8_t *pin = base + (ml + th) * S, *pout = base + ml * S;
-                m32_slide1<F>(*reinterpret_cast<const uint32_t *>(pin + 4 * w0),
-                              *reinterpret_cast<const uint32_t *>(pout + 4 * w0), c0);
-                m32_slide1<F>(*reinterpret_cast<const uint32_t *>(pin + 4 * w1),
-                              *reinterpret_cast<const uint32_t *>(pout + 4 * w1), c1);
+    const int d = (tw - 1) >> 2, rr = (tw - 1) & 3;  // wave-uniform
+    const int la = min(lane + d, 63), lb = min(lane + d + 1, 63), lp = max(lane - 1, 0);
+    // the words leaving and entering the column sums for the next row, loaded
+    // one row ahead so the LDS latency overlaps this row's scan and shuffles
+    uint32_t w_in = *reinterpret_cast<const uint32_t *>(img + th * S + 4 * wd);
+    uint32_t w_out = *reinterpret_cast<const uint32_t *>(img + 4 * wd);
+    for (int m = 0; m < M32_TY; ++m) {
+        const uint32_t v0 = c[0] + add, v1 = c[1] + add, v2 = c[2] + add, v3 = c[3] + add;
+        if (m + 1 < M32_TY) {
+            m32_slide1<F>(w_in, w_out, c);
+            if (m + 2 < M32_TY) {
+                w_in = *reinterpret_cast<const uint32_t *>(img + (m + 1 + th) * S + 4 * wd);
+                w_out = *reinterpret_cast<const uint32_t *>(img + (m + 1) * S + 4 * wd);
             }
         }
-        // the batch rows are this wave's own writes: LDS requests of one wave
-        // complete in order, the wait keeps the compiler from moving reads up
-        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-        __builtin_amdgcn_wave_barrier();
-        {
-            // the first window of the lane as 16-byte reads (vr is 16-byte
-            // aligned), four at a time so their latencies overlap
-            const uint32_t *vr = vb + hr * M32_RSV + 16 * hs;
-            uint32_t acc = 0u;
-            int c = 0;
-            for (; c + 16 <= tw; c += 16) {
-                uint4 q[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    q[i] = *reinterpret_cast<const uint4 *>(vr + c + 4 * i);
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    acc += q[i].x + q[i].y + q[i].z + q[i].w;
-            }
-            for (; c + 4 <= tw; c += 4) {
-                const uint4 q = *reinterpret_cast<const uint4 *>(vr + c);
-                acc += q.x + q.y + q.z + q.w;
-            }
-            for (; c < tw; ++c)
-                acc += vr[c];
-            uint32_t *so = sf + (16 * h + M32_VB * b + hr) * M32_SRS + 16 * hs;
-            so[0] = acc;
-#pragma unroll
-            for (int j = 1; j < 16; ++j) {
-                acc += vr[j - 1 + tw] - vr[j - 1];
-                so[j] = acc;
-            }
+        const uint32_t p1 = v0 + v1, p2 = p1 + v2, t = p2 + v3;
+        const uint32_t before = m32_wave_scan(t) - t;
+        const uint32_t pre[4] = {before + v0, before + p1, before + p2, before + t};
+        const uint32_t a[4] = {(uint32_t)__shfl((int)pre[0], la, 64), (uint32_t)__shfl((int)pre[1], la, 64),
+                               (uint32_t)__shfl((int)pre[2], la, 64), (uint32_t)__shfl((int)pre[3], la, 64)};
+        const uint32_t b[3] = {(uint32_t)__shfl((int)pre[0], lb, 64), (uint32_t)__shfl((int)pre[1], lb, 64),
+                               (uint32_t)__shfl((int)pre[2], lb, 64)};
+        // every lane takes part in the permute (a masked-off source lane reads
+        // as zero), then lane 0 drops it
+        const uint32_t left = (uint32_t)__shfl((int)pre[3], lp, 64);
+        const uint32_t prev = lane > 0 ? left : 0u;
+        // hi[k] = prefix at column 4l + k + tw - 1: component k + rr of lane
+        // l + d, continuing into lane l + d + 1
+        uint4 hi;
+        switch (rr) {
+        case 0: hi = make_uint4(a[0], a[1], a[2], a[3]); break;
+        case 1: hi = make_uint4(a[1], a[2], a[3], b[0]); break;
+        case 2: hi = make_uint4(a[2], a[3], b[0], b[1]); break;
+        default: hi = make_uint4(a[3], b[0], b[1], b[2]); break;
         }
-        __builtin_amdgcn_s_waitcnt(0xc07f);
-        __builtin_amdgcn_wave_barrier();
+        if (lane < M32_TX / 4)
+            *reinterpret_cast<uint4 *>(srow + m * M32_SRS + 4 * lane) =
+                make_uint4(hi.x - prev, hi.y - pre[0], hi.z - pre[1], hi.w - pre[2]);
     }
 }
 
 // Workgroup roles (wave-uniform): waves 0..3 run the matrix cores over a
-// quarter of the template rows each, for all 256 columns of the tile; waves
-// 4..7 are the helpers (field = wave & 1, row half = (wave - 4) >> 1; wave 4
-// also sums the template).  Every wave stages, and every wave takes part in
-// the epilogue.
+// quarter of the template rows each, for all 128 columns of the tile; waves
+// 4 and 5 are the helpers (pixels, squares); wave 0 also sums the template after its walk.
+// Every wave stages, and every wave takes part in the epilogue.
 template <int NKB>
-__global__ __launch_bounds__(M32_THREADS) void ncc_u8_mfma32_kernel(NccArgs a)
+__global__ __launch_bounds__(M32_THREADS) __attribute__((amdgpu_waves_per_eu(3)))
+void ncc_u8_mfma32_kernel(NccArgs a)
 {
     extern __shared__ uint4 m32_smem[];
     const M32Plan P = m32_plan(a.t_width, a.t_height);
     uint8_t *const img = reinterpret_cast<uint8_t *>(m32_smem);
     uint8_t *const tpl = img + P.img;
-    uint32_t *const vb = reinterpret_cast<uint32_t *>(tpl + P.tpl);
-    uint32_t *const sb = vb + P.vb / 4;
+    uint32_t *const sb = reinterpret_cast<uint32_t *>(tpl + P.tpl);
     uint32_t *const tsum = sb + P.sb / 4;
     int32_t *const sit = reinterpret_cast<int32_t *>(img);
 
@@ -415,10 +405,7 @@ __global__ __launch_bounds__(M32_THREADS) void ncc_u8_mfma32_kernel(NccArgs a)
             m32_walk<NKB, true>(img, tpl, r0, r1, tv, acc);
         else
             m32_walk<NKB, false>(img, tpl, r0, r1, tv, acc);
-    } else {
-        const int hw = wave - M32_MW;
-        uint32_t *const vbw = vb + hw * M32_VB * M32_RSV;
-        if (hw == 0) {
+        if (wave == 0) {  // the helpers are still busy when the walks end
             uint32_t ts, tq;
             template_sums(a.tmpl, tw, th, ts, tq);
             if (lane == 0) {
@@ -426,10 +413,12 @@ __global__ __launch_bounds__(M32_THREADS) void ncc_u8_mfma32_kernel(NccArgs a)
                 tsum[1] = tq;
             }
         }
-        if ((hw & 1) == 0)
-            m32_helper<0>(img, P.s, th, tw, hw >> 1, P.nwd, vbw, sb);
+    } else {
+        const int hw = wave - M32_MW;
+        if (hw == 0)
+            m32_helper<0>(img, P.s, th, tw, P.nwd, sb);
         else
-            m32_helper<1>(img, P.s, th, tw, hw >> 1, P.nwd, vbw, sb + M32_TY * M32_SRS);
+            m32_helper<1>(img, P.s, th, tw, P.nwd, sb + M32_TY * M32_SRS);
     }
     __syncthreads();  // the image tile is free; SumI, SumISq and the template sums are in LDS
 
@@ -462,7 +451,7 @@ __global__ __launch_bounds__(M32_THREADS) void ncc_u8_mfma32_kernel(NccArgs a)
     const double vt = fma(nd, (double)sum_tsq, -(std_ * std_));
     const uint32_t *const s_i = sb, *const s_q = sb + M32_TY * M32_SRS;
 
-    // one output column per lane, rows advancing by 2 (512 threads)
+    // one output column per lane, rows advancing by 3 (384 threads)
     const int x = threadIdx.x & (M32_TX - 1), gx = x0 + x;
     const size_t o0 = (size_t)y0 * a.out_w + x0;
     uint32_t *const out_i = a.sum_i ? a.sum_i + o0 : nullptr;

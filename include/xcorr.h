@@ -144,13 +144,12 @@ int ncc_u8_run(const uint8_t *image, int width, int height, int pitch_bytes,
  *                        the operands turned round: the image rows as they
  *                        are staged (no byte shifts) against the template
  *                        row shifted by each output column (the Toeplitz
- *                        operand), 32 x 256 outputs per workgroup, template
+ *                        operand), 32 x 128 outputs per workgroup, template
  *                        rows split over four waves; SumI and SumISq as
- *                        sliding sums in four waves beside them.  An
- *                        ablation point (slower than XC_NCC_MFMA on the
- *                        shapes measured).  t_width <= 65 and templates
- *                        short enough for the tile's LDS plan (136 rows at
- *                        width 64), else XC_ERR_SHAPE.
+ *                        sliding column sums and row prefixes in two waves
+ *                        beside them.  t_width <= 65 and templates short
+ *                        enough for the tile's LDS plan (350 rows at width
+ *                        64), else XC_ERR_SHAPE.
  */
 #define XC_NCC_AUTO 0
 #define XC_NCC_DOT4_ILP 1

@@ -26,15 +26,15 @@ MFMA_MAX_T_WIDTH = {_lib.XC_NCC_MFMA: 256, _lib.XC_NCC_MFMA_W4: 256, _lib.XC_NCC
 
 def mfma32_fits(th: int, tw: int) -> bool:
     """Whether XC_NCC_MFMA32 takes a th x tw template: t_width <= 65 and its
-    tile plan (staged image rows, padded template rows, helper batches, window
-    sums) within 160 KiB of LDS, as the library computes it."""
+    tile plan (staged image rows, padded template rows, window sums) within
+    160 KiB of LDS, as the library computes it."""
     if tw > 65:
         return False
     nkb = 2 if tw < 2 else (tw + 62) // 32
-    s = 32 * (8 + nkb - 1) + 16
-    img = -(-max((32 + th) * s, 32 * 264 * 4) // 16) * 16
+    s = 32 * (4 + nkb - 1) + 16
+    img = -(-max((32 + th) * s, 32 * 136 * 4) // 16) * 16
     tpl = (th + 1) * (32 * nkb + 48)
-    return img + tpl + 4 * 4 * 324 * 4 + 2 * 32 * 260 * 4 + 16 <= 160 * 1024
+    return img + tpl + 2 * 32 * 132 * 4 + 16 <= 160 * 1024
 
 
 def ncc_takes(variant: int, th: int, tw: int) -> bool:

@@ -63,7 +63,7 @@ FAKE = 1 << 20  # a 16-byte aligned non-null address; never dereferenced (valida
     (dict(t_width=300, width=400, pitch=400, variant=_lib.XC_NCC_MFMA_W4), _lib.XC_ERR_SHAPE),
     # the 32x32x32 recast: rows up to 65 bytes, templates short enough for its LDS plan
     (dict(t_width=66, width=200, pitch=208, variant=_lib.XC_NCC_MFMA32), _lib.XC_ERR_SHAPE),
-    (dict(t_width=64, t_height=137, width=200, height=200, pitch=208, variant=_lib.XC_NCC_MFMA32),
+    (dict(t_width=64, t_height=351, width=200, height=400, pitch=208, variant=_lib.XC_NCC_MFMA32),
      _lib.XC_ERR_SHAPE),
     (dict(variant=-1), _lib.XC_ERR_VARIANT),
 ])

@@ -1,6 +1,6 @@
 """GPU parity of the 32x32x32 matrix-core NCC variant (XC_NCC_MFMA32): the
 template as the Toeplitz operand, template rows split over four waves, SumI
-and SumISq from sliding column and row sums in helper waves.
+and SumISq from sliding column sums and row prefixes in two helper waves.
 
 Sums bit-exact and the coefficient within 1e-5 of the oracle; at full 1080p
 size every output bit-identical to the packed-byte kernel's.  Shapes cover
@@ -51,7 +51,8 @@ def test_mfma32_256_t16_cut():
     (16, 16, 16, 16, 0),      # template = image: one output
     (1, 64, 1, 64, 0),        # one pixel row
     (65, 1000, 3, 40, 0),     # 63 output rows: two row tiles, the second one short
-    (200, 300, 136, 64, 0),   # tallest 64-wide template within the LDS plan
+    (380, 300, 350, 64, 0),   # tallest 64-wide template within the LDS plan (one workgroup per CU)
+    (150, 400, 113, 64, 16),  # the first 64-wide height past two workgroups per CU
 ])
 def test_mfma32_shapes(shape):
     h, w, th, tw, extra = shape
@@ -67,7 +68,7 @@ def test_mfma32_shapes(shape):
 def test_mfma32_cut_every_byte_phase(ox_mod):
     rng = np.random.default_rng(700 + ox_mod)
     img = u8_uniform(rng, (80, 520))
-    oy, ox = 33, 250 + ox_mod  # the window straddles the two 256-column tiles' boundary
+    oy, ox = 33, 250 + ox_mod  # the window straddles the second and third 128-column tiles' boundary
     tmpl = img[oy:oy + 24, ox:ox + 40]
     case = _case(img, tmpl)
     _gpu.log(f"mfma32 cut template ox%4={ox_mod}")
@@ -145,7 +146,7 @@ def test_mfma32_peak():
     assert best[:2] == tuple(case.cut) and best[2] == 1.0
 
 
-@pytest.mark.parametrize("th,tw", [(5, 66), (137, 64), (300, 20)])
+@pytest.mark.parametrize("th,tw", [(5, 66), (351, 64), (432, 20)])
 def test_mfma32_refuses_unsupported_shapes(th, tw):
     rng = np.random.default_rng(712)
     case = _case(u8_uniform(rng, (max(th, 8) + 4, 400)), u8_uniform(rng, (th, tw)))
