@@ -657,10 +657,13 @@ def main():
 
         out["cpu_baseline"] = cpu_baseline(args, inputs, oracle)
     line = json.dumps(out)
+    print(line, flush=True)
     if args.json_out:
+        # the folder may not exist yet (a profiler creates its output folder
+        # only when the program ends)
+        os.makedirs(os.path.dirname(os.path.abspath(args.json_out)), exist_ok=True)
         with open(args.json_out, "w") as f:
             f.write(line + "\n")
-    print(line, flush=True)
 
 
 if __name__ == "__main__":
