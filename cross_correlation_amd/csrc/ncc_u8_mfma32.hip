@@ -25,10 +25,11 @@
 //     products is against the zero bytes around the template row.
 //   * Template rows are split over the four matrix-core waves; their partial
 //     sums are added in LDS (exact integer adds, so the order does not matter).
-//   * SumI, SumISq: two helper waves (pixels, squares) run beside the
-//     products.  Each keeps exact column sums over the template's rows for 4
-//     image columns per lane (every image word of the tile's windows, one
-//     per lane) and slides them down the 32 output rows; for each row it
+//   * SumI, SumISq: four helper waves (pixels or squares, for the first or
+//     second 16 output rows) run beside the products.  Each keeps exact
+//     column sums over the template's rows for 4 image columns per lane
+//     (every image word of the tile's windows, one per lane) and slides them
+//     down its 16 output rows; for each row it
 //     takes the prefix along the row (in the lane, then a DPP scan across
 //     lanes) and forms the window sums as differences of two prefix entries
 //     read across lanes, writing SumI or SumISq to LDS.
@@ -52,7 +53,8 @@ constexpr int M32_TY = 32;     // output rows per workgroup (the MFMA's M)
 constexpr int M32_TX = 128;    // output columns per workgroup
 constexpr int M32_NT = 4;      // 32-column tiles per matrix-core wave
 constexpr int M32_MW = 4;      // matrix-core waves (template rows split four ways)
-constexpr int M32_HW = 2;      // helper waves: one per field
+constexpr int M32_HW = 4;      // helper waves: field x half of the tile's rows
+constexpr int M32_HROWS = M32_TY / 2;  // output rows per helper wave
 constexpr int M32_THREADS = 64 * (M32_MW + M32_HW);
 constexpr int M32_ACCS = 136;  // i32 per row of the merged SumIT' (the two row groups of a
                                // write sit 32 banks apart)
@@ -308,7 +310,7 @@ __device__ __forceinline__ uint32_t m32_wave_scan(uint32_t v)
 // stored by the lanes of the 128 outputs, and the slide to the next row.
 // All u32, exact (every window sum is below 2^32).
 template <int F>
-__device__ __forceinline__ void m32_helper(const uint8_t *img, int S, int th, int tw, int nwd, uint32_t *srow)
+__device__ __forceinline__ void m32_helper(const uint8_t *img, int S, int th, int tw, int nwd, int row0, uint32_t *srow)
 {
     const int lane = threadIdx.x & 63;
     const int wd = lane < nwd ? lane : nwd - 1;
@@ -319,23 +321,24 @@ __device__ __forceinline__ void m32_helper(const uint8_t *img, int S, int th, in
         uint32_t u[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-            u[q] = *reinterpret_cast<const uint32_t *>(img + (r + q) * S + 4 * wd);
+            u[q] = *reinterpret_cast<const uint32_t *>(img + (row0 + r + q) * S + 4 * wd);
         m32_col4<F>(u, c);
     }
     for (; r < th; ++r)
-        m32_col1<F>(*reinterpret_cast<const uint32_t *>(img + r * S + 4 * wd), c);
+        m32_col1<F>(*reinterpret_cast<const uint32_t *>(img + (row0 + r) * S + 4 * wd), c);
     const uint32_t add = F == 0 ? 128u * (uint32_t)th : 0u;
     const int d = (tw - 1) >> 2, rr = (tw - 1) & 3;  // wave-uniform
     const int la = min(lane + d, 63), lb = min(lane + d + 1, 63), lp = max(lane - 1, 0);
     // the words leaving and entering the column sums for the next row, loaded
     // one row ahead so the LDS latency overlaps this row's scan and shuffles
-    uint32_t w_in = *reinterpret_cast<const uint32_t *>(img + th * S + 4 * wd);
-    uint32_t w_out = *reinterpret_cast<const uint32_t *>(img + 4 * wd);
-    for (int m = 0; m < M32_TY; ++m) {
+    uint32_t w_in = *reinterpret_cast<const uint32_t *>(img + (row0 + th) * S + 4 * wd);
+    uint32_t w_out = *reinterpret_cast<const uint32_t *>(img + row0 * S + 4 * wd);
+    const int row1 = row0 + M32_HROWS;
+    for (int m = row0; m < row1; ++m) {
         const uint32_t v0 = c[0] + add, v1 = c[1] + add, v2 = c[2] + add, v3 = c[3] + add;
-        if (m + 1 < M32_TY) {
+        if (m + 1 < row1) {
             m32_slide1<F>(w_in, w_out, c);
-            if (m + 2 < M32_TY) {
+            if (m + 2 < row1) {
                 w_in = *reinterpret_cast<const uint32_t *>(img + (m + 1 + th) * S + 4 * wd);
                 w_out = *reinterpret_cast<const uint32_t *>(img + (m + 1) * S + 4 * wd);
             }
@@ -368,7 +371,8 @@ __device__ __forceinline__ void m32_helper(const uint8_t *img, int S, int th, in
 
 // Workgroup roles (wave-uniform): waves 0..3 run the matrix cores over a
 // quarter of the template rows each, for all 128 columns of the tile; waves
-// 4 and 5 are the helpers (pixels, squares); wave 0 also sums the template after its walk.
+// 4..7 are the helpers (pixels for rows 0..15, squares for rows 0..15, then
+// the same for rows 16..31); wave 0 also sums the template after its walk.
 // Every wave stages, and every wave takes part in the epilogue.
 template <int NKB>
 __global__ __launch_bounds__(M32_THREADS) __attribute__((amdgpu_waves_per_eu(3)))
@@ -414,11 +418,11 @@ void ncc_u8_mfma32_kernel(NccArgs a)
             }
         }
     } else {
-        const int hw = wave - M32_MW;
-        if (hw == 0)
-            m32_helper<0>(img, P.s, th, tw, P.nwd, sb);
+        const int hw = wave - M32_MW, row0 = (hw >> 1) * M32_HROWS;
+        if ((hw & 1) == 0)
+            m32_helper<0>(img, P.s, th, tw, P.nwd, row0, sb);
         else
-            m32_helper<1>(img, P.s, th, tw, P.nwd, sb + M32_TY * M32_SRS);
+            m32_helper<1>(img, P.s, th, tw, P.nwd, row0, sb + M32_TY * M32_SRS);
     }
     __syncthreads();  // the image tile is free; SumI, SumISq and the template sums are in LDS
 

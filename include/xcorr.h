@@ -146,7 +146,7 @@ int ncc_u8_run(const uint8_t *image, int width, int height, int pitch_bytes,
  *                        row shifted by each output column (the Toeplitz
  *                        operand), 32 x 128 outputs per workgroup, template
  *                        rows split over four waves; SumI and SumISq as
- *                        sliding column sums and row prefixes in two waves
+ *                        sliding column sums and row prefixes in four waves
  *                        beside them.  t_width <= 65 and templates short
  *                        enough for the tile's LDS plan (350 rows at width
  *                        64), else XC_ERR_SHAPE.

@@ -1,6 +1,7 @@
 """GPU parity of the 32x32x32 matrix-core NCC variant (XC_NCC_MFMA32): the
 template as the Toeplitz operand, template rows split over four waves, SumI
-and SumISq from sliding column sums and row prefixes in two helper waves.
+and SumISq from sliding column sums and row prefixes in four helper waves
+(field x half of the tile's rows).
 
 Sums bit-exact and the coefficient within 1e-5 of the oracle; at full 1080p
 size every output bit-identical to the packed-byte kernel's.  Shapes cover
